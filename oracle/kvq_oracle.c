@@ -1,0 +1,334 @@
+/*
+ * kvq_oracle.c -- CPU oracle for the int4 group-wise KV cache and the
+ * decode-phase attention that reads it.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this code: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source, header, table or helper with
+ * the HIP library; the only thing both sides receive is the same input
+ * bytes.
+ *
+ * Plain, scalar, slow on purpose.  Every step follows the text it cites:
+ *
+ *  [FG-blog]   "FlexGen: High-Throughput Generative Inference of Large
+ *              Language Models with a Single GPU [ICML'23]" (qingweiji blog),
+ *              sections "P/D阶段计算 / 解码阶段" (decode-phase KV update and
+ *              attention) and "KV Cache" (the [b, s, a, h/a] cache shape).
+ *  [FG-report] "FlexGen研究学术报告" (fmread), section 三.2(C) "近似方法的应用":
+ *              group-wise asymmetric 4-bit quantisation, 64 contiguous
+ *              elements per group, tensors dequantised to FP16 before
+ *              compute; and top-10% sparse attention (load only the KV
+ *              entries with the highest attention values).
+ *  [Survey]    notes on "A Survey on Efficient Inference for Large Language
+ *              Models" (gumorming), eq. (2): Softmax(Q K^T / sqrt(d_k)) V
+ *              with d_k the query/key dimension.
+ *
+ * Precision.  The codec decides integers (the 4-bit codes), so it runs in
+ * binary32 with one rounding per operation (built with -ffp-contract=off,
+ * no fast-math), in the order listed at oracle_quantize_group.  Dequantised
+ * values are rounded to binary16, as the report states.  Attention over the
+ * dequantised values runs in binary64 (the pages fix no precision for it).
+ *
+ * Readings taken where the pages are silent (each one is listed in the
+ * design notes with its reason):
+ *   - the group runs along head_dim (64 contiguous head_dim elements);
+ *   - asymmetric = min/max affine code: scale = (max-min)/15, 16 levels
+ *     min + c*scale, code = round_half_even((x-min)*(15/(max-min))),
+ *     clamped to 0..15;
+ *   - a constant group (max == min) stores scale 0 and codes 0;
+ *   - a stored min/max of -0 is canonicalised to +0;
+ *   - two codes per byte, the even element in the low nibble;
+ *   - attention scale 1/sqrt(d), d = head_dim = h/a (the survey's d_k);
+ *   - top-k ranks tokens by score (softmax is monotone), larger score
+ *     first, ties to the smaller token index; the softmax is renormalised
+ *     over the kept tokens.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_GROUP 64
+
+/* ------------------------------------------------------------------------
+ * IEEE 754 binary16 <-> binary32, from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0 holds
+ * the subnormals (fraction * 2^-24), exponent 31 holds inf/NaN.
+ * --------------------------------------------------------------------- */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int frac = h & 1023;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)frac, -24);
+    else if (e == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + frac), e - 25);
+    return sign ? -v : v;
+}
+
+/* Round a binary32 value to the nearest binary16 value, ties to even. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    if (isnan(f))
+        return 0x7e00u;
+    double a = fabs((double)f);
+    if (a == 0.0)
+        return sign;
+    /* Quantum (spacing of binary16 values) in the binade of a. */
+    int e;
+    frexp(a, &e); /* a = m * 2^e, m in [0.5, 1): binade [2^(e-1), 2^e) */
+    int unbiased = e - 1;
+    double quantum = (unbiased < -14) ? ldexp(1.0, -24) : ldexp(1.0, unbiased - 10);
+    double r = nearbyint(a / quantum) * quantum; /* exact scaling; ties to even */
+    if (r > 65504.0)
+        return (uint16_t)(sign | 0x7c00u); /* rounds beyond the largest finite: inf */
+    if (r < ldexp(1.0, -14)) {
+        /* subnormal (or zero): fraction counts units of 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    }
+    int er;
+    double m = frexp(r, &er); /* r = m * 2^er, m in [0.5, 1) */
+    uint16_t exp_field = (uint16_t)(er - 1 + 15);
+    uint16_t frac = (uint16_t)((2.0 * m - 1.0) * 1024.0);
+    return (uint16_t)(sign | (exp_field << 10) | frac);
+}
+
+/* ------------------------------------------------------------------------
+ * Codec: one group of 64 consecutive head_dim elements ([FG-report] 三.2(C)).
+ * --------------------------------------------------------------------- */
+
+/* Quantise 64 fp16 values.  Writes 32 code bytes, the group min and scale.
+ * Steps, each a single binary32 rounding:
+ *   widen to binary32 (exact);
+ *   mn = min, mx = max (exact), then -0 -> +0 by adding +0;
+ *   rng = mx - mn;
+ *   rng == 0: scale = 0, every code 0;
+ *   else scale = rng / 15, inv = 15 / rng (correctly rounded divisions),
+ *        code = clamp(rint_half_even((x - mn) * inv), 0, 15);
+ *   byte j = code[2j] | code[2j+1] << 4.                                   */
+void oracle_quantize_group(const uint16_t *x, uint8_t *codes, float *out_min, float *out_scale)
+{
+    float f[ORACLE_GROUP];
+    int c[ORACLE_GROUP];
+    for (int i = 0; i < ORACLE_GROUP; ++i)
+        f[i] = oracle_f16_to_f32(x[i]);
+    float mn = f[0], mx = f[0];
+    for (int i = 1; i < ORACLE_GROUP; ++i) {
+        if (f[i] < mn)
+            mn = f[i];
+        if (f[i] > mx)
+            mx = f[i];
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    float rng = mx - mn;
+    float scale;
+    if (rng == 0.0f) {
+        scale = 0.0f;
+        for (int i = 0; i < ORACLE_GROUP; ++i)
+            c[i] = 0;
+    } else {
+        scale = rng / 15.0f;
+        float inv = 15.0f / rng;
+        for (int i = 0; i < ORACLE_GROUP; ++i) {
+            float t = f[i] - mn;
+            t = t * inv;
+            float r = rintf(t); /* default rounding mode: nearest, ties to even */
+            if (r < 0.0f)
+                r = 0.0f;
+            if (r > 15.0f)
+                r = 15.0f;
+            c[i] = (int)r;
+        }
+    }
+    for (int j = 0; j < ORACLE_GROUP / 2; ++j)
+        codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+    *out_min = mn;
+    *out_scale = scale;
+}
+
+/* Quantise one token row of d fp16 values (d a multiple of 64): group g
+ * covers elements 64g..64g+63; codes[d/2], mins[d/64], scales[d/64].      */
+void oracle_quantize_row(int d, const uint16_t *x, uint8_t *codes, float *mins, float *scales)
+{
+    for (int g = 0; g < d / ORACLE_GROUP; ++g)
+        oracle_quantize_group(x + g * ORACLE_GROUP, codes + g * (ORACLE_GROUP / 2), mins + g, scales + g);
+}
+
+/* nrows independent rows, packed back to back (row r at x + r*d). */
+void oracle_quantize_rows(int nrows, int d, const uint16_t *x, uint8_t *codes, float *mins, float *scales)
+{
+    int G = d / ORACLE_GROUP;
+    for (int r = 0; r < nrows; ++r)
+        oracle_quantize_row(d, x + (size_t)r * d, codes + (size_t)r * (d / 2), mins + (size_t)r * G,
+                            scales + (size_t)r * G);
+}
+
+/* Code of element i of a row (low nibble = even element). */
+int oracle_code_at(const uint8_t *row_codes, int i)
+{
+    uint8_t byte = row_codes[i / 2];
+    return (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+}
+
+/* Dequantise element i of a row to fp16: v = code*scale, then v + min
+ * (two binary32 roundings), then round to binary16 ([FG-report] 三.2(C):
+ * dequantised to FP16 before compute).                                     */
+uint16_t oracle_dequant_elem(const uint8_t *row_codes, const float *row_mins, const float *row_scales, int i)
+{
+    int g = i / ORACLE_GROUP;
+    float v = (float)oracle_code_at(row_codes, i) * row_scales[g];
+    v = v + row_mins[g];
+    return oracle_f32_to_f16(v);
+}
+
+void oracle_dequant_rows(int nrows, int d, const uint8_t *codes, const float *mins, const float *scales,
+                         uint16_t *out)
+{
+    int G = d / ORACLE_GROUP;
+    for (int r = 0; r < nrows; ++r)
+        for (int i = 0; i < d; ++i)
+            out[(size_t)r * d + i] = oracle_dequant_elem(codes + (size_t)r * (d / 2), mins + (size_t)r * G,
+                                                         scales + (size_t)r * G, i);
+}
+
+/* ------------------------------------------------------------------------
+ * Decode attention for one (batch row, head) over a quantised cache
+ * ([FG-blog] 解码阶段: t_out = softmax(t_Q x_K^T / sqrt(.)) x_V, stopping
+ * before W_O; scale 1/sqrt(d) per [Survey] eq. (2)).
+ * Cache of one (batch row, head): codes [T][d/2], mins/scales [T][d/64].
+ * --------------------------------------------------------------------- */
+
+static double kdot(int d, const uint16_t *q, const uint8_t *kc, const float *kmin, const float *ksc, int t)
+{
+    int G = d / ORACLE_GROUP;
+    double acc = 0.0;
+    for (int i = 0; i < d; ++i) {
+        double qi = (double)oracle_f16_to_f32(q[i]);
+        double ki = (double)oracle_f16_to_f32(
+            oracle_dequant_elem(kc + (size_t)t * (d / 2), kmin + (size_t)t * G, ksc + (size_t)t * G, i));
+        acc += qi * ki;
+    }
+    return acc;
+}
+
+/* Scores s_t = (q . k_t) / sqrt(d) for t = 0..T-1. */
+void oracle_scores(int d, int T, const uint16_t *q, const uint8_t *kc, const float *kmin, const float *ksc,
+                   double *scores)
+{
+    double c = 1.0 / sqrt((double)d);
+    for (int t = 0; t < T; ++t)
+        scores[t] = kdot(d, q, kc, kmin, ksc, t) * c;
+}
+
+/* Dense decode attention: out[i] = sum_t p_t v_t[i] / sum_t p_t,
+ * p_t = exp(s_t - max_s).                                                  */
+void oracle_attend(int d, int T, const uint16_t *q, const uint8_t *kc, const float *kmin, const float *ksc,
+                   const uint8_t *vc, const float *vmin, const float *vsc, double *out)
+{
+    int G = d / ORACLE_GROUP;
+    if (T < 1)
+        return;
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    oracle_scores(d, T, q, kc, kmin, ksc, s);
+    double m = s[0];
+    for (int t = 1; t < T; ++t)
+        if (s[t] > m)
+            m = s[t];
+    double l = 0.0;
+    for (int t = 0; t < T; ++t) {
+        s[t] = exp(s[t] - m);
+        l += s[t];
+    }
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int t = 0; t < T; ++t) {
+            double vi = (double)oracle_f16_to_f32(
+                oracle_dequant_elem(vc + (size_t)t * (d / 2), vmin + (size_t)t * G, vsc + (size_t)t * G, i));
+            acc += s[t] * vi;
+        }
+        out[i] = acc / l;
+    }
+    free(s);
+}
+
+/* Attention restricted to the token set idx[0..nidx-1]: the softmax is
+ * taken over those tokens' scores only.                                    */
+void oracle_attend_subset(int d, int nidx, const int32_t *idx, const uint16_t *q, const uint8_t *kc,
+                          const float *kmin, const float *ksc, const uint8_t *vc, const float *vmin,
+                          const float *vsc, double *out)
+{
+    int G = d / ORACLE_GROUP;
+    double c = 1.0 / sqrt((double)d);
+    if (nidx < 1)
+        return;
+    double *p = (double *)malloc(sizeof(double) * (size_t)nidx);
+    for (int j = 0; j < nidx; ++j)
+        p[j] = kdot(d, q, kc, kmin, ksc, idx[j]) * c;
+    double m = p[0];
+    for (int j = 1; j < nidx; ++j)
+        if (p[j] > m)
+            m = p[j];
+    double l = 0.0;
+    for (int j = 0; j < nidx; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < nidx; ++j) {
+            int t = idx[j];
+            double vi = (double)oracle_f16_to_f32(
+                oracle_dequant_elem(vc + (size_t)t * (d / 2), vmin + (size_t)t * G, vsc + (size_t)t * G, i));
+            acc += p[j] * vi;
+        }
+        out[i] = acc / l;
+    }
+    free(p);
+}
+
+/* Top-k selection: the k tokens with the largest scores, larger score
+ * first and ties to the smaller index; returned in ascending token order.
+ * Plain selection by repeated scans (k passes over T) -- slow and obvious.  */
+void oracle_select_topk(int T, const double *scores, int k, int32_t *sel)
+{
+    unsigned char *taken = (unsigned char *)calloc((size_t)T, 1);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int t = 0; t < T; ++t) {
+            if (taken[t])
+                continue;
+            if (best < 0 || scores[t] > scores[best])
+                best = t; /* strict '>' keeps the smaller index on ties */
+        }
+        taken[best] = 1;
+    }
+    int n = 0;
+    for (int t = 0; t < T; ++t)
+        if (taken[t])
+            sel[n++] = t;
+    free(taken);
+}
+
+/* Sparse decode attention ([FG-report] 三.2(C)): rank all T scores, keep the
+ * top k, softmax and P.V over the kept tokens only.  sel (may be NULL)
+ * receives the kept token indices in ascending order.                      */
+void oracle_attend_topk(int d, int T, int k, const uint16_t *q, const uint8_t *kc, const float *kmin,
+                        const float *ksc, const uint8_t *vc, const float *vmin, const float *vsc, double *out,
+                        int32_t *sel)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)T);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    oracle_scores(d, T, q, kc, kmin, ksc, s);
+    oracle_select_topk(T, s, k, idx);
+    oracle_attend_subset(d, k, idx, q, kc, kmin, ksc, vc, vmin, vsc, out);
+    if (sel)
+        memcpy(sel, idx, sizeof(int32_t) * (size_t)k);
+    free(idx);
+    free(s);
+}

@@ -1,0 +1,366 @@
+"""Pins of the CPU oracle against facts the pages and mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle currently in use
+(``oracle.lib()``) disagrees with something that does not come from the
+oracle itself: the IEEE binary16 conversions of numpy, exact rational
+arithmetic, hand-derived worked examples, closed forms of softmax, a
+library attention routine (torch's scaled_dot_product_attention in float64)
+and library sorts.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` runs them on copies of the oracle with a planted
+mistake and requires each copy to fail at least one pin.
+
+Passages pinned:
+* the codec -- "FlexGen研究学术报告", section 三.2(C) (group-wise asymmetric
+  4-bit, 64 contiguous elements, dequantised to FP16);
+* dense decode attention -- the FlexGen blog, section "解码阶段", with the
+  1/sqrt(d_k) scale of eq. (2) in the efficient-inference survey notes;
+* top-10% sparse attention -- the report's section 三.2(C).
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+def _expand(tokens):
+    out = []
+    for tok in tokens:
+        if "*" in tok:
+            v, n = tok.split("*")
+            out += [v] * int(n)
+        else:
+            out.append(tok)
+    return out
+
+
+def load_codec_examples():
+    """Parse tests/golden/codec_examples.txt into a list of dicts."""
+    ex, cur = [], None
+    with open(os.path.join(GOLDEN, "codec_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *rest = line.split()
+            if key == "example":
+                cur = {"name": rest[0]}
+                ex.append(cur)
+            elif key == "x":
+                cur["x"] = np.array([float(v) for v in _expand(rest)], np.float16)
+            elif key in ("min", "scale"):
+                cur[key] = float(rest[0])
+            elif key == "codes":
+                cur["codes"] = np.array([int(v) for v in _expand(rest)])
+            elif key == "bytes":
+                cur["bytes"] = np.array([int(v) for v in _expand(rest)], np.uint8)
+    return ex
+
+
+def unpack(codes_bytes: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] -> codes [..., 2n]: even element = low nibble."""
+    lo = codes_bytes & 15
+    hi = codes_bytes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*codes_bytes.shape[:-1], -1).astype(np.int64)
+
+
+def _groups(seed: int, n: int = 64) -> list[np.ndarray]:
+    """Varied fp16 groups: normal, uniform, outliers, tiny, huge, ties, duplicates."""
+    r = np.random.default_rng(seed)
+    gs = []
+    for _ in range(n):
+        kind = r.integers(0, 7)
+        if kind == 0:
+            x = r.standard_normal(64)
+        elif kind == 1:
+            x = r.uniform(-5, 5, 64)
+        elif kind == 2:
+            x = r.standard_normal(64)
+            x[r.integers(0, 64, 2)] *= 40.0
+        elif kind == 3:
+            x = r.standard_normal(64) * 1e-6          # fp16 subnormals
+        elif kind == 4:
+            x = r.uniform(-60000, 60000, 64)
+        elif kind == 5:
+            x = r.integers(-3, 4, 64).astype(float) * 0.25   # many duplicates
+        else:
+            x = np.full(64, r.standard_normal())
+            x[r.integers(0, 64)] += 1.0
+        gs.append(x.astype(np.float16))
+    return gs
+
+
+def _exact(x16) -> list[Fraction]:
+    return [Fraction(float(v)) for v in np.asarray(x16, np.float16)]
+
+
+# ------------------------------------------------------ binary16 conversions
+def pin_f16_to_f32_exhaustive():
+    """Every one of the 65536 binary16 bit patterns widens exactly as numpy's IEEE conversion."""
+    L = oracle.lib()
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([L.oracle_f16_to_f32(int(b)) for b in bits], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def pin_f32_to_f16_round_to_nearest_even():
+    """Narrowing agrees with numpy's IEEE RNE conversion on every binary16 value, every
+    midpoint between neighbours (exact ties), values one binary32 ulp off each midpoint,
+    the overflow edge and random binary32 values across the whole range."""
+    L = oracle.lib()
+    all16 = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = all16[np.isfinite(all16)].astype(np.float64)
+    fin = np.unique(fin)
+    mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)          # exact in binary32
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    edges = np.array([65504, 65519.996, 65520, 65536, 1e9, -65520, 2.0 ** -25, 2.0 ** -26,
+                      3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25], np.float32)
+    r = np.random.default_rng(7)
+    rnd = (r.standard_normal(20000) * np.exp(r.uniform(-20, 12, 20000))).astype(np.float32)
+    vals = np.concatenate([fin.astype(np.float32), mids, up, dn, edges, rnd])
+    vals = vals[r.permutation(vals.size)[:60000]] if vals.size > 60000 else vals
+    vals = np.concatenate([vals, edges, mids[::97], mids[-50:], mids[:50]])
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([L.oracle_f32_to_f16(float(v)) for v in vals], np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (vals[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+# --------------------------------------------------------------------- codec
+def pin_codec_worked_examples():
+    """Hand-derived examples in tests/golden/codec_examples.txt (ties to even, signed
+    zeros, constant groups, fp16 extremes, nibble order)."""
+    for ex in load_codec_examples():
+        codes, mn, sc = oracle.quantize_group(ex["x"])
+        got = unpack(codes[None])[0]
+        assert np.array_equal(got, ex["codes"]), (ex["name"], got, ex["codes"])
+        assert np.float32(mn).tobytes() == np.float32(ex["min"]).tobytes(), (ex["name"], mn)
+        if "scale" in ex:
+            assert np.float32(sc).tobytes() == np.float32(ex["scale"]).tobytes(), (ex["name"], sc)
+        else:
+            xs = ex["x"].astype(np.float64)
+            exact = Fraction(float(xs.max())) - Fraction(float(xs.min()))
+            assert abs(Fraction(float(sc)) - exact / 15) <= exact / 15 * Fraction(1, 2 ** 22)
+        if "bytes" in ex:
+            assert np.array_equal(codes, ex["bytes"]), (ex["name"], codes)
+
+
+def pin_codec_nearest_level_bruteforce():
+    """Each code is the nearest of the 16 levels min + c*scale (exact rational distances);
+    only values within 1e-5 of a level midpoint may take either neighbour."""
+    for x in _groups(11, 80):
+        codes, mn, sc = oracle.quantize_group(x)
+        c = unpack(codes[None])[0]
+        xs = _exact(x)
+        lo, hi = min(xs), max(xs)
+        if hi == lo:
+            assert sc == 0 and not c.any()
+            continue
+        for xi, ci in zip(xs, c):
+            r = (xi - lo) * 15 / (hi - lo)              # exact position on the code axis
+            dist = [abs(r - k) for k in range(16)]
+            best = min(dist)
+            assert dist[ci] <= best + Fraction(1, 100000), (float(r), ci)
+            if abs(r - math.floor(r) - Fraction(1, 2)) > Fraction(1, 100000):
+                assert dist[ci] == best, (float(r), ci)
+
+
+def pin_codec_extremes_and_scale():
+    """Stored min is the exact group minimum; the minimum maps to code 0 and the maximum
+    to code 15; scale is (max - min)/15 within two binary32 roundings."""
+    for x in _groups(12, 80):
+        codes, mn, sc = oracle.quantize_group(x)
+        c = unpack(codes[None])[0]
+        xs = _exact(x)
+        lo, hi = min(xs), max(xs)
+        assert Fraction(float(mn)) == lo
+        if lo == 0:
+            assert np.float32(mn).tobytes() == np.float32(0.0).tobytes()   # +0, never -0
+        if hi == lo:
+            continue
+        assert c[int(np.argmin(x))] == 0 and c[int(np.argmax(x))] == 15
+        exact = (hi - lo) / 15
+        assert abs(Fraction(float(sc)) - exact) <= abs(exact) * Fraction(1, 2 ** 22)
+
+
+def pin_codec_error_bound():
+    """Dequantised error per element: |x - (min + c*scale)| <= scale/2 (+ rounding slack),
+    and after the fp16 rounding of the dequantised value, + half an fp16 ulp."""
+    for x in _groups(13, 80):
+        codes, mn, sc = oracle.quantize_group(x)
+        xhat = oracle.dequant_rows(codes[None], np.array([[mn]], np.float32),
+                                   np.array([[sc]], np.float32))[0].astype(np.float64)
+        xs = x.astype(np.float64)
+        c = unpack(codes[None])[0]
+        big = max(abs(xs.max()), abs(xs.min()))
+        lvl = float(mn) + c * float(sc)
+        assert np.all(np.abs(xs - lvl) <= float(sc) / 2 * (1 + 1e-5) + big * 2.0 ** -22)
+        ulp16 = np.array([np.spacing(np.float16(v)) for v in xhat], np.float64)
+        assert np.all(np.abs(xs - xhat) <= float(sc) / 2 * (1 + 1e-5) + big * 2.0 ** -22 + ulp16 / 2)
+
+
+def pin_codec_constant_group_roundtrip():
+    """A constant group stores scale 0 and codes 0 and dequantises to itself exactly."""
+    r = np.random.default_rng(14)
+    for v in list(r.standard_normal(20)) + [0.0, -0.0, 65504.0, -65504.0, 6e-8, -3.5]:
+        x = np.full(64, v, np.float16)
+        codes, mn, sc = oracle.quantize_group(x)
+        assert sc == 0 and not codes.any()
+        xhat = oracle.dequant_rows(codes[None], np.array([[mn]], np.float32), np.array([[sc]], np.float32))[0]
+        assert np.array_equal(xhat.astype(np.float32), x.astype(np.float32))
+
+
+def pin_codec_rows_are_groupwise():
+    """A row of d = 64*G values is G independent groups of 64 contiguous head_dim elements
+    (group axis = head_dim), laid out group after group."""
+    r = np.random.default_rng(15)
+    x = (r.standard_normal((3, 5, 256)) * r.uniform(0.1, 10, (3, 5, 1))).astype(np.float16)
+    codes, mins, scales = oracle.quantize_rows(x)
+    assert codes.shape == (3, 5, 128) and mins.shape == (3, 5, 4)
+    for i in range(3):
+        for j in range(5):
+            for g in range(4):
+                c1, m1, s1 = oracle.quantize_group(x[i, j, 64 * g:64 * g + 64])
+                assert np.array_equal(codes[i, j, 32 * g:32 * g + 32], c1)
+                assert mins[i, j, g] == m1 and scales[i, j, g] == s1
+
+
+# ----------------------------------------------------------------- attention
+def _rand_head(seed: int, T: int, d: int, std=1.0, kfix=None):
+    r = np.random.default_rng(seed)
+    K = (r.standard_normal((T, d)) * std).astype(np.float16)
+    if kfix is not None:
+        K = kfix(K)
+    V = (r.standard_normal((T, d)) * std).astype(np.float16)
+    q = (r.standard_normal(d) * std).astype(np.float16)
+    kc, kmin, ksc = oracle.quantize_rows(K)
+    vc, vmin, vsc = oracle.quantize_rows(V)
+    hc = oracle.HeadCache(kc, kmin, ksc, vc, vmin, vsc)
+    Kh = oracle.dequant_rows(kc, kmin, ksc).astype(np.float64)
+    Vh = oracle.dequant_rows(vc, vmin, vsc).astype(np.float64)
+    return q, K, V, hc, Kh, Vh
+
+
+def _sdpa(q, Kh, Vh, mask=None):
+    """torch's attention routine in float64 on the CPU (default scale 1/sqrt(d))."""
+    qt = torch.from_numpy(np.asarray(q, np.float64).reshape(1, 1, 1, -1))
+    kt = torch.from_numpy(np.ascontiguousarray(Kh)).reshape(1, 1, *Kh.shape)
+    vt = torch.from_numpy(np.ascontiguousarray(Vh)).reshape(1, 1, *Vh.shape)
+    am = None
+    if mask is not None:
+        am = torch.from_numpy(mask).reshape(1, 1, 1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=am).reshape(-1).numpy()
+
+
+def pin_attention_matches_library_sdpa():
+    """Dense attention equals torch's float64 scaled_dot_product_attention on the
+    dequantised K and V (pins the 1/sqrt(d) scale, the softmax and P.V)."""
+    for seed, T, d, std in [(21, 1, 64, 1.0), (22, 7, 64, 1.0), (23, 33, 128, 0.5), (24, 130, 128, 3.0),
+                            (25, 20, 256, 1.0), (26, 64, 64, 8.0)]:
+        q, K, V, hc, Kh, Vh = _rand_head(seed, T, d, std)
+        ref = _sdpa(q.astype(np.float64), Kh, Vh)
+        got = oracle.attend(q, hc)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), np.abs(got - ref).max()
+        for Tp in (1, max(1, T // 2)):
+            ref = _sdpa(q.astype(np.float64), Kh[:Tp], Vh[:Tp])
+            assert np.allclose(oracle.attend(q, hc, Tp), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_scores_match_library_matmul():
+    """Scores are q . k_t / sqrt(d) over the dequantised keys (library matmul in float64)."""
+    q, K, V, hc, Kh, Vh = _rand_head(31, 50, 128, 1.0)
+    ref = (Kh @ q.astype(np.float64)) / math.sqrt(128)
+    assert np.allclose(oracle.scores(q, hc), ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_attention_single_token():
+    """T = 1: softmax of one score is 1, so the output is the dequantised V row exactly."""
+    for seed, d in [(41, 64), (42, 128)]:
+        q, K, V, hc, Kh, Vh = _rand_head(seed, 5, d, 2.0)
+        assert np.array_equal(oracle.attend(q, hc, 1), Vh[0])
+
+
+def pin_attention_identical_keys_and_zero_query():
+    """Identical keys (or q = 0) give a uniform softmax: the output is the mean of the
+    dequantised V, and within the codec's error bound of the mean of V itself."""
+    for seed, T, d in [(51, 9, 64), (52, 100, 128)]:
+        q, K, V, hc, Kh, Vh = _rand_head(seed, T, d, 1.0, kfix=lambda K: np.repeat(K[:1], K.shape[0], 0))
+        mean_hat = Vh.mean(axis=0)
+        got = oracle.attend(q, hc)
+        assert np.allclose(got, mean_hat, rtol=0, atol=1e-12)
+        vc_, vmin, vsc = hc.vc, hc.vmin, hc.vsc
+        bound = vsc.max() / 2 * (1 + 1e-5) + np.abs(V.astype(np.float64)).max() * 2.0 ** -22 + 2.0 ** -10 * \
+            np.abs(V.astype(np.float64)).max()
+        assert np.all(np.abs(got - V.astype(np.float64).mean(axis=0)) <= bound)
+        z = np.zeros(d, np.float16)
+        q2, K2, V2, hc2, Kh2, Vh2 = _rand_head(seed + 100, T, d, 1.0)
+        assert np.allclose(oracle.attend(z, hc2), Vh2.mean(axis=0), rtol=0, atol=1e-12)
+
+
+def pin_attention_two_token_closed_form():
+    """T = 2: out = (v0 + e^D v1) / (1 + e^D) with D = (s1 - s0), s_t = q.k_t/sqrt(d)."""
+    q, K, V, hc, Kh, Vh = _rand_head(61, 2, 128, 1.5)
+    s = Kh @ q.astype(np.float64) / math.sqrt(128)
+    D = s[1] - s[0]
+    ref = (Vh[0] + math.exp(D) * Vh[1]) / (1 + math.exp(D))
+    assert np.allclose(oracle.attend(q, hc), ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------- top-k
+def pin_topk_selection_matches_library_sort():
+    """Selection = first k of a stable library sort by (score descending, index ascending),
+    returned ascending; exercised with heavy ties."""
+    r = np.random.default_rng(71)
+    for T, k in [(10, 1), (10, 10), (50, 5), (300, 31), (2048, 205)]:
+        for tie in (False, True):
+            s = r.standard_normal(T)
+            if tie:
+                s = np.round(s * 2) / 2
+            order = np.lexsort((np.arange(T), -s))
+            ref = np.sort(order[:k])
+            assert np.array_equal(oracle.select_topk(s, k), ref)
+
+
+def pin_topk_full_equals_dense_and_top1_is_argmax():
+    """k = T reduces to dense attention; k = 1 returns the dequantised V row of the
+    highest-scoring key (smallest index on ties)."""
+    q, K, V, hc, Kh, Vh = _rand_head(81, 40, 128, 1.0)
+    out, sel = oracle.attend_topk(q, hc, 40)
+    assert np.array_equal(sel, np.arange(40))
+    assert np.allclose(out, oracle.attend(q, hc), rtol=1e-13, atol=1e-14)
+    s = Kh @ q.astype(np.float64)
+    out1, sel1 = oracle.attend_topk(q, hc, 1)
+    assert sel1[0] == int(np.argmax(s)) and np.array_equal(out1, Vh[sel1[0]])
+
+
+def pin_topk_matches_masked_library_sdpa():
+    """Top-k output equals torch's float64 attention with every unselected key masked
+    out (-inf), i.e. the softmax renormalised over the kept keys."""
+    boost = lambda K: K * np.where(np.random.default_rng(5).random((K.shape[0], 1)) < 0.05, 3, 1).astype(np.float16)
+    for seed, T, d in [(91, 200, 128), (92, 64, 64), (93, 2048, 128)]:
+        q, K, V, hc, Kh, Vh = _rand_head(seed, T, d, 1.0, kfix=boost)
+        k = math.ceil(0.1 * T)
+        out, sel = oracle.attend_topk(q, hc, k)
+        s = Kh @ q.astype(np.float64)
+        order = np.lexsort((np.arange(T), -s))
+        assert np.array_equal(sel, np.sort(order[:k]))
+        mask = np.full(T, -np.inf)
+        mask[sel] = 0.0
+        ref = _sdpa(q.astype(np.float64), Kh, Vh, mask)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+        assert np.allclose(oracle.attend_subset(q, hc, sel), ref, rtol=1e-12, atol=1e-12)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

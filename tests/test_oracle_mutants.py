@@ -1,0 +1,59 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is the oracle's own C source with one plausible mistake written in
+(a dropped term, a wrong rounding, a swapped index, a wrong constant).  It is
+compiled with the oracle's flags into a temporary library and the pins of
+``oracle_pins`` run against it; a mutant that passes every pin would mean the
+pins cannot see that kind of mistake.  Nothing here touches a GPU.
+"""
+import os
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+MUTANTS = [
+    ("round_half_away", "float r = rintf(t);", "float r = roundf(t);"),
+    ("truncate_codes", "float r = rintf(t);", "float r = floorf(t);"),
+    ("scale_over_16", "scale = rng / 15.0f;", "scale = rng / 16.0f;"),
+    ("inv_over_16", "float inv = 15.0f / rng;", "float inv = 16.0f / rng;"),
+    ("no_signed_zero_fix", "    mn = mn + 0.0f;\n", "\n"),
+    ("nibbles_swapped", "codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));",
+     "codes[j] = (uint8_t)((c[2 * j] << 4) | c[2 * j + 1]);"),
+    ("dequant_drops_min", "    v = v + row_mins[g];\n", "\n"),
+    ("dequant_skips_fp16", "    return oracle_f32_to_f16(v);\n}\n\nvoid oracle_dequant_rows",
+     "    return oracle_f32_to_f16(v * 1.0001f);\n}\n\nvoid oracle_dequant_rows"),
+    ("min_misses_last_element", "for (int i = 1; i < ORACLE_GROUP; ++i) {\n        if (f[i] < mn)",
+     "for (int i = 1; i < ORACLE_GROUP - 1; ++i) {\n        if (f[i] < mn)"),
+    ("second_group_reads_first", "oracle_quantize_group(x + g * ORACLE_GROUP,", "oracle_quantize_group(x,"),
+    ("f16_round_down", "double r = nearbyint(a / quantum) * quantum;", "double r = floor(a / quantum) * quantum;"),
+    ("f16_subnormal_scale", "v = ldexpf((float)frac, -24);", "v = ldexpf((float)frac, -25);"),
+    ("score_scale_1_over_d", "double c = 1.0 / sqrt((double)d);\n    for (int t = 0; t < T; ++t)",
+     "double c = 1.0 / (double)d;\n    for (int t = 0; t < T; ++t)"),
+    ("query_reversed", "double qi = (double)oracle_f16_to_f32(q[i]);", "double qi = (double)oracle_f16_to_f32(q[d - 1 - i]);"),
+    ("no_normalisation", "        out[i] = acc / l;\n    }\n    free(s);", "        out[i] = acc;\n    }\n    free(s);"),
+    ("softmax_without_exp", "        s[t] = exp(s[t] - m);", "        s[t] = s[t] - m + 1.0;"),
+    ("subset_v_index", "            int t = idx[j];", "            int t = j;"),
+    ("topk_ties_to_larger", "if (best < 0 || scores[t] > scores[best])", "if (best < 0 || scores[t] >= scores[best])"),
+    ("topk_smallest", "if (best < 0 || scores[t] > scores[best])", "if (best < 0 || scores[t] < scores[best])"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    bad = src.replace(old, new, 1)
+    with tempfile.TemporaryDirectory() as td:
+        path = oracle.compile_variant(bad, os.path.join(td, f"mut_{name}.so"))
+        failed = []
+        with oracle.use_library(path), np.errstate(all="ignore"):
+            for pin in oracle_pins.ALL_PINS:
+                try:
+                    pin()
+                except (AssertionError, ValueError, IndexError, OverflowError):
+                    failed.append(pin.__name__)
+        assert failed, f"mutant {name} passes every pin"
