@@ -10,7 +10,9 @@ and marshals numpy arrays into it.  What each function computes and which
 page passage it follows is stated in the C source:
 
 * codec -- "FlexGen研究学术报告", section 三.2(C): group-wise asymmetric
-  4-bit quantisation, 64 contiguous elements per group, dequantised to FP16;
+  4-bit quantisation, 64 contiguous elements per group; attention uses the
+  dequantised values min + code*scale exactly (the report's FP16 form is
+  available as ``dequant_rows_f16``);
 * dense attention -- the FlexGen blog's decode-phase equation (section
   "解码阶段") with the 1/sqrt(d_k) scale of the efficient-inference survey's
   eq. (2);
@@ -53,12 +55,14 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_quantize_group.argtypes = [P, P, P, P]
     L.oracle_quantize_rows.argtypes = [I, I, P, P, P, P]
     L.oracle_dequant_rows.argtypes = [I, I, P, P, P, P]
+    L.oracle_dequant_rows_f16.argtypes = [I, I, P, P, P, P]
     L.oracle_scores.argtypes = [I, I, P, P, P, P, P]
     L.oracle_attend.argtypes = [I, I, P, P, P, P, P, P, P, P]
     L.oracle_attend_subset.argtypes = [I, I, P, P, P, P, P, P, P, P, P]
     L.oracle_select_topk.argtypes = [I, P, I, P]
     L.oracle_attend_topk.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P]
-    for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_dequant_rows", "oracle_scores",
+    for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_dequant_rows", "oracle_dequant_rows_f16",
+              "oracle_scores",
               "oracle_attend", "oracle_attend_subset", "oracle_select_topk", "oracle_attend_topk"):
         getattr(L, f).restype = None
     return L
@@ -167,16 +171,29 @@ def quantize_rows(x):
     return codes, mins, scales
 
 
-def dequant_rows(codes, mins, scales):
-    """Inverse map to fp16: codes [..., d/2], mins/scales [..., d/64] -> float16 [..., d]."""
+def _dequant_args(codes, mins, scales):
     codes = np.ascontiguousarray(codes, np.uint8)
     mins = np.ascontiguousarray(mins, np.float32)
     scales = np.ascontiguousarray(scales, np.float32)
     d = codes.shape[-1] * 2
     lead = codes.shape[:-1]
     n = int(np.prod(lead)) if lead else 1
-    out = np.zeros(lead + (d,), np.uint16)
+    return codes, mins, scales, d, lead, n
+
+
+def dequant_rows(codes, mins, scales) -> np.ndarray:
+    """Dequantised values min + code*scale (float64): codes [..., d/2], mins/scales [..., d/64] -> [..., d]."""
+    codes, mins, scales, d, lead, n = _dequant_args(codes, mins, scales)
+    out = np.zeros(lead + (d,), np.float64)
     lib().oracle_dequant_rows(n, d, _ptr(codes), _ptr(mins), _ptr(scales), _ptr(out))
+    return out
+
+
+def dequant_rows_f16(codes, mins, scales) -> np.ndarray:
+    """The report's FP16 form of the dequantised values (float16 [..., d]); reference only."""
+    codes, mins, scales, d, lead, n = _dequant_args(codes, mins, scales)
+    out = np.zeros(lead + (d,), np.uint16)
+    lib().oracle_dequant_rows_f16(n, d, _ptr(codes), _ptr(mins), _ptr(scales), _ptr(out))
     return out.view(np.float16)
 
 

@@ -25,9 +25,15 @@
  *
  * Precision.  The codec decides integers (the 4-bit codes), so it runs in
  * binary32 with one rounding per operation (built with -ffp-contract=off,
- * no fast-math), in the order listed at oracle_quantize_group.  Dequantised
- * values are rounded to binary16, as the report states.  Attention over the
- * dequantised values runs in binary64 (the pages fix no precision for it).
+ * no fast-math), in the order listed at oracle_quantize_group.  Attention
+ * runs in binary64 over the dequantised values min + code*scale taken
+ * exactly (oracle_dequant_value).  The report's "dequantised to FP16 before
+ * compute" describes the data type of FlexGen's own GPU compute; it is kept
+ * as oracle_dequant_elem_f16 but not used by attention: with the OPT-30B
+ * style outlier channels (queries and keys x8) the FP16 rounding of a
+ * dequantised key alone moves a logit by ~1e-2, more than the tolerance the
+ * GPU path is held to, so an FP16-rounded reference would measure rounding
+ * noise rather than the method.
  *
  * Readings taken where the pages are silent (each one is listed in the
  * design notes with its reason):
@@ -176,10 +182,21 @@ int oracle_code_at(const uint8_t *row_codes, int i)
     return (i % 2 == 0) ? (byte & 15) : (byte >> 4);
 }
 
-/* Dequantise element i of a row to fp16: v = code*scale, then v + min
- * (two binary32 roundings), then round to binary16 ([FG-report] 三.2(C):
- * dequantised to FP16 before compute).                                     */
-uint16_t oracle_dequant_elem(const uint8_t *row_codes, const float *row_mins, const float *row_scales, int i)
+/* Dequantised value of element i of a row: min + code * scale, the affine
+ * map of the asymmetric code, taken exactly (binary64 holds the product of a
+ * 4-bit integer and a binary32 scale, and the sum with the binary32 min, to
+ * far below the tolerances used here).  This is the value attention uses.  */
+double oracle_dequant_value(const uint8_t *row_codes, const float *row_mins, const float *row_scales, int i)
+{
+    int g = i / ORACLE_GROUP;
+    return (double)oracle_code_at(row_codes, i) * (double)row_scales[g] + (double)row_mins[g];
+}
+
+/* The same value as the report writes it for its GPU: dequantised to FP16
+ * ([FG-report] 三.2(C)): v = code*scale, then v + min (two binary32
+ * roundings), then rounded to binary16.  Kept as a reference: the attention
+ * functions below use oracle_dequant_value (see the header note).          */
+uint16_t oracle_dequant_elem_f16(const uint8_t *row_codes, const float *row_mins, const float *row_scales, int i)
 {
     int g = i / ORACLE_GROUP;
     float v = (float)oracle_code_at(row_codes, i) * row_scales[g];
@@ -188,13 +205,23 @@ uint16_t oracle_dequant_elem(const uint8_t *row_codes, const float *row_mins, co
 }
 
 void oracle_dequant_rows(int nrows, int d, const uint8_t *codes, const float *mins, const float *scales,
-                         uint16_t *out)
+                         double *out)
 {
     int G = d / ORACLE_GROUP;
     for (int r = 0; r < nrows; ++r)
         for (int i = 0; i < d; ++i)
-            out[(size_t)r * d + i] = oracle_dequant_elem(codes + (size_t)r * (d / 2), mins + (size_t)r * G,
-                                                         scales + (size_t)r * G, i);
+            out[(size_t)r * d + i] = oracle_dequant_value(codes + (size_t)r * (d / 2), mins + (size_t)r * G,
+                                                          scales + (size_t)r * G, i);
+}
+
+void oracle_dequant_rows_f16(int nrows, int d, const uint8_t *codes, const float *mins, const float *scales,
+                             uint16_t *out)
+{
+    int G = d / ORACLE_GROUP;
+    for (int r = 0; r < nrows; ++r)
+        for (int i = 0; i < d; ++i)
+            out[(size_t)r * d + i] = oracle_dequant_elem_f16(codes + (size_t)r * (d / 2), mins + (size_t)r * G,
+                                                             scales + (size_t)r * G, i);
 }
 
 /* ------------------------------------------------------------------------
@@ -210,8 +237,7 @@ static double kdot(int d, const uint16_t *q, const uint8_t *kc, const float *kmi
     double acc = 0.0;
     for (int i = 0; i < d; ++i) {
         double qi = (double)oracle_f16_to_f32(q[i]);
-        double ki = (double)oracle_f16_to_f32(
-            oracle_dequant_elem(kc + (size_t)t * (d / 2), kmin + (size_t)t * G, ksc + (size_t)t * G, i));
+        double ki = oracle_dequant_value(kc + (size_t)t * (d / 2), kmin + (size_t)t * G, ksc + (size_t)t * G, i);
         acc += qi * ki;
     }
     return acc;
@@ -248,8 +274,7 @@ void oracle_attend(int d, int T, const uint16_t *q, const uint8_t *kc, const flo
     for (int i = 0; i < d; ++i) {
         double acc = 0.0;
         for (int t = 0; t < T; ++t) {
-            double vi = (double)oracle_f16_to_f32(
-                oracle_dequant_elem(vc + (size_t)t * (d / 2), vmin + (size_t)t * G, vsc + (size_t)t * G, i));
+            double vi = oracle_dequant_value(vc + (size_t)t * (d / 2), vmin + (size_t)t * G, vsc + (size_t)t * G, i);
             acc += s[t] * vi;
         }
         out[i] = acc / l;
@@ -283,8 +308,7 @@ void oracle_attend_subset(int d, int nidx, const int32_t *idx, const uint16_t *q
         double acc = 0.0;
         for (int j = 0; j < nidx; ++j) {
             int t = idx[j];
-            double vi = (double)oracle_f16_to_f32(
-                oracle_dequant_elem(vc + (size_t)t * (d / 2), vmin + (size_t)t * G, vsc + (size_t)t * G, i));
+            double vi = oracle_dequant_value(vc + (size_t)t * (d / 2), vmin + (size_t)t * G, vsc + (size_t)t * G, i);
             acc += p[j] * vi;
         }
         out[i] = acc / l;

@@ -23,8 +23,11 @@ MUTANTS = [
     ("no_signed_zero_fix", "    mn = mn + 0.0f;\n", "\n"),
     ("nibbles_swapped", "codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));",
      "codes[j] = (uint8_t)((c[2 * j] << 4) | c[2 * j + 1]);"),
-    ("dequant_drops_min", "    v = v + row_mins[g];\n", "\n"),
-    ("dequant_skips_fp16", "    return oracle_f32_to_f16(v);\n}\n\nvoid oracle_dequant_rows",
+    ("dequant_drops_min", "* (double)row_scales[g] + (double)row_mins[g];", "* (double)row_scales[g];"),
+    ("dequant_uses_next_group_scale", "(double)row_scales[g] + (double)row_mins[g]",
+     "(double)row_scales[g ? g - 1 : g + 1] + (double)row_mins[g]"),
+    ("dequant_f16_drops_min", "    v = v + row_mins[g];\n", "\n"),
+    ("dequant_f16_scaled", "    return oracle_f32_to_f16(v);\n}\n\nvoid oracle_dequant_rows",
      "    return oracle_f32_to_f16(v * 1.0001f);\n}\n\nvoid oracle_dequant_rows"),
     ("min_misses_last_element", "for (int i = 1; i < ORACLE_GROUP; ++i) {\n        if (f[i] < mn)",
      "for (int i = 1; i < ORACLE_GROUP - 1; ++i) {\n        if (f[i] < mn)"),
