@@ -1,0 +1,159 @@
+/*
+ * kvq4.h -- int4 group-wise KV cache and decode-phase attention for MI355X
+ * (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What is computed, and where the pages define it:
+ *
+ *  - The KV cache of one transformer layer, prompt phase and decode phase:
+ *    the FlexGen blog ("FlexGen: High-Throughput Generative Inference of
+ *    Large Language Models with a Single GPU [ICML'23]", qingweiji blog),
+ *    sections "预填充阶段" (prompt K/V of shape b x s x h) and "解码阶段"
+ *    (each decode step concatenates the new token's K/V along the sequence
+ *    axis, then attends with the single new query); section "KV Cache" gives
+ *    the multi-head shape [b, s, a, h/a].  The notes on "A Survey on
+ *    Efficient Inference for Large Language Models", section "Inference
+ *    Process of LLMs", give the same prefill/decode split.
+ *  - The cache is held compressed: "FlexGen研究学术报告" section 三.2(C)
+ *    describes group-wise asymmetric 4-bit quantisation of the KV cache with
+ *    64 contiguous elements per group, dequantised to FP16 before compute.
+ *  - Attention scale 1/sqrt(d), d = h/a the per-head query/key dimension:
+ *    the survey notes, eq. (2).
+ *  - Sparse variant: the same report section, top-10% sparse attention
+ *    (only the KV entries with the highest attention values are used).
+ *
+ * Readings taken where the pages are silent:
+ *  - group axis = head_dim: group g of token row (b, t, a) is elements
+ *    64g..64g+63 of that row; d must be a multiple of 64;
+ *  - min/max affine code: scale = (max-min)/15, code = round_half_even(
+ *    (x-min)*(15/(max-min))) clamped to 0..15, in binary32 with one rounding
+ *    per operation; a constant group stores scale 0 and codes 0; a min of -0
+ *    is stored as +0;
+ *  - two codes per byte, the even element in the low nibble;
+ *  - per-group min and scale kept as binary32 planes beside the codes.
+ *
+ * Device layout of one layer's cache (all planes caller-allocated):
+ *    S = s + n token slots per (batch row, head);  G = d / 64
+ *    k_codes, v_codes : uint8  [b][a][S][d/2]
+ *    k_min, k_scale, v_min, v_scale : float32 [b][a][S][G]
+ *  Slot t of (batch row bi, head ai) is row (bi*a + ai)*S + t.
+ *  Activations passed in: fp16 (IEEE binary16), row-major, 16-byte aligned:
+ *    prompt K/V      [b][s_len][a][d]
+ *    q, new K/V, out [b][1][a][d]
+ *
+ * Conventions shared by every call:
+ *  - Every pointer except the optional ones is a device pointer owned by
+ *    the caller, who keeps it alive until the enqueued work has finished.
+ *    Nothing here allocates, frees or synchronises: each call checks its
+ *    arguments on the host, enqueues kernels on `hip_stream` (a
+ *    hipStream_t; NULL = the default stream) and returns.  A kernel fault
+ *    surfaces at the caller's next synchronisation.
+ *  - Argument errors are reported before anything is enqueued, as a
+ *    negative status; KVQ_OK (0) means the work was enqueued.
+ *  - Inputs must be finite.  Overlapping calls that write the same cache
+ *    slots race; calls on one stream are ordered.
+ */
+#ifndef KVQ4_H
+#define KVQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    KVQ_OK = 0,
+    KVQ_EINVAL = -1,        /* null or misaligned pointer, non-positive size, h % a != 0, d % 64 != 0 */
+    KVQ_ERANGE = -2,        /* s_len, pos, ctx_len, k_top or num_splits outside its range            */
+    KVQ_EUNSUPPORTED = -3,  /* group != 64, metadata type not F32, d not 64/128/256, context too long */
+    KVQ_ENOSPACE = -4,      /* workspace smaller than kvq_workspace_bytes() asks for                 */
+    KVQ_ELAUNCH = -5        /* the HIP runtime refused a launch                                      */
+};
+
+/* Metadata (min/scale) plane type.  Only F32 is implemented. */
+enum { KVQ_META_F32 = 0 };
+
+#define KVQ_GROUP 64            /* elements per quantisation group                          */
+#define KVQ_MAX_HEAD_DIM 256    /* d = h/a must be 64, 128 or 256                            */
+#define KVQ_MAX_SPLITS 256      /* largest num_splits accepted by decode_attention_q4       */
+#define KVQ_TOPK_MAX_CTX 8192   /* longest context decode_attention_q4_topk accepts        */
+
+/* Problem dimensions in the pages' notation: b batch (the effective batch of
+ * one launch), a heads, h hidden size (d = h/a per head), s prompt length,
+ * n generated tokens; the cache holds S = s + n slots. */
+typedef struct kvq_dims {
+    int32_t b, a, h, s, n;
+    int32_t group;      /* must be KVQ_GROUP */
+    int32_t meta_dtype; /* must be KVQ_META_F32 */
+} kvq_dims;
+
+/* One layer's quantised cache: device pointers in the layout above. */
+typedef struct kvq_cache {
+    kvq_dims dims;
+    uint8_t *k_codes, *v_codes;
+    void *k_min, *k_scale, *v_min, *v_scale;
+} kvq_cache;
+
+/* Bytes of one code plane (k_codes or v_codes: b*a*S*d/2) and of one metadata
+ * plane (each of k_min, k_scale, v_min, v_scale: b*a*S*(d/64)*4).  Either
+ * output pointer may be NULL.  Host only; returns a status.
+ * With precision 0.5 byte per element this is the blog's KV-cache size
+ * 2*precision*layers*h*seq_len*batch (section "KV Cache") for one layer,
+ * plus the metadata planes. */
+int kvq_cache_bytes(const kvq_dims *dims, size_t *codes_bytes_per_plane, size_t *meta_bytes_per_plane);
+
+/* Prompt phase: quantise the prompt's K and V (fp16 [b][s_len][a][d]) into
+ * slots 0..s_len-1 of every (batch row, head).  1 <= s_len <= s+n. */
+int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t s_len,
+                        void *hip_stream);
+
+/* Decode phase, KV update: quantise the new token's K and V (fp16
+ * [b][1][a][d]) into slot `pos` of every (batch row, head), 0 <= pos < s+n.
+ * Decode step j (1-based) appends at pos = s+j-1 and then attends over
+ * ctx_len = s+j tokens. */
+int kv_append_quant(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos,
+                    void *hip_stream);
+
+/* Workspace bytes decode_attention_q4 needs for (ctx_len, num_splits), or
+ * decode_attention_q4_topk when k_top > 0 (always 0 today).  0 when the
+ * resolved split count is 1.  Host only; returns 0 on invalid arguments. */
+size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_splits, int32_t k_top);
+
+/* Decode-phase attention over slots 0..ctx_len-1 (1 <= ctx_len <= s+n) of
+ * every (batch row, head):
+ *     out = softmax(q . K^T / sqrt(d)) . V      (per head; no W_O, no residual)
+ * with K, V the dequantised cache.  q and out are fp16 [b][1][a][d].
+ * num_splits: 0 = choose automatically; k > 0 splits each context into k
+ * ranges handled by separate workgroups and merged by a second pass
+ * (log-sum-exp).  ws: device workspace of ws_bytes >= kvq_workspace_bytes()
+ * (may be NULL when that is 0). */
+int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                        int32_t num_splits, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* As decode_attention_q4 with the kernel's launch shape fixed by the caller:
+ * unroll = tokens per lane per iteration (1, 2 or 4) and waves_per_pair =
+ * waves sharing one (batch row, head) inside a workgroup (1, 2 or 4).
+ * Results agree with decode_attention_q4 to rounding; for tuning and tests. */
+int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                              int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
+                              size_t ws_bytes, void *hip_stream);
+
+/* Sparse decode attention: for every (batch row, head) score all ctx_len
+ * tokens, keep the k_top highest scores (ties to the smaller token index),
+ * and take the softmax and P.V over the kept tokens only.
+ * 1 <= k_top <= ctx_len <= min(s+n, KVQ_TOPK_MAX_CTX); the pages' rule keeps
+ * k_top = ceil(0.1 * ctx_len).  sel_idx (device int32 [b][a][k_top], may be
+ * NULL) receives the kept token indices in ascending order. */
+int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
+                             void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream);
+
+/* Static text for a status code. */
+const char *kvq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ4_H */

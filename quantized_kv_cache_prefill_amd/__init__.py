@@ -1,0 +1,247 @@
+"""Python binding of libkvq4.so -- int4 group-wise KV cache and decode attention on MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``csrc/``.  PyTorch supplies device memory and the current stream.  The
+functions mirror the C entry points declared in ``include/kvq4.h`` (same
+names, same semantics); see that header for the operation each one performs
+and the passage of the FlexGen pages it follows.
+
+If ``libkvq4.so`` has not been built, importing works but every call raises
+``RuntimeError`` -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KvqError", "QuantKVCache", "kvq_cache_bytes", "kvq_workspace_bytes", "kv_quantize_prefill",
+    "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "decode_attention_q4_topk",
+    "library_path", "load_library", "GROUP",
+]
+
+GROUP = 64
+META_F32 = 0
+KVQ_TOPK_MAX_CTX = 8192
+KVQ_MAX_SPLITS = 256
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvq4.so")
+
+EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_append_quant", "kvq_workspace_bytes",
+            "decode_attention_q4", "decode_attention_q4_tuned", "decode_attention_q4_topk", "kvq_strerror")
+
+
+class KvqDims(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int32), ("a", ctypes.c_int32), ("h", ctypes.c_int32), ("s", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("group", ctypes.c_int32), ("meta_dtype", ctypes.c_int32)]
+
+
+class KvqCache(ctypes.Structure):
+    _fields_ = [("dims", KvqDims), ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_min", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_min", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_strerror(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkvq4.so (raises RuntimeError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m quantized_kv_cache_prefill_amd.build`"
+                           " (there is no CPU fallback)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    PD, PC = ctypes.POINTER(KvqDims), ctypes.POINTER(KvqCache)
+    L.kvq_cache_bytes.argtypes = [PD, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    L.kvq_cache_bytes.restype = ctypes.c_int
+    L.kv_quantize_prefill.argtypes = [PC, P, P, I32, P]
+    L.kv_quantize_prefill.restype = ctypes.c_int
+    L.kv_append_quant.argtypes = [PC, P, P, I32, P]
+    L.kv_append_quant.restype = ctypes.c_int
+    L.kvq_workspace_bytes.argtypes = [PD, I32, I32, I32]
+    L.kvq_workspace_bytes.restype = SZ
+    L.decode_attention_q4.argtypes = [PC, P, I32, P, I32, P, SZ, P]
+    L.decode_attention_q4.restype = ctypes.c_int
+    L.decode_attention_q4_tuned.argtypes = [PC, P, I32, P, I32, I32, I32, P, SZ, P]
+    L.decode_attention_q4_tuned.restype = ctypes.c_int
+    L.decode_attention_q4_topk.argtypes = [PC, P, I32, I32, P, P, P, SZ, P]
+    L.decode_attention_q4_topk.restype = ctypes.c_int
+    L.kvq_strerror.argtypes = [ctypes.c_int]
+    L.kvq_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _strerror(status: int) -> str:
+    try:
+        return load_library().kvq_strerror(status).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error message
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KvqError(status, what)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_dims(b: int, a: int, h: int, s: int, n: int) -> KvqDims:
+    return KvqDims(b, a, h, s, n, GROUP, META_F32)
+
+
+class QuantKVCache:
+    """One layer's int4 KV cache in device memory (planes owned by torch).
+
+    k_codes, v_codes : uint8   [b, a, S, d/2]   (two codes per byte, even element low nibble)
+    k_min, k_scale, v_min, v_scale : float32 [b, a, S, d/64]
+    with S = s + n slots, d = h / a.
+    """
+
+    def __init__(self, b: int, a: int, h: int, s: int, n: int, device="cuda", fill: int | None = None):
+        if h % a != 0:
+            raise ValueError("h must be a multiple of a")
+        self.b, self.a, self.h, self.s, self.n = b, a, h, s, n
+        self.d = h // a
+        self.S = s + n
+        G = self.d // GROUP
+        alloc = torch.empty if fill is None else (lambda *sh, **kw: torch.full(sh, fill, **kw))
+        self.k_codes = alloc(b, a, self.S, self.d // 2, dtype=torch.uint8, device=device)
+        self.v_codes = alloc(b, a, self.S, self.d // 2, dtype=torch.uint8, device=device)
+        meta = [alloc(b, a, self.S, G, dtype=torch.float32, device=device) for _ in range(4)]
+        self.k_min, self.k_scale, self.v_min, self.v_scale = meta
+        self._struct = KvqCache(make_dims(b, a, h, s, n), self.k_codes.data_ptr(), self.v_codes.data_ptr(),
+                                self.k_min.data_ptr(), self.k_scale.data_ptr(), self.v_min.data_ptr(),
+                                self.v_scale.data_ptr())
+
+    @property
+    def dims(self) -> KvqDims:
+        return self._struct.dims
+
+    def struct_ref(self):
+        return ctypes.byref(self._struct)
+
+    def planes(self):
+        return (self.k_codes, self.k_min, self.k_scale, self.v_codes, self.v_min, self.v_scale)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.planes())
+
+
+def _act(t: torch.Tensor, shape, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float16 CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def kvq_cache_bytes(b: int, a: int, h: int, s: int, n: int) -> tuple[int, int]:
+    """(bytes of one code plane, bytes of one metadata plane)."""
+    cb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().kvq_cache_bytes(ctypes.byref(make_dims(b, a, h, s, n)), ctypes.byref(cb),
+                                          ctypes.byref(mb)), "kvq_cache_bytes")
+    return cb.value, mb.value
+
+
+def kvq_workspace_bytes(cache: QuantKVCache, ctx_len: int, num_splits: int = 0, k_top: int = 0) -> int:
+    return load_library().kvq_workspace_bytes(ctypes.byref(cache.dims), ctx_len, num_splits, k_top)
+
+
+def kv_quantize_prefill(cache: QuantKVCache, k: torch.Tensor, v: torch.Tensor, stream=None):
+    """Quantise the prompt's K and V (fp16 [b, s_len, a, d]) into slots 0..s_len-1."""
+    s_len = k.shape[1] if k.dim() == 4 else -1
+    _act(k, (cache.b, s_len, cache.a, cache.d), "k")
+    _act(v, (cache.b, s_len, cache.a, cache.d), "v")
+    _check(load_library().kv_quantize_prefill(cache.struct_ref(), _ptr(k), _ptr(v), s_len, _stream(stream)),
+           "kv_quantize_prefill")
+
+
+def kv_append_quant(cache: QuantKVCache, k_new: torch.Tensor, v_new: torch.Tensor, pos: int, stream=None):
+    """Quantise one new token's K and V (fp16 [b, 1, a, d]) into slot `pos`."""
+    _act(k_new, (cache.b, 1, cache.a, cache.d), "k_new")
+    _act(v_new, (cache.b, 1, cache.a, cache.d), "v_new")
+    _check(load_library().kv_append_quant(cache.struct_ref(), _ptr(k_new), _ptr(v_new), pos, _stream(stream)),
+           "kv_append_quant")
+
+
+def _workspace(cache, ctx_len, num_splits, ws):
+    need = kvq_workspace_bytes(cache, ctx_len, num_splits)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need // 4, dtype=torch.float32, device=cache.k_codes.device)
+    return ws, need
+
+
+def decode_attention_q4(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, out: torch.Tensor | None = None,
+                        num_splits: int = 0, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """softmax(q K^T / sqrt(d)) V over slots 0..ctx_len-1; q, out fp16 [b, 1, a, d]."""
+    _act(q, (cache.b, 1, cache.a, cache.d), "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _act(out, q.shape, "out")
+    ws, need = _workspace(cache, ctx_len, num_splits, ws)
+    _check(load_library().decode_attention_q4(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
+                                              _ptr(ws), need, _stream(stream)), "decode_attention_q4")
+    return out
+
+
+def decode_attention_q4_tuned(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, unroll: int,
+                              waves_per_pair: int, out: torch.Tensor | None = None, num_splits: int = 0,
+                              ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """decode_attention_q4 with an explicit kernel launch shape (unroll 1/2/4, waves per pair 1/2/4)."""
+    _act(q, (cache.b, 1, cache.a, cache.d), "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _act(out, q.shape, "out")
+    ws, need = _workspace(cache, ctx_len, num_splits, ws)
+    _check(load_library().decode_attention_q4_tuned(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
+                                                    unroll, waves_per_pair, _ptr(ws), need, _stream(stream)),
+           "decode_attention_q4_tuned")
+    return out
+
+
+def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, k_top: int,
+                             out: torch.Tensor | None = None, sel_idx: torch.Tensor | bool | None = True,
+                             stream=None):
+    """Top-k sparse decode attention.  Returns (out fp16 [b,1,a,d], sel_idx int32 [b,a,k_top] or None)."""
+    _act(q, (cache.b, 1, cache.a, cache.d), "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _act(out, q.shape, "out")
+    if sel_idx is True:
+        sel_idx = torch.empty((cache.b, cache.a, k_top), dtype=torch.int32, device=q.device)
+    elif sel_idx is False:
+        sel_idx = None
+    if sel_idx is not None and (sel_idx.dtype != torch.int32 or not sel_idx.is_contiguous()
+                                or sel_idx.numel() != cache.b * cache.a * k_top):
+        raise ValueError("sel_idx must be a contiguous int32 tensor of b*a*k_top elements")
+    _check(load_library().decode_attention_q4_topk(cache.struct_ref(), _ptr(q), ctx_len, k_top, _ptr(out),
+                                                   _ptr(sel_idx), None, 0, _stream(stream)),
+           "decode_attention_q4_topk")
+    return out, sel_idx

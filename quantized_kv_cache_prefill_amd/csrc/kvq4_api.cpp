@@ -1,0 +1,234 @@
+// C-ABI layer: argument checks (all on the host, before anything is
+// enqueued), launch-shape choice, and the calls into the HIP kernels.
+// The operations and their sources on the pages are documented in
+// include/kvq4.h.
+#include "kvq4.h"
+
+#include <stdint.h>
+
+#include <algorithm>
+
+#include <hip/hip_runtime_api.h>
+
+#include "kvq4_launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every call; fills the kernel-side view of the cache.
+int check_dims(const kvq_dims *d)
+{
+    if (d == nullptr)
+        return KVQ_EINVAL;
+    if (d->b <= 0 || d->a <= 0 || d->h <= 0 || d->s <= 0 || d->n < 0)
+        return KVQ_EINVAL;
+    if (d->h % d->a != 0)
+        return KVQ_EINVAL;
+    const int hd = d->h / d->a;
+    if (hd % KVQ_GROUP != 0)
+        return KVQ_EINVAL;
+    if (d->group != KVQ_GROUP || d->meta_dtype != KVQ_META_F32)
+        return KVQ_EUNSUPPORTED;
+    if (hd != 64 && hd != 128 && hd != 256)
+        return KVQ_EUNSUPPORTED;
+    if ((int64_t)d->s + d->n > INT32_MAX / 2)
+        return KVQ_ERANGE;
+    if ((int64_t)d->b * d->a > INT32_MAX / 4)
+        return KVQ_ERANGE;
+    return KVQ_OK;
+}
+
+int check_cache(const kvq_cache *c, kvq::CachePlanes *planes)
+{
+    if (c == nullptr)
+        return KVQ_EINVAL;
+    int st = check_dims(&c->dims);
+    if (st != KVQ_OK)
+        return st;
+    const void *ptrs[6] = {c->k_codes, c->v_codes, c->k_min, c->k_scale, c->v_min, c->v_scale};
+    for (const void *p : ptrs)
+        if (p == nullptr || !aligned16(p))
+            return KVQ_EINVAL;
+    planes->k_codes = c->k_codes;
+    planes->v_codes = c->v_codes;
+    planes->k_min = static_cast<float *>(c->k_min);
+    planes->k_scale = static_cast<float *>(c->k_scale);
+    planes->v_min = static_cast<float *>(c->v_min);
+    planes->v_scale = static_cast<float *>(c->v_scale);
+    planes->a = c->dims.a;
+    planes->d = c->dims.h / c->dims.a;
+    planes->S = c->dims.s + c->dims.n;
+    return KVQ_OK;
+}
+
+int check_act(const void *p) { return (p == nullptr || !aligned16(p)) ? KVQ_EINVAL : KVQ_OK; }
+
+int status_of(int hip_err) { return hip_err == 0 ? KVQ_OK : KVQ_ELAUNCH; }
+
+// Launch shape for the dense decode kernel.  unroll/waves_per_pair: the
+// default (2, 4) keeps ~8 KB of loads in flight per wave-iteration and puts
+// one (batch row, head) on a whole workgroup.  Automatic splits: enough
+// workgroups to occupy every CU several times over (256 CUs x 8), never more
+// than one split per two workgroup iterations of context.  The automatic
+// choice depends on (pairs, d, ctx) only, so kvq_workspace_bytes() is exact
+// for every launch shape.
+constexpr int kDefaultUnroll = 2;
+constexpr int kDefaultWavesPerPair = 4;
+constexpr int64_t kTargetWorkgroups = 256 * 8;
+
+int resolve_splits(int pairs, int d, int ctx, int num_splits, int *split_len)
+{
+    int s;
+    if (num_splits > 0) {
+        s = num_splits;
+    } else {
+        const int per_iter = kvq::decode_tokens_per_iter(d, kDefaultUnroll, kDefaultWavesPerPair);
+        const int64_t want = (kTargetWorkgroups + pairs - 1) / pairs;
+        const int64_t cap = std::max<int64_t>(1, ctx / (2 * per_iter));
+        s = (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 64}));
+    }
+    s = std::min(s, ctx);
+    const int len = (ctx + s - 1) / s;
+    s = (ctx + len - 1) / len; // no empty split
+    *split_len = len;
+    return s;
+}
+
+} // namespace
+
+extern "C" {
+
+int kvq_cache_bytes(const kvq_dims *dims, size_t *codes_bytes_per_plane, size_t *meta_bytes_per_plane)
+{
+    int st = check_dims(dims);
+    if (st != KVQ_OK)
+        return st;
+    const size_t slots = (size_t)dims->b * (size_t)dims->a * (size_t)(dims->s + dims->n);
+    const size_t hd = (size_t)(dims->h / dims->a);
+    if (codes_bytes_per_plane)
+        *codes_bytes_per_plane = slots * hd / 2;
+    if (meta_bytes_per_plane)
+        *meta_bytes_per_plane = slots * (hd / KVQ_GROUP) * sizeof(float);
+    return KVQ_OK;
+}
+
+int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t s_len,
+                        void *hip_stream)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if ((st = check_act(k_f16)) != KVQ_OK || (st = check_act(v_f16)) != KVQ_OK)
+        return st;
+    if (s_len < 1 || s_len > c.S)
+        return KVQ_ERANGE;
+    return status_of(kvq::launch_quantize(c, k_f16, v_f16, cache->dims.b, s_len, 0,
+                                          static_cast<hipStream_t>(hip_stream)));
+}
+
+int kv_append_quant(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos, void *hip_stream)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if ((st = check_act(k_f16)) != KVQ_OK || (st = check_act(v_f16)) != KVQ_OK)
+        return st;
+    if (pos < 0 || pos >= c.S)
+        return KVQ_ERANGE;
+    return status_of(kvq::launch_quantize(c, k_f16, v_f16, cache->dims.b, 1, pos,
+                                          static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_splits, int32_t k_top)
+{
+    if (check_dims(dims) != KVQ_OK)
+        return 0;
+    const int S = dims->s + dims->n;
+    if (ctx_len < 1 || ctx_len > S || num_splits < 0 || num_splits > KVQ_MAX_SPLITS)
+        return 0;
+    if (k_top > 0)
+        return 0;
+    const int pairs = dims->b * dims->a;
+    const int hd = dims->h / dims->a;
+    int len;
+    const int s = resolve_splits(pairs, hd, ctx_len, num_splits, &len);
+    return kvq::decode_ws_floats(pairs, hd, s) * sizeof(float);
+}
+
+int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                              int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
+                              size_t ws_bytes, void *hip_stream)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if ((st = check_act(q_f16)) != KVQ_OK || (st = check_act(out_f16)) != KVQ_OK)
+        return st;
+    if (ctx_len < 1 || ctx_len > c.S)
+        return KVQ_ERANGE;
+    if (num_splits < 0 || num_splits > KVQ_MAX_SPLITS)
+        return KVQ_ERANGE;
+    if ((unroll != 1 && unroll != 2 && unroll != 4) || (waves_per_pair != 1 && waves_per_pair != 2 &&
+                                                         waves_per_pair != 4))
+        return KVQ_EINVAL;
+    const int pairs = cache->dims.b * cache->dims.a;
+    kvq::DecodeShape sh;
+    sh.unroll = unroll;
+    sh.waves_per_pair = waves_per_pair;
+    sh.splits = resolve_splits(pairs, c.d, ctx_len, num_splits, &sh.split_len);
+    const size_t need = kvq::decode_ws_floats(pairs, c.d, sh.splits) * sizeof(float);
+    if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need))
+        return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
+    return status_of(kvq::launch_decode(c, pairs, q_f16, ctx_len, out_f16, sh, static_cast<float *>(ws),
+                                        static_cast<hipStream_t>(hip_stream)));
+}
+
+int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                        int32_t num_splits, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    return decode_attention_q4_tuned(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll,
+                                     kDefaultWavesPerPair, ws, ws_bytes, hip_stream);
+}
+
+int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
+                             void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    (void)ws;
+    (void)ws_bytes;
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if ((st = check_act(q_f16)) != KVQ_OK || (st = check_act(out_f16)) != KVQ_OK)
+        return st;
+    if (ctx_len < 1 || ctx_len > c.S)
+        return KVQ_ERANGE;
+    if (ctx_len > KVQ_TOPK_MAX_CTX)
+        return KVQ_EUNSUPPORTED;
+    if (k_top < 1 || k_top > ctx_len)
+        return KVQ_ERANGE;
+    if (sel_idx != nullptr && (reinterpret_cast<uintptr_t>(sel_idx) & 3u) != 0)
+        return KVQ_EINVAL;
+    const int pairs = cache->dims.b * cache->dims.a;
+    return status_of(kvq::launch_topk(c, pairs, q_f16, ctx_len, k_top, out_f16, sel_idx,
+                                      static_cast<hipStream_t>(hip_stream)));
+}
+
+const char *kvq_strerror(int status)
+{
+    switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument (null or misaligned pointer, bad dimension)";
+    case KVQ_ERANGE: return "argument out of range (s_len, pos, ctx_len, k_top or num_splits)";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration (group, metadata type, head_dim or context length)";
+    case KVQ_ENOSPACE: return "workspace too small";
+    case KVQ_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+} // extern "C"

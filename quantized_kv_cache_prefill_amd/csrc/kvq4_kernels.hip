@@ -1,0 +1,810 @@
+// HIP kernels for gfx950: int4 group-wise KV-cache quantisation, dense
+// decode attention over the int4 cache (with a split-context reduce pass),
+// and top-k sparse decode attention.
+//
+// Definitions followed (page titles and sections):
+//  * codec: "FlexGen研究学术报告" section 三.2(C) -- group-wise asymmetric
+//    4-bit quantisation, 64 contiguous elements per group, dequantised to
+//    FP16 before compute; group axis = head_dim, min/max affine code with
+//    scale (max-min)/15 and round-half-even codes (readings stated in
+//    include/kvq4.h);
+//  * decode attention: the FlexGen blog, section "解码阶段":
+//    t_out = softmax(t_Q x_K^T / sqrt(.)) x_V, stopping before W_O, with the
+//    per-head 1/sqrt(d_k) scale of eq. (2) in the efficient-inference survey
+//    notes;
+//  * sparse variant: the report's section 三.2(C), top-10% sparse attention.
+//
+// Everything here streams HBM once: the path is bandwidth-bound (the survey
+// notes' "Efficiency Analysis" gives decoding a very low compute-to-memory
+// ratio), so the kernels are shaped around 16-byte coalesced loads, no LDS
+// staging of the cache, and a VALU budget of a few operations per element.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq4_launch.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// DPP controls (GFX9 encoding).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kHalfRowMirror = 0x141; // lane i <-> lane 7-i inside each 8-lane group
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                                 false));
+}
+
+__device__ __forceinline__ float h2f_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float h2f_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// ---------------------------------------------------------------------------
+// Nibble unpack.  A 32-bit word of codes holds elements e0..e7 (nibble k at
+// bits 4k..4k+3, even element in the low nibble of each byte).  Moving one
+// nibble of each 16-bit half to bits 4..7 and OR-ing the fp16 pattern of 64.0
+// yields the exact fp16 value 64 + code in that half (the fraction's bits
+// 4..7 weigh 1 at exponent 6).  The four pairs come out as (e0,e4), (e1,e5),
+// (e2,e6), (e3,e7): one shift + one and-or per pair, no conversion.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNibMask = 0x00F000F0u;
+constexpr float kBias = 64.0f;
+
+// The OR constant is held in a VGPR (opaque to the compiler) so each pair
+// compiles to a single v_and_or_b32 with the mask in an SGPR: GFX9's VOP3
+// takes no literal and at most one scalar operand.
+__device__ __forceinline__ uint32_t magic64_vgpr()
+{
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t pair0(uint32_t x, uint32_t mg) { return ((x << 4) & kNibMask) | mg; }
+__device__ __forceinline__ uint32_t pair1(uint32_t x, uint32_t mg) { return (x & kNibMask) | mg; }
+__device__ __forceinline__ uint32_t pair2(uint32_t x, uint32_t mg) { return ((x >> 4) & kNibMask) | mg; }
+__device__ __forceinline__ uint32_t pair3(uint32_t x, uint32_t mg) { return ((x >> 8) & kNibMask) | mg; }
+
+__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+// One lane's 32-element slice of q, regrouped into the unpack's pair order,
+// plus the slice's sum (for the bias and the group min).
+struct QSlice {
+    uint32_t qp[16];
+    float qsum;
+};
+
+__device__ __forceinline__ QSlice load_q_slice(const uint4 *__restrict__ qrow)
+{
+    QSlice s;
+    s.qsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint4 v = qrow[w]; // elements 8w..8w+7: x=(e0,e1) y=(e2,e3) z=(e4,e5) w=(e6,e7)
+        s.qp[4 * w + 0] = (v.x & 0xFFFFu) | (v.z << 16);
+        s.qp[4 * w + 1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
+        s.qp[4 * w + 2] = (v.y & 0xFFFFu) | (v.w << 16);
+        s.qp[4 * w + 3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+        s.qsum += h2f_lo(v.x) + h2f_hi(v.x) + h2f_lo(v.y) + h2f_hi(v.y) + h2f_lo(v.z) + h2f_hi(v.z) + h2f_lo(v.w) +
+                  h2f_hi(v.w);
+    }
+    return s;
+}
+
+// sum_i q_i * (64 + c_i) over the lane's 32 elements.
+__device__ __forceinline__ float dot_biased(const QSlice &q, const uint4 kx, uint32_t mg)
+{
+    const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        acc = fdot2(q.qp[4 * j + 0], pair0(w[j], mg), acc);
+        acc = fdot2(q.qp[4 * j + 1], pair1(w[j], mg), acc);
+        acc = fdot2(q.qp[4 * j + 2], pair2(w[j], mg), acc);
+        acc = fdot2(q.qp[4 * j + 3], pair3(w[j], mg), acc);
+    }
+    return acc;
+}
+
+// acc[i] += ps * (64 + c_i) for the lane's 32 elements (natural order).
+__device__ __forceinline__ void axpy_biased(float (&acc)[32], float ps, const uint4 vx, uint32_t mg)
+{
+    const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p0 = pair0(w[j], mg), p1 = pair1(w[j], mg), p2 = pair2(w[j], mg), p3 = pair3(w[j], mg);
+        acc[8 * j + 0] = __builtin_fmaf(ps, h2f_lo(p0), acc[8 * j + 0]);
+        acc[8 * j + 4] = __builtin_fmaf(ps, h2f_hi(p0), acc[8 * j + 4]);
+        acc[8 * j + 1] = __builtin_fmaf(ps, h2f_lo(p1), acc[8 * j + 1]);
+        acc[8 * j + 5] = __builtin_fmaf(ps, h2f_hi(p1), acc[8 * j + 5]);
+        acc[8 * j + 2] = __builtin_fmaf(ps, h2f_lo(p2), acc[8 * j + 2]);
+        acc[8 * j + 6] = __builtin_fmaf(ps, h2f_hi(p2), acc[8 * j + 6]);
+        acc[8 * j + 3] = __builtin_fmaf(ps, h2f_lo(p3), acc[8 * j + 3]);
+        acc[8 * j + 7] = __builtin_fmaf(ps, h2f_hi(p3), acc[8 * j + 7]);
+    }
+}
+
+// Sum over the LPT lanes that hold one token row.
+template <int LPT>
+__device__ __forceinline__ float token_sum(float v)
+{
+    if constexpr (LPT >= 2)
+        v += dpp<kQuadXor1>(v);
+    if constexpr (LPT >= 4)
+        v += dpp<kQuadXor2>(v);
+    if constexpr (LPT >= 8)
+        v += dpp<kHalfRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ===========================================================================
+// Quantise.  Each lane loads 8 fp16 values (16 bytes); 8 consecutive lanes
+// hold one 64-element group and reduce its min/max with three DPP steps.
+// Row r of the flattened work list is (pair, token) = (r / s_src, r % s_src),
+// so lanes with consecutive rows write consecutive cache slots: the 16-byte
+// reads are full 256-byte rows and the code/metadata writes are contiguous.
+// ===========================================================================
+template <int D, int R>
+__global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_src, const uint4 *__restrict__ v_src,
+                                                  int64_t rows, int s_src, int a, int S, int t_dst0,
+                                                  uint32_t *__restrict__ k_codes, uint32_t *__restrict__ v_codes,
+                                                  float *__restrict__ k_min, float *__restrict__ k_scale,
+                                                  float *__restrict__ v_min, float *__restrict__ v_scale)
+{
+#pragma clang fp contract(off)
+    constexpr int LPR = D / 8;   // lanes per token row
+    constexpr int RPB = 256 / LPR;
+    constexpr int G = D / 64;
+    const bool is_v = blockIdx.y != 0;
+    const uint4 *__restrict__ src = is_v ? v_src : k_src;
+    uint32_t *__restrict__ codes = is_v ? v_codes : k_codes;
+    float *__restrict__ mins = is_v ? v_min : k_min;
+    float *__restrict__ scales = is_v ? v_scale : k_scale;
+    const int lir = threadIdx.x % LPR;
+    const int64_t row0 = (int64_t)blockIdx.x * (RPB * R) + threadIdx.x / LPR;
+
+    uint4 x[R];
+    int64_t slot[R];
+    bool ok[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int64_t row = row0 + (int64_t)u * RPB;
+        ok[u] = row < rows;
+        const int64_t rc = ok[u] ? row : rows - 1;
+        const int64_t pair = rc / s_src;
+        const int64_t ti = rc - pair * s_src;
+        const int64_t bi = pair / a;
+        const int64_t ai = pair - bi * a;
+        x[u] = src[((bi * s_src + ti) * a + ai) * (D / 8) + lir];
+        slot[u] = pair * S + t_dst0 + ti;
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = h2f_lo(w[j]);
+            f[2 * j + 1] = h2f_hi(w[j]);
+        }
+        float mn = f[0], mx = f[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            mn = fminf(mn, f[i]);
+            mx = fmaxf(mx, f[i]);
+        }
+        mn = fminf(mn, dpp<kQuadXor1>(mn));
+        mx = fmaxf(mx, dpp<kQuadXor1>(mx));
+        mn = fminf(mn, dpp<kQuadXor2>(mn));
+        mx = fmaxf(mx, dpp<kQuadXor2>(mx));
+        mn = fminf(mn, dpp<kHalfRowMirror>(mn));
+        mx = fmaxf(mx, dpp<kHalfRowMirror>(mx));
+        mn = mn + 0.0f; // -0 -> +0
+        mx = mx + 0.0f;
+        const float rng = mx - mn;
+        uint32_t word = 0;
+        float scale = 0.0f;
+        if (rng != 0.0f) {
+            scale = rng / 15.0f;          // correctly rounded (HIP default division)
+            const float inv = 15.0f / rng;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float t = f[i] - mn;
+                t = t * inv;
+                float r = __builtin_rintf(t); // ties to even
+                r = fminf(fmaxf(r, 0.0f), 15.0f);
+                word |= (uint32_t)r << (4 * i);
+            }
+        }
+        if (ok[u]) {
+            codes[slot[u] * (D / 8) + lir] = word;
+            if ((lir & 7) == 0) {
+                mins[slot[u] * G + (lir >> 3)] = mn;
+                scales[slot[u] * G + (lir >> 3)] = scale;
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Dense decode attention.
+//
+// Lane layout: a token row of d codes is d/2 bytes = LPT lanes x 16 bytes, so
+// one 16-byte load per lane covers TPW = 64/LPT tokens per wave (1 KB for
+// d = 128).  Lane `part` = lane % LPT owns elements 32*part..32*part+31 of
+// every token it visits (all inside group part/2); lane lt = lane / LPT walks
+// its own token sequence with a private online-softmax state.  The states of
+// the TPW token lanes are merged once at the end (log-sum-exp), then across
+// the waves sharing a (batch row, head), then (split > 1) by k_reduce.
+//
+// The dequantisation x = min + c*scale is folded out of the inner loops:
+//   q.x      = scale * sum q_i(64+c_i) + (min - 64*scale) * sum q_i
+//   sum p.x  = sum (p*scale)(64+c_i)   + sum p*(min - 64*scale)
+// so the per-element work is the nibble unpack plus one dot2 (K) or one
+// mixed-precision FMA (V).  Scores are kept in log2 units (z = s*log2e/sqrt(d)).
+// ===========================================================================
+template <int D, int U, int WPP>
+__global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ kc, const uint8_t *__restrict__ vc,
+                                                const float *__restrict__ kmin, const float *__restrict__ ksc,
+                                                const float *__restrict__ vmin, const float *__restrict__ vsc,
+                                                const uint4 *__restrict__ q, uint4 *__restrict__ out,
+                                                float *__restrict__ ws, int pairs, int S, int T, int splits,
+                                                int split_len, float c2)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+    constexpr int PPB = 4 / WPP;
+    constexpr int TPI = U * TPW;
+    __shared__ float sm_acc[WPP > 1 ? 4 : 1][WPP > 1 ? D : 1];
+    __shared__ float sm_ml[4][2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wp = wave % WPP;
+    const int pslot = wave / WPP;
+    const int split = blockIdx.x % splits;
+    const int pair = (blockIdx.x / splits) * PPB + pslot;
+    const bool pair_ok = pair < pairs;
+    const int64_t pc = pair_ok ? pair : pairs - 1;
+    const int part = lane % LPT;
+    const int lt = lane / LPT;
+    const int g = part >> 1;
+    const int t_begin = split * split_len;
+    const int t_end = min(T, t_begin + split_len);
+    const int n_tok = max(0, t_end - t_begin);
+    const int n_iter = (n_tok + WPP * TPI - 1) / (WPP * TPI);
+
+    const QSlice qs = load_q_slice(q + pc * (D / 8) + part * 4);
+    const uint32_t mg = magic64_vgpr();
+
+    const uint8_t *__restrict__ kb = kc + pc * S * (D / 2) + part * 16;
+    const uint8_t *__restrict__ vb = vc + pc * S * (D / 2) + part * 16;
+    const float *__restrict__ kmb = kmin + pc * S * G + g;
+    const float *__restrict__ ksb = ksc + pc * S * G + g;
+    const float *__restrict__ vmb = vmin + pc * S * G + g;
+    const float *__restrict__ vsb = vsc + pc * S * G + g;
+
+    float m = -INFINITY, l = 0.0f, bsum = 0.0f;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] = 0.0f;
+
+    for (int it = 0; it < n_iter; ++it) {
+        const int tb = t_begin + (it * WPP + wp) * TPI + lt;
+        uint4 kx[U], vx[U];
+        float km[U], ks[U], vm[U], vs[U];
+        bool valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + u * TPW;
+            valid[u] = t < t_end;
+            const int64_t tcl = valid[u] ? t : t_end - 1;
+            kx[u] = *reinterpret_cast<const uint4 *>(kb + tcl * (D / 2));
+            vx[u] = *reinterpret_cast<const uint4 *>(vb + tcl * (D / 2));
+            km[u] = kmb[tcl * G];
+            ks[u] = ksb[tcl * G];
+            vm[u] = vmb[tcl * G];
+            vs[u] = vsb[tcl * G];
+        }
+        float z[U];
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float dq = dot_biased(qs, kx[u], mg);
+            float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
+            sp = token_sum<LPT>(sp);
+            z[u] = valid[u] ? sp * c2 : -INFINITY;
+            mx = fmaxf(mx, z[u]);
+        }
+        const float mref = (mx == -INFINITY) ? 0.0f : mx;
+        if (__any(mx != m)) {
+            const float alpha = exp2_fast(m - mref);
+            l *= alpha;
+            bsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                acc[i] *= alpha;
+        }
+        m = mx;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = exp2_fast(z[u] - mref);
+            l += p;
+            bsum = __builtin_fmaf(p, __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
+            axpy_biased(acc, p * vs[u], vx[u], mg);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] += bsum;
+
+    // Merge the TPW token lanes that share `part`.
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+        const float mo = __shfl_xor(m, off);
+        const float lo = __shfl_xor(l, off);
+        const float M = fmaxf(m, mo);
+        const float Mr = (M == -INFINITY) ? 0.0f : M;
+        const float a1 = exp2_fast(m - Mr), a2 = exp2_fast(mo - Mr);
+        l = l * a1 + lo * a2;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            acc[i] = acc[i] * a1 + __shfl_xor(acc[i], off) * a2;
+        m = M;
+    }
+
+    if constexpr (WPP == 1) {
+        if (!pair_ok || lt != 0)
+            return;
+        if (splits == 1) {
+            const float inv = 1.0f / l;
+            uint32_t h[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const _Float16 lo16 = (_Float16)(acc[2 * i] * inv);
+                const _Float16 hi16 = (_Float16)(acc[2 * i + 1] * inv);
+                h[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo16) | ((uint32_t)__builtin_bit_cast(uint16_t, hi16) << 16);
+            }
+            uint4 *dst = out + pc * (D / 8) + part * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+        } else {
+            const int64_t item = (int64_t)split * pairs + pc;
+            if (part == 0) {
+                ws[item * 2] = m;
+                ws[item * 2 + 1] = l;
+            }
+            float4 *dst = reinterpret_cast<float4 *>(ws + (int64_t)2 * splits * pairs + item * D + part * 32);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                dst[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+        }
+    } else {
+        if (lt == 0) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                sm_acc[wave][part * 32 + i] = acc[i];
+            if (part == 0) {
+                sm_ml[wave][0] = m;
+                sm_ml[wave][1] = l;
+            }
+        }
+        __syncthreads();
+        if (wp != 0 || !pair_ok)
+            return;
+        const int w0 = pslot * WPP;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WPP; ++w)
+            M = fmaxf(M, sm_ml[w0 + w][0]);
+        const float Mr = (M == -INFINITY) ? 0.0f : M;
+        float wt[WPP];
+        float L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPP; ++w) {
+            wt[w] = exp2_fast(sm_ml[w0 + w][0] - Mr);
+            L += wt[w] * sm_ml[w0 + w][1];
+        }
+        if (splits == 1) {
+            const float inv = 1.0f / L;
+            _Float16 *dst = reinterpret_cast<_Float16 *>(out) + pc * D;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) {
+                float o = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPP; ++w)
+                    o += wt[w] * sm_acc[w0 + w][lane + 64 * j];
+                dst[lane + 64 * j] = (_Float16)(o * inv);
+            }
+        } else {
+            const int64_t item = (int64_t)split * pairs + pc;
+            if (lane == 0) {
+                ws[item * 2] = M;
+                ws[item * 2 + 1] = L;
+            }
+            float *dst = ws + (int64_t)2 * splits * pairs + item * D;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) {
+                float o = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPP; ++w)
+                    o += wt[w] * sm_acc[w0 + w][lane + 64 * j];
+                dst[lane + 64 * j] = o;
+            }
+        }
+    }
+}
+
+// Split-context reduce: one wave per (batch row, head).
+//   M = max m_k,  L = sum 2^(m_k-M) l_k,  out = sum 2^(m_k-M) o_k / L
+template <int D>
+__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ ws, _Float16 *__restrict__ out, int pairs,
+                                                int splits)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= pairs)
+        return;
+    const float *__restrict__ accp = ws + (int64_t)2 * splits * pairs;
+    float M = -INFINITY;
+    for (int k = 0; k < splits; ++k)
+        M = fmaxf(M, ws[((int64_t)k * pairs + pair) * 2]);
+    const float Mr = (M == -INFINITY) ? 0.0f : M;
+    float L = 0.0f;
+    float o[D / 64];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j)
+        o[j] = 0.0f;
+    for (int k = 0; k < splits; ++k) {
+        const int64_t item = (int64_t)k * pairs + pair;
+        const float w = exp2_fast(ws[item * 2] - Mr);
+        L += w * ws[item * 2 + 1];
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+            o[j] += w * accp[item * D + lane + 64 * j];
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j)
+        out[pair * D + lane + 64 * j] = (_Float16)(o[j] * inv);
+}
+
+// ===========================================================================
+// Top-k sparse decode attention: one 256-thread workgroup per (batch row,
+// head).  (1) every key is scored into LDS (same lane layout and folded codec
+// as k_decode); (2) the k-th largest score is found exactly by a 4-pass
+// 8-bit radix select on order-preserving 32-bit keys; (3) the kept tokens
+// (larger keys, plus the smallest-index ties) are compacted in ascending
+// token order; (4) softmax over the kept scores and P.V over their V rows.
+// ===========================================================================
+__device__ __forceinline__ uint32_t order_key(float z)
+{
+    const uint32_t b = __builtin_bit_cast(uint32_t, z + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int n = __shfl_up(v, off);
+        if (lane >= off)
+            v += n;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the 256 threads of the block (in thread order).
+__device__ __forceinline__ int block_excl_scan(int v, int *tmp4)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v, lane);
+    if (lane == 63)
+        tmp4[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w)
+        base += tmp4[w];
+    __syncthreads();
+    return base + incl - v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_topk(const uint8_t *__restrict__ kc, const uint8_t *__restrict__ vc,
+                                              const float *__restrict__ kmin, const float *__restrict__ ksc,
+                                              const float *__restrict__ vmin, const float *__restrict__ vsc,
+                                              const uint4 *__restrict__ q, _Float16 *__restrict__ out,
+                                              int32_t *__restrict__ sel_out, int S, int T, int k_top, float c2)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+    constexpr int U = 2;
+    extern __shared__ float sm_dyn[];
+    float *__restrict__ sc = sm_dyn;                                        // [T] scores, log2 units
+    uint16_t *__restrict__ sel = reinterpret_cast<uint16_t *>(sm_dyn + T);  // [k_top] kept tokens
+    __shared__ int hist[256];
+    __shared__ int tmp4[4];
+    __shared__ float red[4];
+    __shared__ float sm_acc[4][D];
+    __shared__ int sh_digit, sh_above;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t pair = blockIdx.x;
+    const int part = lane % LPT, lt = lane / LPT, g = part >> 1;
+
+    const QSlice qs = load_q_slice(q + pair * (D / 8) + part * 4);
+    const uint32_t mg = magic64_vgpr();
+    const uint8_t *__restrict__ kb = kc + pair * S * (D / 2) + part * 16;
+    const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
+    const float *__restrict__ kmb = kmin + pair * S * G + g;
+    const float *__restrict__ ksb = ksc + pair * S * G + g;
+    const float *__restrict__ vmb = vmin + pair * S * G + g;
+    const float *__restrict__ vsb = vsc + pair * S * G + g;
+
+    // (1) scores
+    float zmax = -INFINITY;
+    for (int t0 = wave * (U * TPW); t0 < T; t0 += 4 * U * TPW) {
+        uint4 kx[U];
+        float km[U], ks[U];
+        bool valid[U];
+        int tt[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            tt[u] = t0 + u * TPW + lt;
+            valid[u] = tt[u] < T;
+            const int64_t tcl = valid[u] ? tt[u] : T - 1;
+            kx[u] = *reinterpret_cast<const uint4 *>(kb + tcl * (D / 2));
+            km[u] = kmb[tcl * G];
+            ks[u] = ksb[tcl * G];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float dq = dot_biased(qs, kx[u], mg);
+            float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
+            sp = token_sum<LPT>(sp);
+            const float z = sp * c2;
+            if (valid[u]) {
+                zmax = fmaxf(zmax, z);
+                if (part == 0)
+                    sc[tt[u]] = z;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        zmax = fmaxf(zmax, __shfl_xor(zmax, off));
+    if (lane == 0)
+        red[wave] = zmax;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+    // (2) radix select of the k_top-th largest key
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = k_top;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        for (int t = tid; t < T; t += 256) {
+            const uint32_t key = order_key(sc[t]);
+            if ((key & pmask) == prefix)
+                atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
+        __syncthreads();
+        const int cnt = hist[255 - tid];           // thread i looks at digit 255-i
+        const int before = block_excl_scan(cnt, tmp4); // keys with a larger digit
+        if (before < remaining && remaining <= before + cnt) {
+            sh_digit = 255 - tid;
+            sh_above = before;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh_digit << shift;
+        pmask |= 255u << shift;
+        remaining -= sh_above;
+        __syncthreads();
+    }
+    const uint32_t thr = prefix; // exact key of the k_top-th largest score
+    // `remaining` keys equal to thr are kept: the ones with the smallest index.
+
+    // (3) compaction in ascending token order: thread tid owns a contiguous chunk
+    const int chunk = (T + 255) / 256;
+    const int c0 = min(T, tid * chunk), c1 = min(T, c0 + chunk);
+    int neq = 0;
+    for (int t = c0; t < c1; ++t)
+        neq += order_key(sc[t]) == thr;
+    const int eq_before = block_excl_scan(neq, tmp4);
+    int nsel = 0;
+    {
+        int e = eq_before;
+        for (int t = c0; t < c1; ++t) {
+            const uint32_t key = order_key(sc[t]);
+            const bool keep = key > thr || (key == thr && e < remaining);
+            e += key == thr;
+            nsel += keep;
+        }
+    }
+    int pos = block_excl_scan(nsel, tmp4);
+    {
+        int e = eq_before;
+        for (int t = c0; t < c1; ++t) {
+            const uint32_t key = order_key(sc[t]);
+            const bool keep = key > thr || (key == thr && e < remaining);
+            e += key == thr;
+            if (keep)
+                sel[pos++] = (uint16_t)t;
+        }
+    }
+    __syncthreads();
+
+    // (4) softmax over the kept scores and P.V over their V rows
+    const float Mr = M;
+    float l = 0.0f, bsum = 0.0f;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] = 0.0f;
+    for (int j0 = wave * TPW; j0 < k_top; j0 += 4 * TPW) {
+        const int j = j0 + lt;
+        const bool valid = j < k_top;
+        const int64_t t = sel[valid ? j : k_top - 1];
+        const uint4 vx = *reinterpret_cast<const uint4 *>(vb + t * (D / 2));
+        const float vm = vmb[t * G], vs = vsb[t * G];
+        const float p = valid ? exp2_fast(sc[t] - Mr) : 0.0f;
+        l += p;
+        bsum = __builtin_fmaf(p, __builtin_fmaf(-kBias, vs, vm), bsum);
+        axpy_biased(acc, p * vs, vx, mg);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] += bsum;
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+        l += __shfl_xor(l, off);
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            acc[i] += __shfl_xor(acc[i], off);
+    }
+    if (lt == 0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            sm_acc[wave][part * 32 + i] = acc[i];
+        if (part == 0)
+            red[wave] = l;
+    }
+    __syncthreads();
+    const float L = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / L;
+    for (int i = tid; i < D; i += 256)
+        out[pair * D + i] = (_Float16)((sm_acc[0][i] + sm_acc[1][i] + sm_acc[2][i] + sm_acc[3][i]) * inv);
+    if (sel_out != nullptr)
+        for (int j = tid; j < k_top; j += 256)
+            sel_out[pair * k_top + j] = sel[j];
+}
+
+// ---------------------------------------------------------------------------
+template <int D>
+int launch_quantize_d(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
+                      hipStream_t st)
+{
+    const int64_t rows = (int64_t)b * c.a * s_src;
+    const int R = (s_src == 1) ? 1 : 4;
+    const int64_t rows_per_block = (int64_t)(256 / (D / 8)) * R;
+    const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block), 2);
+    auto *kc = reinterpret_cast<uint32_t *>(c.k_codes);
+    auto *vc = reinterpret_cast<uint32_t *>(c.v_codes);
+    const auto *ks = static_cast<const uint4 *>(k);
+    const auto *vs = static_cast<const uint4 *>(v);
+    if (R == 1)
+        hipLaunchKernelGGL((k_quantize<D, 1>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc, vc,
+                           c.k_min, c.k_scale, c.v_min, c.v_scale);
+    else
+        hipLaunchKernelGGL((k_quantize<D, 4>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc, vc,
+                           c.k_min, c.k_scale, c.v_min, c.v_scale);
+    return (int)hipGetLastError();
+}
+
+template <int D, int U, int WPP>
+int launch_decode_k(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
+                    float *ws, hipStream_t st)
+{
+    constexpr int PPB = 4 / WPP;
+    const float c2 = 1.4426950408889634f / sqrtf((float)D);
+    const int64_t blocks = (int64_t)((pairs + PPB - 1) / PPB) * sh.splits;
+    hipLaunchKernelGGL((k_decode<D, U, WPP>), dim3((unsigned)blocks), dim3(256), 0, st, c.k_codes, c.v_codes,
+                       c.k_min, c.k_scale, c.v_min, c.v_scale, static_cast<const uint4 *>(q),
+                       static_cast<uint4 *>(out), ws, pairs, c.S, T, sh.splits, sh.split_len, c2);
+    int e = (int)hipGetLastError();
+    if (e != 0 || sh.splits == 1)
+        return e;
+    hipLaunchKernelGGL((k_reduce<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, ws,
+                       static_cast<_Float16 *>(out), pairs, sh.splits);
+    return (int)hipGetLastError();
+}
+
+template <int D, int U>
+int launch_decode_u(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
+                    float *ws, hipStream_t st)
+{
+    switch (sh.waves_per_pair) {
+    case 1: return launch_decode_k<D, U, 1>(c, pairs, q, T, out, sh, ws, st);
+    case 2: return launch_decode_k<D, U, 2>(c, pairs, q, T, out, sh, ws, st);
+    default: return launch_decode_k<D, U, 4>(c, pairs, q, T, out, sh, ws, st);
+    }
+}
+
+template <int D>
+int launch_decode_d(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
+                    float *ws, hipStream_t st)
+{
+    switch (sh.unroll) {
+    case 1: return launch_decode_u<D, 1>(c, pairs, q, T, out, sh, ws, st);
+    case 2: return launch_decode_u<D, 2>(c, pairs, q, T, out, sh, ws, st);
+    default: return launch_decode_u<D, 4>(c, pairs, q, T, out, sh, ws, st);
+    }
+}
+
+template <int D>
+int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
+                  hipStream_t st)
+{
+    const float c2 = 1.4426950408889634f / sqrtf((float)D);
+    const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
+    hipLaunchKernelGGL((k_topk<D>), dim3((unsigned)pairs), dim3(256), lds, st, c.k_codes, c.v_codes, c.k_min,
+                       c.k_scale, c.v_min, c.v_scale, static_cast<const uint4 *>(q), static_cast<_Float16 *>(out),
+                       sel, c.S, T, k_top, c2);
+    return (int)hipGetLastError();
+}
+
+} // namespace
+
+int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
+                    hipStream_t st)
+{
+    switch (c.d) {
+    case 64: return launch_quantize_d<64>(c, k, v, b, s_src, t_dst0, st);
+    case 128: return launch_quantize_d<128>(c, k, v, b, s_src, t_dst0, st);
+    default: return launch_quantize_d<256>(c, k, v, b, s_src, t_dst0, st);
+    }
+}
+
+int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
+                  float *ws, hipStream_t st)
+{
+    switch (c.d) {
+    case 64: return launch_decode_d<64>(c, pairs, q, T, out, sh, ws, st);
+    case 128: return launch_decode_d<128>(c, pairs, q, T, out, sh, ws, st);
+    default: return launch_decode_d<256>(c, pairs, q, T, out, sh, ws, st);
+    }
+}
+
+size_t decode_ws_floats(int pairs, int d, int splits)
+{
+    return splits > 1 ? (size_t)splits * (size_t)pairs * (size_t)(d + 2) : 0;
+}
+
+int decode_tokens_per_iter(int d, int unroll, int waves_per_pair) { return (64 / (d / 32)) * unroll * waves_per_pair; }
+
+int launch_topk(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
+                hipStream_t st)
+{
+    switch (c.d) {
+    case 64: return launch_topk_d<64>(c, pairs, q, T, k_top, out, sel, st);
+    case 128: return launch_topk_d<128>(c, pairs, q, T, k_top, out, sel, st);
+    default: return launch_topk_d<256>(c, pairs, q, T, k_top, out, sel, st);
+    }
+}
+
+} // namespace kvq

@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (kvq4_api.cpp) and the HIP
+// kernels (kvq4_kernels.hip).  Arguments are already validated when these
+// are called; each returns a hipError_t cast to int (0 = launched).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace kvq {
+
+struct CachePlanes {
+    uint8_t *k_codes, *v_codes;
+    float *k_min, *k_scale, *v_min, *v_scale;
+    int a;       // heads
+    int d;       // head_dim (64, 128 or 256)
+    int S;       // token slots per (batch row, head)
+};
+
+// Quantise b*a*s_src token rows of fp16 K and V ([b][s_src][a][d]) into
+// slots t_dst0 .. t_dst0+s_src-1.  Covers both the prompt (t_dst0 = 0) and
+// the one-token append (s_src = 1, t_dst0 = pos).
+int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
+                    hipStream_t st);
+
+// Dense decode attention.  splits ranges of split_len tokens each; when
+// splits > 1 the partial (max, sum, unnormalised output) go to ws and the
+// reduce pass writes out.
+struct DecodeShape {
+    int unroll;          // tokens per lane per iteration: 1, 2, 4
+    int waves_per_pair;  // 1, 2, 4
+    int splits;
+    int split_len;
+};
+int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
+                  float *ws, hipStream_t st);
+
+// Workspace floats needed by launch_decode for `splits` > 1.
+size_t decode_ws_floats(int pairs, int d, int splits);
+
+// Tokens one workgroup iteration covers (for the split heuristic).
+int decode_tokens_per_iter(int d, int unroll, int waves_per_pair);
+
+// Top-k sparse decode attention, one workgroup per (batch row, head).
+int launch_topk(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
+                hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,128 @@
+"""Helpers shared by the GPU parity tests: move tensors to the oracle, compare.
+
+The oracle only ever receives the fp16 inputs (copied to the host) and its own
+quantised planes; nothing produced by the HIP path is fed back into it.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+ATOL = 2e-3
+RTOL = 1e-2
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU (run with -m 'not gpu' on CPU)"
+
+
+def f16_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().numpy().view(np.uint16)
+
+
+def oracle_planes_from_prompt(k: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Prompt rows [b][s][a][d] (fp16 bits) -> oracle planes in cache order [b][a][s][...]."""
+    codes, mins, scales = oracle.quantize_rows(k)
+    return (np.ascontiguousarray(codes.transpose(0, 2, 1, 3)), np.ascontiguousarray(mins.transpose(0, 2, 1, 3)),
+            np.ascontiguousarray(scales.transpose(0, 2, 1, 3)))
+
+
+def oracle_row(x: np.ndarray):
+    """New-token rows [b][1][a][d] -> oracle planes [b][a][...] of that slot."""
+    codes, mins, scales = oracle.quantize_rows(x[:, 0])
+    return codes, mins, scales
+
+
+def assert_bits_equal(gpu: torch.Tensor, ref: np.ndarray, what: str):
+    g = gpu.detach().cpu().contiguous().numpy()
+    if g.dtype == np.float32:
+        g = g.view(np.uint32)
+        ref = np.ascontiguousarray(ref, np.float32).view(np.uint32)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    bad = np.argwhere(g != ref)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:3].tolist()}: gpu {g[tuple(bad[0])]} ref {ref[tuple(bad[0])]}"
+
+
+class HostCache:
+    """The oracle's own copy of a layer's planes, [b][a][S][...], filled from inputs."""
+
+    def __init__(self, b, a, d, S):
+        G = d // 64
+        self.kc = np.zeros((b, a, S, d // 2), np.uint8)
+        self.vc = np.zeros((b, a, S, d // 2), np.uint8)
+        self.kmin = np.zeros((b, a, S, G), np.float32)
+        self.ksc = np.zeros((b, a, S, G), np.float32)
+        self.vmin = np.zeros((b, a, S, G), np.float32)
+        self.vsc = np.zeros((b, a, S, G), np.float32)
+
+    def prefill(self, k: np.ndarray, v: np.ndarray, pairs=None):
+        """k, v: [b][s][a][d] fp16 bits.  pairs: optional list of (bi, ai) to quantise only."""
+        s = k.shape[1]
+        if pairs is None:
+            kc, km, ks = oracle_planes_from_prompt(k)
+            vc, vm, vs = oracle_planes_from_prompt(v)
+            self.kc[:, :, :s], self.kmin[:, :, :s], self.ksc[:, :, :s] = kc, km, ks
+            self.vc[:, :, :s], self.vmin[:, :, :s], self.vsc[:, :, :s] = vc, vm, vs
+        else:
+            for bi, ai in pairs:
+                c, m, sc = oracle.quantize_rows(np.ascontiguousarray(k[bi, :, ai]))
+                self.kc[bi, ai, :s], self.kmin[bi, ai, :s], self.ksc[bi, ai, :s] = c, m, sc
+                c, m, sc = oracle.quantize_rows(np.ascontiguousarray(v[bi, :, ai]))
+                self.vc[bi, ai, :s], self.vmin[bi, ai, :s], self.vsc[bi, ai, :s] = c, m, sc
+
+    def append(self, k_new: np.ndarray, v_new: np.ndarray, pos: int):
+        c, m, s = oracle_row(k_new)
+        self.kc[:, :, pos], self.kmin[:, :, pos], self.ksc[:, :, pos] = c, m, s
+        c, m, s = oracle_row(v_new)
+        self.vc[:, :, pos], self.vmin[:, :, pos], self.vsc[:, :, pos] = c, m, s
+
+    def head(self, bi, ai, T):
+        return oracle.HeadCache(self.kc[bi, ai, :T], self.kmin[bi, ai, :T], self.ksc[bi, ai, :T], self.vc[bi, ai, :T],
+                                self.vmin[bi, ai, :T], self.vsc[bi, ai, :T])
+
+
+def _pool():
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    return cf.ThreadPoolExecutor(n)
+
+
+def oracle_attend_pairs(hc: HostCache, q: np.ndarray, T: int, pairs) -> np.ndarray:
+    """Dense oracle output for the given (bi, ai) pairs; q [b][1][a][d] fp16 bits."""
+    with _pool() as ex:
+        outs = list(ex.map(lambda p: oracle.attend(np.ascontiguousarray(q[p[0], 0, p[1]]), hc.head(p[0], p[1], T), T),
+                           pairs))
+    return np.stack(outs)
+
+
+def assert_close(gpu_rows: np.ndarray, ref_rows: np.ndarray, what: str):
+    """|gpu - ref| <= ATOL + RTOL*|ref| element-wise (ref = fp64 oracle)."""
+    g = gpu_rows.astype(np.float64)
+    err = np.abs(g - ref_rows)
+    lim = ATOL + RTOL * np.abs(ref_rows)
+    bad = np.argwhere(~(err <= lim))
+    maxabs = float(err.max()) if err.size else 0.0
+    assert bad.size == 0, (f"{what}: {len(bad)} elements out of tolerance, max abs err {maxabs:.3g}, "
+                           f"first {bad[:3].tolist()}")
+    return maxabs
+
+
+def all_pairs(b, a):
+    return [(bi, ai) for bi in range(b) for ai in range(a)]
+
+
+def sample_pairs(b, a, n, seed):
+    r = np.random.default_rng(seed)
+    idx = r.choice(b * a, size=min(n, b * a), replace=False)
+    ps = {(0, 0), (b - 1, a - 1)} | {(int(i) // a, int(i) % a) for i in idx}
+    return sorted(ps)

@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before anything is
+enqueued (every call below fails validation, so no HIP launch happens).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_kv_cache_prefill_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq4.h")
+
+KVQ_OK, KVQ_EINVAL, KVQ_ERANGE, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_ELAUNCH = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000  # aligned, non-null; never dereferenced because validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return kvq.load_library()
+
+
+def test_header_declares_the_four_calls():
+    fns = declared_functions()
+    for f in ("kv_quantize_prefill", "kv_append_quant", "decode_attention_q4", "decode_attention_q4_topk"):
+        assert f in fns
+    assert set(kvq.EXPORTED) == set(fns)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for f in declared_functions():
+        assert hasattr(L, f), f
+
+
+def test_library_links_no_oracle():
+    data = open(kvq.library_path(), "rb").read()
+    assert b"oracle_" not in data
+
+
+def dims(b=2, a=2, h=128, s=16, n=4, group=64, meta=0):
+    return kvq.KvqDims(b, a, h, s, n, group, meta)
+
+
+def cache(d=None, ptrs=(FAKE,) * 6):
+    d = dims() if d is None else d
+    return kvq.KvqCache(d, *ptrs)
+
+
+def test_cache_bytes_closed_form(L):
+    """One layer: codes = 2 planes x 0.5 byte x h x (s+n) x b (the blog's KV-cache size with
+    precision 0.5 and one layer); metadata = (h/64) groups x 4 bytes, per plane."""
+    for (b, a, h, s, n) in [(2, 2, 128, 16, 4), (144, 96, 12288, 512, 32), (256, 56, 7168, 512, 32)]:
+        cb, mb = kvq.kvq_cache_bytes(b, a, h, s, n)
+        assert 2 * cb == 2 * 0.5 * h * (s + n) * b
+        assert mb == b * (s + n) * (h // 64) * 4
+
+
+@pytest.mark.parametrize("mut,status", [
+    (dict(b=0), KVQ_EINVAL), (dict(a=0), KVQ_EINVAL), (dict(h=100), KVQ_EINVAL), (dict(s=0), KVQ_EINVAL),
+    (dict(h=2 * 96), KVQ_EINVAL), (dict(group=32), KVQ_EUNSUPPORTED), (dict(meta=1), KVQ_EUNSUPPORTED),
+    (dict(h=2 * 192), KVQ_EUNSUPPORTED), (dict(h=2 * 512), KVQ_EUNSUPPORTED), (dict(n=-1), KVQ_EINVAL),
+])
+def test_bad_dims(L, mut, status):
+    d = dims(**mut)
+    cb = ctypes.c_size_t()
+    assert L.kvq_cache_bytes(ctypes.byref(d), ctypes.byref(cb), None) == status
+    c = cache(d)
+    st = ctypes.c_void_p(0)
+    assert L.kv_quantize_prefill(ctypes.byref(c), FAKE, FAKE, 4, st) == status
+    assert L.kv_append_quant(ctypes.byref(c), FAKE, FAKE, 0, st) == status
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4, FAKE, 0, None, 0, st) == status
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, FAKE, None, None, 0, st) == status
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 4, 0, 0) == 0
+
+
+def test_null_and_misaligned_pointers(L):
+    st = ctypes.c_void_p(0)
+    assert L.kv_quantize_prefill(None, FAKE, FAKE, 4, st) == KVQ_EINVAL
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = 0
+        assert L.kv_quantize_prefill(ctypes.byref(cache(ptrs=ptrs)), FAKE, FAKE, 4, st) == KVQ_EINVAL
+        ptrs[i] = FAKE + 4
+        assert L.decode_attention_q4(ctypes.byref(cache(ptrs=ptrs)), FAKE, 4, FAKE, 0, None, 0, st) == KVQ_EINVAL
+    c = cache()
+    assert L.kv_quantize_prefill(ctypes.byref(c), None, FAKE, 4, st) == KVQ_EINVAL
+    assert L.kv_quantize_prefill(ctypes.byref(c), FAKE, FAKE + 2, 4, st) == KVQ_EINVAL
+    assert L.kv_append_quant(ctypes.byref(c), FAKE, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4(ctypes.byref(c), None, 4, FAKE, 0, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4, FAKE + 8, 0, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, None, None, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, FAKE, FAKE + 2, None, 0, st) == KVQ_EINVAL
+
+
+def test_ranges(L):
+    st = ctypes.c_void_p(0)
+    c = cache()  # S = 20
+    assert L.kv_quantize_prefill(ctypes.byref(c), FAKE, FAKE, 0, st) == KVQ_ERANGE
+    assert L.kv_quantize_prefill(ctypes.byref(c), FAKE, FAKE, 21, st) == KVQ_ERANGE
+    assert L.kv_append_quant(ctypes.byref(c), FAKE, FAKE, -1, st) == KVQ_ERANGE
+    assert L.kv_append_quant(ctypes.byref(c), FAKE, FAKE, 20, st) == KVQ_ERANGE
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 0, FAKE, 0, None, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 21, FAKE, 0, None, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4, FAKE, -1, None, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4, FAKE, 257, None, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4_tuned(ctypes.byref(c), FAKE, 4, FAKE, 1, 3, 1, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_tuned(ctypes.byref(c), FAKE, 4, FAKE, 1, 2, 8, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 10, 0, FAKE, None, None, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 10, 11, FAKE, None, None, 0, st) == KVQ_ERANGE
+    big = cache(dims(s=9000, n=0))
+    assert L.decode_attention_q4_topk(ctypes.byref(big), FAKE, 8193, 5, FAKE, None, None, 0, st) == KVQ_EUNSUPPORTED
+
+
+def test_workspace_sizing_and_enospace(L):
+    st = ctypes.c_void_p(0)
+    d = dims(b=1, a=1, h=128, s=4000, n=96)
+    c = cache(d)
+    # one split: no workspace
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 100, 1, 0) == 0
+    # explicit splits: splits x pairs x (d + 2) floats
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 4096, 7, 0) == 7 * 1 * 130 * 4
+    # automatic: a single (batch row, head) with a long context is split
+    auto = L.kvq_workspace_bytes(ctypes.byref(d), 4096, 0, 0)
+    assert auto > 0 and auto % (130 * 4) == 0
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4096, FAKE, 7, FAKE, 7 * 130 * 4 - 4, st) == KVQ_ENOSPACE
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4096, FAKE, 7, None, 0, st) == KVQ_ENOSPACE
+    # the top-k path needs no workspace
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 2048, 0, 205) == 0
+
+
+def test_strerror(L):
+    for s in (0, -1, -2, -3, -4, -5, -99):
+        assert len(L.kvq_strerror(s)) > 0
