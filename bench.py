@@ -1,0 +1,348 @@
+"""Benchmark of the int4 KV-cache path on one MI355X.
+
+One step is the whole hot path over one batch of the OPT-175B layer shape
+(b=144, a=96, d=128, h=12288, prompt s=512, n=32 generated tokens, 96 layers
+whose int4 caches stay resident in HBM):
+
+  * prefill: kv_quantize_prefill of every layer's prompt K and V;
+  * decode:  for j = 1..32, for every layer: kv_append_quant at slot s+j-1,
+             then decode_attention_q4 over s+j tokens.
+
+value = algorithmic HBM bytes of the step / step time (GB/s).  Algorithmic
+bytes: quantise 2 B in + 0.5 B codes + 0.125 B metadata per element; decode
+attention 160 B per (batch row, head, token) (64 B K codes + 64 B V codes +
+32 B fp32 min/scale) plus q and out; append as quantise on one token.  The
+decode attention kernel is timed live with HIP events on the stream it runs
+on; its achieved bandwidth against the 8 TB/s HBM peak is the `roofline`
+entry.  The sparse top-10% variant is timed on its own workload (b=32, a=96,
+context 2048) and reported beside it.  `cpu_baseline` times the CPU oracle
+on a bounded sample of the same job.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention int4-KV HBM GB/s (% of peak) + layer-tokens/s, OPT-175B shape"
+HBM_PEAK_GBS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k_decode_opt175b_pmc.md")
+KERNEL_SRC = os.path.join(ROOT, "quantized_kv_cache_prefill_amd", "csrc", "kvq4_kernels.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic bytes
+def bytes_quantize(rows: int, d: int) -> int:
+    """fp16 in (2 B/elem) + codes (0.5 B/elem) + fp32 min and scale per 64 elements."""
+    return rows * d * 2 + rows * d // 2 + rows * (d // 64) * 8
+
+
+def bytes_decode(pairs: int, T: int, d: int) -> int:
+    """K and V codes + fp32 min/scale for T tokens, plus q and out (fp16)."""
+    per_token = d + 4 * 4 * (d // 64)          # 2 * d/2 code bytes + 4 fp32 per group
+    return pairs * (T * per_token + 2 * d * 2)
+
+
+def bytes_topk(pairs: int, T: int, k: int, d: int) -> int:
+    """All K (codes + metadata), the k kept V rows, q, out and the kept indices."""
+    half = d // 2 + 2 * 4 * (d // 64)
+    return pairs * ((T + k) * half + 2 * d * 2 + 4 * k)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """Measured HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(PROFILE_PMC) as f:
+            for line in f:
+                if line.startswith("<!-- traffic "):
+                    rec = json.loads(line[len("<!-- traffic "):].rsplit("-->", 1)[0])
+                    if rec.get("kernel_source_sha256_16") == kernel_source_hash():
+                        return rec
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------- GPU job
+class Job:
+    def __init__(self, args):
+        import torch
+
+        import quantized_kv_cache_prefill_amd as kvq
+        import workloads as W
+
+        self.torch, self.kvq, self.W = torch, kvq, W
+        w = self.w = W.OPT_175B
+        self.L = args.layers or w.layers
+        self.n = args.decode_steps or w.n
+        dev = self.dev = "cuda"
+        torch.cuda.set_device(0)
+        log(f"[bench] allocating {self.L} int4 caches of b={w.b} a={w.a} d={w.d} S={w.S}")
+        self.caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=dev) for _ in range(self.L)]
+        # prompt K/V: a few distinct seeded buffers used in rotation (one layer's prompt is 3.6 GB)
+        self.n_prompt = min(4, self.L)
+        self.prompts = [W.prefill_kv(w, l, dev) for l in range(self.n_prompt)]
+        # decode inputs for every (layer, step): q, k_new, v_new [b][1][a][d]
+        log(f"[bench] generating decode inputs for {self.L} layers x {self.n} steps")
+        self.dec = []
+        for l in range(self.L):
+            per = []
+            for j in range(1, self.n + 1):
+                per.append(W.decode_inputs(w, l, j, dev))
+            self.dec.append(per)
+        self.out = torch.empty((self.L, w.b, 1, w.a, w.d), dtype=torch.float16, device=dev)
+        self.stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        # algorithmic bytes of one step
+        pairs = w.b * w.a
+        self.b_prefill = 2 * self.L * bytes_quantize(w.b * w.a * w.s, w.d)
+        self.b_append = 2 * self.L * self.n * bytes_quantize(pairs, w.d)
+        self.b_decode_per_launch = [bytes_decode(pairs, w.s + j, w.d) for j in range(1, self.n + 1)]
+        self.b_decode = self.L * sum(self.b_decode_per_launch)
+        self.b_step = self.b_prefill + self.b_append + self.b_decode
+
+    def step(self, events=None):
+        kvq, w = self.kvq, self.w
+        for l in range(self.L):
+            k, v = self.prompts[l % self.n_prompt]
+            kvq.kv_quantize_prefill(self.caches[l], k, v)
+        for j in range(1, self.n + 1):
+            for l in range(self.L):
+                q, kn, vn = self.dec[l][j - 1]
+                kvq.kv_append_quant(self.caches[l], kn, vn, w.s + j - 1)
+                if events is not None:
+                    e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+                    e0.record(self.stream)
+                kvq.decode_attention_q4(self.caches[l], q, w.s + j, out=self.out[l])
+                if events is not None:
+                    e1.record(self.stream)
+                    events.append((e0, e1, self.b_decode_per_launch[j - 1]))
+
+
+def time_topk(reps: int = 20):
+    """Sparse top-10% decode attention on b=32, a=96, context 2048 (k = 205)."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    w = W.SPARSE
+    T = w.s + w.n
+    k_top = w.k_top(T)
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda")
+    k, v = W.prefill_kv(w, 0, "cuda")
+    kvq.kv_quantize_prefill(cache, k, v)
+    q, kn, vn = W.decode_inputs(w, 0, 1, "cuda")
+    kvq.kv_append_quant(cache, kn, vn, w.s)
+    del k, v
+    out = torch.empty_like(q)
+    sel = torch.empty((w.b, w.a, k_top), dtype=torch.int32, device="cuda")
+    # a second cache-sized buffer is touched between launches so the 256 MB
+    # Infinity Cache cannot serve a repeat of the same K planes
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    times = []
+    st = torch.cuda.current_stream()
+    for r in range(reps + 3):
+        flush.add_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        kvq.decode_attention_q4_topk(cache, q, T, k_top, out=out, sel_idx=sel)
+        e1.record(st)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in times[3:]]
+    ms.sort()
+    med = ms[len(ms) // 2]
+    nbytes = bytes_topk(w.b * w.a, T, k_top, w.d)
+    dense_bytes = bytes_decode(w.b * w.a, T, w.d)
+    return {"workload": f"sparse top-10%: b={w.b} a={w.a} d={w.d} context {T}, k={k_top}",
+            "ms_per_launch_median": round(med, 4), "algorithmic_bytes": nbytes,
+            "gbs": round(nbytes / med / 1e6, 1), "frac_of_hbm_peak": round(nbytes / med / 1e6 / HBM_PEAK_GBS, 4),
+            "dense_equivalent_bytes": dense_bytes}
+
+
+def hbm_ceilings():
+    """Practical HBM ceilings from plain torch kernels on 4 GiB: a device copy (read + write
+    bytes / time) and a max-reduction (read bytes / time)."""
+    import torch
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    af = a.view(torch.float32)
+
+    def best_ms(fn):
+        ms = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return min(ms[1:])
+
+    copy_gbs = 2 * n / best_ms(lambda: b.copy_(a)) / 1e6
+    read_gbs = n / best_ms(lambda: torch.amax(af)) / 1e6
+    del a, b, af
+    return {"copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1)}
+
+
+# ------------------------------------------------------------- CPU baseline
+def cpu_baseline(budget_s: float = 12.0):
+    """The oracle on a sample of the same job: for a sample of (batch row, head) pairs of
+    one OPT-175B layer, quantise the 512-token prompt, then 32 decode steps of append +
+    dense attention.  Pairs are spread over a thread pool (ctypes releases the GIL)."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    w = W.OPT_175B
+    r = np.random.default_rng(1234)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.lib()
+
+    G = w.d // 64
+
+    def one_pair(seed):
+        rr = np.random.default_rng(seed)
+        K = rr.standard_normal((w.S, w.d)).astype(np.float16)
+        V = rr.standard_normal((w.S, w.d)).astype(np.float16)
+        Q = rr.standard_normal((w.n, w.d)).astype(np.float16)
+        t0 = time.perf_counter()
+        planes = []
+        for X in (K, V):
+            c, m, s = (np.zeros((w.S, w.d // 2), np.uint8), np.zeros((w.S, G), np.float32),
+                       np.zeros((w.S, G), np.float32))
+            c[:w.s], m[:w.s], s[:w.s] = oracle.quantize_rows(X[:w.s])
+            planes.append((c, m, s))
+        for j in range(1, w.n + 1):
+            pos = w.s + j - 1
+            for X, (c, m, s) in zip((K, V), planes):
+                c[pos:pos + 1], m[pos:pos + 1], s[pos:pos + 1] = oracle.quantize_rows(X[pos:pos + 1])
+            oracle.attend(Q[j - 1], oracle.HeadCache(*planes[0], *planes[1]), pos + 1)
+        return time.perf_counter() - t0
+
+    # calibrate on one parallel batch (one pair per thread), then size the sample to the budget
+    with cf.ThreadPoolExecutor(cores) as ex:
+        tb = time.perf_counter()
+        list(ex.map(one_pair, list(r.integers(0, 2**31, cores))))
+        batch = time.perf_counter() - tb
+        n_pairs = int(min(w.b * w.a, max(1, budget_s / max(batch, 1e-3)) * cores))
+        seeds = list(r.integers(0, 2**31, n_pairs))
+        t0 = time.perf_counter()
+        list(ex.map(one_pair, seeds))
+        wall = time.perf_counter() - t0
+    per_pair_bytes = (2 * bytes_quantize(w.s, w.d) + w.n * 2 * bytes_quantize(1, w.d)
+                      + sum(bytes_decode(1, w.s + j, w.d) for j in range(1, w.n + 1)))
+    gbs = n_pairs * per_pair_bytes / wall / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{n_pairs} of the {w.b * w.a} (batch row, head) pairs of one OPT-175B layer: "
+                       f"prompt quantise (512 tokens) + 32 x (append + dense attention, context 513..544); "
+                       f"{wall:.1f} s wall on {cores} threads"),
+            "layer_tokens_per_s": round(n_pairs / w.a * w.n / wall, 3)}
+
+
+# --------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=0, help="layers in the stack (default: the workload's 96)")
+    ap.add_argument("--decode-steps", type=int, default=0, help="decode steps per job (default 32)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-topk", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step and this build runs on "
+              "a single MI355X.  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    job = Job(args)
+    w = job.w
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        job.step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        job.step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    dec_ms = [a.elapsed_time(b) for a, b, _ in events]
+    dec_bytes = [nb for _, _, nb in events]
+    avg_ms = sum(dec_ms) / len(dec_ms)
+    avg_bytes = sum(dec_bytes) / len(dec_bytes)
+    achieved = avg_bytes / avg_ms / 1e6
+    decode_ms_per_step = sum(dec_ms) / args.steps
+    value = job.b_step / (ms_step / 1e3) / 1e9
+
+    traffic = stored_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic["bytes_per_launch"] if traffic else None,
+                "kernel": "k_decode<128,4,2> (decode_attention_q4)",
+                "algorithmic_bytes_per_launch": int(avg_bytes),
+                "avg_launch_ms": round(avg_ms, 5), "launches_timed": len(events)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"OPT-175B layer stack: b={w.b} a={w.a} d={w.d} h={w.h}, prompt {w.s}, "
+                               f"{job.n} decode steps, {job.L} int4 caches resident",
+                   "b": w.b, "a": w.a, "d": w.d, "h": w.h, "s": w.s, "n": job.n, "layers": job.L,
+                   "step": "prefill quantise all layers + n x (append + decode attention) all layers",
+                   "parallelism": "1 GPU"},
+        "roofline": roofline,
+        "decode_attention": {"gbs": round(achieved, 1), "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+                             "layer_tokens_per_s": round(w.b / (avg_ms / 1e3), 1),
+                             "stack_tokens_per_s": round(w.b * job.n / (decode_ms_per_step / 1e3), 1)},
+        "step_bytes": {"prefill": job.b_prefill, "append": job.b_append, "decode": job.b_decode},
+    }
+    log(f"[bench] step {ms_step:.1f} ms, decode kernel {achieved:.0f} GB/s")
+    if not args.no_topk:
+        log("[bench] sparse top-k leg")
+        res["sparse_topk"] = time_topk()
+    del job
+    torch.cuda.empty_cache()
+    res["hbm_ceilings"] = hbm_ceilings()
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

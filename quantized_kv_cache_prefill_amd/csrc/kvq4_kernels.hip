@@ -235,6 +235,71 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
     }
 }
 
+// One iteration of the dense decode loop for one lane: UU tokens spaced TPW
+// apart starting at token tb (tokens >= t_end are masked; their loads are
+// clamped to t_end-1 so they stay inside the written cache).  Updates the
+// lane's online-softmax state (m, l in log2 units; bsum collects the folded
+// min terms; acc the biased P.V sums).
+struct CacheRow {
+    const uint8_t *__restrict__ kb;
+    const uint8_t *__restrict__ vb;
+    const float *__restrict__ kmb;
+    const float *__restrict__ ksb;
+    const float *__restrict__ vmb;
+    const float *__restrict__ vsb;
+};
+
+template <int D, int UU>
+__device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
+                                            float c2, float &m, float &l, float &bsum, float (&acc)[32])
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+    uint4 kx[UU], vx[UU];
+    float km[UU], ks[UU], vm[UU], vs[UU];
+    bool valid[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const int t = tb + u * TPW;
+        valid[u] = t < t_end;
+        const int64_t tcl = valid[u] ? t : t_end - 1;
+        kx[u] = *reinterpret_cast<const uint4 *>(cr.kb + tcl * (D / 2));
+        vx[u] = *reinterpret_cast<const uint4 *>(cr.vb + tcl * (D / 2));
+        km[u] = cr.kmb[tcl * G];
+        ks[u] = cr.ksb[tcl * G];
+        vm[u] = cr.vmb[tcl * G];
+        vs[u] = cr.vsb[tcl * G];
+    }
+    float z[UU];
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const float dq = dot_biased(qs, kx[u], mg);
+        float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
+        sp = token_sum<LPT>(sp);
+        z[u] = valid[u] ? sp * c2 : -INFINITY;
+        mx = fmaxf(mx, z[u]);
+    }
+    const float mref = (mx == -INFINITY) ? 0.0f : mx;
+    if (__any(mx != m)) {
+        const float alpha = exp2_fast(m - mref);
+        l *= alpha;
+        bsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            acc[i] *= alpha;
+    }
+    m = mx;
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const float p = exp2_fast(z[u] - mref);
+        l += p;
+        bsum = __builtin_fmaf(p, __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
+        axpy_biased(acc, p * vs[u], vx[u], mg);
+    }
+}
+
 // ===========================================================================
 // Dense decode attention.
 //
@@ -279,20 +344,22 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ kc, 
     const int part = lane % LPT;
     const int lt = lane / LPT;
     const int g = part >> 1;
-    const int t_begin = split * split_len;
-    const int t_end = min(T, t_begin + split_len);
-    const int n_tok = max(0, t_end - t_begin);
-    const int n_iter = (n_tok + WPP * TPI - 1) / (WPP * TPI);
-
+    // This split's tokens [t0, t1), cut into WPP contiguous per-wave ranges
+    // (whole TPW-token rows so only the last wave has a ragged end).
+    const int t0 = split * split_len;
+    const int t1 = min(T, t0 + split_len);
+    const int n_tok = max(0, t1 - t0);
+    const int per_wave = ((n_tok + WPP - 1) / WPP + TPW - 1) / TPW * TPW;
+    const int w_begin = min(t1, t0 + wp * per_wave);
+    const int t_end = min(t1, w_begin + per_wave);
+    const int n_full = (t_end - w_begin) / TPI;            // iterations with all U rows valid
+    const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW; // single-row tail iterations
     const QSlice qs = load_q_slice(q + pc * (D / 8) + part * 4);
     const uint32_t mg = magic64_vgpr();
 
-    const uint8_t *__restrict__ kb = kc + pc * S * (D / 2) + part * 16;
-    const uint8_t *__restrict__ vb = vc + pc * S * (D / 2) + part * 16;
-    const float *__restrict__ kmb = kmin + pc * S * G + g;
-    const float *__restrict__ ksb = ksc + pc * S * G + g;
-    const float *__restrict__ vmb = vmin + pc * S * G + g;
-    const float *__restrict__ vsb = vsc + pc * S * G + g;
+    const CacheRow cr = {kc + pc * S * (D / 2) + part * 16, vc + pc * S * (D / 2) + part * 16,
+                         kmin + pc * S * G + g, ksc + pc * S * G + g, vmin + pc * S * G + g,
+                         vsc + pc * S * G + g};
 
     float m = -INFINITY, l = 0.0f, bsum = 0.0f;
     float acc[32];
@@ -300,51 +367,11 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ kc, 
     for (int i = 0; i < 32; ++i)
         acc[i] = 0.0f;
 
-    for (int it = 0; it < n_iter; ++it) {
-        const int tb = t_begin + (it * WPP + wp) * TPI + lt;
-        uint4 kx[U], vx[U];
-        float km[U], ks[U], vm[U], vs[U];
-        bool valid[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = tb + u * TPW;
-            valid[u] = t < t_end;
-            const int64_t tcl = valid[u] ? t : t_end - 1;
-            kx[u] = *reinterpret_cast<const uint4 *>(kb + tcl * (D / 2));
-            vx[u] = *reinterpret_cast<const uint4 *>(vb + tcl * (D / 2));
-            km[u] = kmb[tcl * G];
-            ks[u] = ksb[tcl * G];
-            vm[u] = vmb[tcl * G];
-            vs[u] = vsb[tcl * G];
-        }
-        float z[U];
-        float mx = m;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float dq = dot_biased(qs, kx[u], mg);
-            float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
-            sp = token_sum<LPT>(sp);
-            z[u] = valid[u] ? sp * c2 : -INFINITY;
-            mx = fmaxf(mx, z[u]);
-        }
-        const float mref = (mx == -INFINITY) ? 0.0f : mx;
-        if (__any(mx != m)) {
-            const float alpha = exp2_fast(m - mref);
-            l *= alpha;
-            bsum *= alpha;
-#pragma unroll
-            for (int i = 0; i < 32; ++i)
-                acc[i] *= alpha;
-        }
-        m = mx;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float p = exp2_fast(z[u] - mref);
-            l += p;
-            bsum = __builtin_fmaf(p, __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
-            axpy_biased(acc, p * vs[u], vx[u], mg);
-        }
-    }
+    int tb = w_begin + lt;
+    for (int it = 0; it < n_full; ++it, tb += TPI)
+        decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
+    for (int it = 0; it < n_rest; ++it, tb += TPW)
+        decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         acc[i] += bsum;
