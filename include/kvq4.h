@@ -116,9 +116,10 @@ int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v
 int kv_append_quant(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos,
                     void *hip_stream);
 
-/* Workspace bytes decode_attention_q4 needs for (ctx_len, num_splits), or
- * decode_attention_q4_topk when k_top > 0 (always 0 today).  0 when the
- * resolved split count is 1.  Host only; returns 0 on invalid arguments. */
+/* Workspace bytes decode_attention_q4 needs for (ctx_len, num_splits) -- 0
+ * when the resolved split count is 1 -- or, when k_top > 0, the bytes
+ * decode_attention_q4_topk needs (b*a*ctx_len*4: one fp32 score per token).
+ * Host only; returns 0 on invalid arguments. */
 size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_splits, int32_t k_top);
 
 /* Decode-phase attention over slots 0..ctx_len-1 (1 <= ctx_len <= s+n) of
@@ -145,7 +146,9 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
  * and take the softmax and P.V over the kept tokens only.
  * 1 <= k_top <= ctx_len <= min(s+n, KVQ_TOPK_MAX_CTX); the pages' rule keeps
  * k_top = ceil(0.1 * ctx_len).  sel_idx (device int32 [b][a][k_top], may be
- * NULL) receives the kept token indices in ascending order. */
+ * NULL) receives the kept token indices in ascending order.  ws: device
+ * workspace of ws_bytes >= kvq_workspace_bytes(dims, ctx_len, 0, k_top),
+ * 16-byte aligned; it holds the scores between the two kernels. */
 int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
                              void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream);
 

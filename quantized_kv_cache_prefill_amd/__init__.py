@@ -228,7 +228,7 @@ def decode_attention_q4_tuned(cache: QuantKVCache, q: torch.Tensor, ctx_len: int
 
 def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, k_top: int,
                              out: torch.Tensor | None = None, sel_idx: torch.Tensor | bool | None = True,
-                             stream=None):
+                             ws: torch.Tensor | None = None, stream=None):
     """Top-k sparse decode attention.  Returns (out fp16 [b,1,a,d], sel_idx int32 [b,a,k_top] or None)."""
     _act(q, (cache.b, 1, cache.a, cache.d), "q")
     if out is None:
@@ -241,7 +241,10 @@ def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int,
     if sel_idx is not None and (sel_idx.dtype != torch.int32 or not sel_idx.is_contiguous()
                                 or sel_idx.numel() != cache.b * cache.a * k_top):
         raise ValueError("sel_idx must be a contiguous int32 tensor of b*a*k_top elements")
+    need = kvq_workspace_bytes(cache, ctx_len, 0, k_top)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     _check(load_library().decode_attention_q4_topk(cache.struct_ref(), _ptr(q), ctx_len, k_top, _ptr(out),
-                                                   _ptr(sel_idx), None, 0, _stream(stream)),
+                                                   _ptr(sel_idx), _ptr(ws), need, _stream(stream)),
            "decode_attention_q4_topk")
     return out, sel_idx

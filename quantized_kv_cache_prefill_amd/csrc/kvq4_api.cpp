@@ -150,9 +150,9 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
     const int S = dims->s + dims->n;
     if (ctx_len < 1 || ctx_len > S || num_splits < 0 || num_splits > KVQ_MAX_SPLITS)
         return 0;
-    if (k_top > 0)
-        return 0;
     const int pairs = dims->b * dims->a;
+    if (k_top > 0)
+        return kvq::topk_ws_floats(pairs, ctx_len) * sizeof(float);
     const int hd = dims->h / dims->a;
     int len;
     const int s = resolve_splits(pairs, hd, ctx_len, num_splits, &len);
@@ -198,8 +198,6 @@ int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_l
 int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
                              void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     kvq::CachePlanes c;
     int st = check_cache(cache, &c);
     if (st != KVQ_OK)
@@ -215,7 +213,10 @@ int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t 
     if (sel_idx != nullptr && (reinterpret_cast<uintptr_t>(sel_idx) & 3u) != 0)
         return KVQ_EINVAL;
     const int pairs = cache->dims.b * cache->dims.a;
-    return status_of(kvq::launch_topk(c, pairs, q_f16, ctx_len, k_top, out_f16, sel_idx,
+    const size_t need = kvq::topk_ws_floats(pairs, ctx_len) * sizeof(float);
+    if (ws == nullptr || !aligned16(ws) || ws_bytes < need)
+        return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
+    return status_of(kvq::launch_topk(c, pairs, q_f16, ctx_len, k_top, out_f16, sel_idx, static_cast<float *>(ws),
                                       static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -22,6 +22,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kvq4_launch.h"
 
 namespace kvq {
@@ -43,6 +45,17 @@ __device__ __forceinline__ float dpp(float v)
 
 __device__ __forceinline__ float h2f_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
 __device__ __forceinline__ float h2f_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Loads of data that is used exactly once (the cache planes, the prompt
+// K/V): nontemporal, so they stream through without displacing other lines.
+// On MI355X this raises a plain 16-byte streaming read from ~6.3 to ~7.0 TB/s.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float ld_stream(const float *p) { return __builtin_nontemporal_load(p); }
 
 // ---------------------------------------------------------------------------
 // Nibble unpack.  A 32-bit word of codes holds elements e0..e7 (nibble k at
@@ -184,7 +197,7 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
         const int64_t ti = rc - pair * s_src;
         const int64_t bi = pair / a;
         const int64_t ai = pair - bi * a;
-        x[u] = src[((bi * s_src + ti) * a + ai) * (D / 8) + lir];
+        x[u] = ld_stream16(src + ((bi * s_src + ti) * a + ai) * (D / 8) + lir);
         slot[u] = pair * S + t_dst0 + ti;
     }
 #pragma unroll
@@ -264,12 +277,12 @@ __device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_en
         const int t = tb + u * TPW;
         valid[u] = t < t_end;
         const int64_t tcl = valid[u] ? t : t_end - 1;
-        kx[u] = *reinterpret_cast<const uint4 *>(cr.kb + tcl * (D / 2));
-        vx[u] = *reinterpret_cast<const uint4 *>(cr.vb + tcl * (D / 2));
-        km[u] = cr.kmb[tcl * G];
-        ks[u] = cr.ksb[tcl * G];
-        vm[u] = cr.vmb[tcl * G];
-        vs[u] = cr.vsb[tcl * G];
+        kx[u] = ld_stream16(cr.kb + tcl * (D / 2));
+        vx[u] = ld_stream16(cr.vb + tcl * (D / 2));
+        km[u] = ld_stream(cr.kmb + tcl * G);
+        ks[u] = ld_stream(cr.ksb + tcl * G);
+        vm[u] = ld_stream(cr.vmb + tcl * G);
+        vs[u] = ld_stream(cr.vsb + tcl * G);
     }
     float z[UU];
     float mx = m;
@@ -509,12 +522,18 @@ __global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ ws, _F
 }
 
 // ===========================================================================
-// Top-k sparse decode attention: one 256-thread workgroup per (batch row,
-// head).  (1) every key is scored into LDS (same lane layout and folded codec
-// as k_decode); (2) the k-th largest score is found exactly by a 4-pass
-// 8-bit radix select on order-preserving 32-bit keys; (3) the kept tokens
-// (larger keys, plus the smallest-index ties) are compacted in ascending
-// token order; (4) softmax over the kept scores and P.V over their V rows.
+// Top-k sparse decode attention, in two kernels.
+//
+// k_topk_scores streams every key once (same lane layout and folded codec as
+// k_decode; each wave takes a contiguous token range) and writes the scores,
+// in log2 units, to a workspace of 4 bytes per token -- 5% of the key bytes.
+// k_topk_select then runs one 256-thread workgroup per (batch row, head):
+// scores into LDS, the exact k-th largest by a 4-pass 8-bit radix select on
+// order-preserving 32-bit keys, compaction of the kept tokens in ascending
+// order (ties to the smaller index), softmax over the kept scores and P.V
+// over their gathered V rows.  Splitting the stream from the latency-bound
+// selection keeps the stream at full bandwidth; fused, the selection of one
+// workgroup left the memory pipeline idle.
 // ===========================================================================
 __device__ __forceinline__ uint32_t order_key(float z)
 {
@@ -548,18 +567,80 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp4)
     return base + incl - v;
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void k_topk(const uint8_t *__restrict__ kc, const uint8_t *__restrict__ vc,
-                                              const float *__restrict__ kmin, const float *__restrict__ ksc,
-                                              const float *__restrict__ vmin, const float *__restrict__ vsc,
-                                              const uint4 *__restrict__ q, _Float16 *__restrict__ out,
-                                              int32_t *__restrict__ sel_out, int S, int T, int k_top, float c2)
+template <int D, int UU>
+__device__ __forceinline__ void score_iter(const CacheRow &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
+                                           float c2, bool writer, float *__restrict__ srow)
 {
     constexpr int LPT = D / 32;
     constexpr int TPW = 64 / LPT;
     constexpr int G = D / 64;
-    constexpr int U = 2;
-    extern __shared__ float sm_dyn[];
+    uint4 kx[UU];
+    float km[UU], ks[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const int t = tb + u * TPW;
+        const int64_t tcl = t < t_end ? t : t_end - 1;
+        kx[u] = ld_stream16(cr.kb + tcl * (D / 2));
+        km[u] = ld_stream(cr.kmb + tcl * G);
+        ks[u] = ld_stream(cr.ksb + tcl * G);
+    }
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const float dq = dot_biased(qs, kx[u], mg);
+        float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
+        sp = token_sum<LPT>(sp);
+        const int t = tb + u * TPW;
+        if (writer && t < t_end)
+            srow[t] = sp * c2;
+    }
+}
+
+// One wave per (pair, chunk of `chunk` tokens); four waves per workgroup.
+template <int D, int U>
+__global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__ kc, const float *__restrict__ kmin,
+                                                     const float *__restrict__ ksc, const uint4 *__restrict__ q,
+                                                     float *__restrict__ scores, int pairs, int S, int T,
+                                                     int chunk, int n_chunks, float c2)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+    constexpr int TPI = U * TPW;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= (int64_t)pairs * n_chunks)
+        return;
+    const int64_t pair = item / n_chunks;
+    const int c = (int)(item - pair * n_chunks);
+    const int part = lane % LPT, lt = lane / LPT, g = part >> 1;
+    const int w_begin = c * chunk;
+    const int t_end = min(T, w_begin + chunk);
+    const int n_full = (t_end - w_begin) / TPI;
+    const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW;
+    const QSlice qs = load_q_slice(q + pair * (D / 8) + part * 4);
+    const uint32_t mg = magic64_vgpr();
+    const CacheRow cr = {kc + pair * S * (D / 2) + part * 16, nullptr, kmin + pair * S * G + g,
+                         ksc + pair * S * G + g, nullptr, nullptr};
+    float *__restrict__ srow = scores + pair * T;
+    const bool writer = part == 0;
+    int tb = w_begin + lt;
+    for (int it = 0; it < n_full; ++it, tb += TPI)
+        score_iter<D, U>(cr, tb, t_end, qs, mg, c2, writer, srow);
+    for (int it = 0; it < n_rest; ++it, tb += TPW)
+        score_iter<D, 1>(cr, tb, t_end, qs, mg, c2, writer, srow);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__ vc, const float *__restrict__ vmin,
+                                                     const float *__restrict__ vsc, const float *__restrict__ scores,
+                                                     _Float16 *__restrict__ out, int32_t *__restrict__ sel_out,
+                                                     int S, int T, int k_top)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+    constexpr int UG = 4; // gathered rows per lane in flight
+    extern __shared__ __attribute__((aligned(16))) float sm_dyn[];
     float *__restrict__ sc = sm_dyn;                                        // [T] scores, log2 units
     uint16_t *__restrict__ sel = reinterpret_cast<uint16_t *>(sm_dyn + T);  // [k_top] kept tokens
     __shared__ int hist[256];
@@ -573,43 +654,31 @@ __global__ __launch_bounds__(256) void k_topk(const uint8_t *__restrict__ kc, co
     const int64_t pair = blockIdx.x;
     const int part = lane % LPT, lt = lane / LPT, g = part >> 1;
 
-    const QSlice qs = load_q_slice(q + pair * (D / 8) + part * 4);
-    const uint32_t mg = magic64_vgpr();
-    const uint8_t *__restrict__ kb = kc + pair * S * (D / 2) + part * 16;
-    const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
-    const float *__restrict__ kmb = kmin + pair * S * G + g;
-    const float *__restrict__ ksb = ksc + pair * S * G + g;
-    const float *__restrict__ vmb = vmin + pair * S * G + g;
-    const float *__restrict__ vsb = vsc + pair * S * G + g;
-
-    // (1) scores
+    // (1) scores into LDS, and their maximum: 16-byte loads, up to four per
+    // thread in flight (the row of T floats is 16-byte aligned when T % 4 == 0;
+    // otherwise, and for the tail, single floats)
+    const float *__restrict__ srow = scores + pair * T;
     float zmax = -INFINITY;
-    for (int t0 = wave * (U * TPW); t0 < T; t0 += 4 * U * TPW) {
-        uint4 kx[U];
-        float km[U], ks[U];
-        bool valid[U];
-        int tt[U];
+    const int T4 = (T % 4 == 0) ? T / 4 : 0;
+    for (int i0 = tid; i0 < T4; i0 += 256 * 4) {
+        // clamped indices: a lane past the end reloads (and rewrites, with the
+        // same value) the last float4, so no load sits behind a branch
+        uint4 v[4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            tt[u] = t0 + u * TPW + lt;
-            valid[u] = tt[u] < T;
-            const int64_t tcl = valid[u] ? tt[u] : T - 1;
-            kx[u] = *reinterpret_cast<const uint4 *>(kb + tcl * (D / 2));
-            km[u] = kmb[tcl * G];
-            ks[u] = ksb[tcl * G];
-        }
+        for (int u = 0; u < 4; ++u)
+            v[u] = ld_stream16(srow + 4 * min(i0 + u * 256, T4 - 1));
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float dq = dot_biased(qs, kx[u], mg);
-            float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
-            sp = token_sum<LPT>(sp);
-            const float z = sp * c2;
-            if (valid[u]) {
-                zmax = fmaxf(zmax, z);
-                if (part == 0)
-                    sc[tt[u]] = z;
-            }
+        for (int u = 0; u < 4; ++u) {
+            const float z0 = __builtin_bit_cast(float, v[u].x), z1 = __builtin_bit_cast(float, v[u].y);
+            const float z2 = __builtin_bit_cast(float, v[u].z), z3 = __builtin_bit_cast(float, v[u].w);
+            reinterpret_cast<float4 *>(sc)[min(i0 + u * 256, T4 - 1)] = make_float4(z0, z1, z2, z3);
+            zmax = fmaxf(zmax, fmaxf(fmaxf(z0, z1), fmaxf(z2, z3)));
         }
+    }
+    for (int t = 4 * T4 + tid; t < T; t += 256) {
+        const float z = ld_stream(srow + t);
+        sc[t] = z;
+        zmax = fmaxf(zmax, z);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
@@ -631,8 +700,8 @@ __global__ __launch_bounds__(256) void k_topk(const uint8_t *__restrict__ kc, co
                 atomicAdd(&hist[(key >> shift) & 255], 1);
         }
         __syncthreads();
-        const int cnt = hist[255 - tid];           // thread i looks at digit 255-i
-        const int before = block_excl_scan(cnt, tmp4); // keys with a larger digit
+        const int cnt = hist[255 - tid];                // thread i looks at digit 255-i
+        const int before = block_excl_scan(cnt, tmp4);  // keys with a larger digit
         if (before < remaining && remaining <= before + cnt) {
             sh_digit = 255 - tid;
             sh_above = before;
@@ -676,23 +745,36 @@ __global__ __launch_bounds__(256) void k_topk(const uint8_t *__restrict__ kc, co
     }
     __syncthreads();
 
-    // (4) softmax over the kept scores and P.V over their V rows
-    const float Mr = M;
+    // (4) softmax over the kept scores and P.V over their V rows, UG rows per
+    // lane in flight
+    const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
+    const float *__restrict__ vmb = vmin + pair * S * G + g;
+    const float *__restrict__ vsb = vsc + pair * S * G + g;
+    const uint32_t mg = magic64_vgpr();
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         acc[i] = 0.0f;
-    for (int j0 = wave * TPW; j0 < k_top; j0 += 4 * TPW) {
-        const int j = j0 + lt;
-        const bool valid = j < k_top;
-        const int64_t t = sel[valid ? j : k_top - 1];
-        const uint4 vx = *reinterpret_cast<const uint4 *>(vb + t * (D / 2));
-        const float vm = vmb[t * G], vs = vsb[t * G];
-        const float p = valid ? exp2_fast(sc[t] - Mr) : 0.0f;
-        l += p;
-        bsum = __builtin_fmaf(p, __builtin_fmaf(-kBias, vs, vm), bsum);
-        axpy_biased(acc, p * vs, vx, mg);
+    for (int j0 = wave * TPW + lt; j0 < k_top; j0 += 4 * TPW * UG) {
+        uint4 vx[UG];
+        float vm[UG], vs[UG], p[UG];
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            const int j = j0 + u * 4 * TPW;
+            const bool valid = j < k_top;
+            const int64_t t = sel[valid ? j : k_top - 1];
+            vx[u] = ld_stream16(vb + t * (D / 2));
+            vm[u] = ld_stream(vmb + t * G);
+            vs[u] = ld_stream(vsb + t * G);
+            p[u] = valid ? exp2_fast(sc[t] - M) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            l += p[u];
+            bsum = __builtin_fmaf(p[u], __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
+            axpy_biased(acc, p[u] * vs[u], vx[u], mg);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i)
@@ -719,6 +801,159 @@ __global__ __launch_bounds__(256) void k_topk(const uint8_t *__restrict__ kc, co
     if (sel_out != nullptr)
         for (int j = tid; j < k_top; j += 256)
             sel_out[pair * k_top + j] = sel[j];
+}
+
+// Selection for contexts up to 2048 tokens: one wave per (batch row, head),
+// four pairs per workgroup, no workgroup barrier.  Lane l holds the keys of
+// tokens l, l+64, l+128, ... in registers.  The k_top-th largest key is found
+// bit by bit from the top (32 steps; each step counts the keys in the upper
+// half of the current bucket with one ballot per register); the kept tokens
+// are then compacted in ascending order with ballots and mbcnt, ties to the
+// smaller index.  Each kept token's index and softmax weight go to LDS, and
+// the wave gathers the kept V rows.
+template <int D>
+__global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict__ vc,
+                                                       const float *__restrict__ vmin,
+                                                       const float *__restrict__ vsc,
+                                                       const float *__restrict__ scores, uint4 *__restrict__ out,
+                                                       int32_t *__restrict__ sel_out, int pairs, int S, int T,
+                                                       int k_top, int region_bytes)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+    constexpr int KPL = 32; // keys per lane: T <= 64 * KPL
+    constexpr int UG = 4;   // gathered rows per lane in flight
+    extern __shared__ __attribute__((aligned(16))) float sm_dyn[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
+    if (pair >= pairs)
+        return;
+    char *region = reinterpret_cast<char *>(sm_dyn) + (size_t)wave * region_bytes;
+    float *__restrict__ sel_p = reinterpret_cast<float *>(region);                      // [k_top] weights
+    uint16_t *__restrict__ sel_t = reinterpret_cast<uint16_t *>(region + 4 * (size_t)k_top); // [k_top] tokens
+
+    // (1) keys in registers (0 for t >= T: below every finite score's key).
+    // Every load is issued unconditionally (clamped index) and its value used
+    // without a branch, so all KPL loads are in flight together.
+    const float *__restrict__ srow = scores + pair * T;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+        key[j] = __builtin_bit_cast(uint32_t, ld_stream(srow + min(lane + 64 * j, T - 1)));
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const float z = __builtin_bit_cast(float, key[j]);
+        const uint32_t keep = (lane + 64 * j < T) ? 0xFFFFFFFFu : 0u;
+        zmax = fmaxf(zmax, __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, z) & keep) |
+                                                         (0xFF800000u & ~keep))); // -inf when masked
+        key[j] = order_key(z) & keep;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        zmax = fmaxf(zmax, __shfl_xor(zmax, off));
+
+    // (2) exact key of the k_top-th largest score
+    uint32_t prefix = 0;
+    int remaining = k_top;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        const uint32_t hmask = ~((1u << b) - 1u);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            cnt += __popcll(__ballot((key[j] & hmask) == cand));
+        if (cnt >= remaining)
+            prefix = cand;
+        else
+            remaining -= cnt;
+    }
+    const uint32_t thr = prefix;
+
+    // (3) compaction in ascending token order; softmax weights of the kept keys
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const bool eq = key[j] == thr;
+        const uint64_t eqm = __ballot(eq);
+        const int eq_rank = eq_seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
+        const bool keep = key[j] > thr || (eq && eq_rank < remaining);
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+            const uint32_t kb = key[j];
+            const float z = __builtin_bit_cast(float, (kb & 0x80000000u) ? (kb ^ 0x80000000u) : ~kb);
+            sel_p[pos] = exp2_fast(z - zmax);
+            sel_t[pos] = (uint16_t)(lane + 64 * j);
+        }
+        base += __popcll(km);
+        eq_seen += __popcll(eqm);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // (4) P.V over the kept rows
+    const int part = lane % LPT, lt = lane / LPT, g = part >> 1;
+    const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
+    const float *__restrict__ vmb = vmin + pair * S * G + g;
+    const float *__restrict__ vsb = vsc + pair * S * G + g;
+    const uint32_t mg = magic64_vgpr();
+    float l = 0.0f, bsum = 0.0f;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] = 0.0f;
+    for (int j0 = 0; j0 < k_top; j0 += TPW * UG) {
+        uint4 vx[UG];
+        float vm[UG], vs[UG], p[UG];
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            const int j = j0 + u * TPW + lt;
+            const bool valid = j < k_top;
+            const int jc = valid ? j : k_top - 1;
+            const int64_t t = sel_t[jc];
+            vx[u] = ld_stream16(vb + t * (D / 2));
+            vm[u] = ld_stream(vmb + t * G);
+            vs[u] = ld_stream(vsb + t * G);
+            p[u] = valid ? sel_p[jc] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            l += p[u];
+            bsum = __builtin_fmaf(p[u], __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
+            axpy_biased(acc, p[u] * vs[u], vx[u], mg);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] += bsum;
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+        l += __shfl_xor(l, off);
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            acc[i] += __shfl_xor(acc[i], off);
+    }
+    if (lt == 0) {
+        const float inv = 1.0f / l;
+        uint32_t h[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const _Float16 lo16 = (_Float16)(acc[2 * i] * inv);
+            const _Float16 hi16 = (_Float16)(acc[2 * i + 1] * inv);
+            h[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo16) | ((uint32_t)__builtin_bit_cast(uint16_t, hi16) << 16);
+        }
+        uint4 *dst = out + pair * (D / 8) + part * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dst[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+    }
+    if (sel_out != nullptr)
+        for (int j = lane; j < k_top; j += 64)
+            sel_out[pair * k_top + j] = sel_t[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -783,15 +1018,32 @@ int launch_decode_d(const CachePlanes &c, int pairs, const void *q, int T, void 
     }
 }
 
+constexpr int kTopkWaveMaxCtx = 2048; // k_topk_select_w holds 32 keys per lane
+
 template <int D>
 int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
-                  hipStream_t st)
+                  float *ws, hipStream_t st)
 {
+    constexpr int TPW = 64 / (D / 32);
     const float c2 = 1.4426950408889634f / sqrtf((float)D);
-    const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
-    hipLaunchKernelGGL((k_topk<D>), dim3((unsigned)pairs), dim3(256), lds, st, c.k_codes, c.v_codes, c.k_min,
-                       c.k_scale, c.v_min, c.v_scale, static_cast<const uint4 *>(q), static_cast<_Float16 *>(out),
-                       sel, c.S, T, k_top, c2);
+    const int chunk = std::min(128, (T + TPW - 1) / TPW * TPW);
+    const int n_chunks = (T + chunk - 1) / chunk;
+    const int64_t waves = (int64_t)pairs * n_chunks;
+    hipLaunchKernelGGL((k_topk_scores<D, 2>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, c.k_codes,
+                       c.k_min, c.k_scale, static_cast<const uint4 *>(q), ws, pairs, c.S, T, chunk, n_chunks, c2);
+    int e = (int)hipGetLastError();
+    if (e != 0)
+        return e;
+    if (T <= kTopkWaveMaxCtx) {
+        const int region = (int)(((size_t)k_top * (sizeof(float) + sizeof(uint16_t)) + 15) / 16 * 16);
+        hipLaunchKernelGGL((k_topk_select_w<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), (size_t)4 * region, st,
+                           c.v_codes, c.v_min, c.v_scale, ws, static_cast<uint4 *>(out), sel, pairs, c.S, T, k_top,
+                           region);
+    } else {
+        const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
+        hipLaunchKernelGGL((k_topk_select<D>), dim3((unsigned)pairs), dim3(256), lds, st, c.v_codes, c.v_min,
+                           c.v_scale, ws, static_cast<_Float16 *>(out), sel, c.S, T, k_top);
+    }
     return (int)hipGetLastError();
 }
 
@@ -824,13 +1076,15 @@ size_t decode_ws_floats(int pairs, int d, int splits)
 
 int decode_tokens_per_iter(int d, int unroll, int waves_per_pair) { return (64 / (d / 32)) * unroll * waves_per_pair; }
 
+size_t topk_ws_floats(int pairs, int T) { return (size_t)pairs * (size_t)T; }
+
 int launch_topk(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
-                hipStream_t st)
+                float *ws, hipStream_t st)
 {
     switch (c.d) {
-    case 64: return launch_topk_d<64>(c, pairs, q, T, k_top, out, sel, st);
-    case 128: return launch_topk_d<128>(c, pairs, q, T, k_top, out, sel, st);
-    default: return launch_topk_d<256>(c, pairs, q, T, k_top, out, sel, st);
+    case 64: return launch_topk_d<64>(c, pairs, q, T, k_top, out, sel, ws, st);
+    case 128: return launch_topk_d<128>(c, pairs, q, T, k_top, out, sel, ws, st);
+    default: return launch_topk_d<256>(c, pairs, q, T, k_top, out, sel, ws, st);
     }
 }
 

@@ -42,8 +42,13 @@ size_t decode_ws_floats(int pairs, int d, int splits);
 // Tokens one workgroup iteration covers (for the split heuristic).
 int decode_tokens_per_iter(int d, int unroll, int waves_per_pair);
 
-// Top-k sparse decode attention, one workgroup per (batch row, head).
+// Top-k sparse decode attention: a streaming score pass into ws (one float
+// per (pair, token)), then one workgroup per (batch row, head) for the
+// selection and the gathered P.V.
 int launch_topk(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
-                hipStream_t st);
+                float *ws, hipStream_t st);
+
+// Workspace floats needed by launch_topk.
+size_t topk_ws_floats(int pairs, int T);
 
 }  // namespace kvq

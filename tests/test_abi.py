@@ -97,8 +97,9 @@ def test_null_and_misaligned_pointers(L):
     assert L.kv_append_quant(ctypes.byref(c), FAKE, None, 0, st) == KVQ_EINVAL
     assert L.decode_attention_q4(ctypes.byref(c), None, 4, FAKE, 0, None, 0, st) == KVQ_EINVAL
     assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4, FAKE + 8, 0, None, 0, st) == KVQ_EINVAL
-    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, None, None, None, 0, st) == KVQ_EINVAL
-    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, FAKE, FAKE + 2, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, None, None, FAKE, 1 << 20, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, FAKE, FAKE + 2, FAKE, 1 << 20, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, FAKE, None, FAKE + 4, 1 << 20, st) == KVQ_EINVAL
 
 
 def test_ranges(L):
@@ -133,8 +134,11 @@ def test_workspace_sizing_and_enospace(L):
     assert auto > 0 and auto % (130 * 4) == 0
     assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4096, FAKE, 7, FAKE, 7 * 130 * 4 - 4, st) == KVQ_ENOSPACE
     assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4096, FAKE, 7, None, 0, st) == KVQ_ENOSPACE
-    # the top-k path needs no workspace
-    assert L.kvq_workspace_bytes(ctypes.byref(d), 2048, 0, 205) == 0
+    # the top-k path holds one fp32 score per (pair, token) between its two kernels
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 2048, 0, 205) == 1 * 1 * 2048 * 4
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2048, 205, FAKE, None, FAKE, 2048 * 4 - 4,
+                                      st) == KVQ_ENOSPACE
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2048, 205, FAKE, None, None, 0, st) == KVQ_ENOSPACE
 
 
 def test_strerror(L):
