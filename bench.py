@@ -15,7 +15,8 @@ attention 160 B per (batch row, head, token) (64 B K codes + 64 B V codes +
 decode attention kernel is timed live with HIP events on the stream it runs
 on; its achieved bandwidth against the 8 TB/s HBM peak is the `roofline`
 entry.  The sparse top-10% variant is timed on its own workload (b=32, a=96,
-context 2048) and reported beside it.  `cpu_baseline` times the CPU oracle
+context 2048) and the split-context reduce path on one long sequence (b=1,
+a=96, context 65536); both are reported beside it.  `cpu_baseline` times the CPU oracle
 on a bounded sample of the same job.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -178,6 +179,46 @@ def time_topk(reps: int = 6, copies: int = 4):
             "dense_equivalent_bytes": dense_bytes}
 
 
+def time_split_context(T: int = 65536, copies: int = 3, reps: int = 5):
+    """The split-context path (decode_attention_q4 with its automatic split count and the
+    log-sum-exp reduce pass) on one long sequence: b=1, a=96, d=128, context T.  With only
+    96 (batch row, head) pairs the heuristic splits every context across workgroups; the
+    same call with num_splits=1 is timed beside it."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    b, a, d = 1, 96, 128
+    caches = [kvq.QuantKVCache(b, a, a * d, T, 0, device="cuda") for _ in range(copies)]
+    k = W.random_fp16((b, T, a, d), 777, "cuda")
+    v = W.random_fp16((b, T, a, d), 778, "cuda")
+    for c in caches:
+        kvq.kv_quantize_prefill(c, k, v)
+    del k, v
+    q = W.random_fp16((b, 1, a, d), 779, "cuda")
+    out = torch.empty_like(q)
+    st = torch.cuda.current_stream()
+    res = {}
+    for label, ns in (("auto", 0), ("one_split", 1)):
+        need = kvq.kvq_workspace_bytes(caches[0], T, ns)
+        ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
+        times = []
+        for r in range((reps + 1) * copies):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            kvq.decode_attention_q4(caches[r % copies], q, T, out=out, num_splits=ns, ws=ws)
+            e1.record(st)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(x.elapsed_time(y) for x, y in times[copies:])
+        med = ms[len(ms) // 2]
+        res[label] = {"ms_per_call_median": round(med, 4), "workspace_bytes": need,
+                      "gbs": round(bytes_decode(b * a, T, d) / med / 1e6, 1)}
+    res["workload"] = f"one long sequence: b={b} a={a} d={d} context {T}"
+    res["algorithmic_bytes"] = bytes_decode(b * a, T, d)
+    return res
+
+
 def hbm_copy_ceiling():
     """Practical HBM ceiling for mixed read/write streams: a plain 4 GiB device copy
     (torch), read + write bytes / time."""
@@ -328,6 +369,8 @@ def main():
     if not args.no_topk:
         log("[bench] sparse top-k leg")
         res["sparse_topk"] = time_topk()
+        log("[bench] split-context leg")
+        res["split_context"] = time_split_context()
     del job
     torch.cuda.empty_cache()
     res["hbm_copy_ceiling_gbs"] = hbm_copy_ceiling()

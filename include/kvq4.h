@@ -126,9 +126,9 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
  * every (batch row, head):
  *     out = softmax(q . K^T / sqrt(d)) . V      (per head; no W_O, no residual)
  * with K, V the dequantised cache.  q and out are fp16 [b][1][a][d].
- * num_splits: 0 = choose automatically; k > 0 splits each context into k
- * ranges handled by separate workgroups and merged by a second pass
- * (log-sum-exp).  ws: device workspace of ws_bytes >= kvq_workspace_bytes()
+ * num_splits: 0 = choose automatically; k > 0 splits each context into at
+ * most k ranges (when k > 1, each a whole number of 128-token blocks) handled
+ * by separate workgroups and merged by a second pass (log-sum-exp).  ws: device workspace of ws_bytes >= kvq_workspace_bytes()
  * (may be NULL when that is 0). */
 int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
                         int32_t num_splits, void *ws, size_t ws_bytes, void *hip_stream);

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include <hip/hip_runtime_api.h>
 
@@ -67,30 +68,49 @@ int check_act(const void *p) { return (p == nullptr || !aligned16(p)) ? KVQ_EINV
 int status_of(int hip_err) { return hip_err == 0 ? KVQ_OK : KVQ_ELAUNCH; }
 
 // Launch shape for the dense decode kernel.  Default: 4 token rows per lane
-// per iteration and 2 waves per (batch row, head) -- the fastest shape of the
-// measured sweep on the OPT-175B layer (71.5% of HBM peak vs 66% for 4 waves
-// per pair).  Automatic splits: only when the (batch row, head) pairs alone
-// give fewer than 2048 waves (8 per CU), and never more than one split per two
-// workgroup iterations of context.  The automatic choice depends on
-// (pairs, d, ctx) only, so kvq_workspace_bytes() is exact for every shape.
+// per iteration and 2 waves per (batch row, head), two pairs per 256-thread
+// workgroup -- the fastest shape of the measured sweep on the OPT-175B layer
+// (79% of HBM peak vs 70% for 4 waves per pair).
 constexpr int kDefaultUnroll = 4;
 constexpr int kDefaultWavesPerPair = 2;
-constexpr int64_t kTargetWaves = 2048;
+constexpr int kPairsPerGroup = 4 / kDefaultWavesPerPair;
 
-int resolve_splits(int pairs, int d, int ctx, int num_splits, int *split_len)
+// Automatic split count.  The split workgroups of all pairs should spread
+// evenly over MI355X's 256 CUs with at least two workgroups (8 waves) per CU:
+// with x = workgroups / 256, efficiency e = (x / ceil(x)) * min(1, x / 2),
+// and the smallest split count with the best e wins (measured: 11 splits of
+// 48 workgroup groups = 2.06 per CU ran 30% slower than 16 splits = 3 per
+// CU).  A split covers a whole number of 128-token blocks, so every wave
+// starts on a 128-byte boundary of the code and min/scale planes, and is at
+// least 256 tokens long.  The choice depends on (pairs, ctx) only, so
+// kvq_workspace_bytes() is exact for every launch shape.
+constexpr int kCUs = 256;
+constexpr int kSplitAlign = 128;
+constexpr int kMaxAutoSplits = 64;
+
+int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
 {
     int s;
     if (num_splits > 0) {
         s = num_splits;
     } else {
-        const int per_iter = kvq::decode_tokens_per_iter(d, kDefaultUnroll, kDefaultWavesPerPair);
-        const int64_t waves = (int64_t)pairs * kDefaultWavesPerPair;
-        const int64_t want = (kTargetWaves + waves - 1) / waves;
-        const int64_t cap = std::max<int64_t>(1, ctx / (2 * per_iter));
-        s = (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 64}));
+        const int64_t groups = (pairs + kPairsPerGroup - 1) / kPairsPerGroup;
+        const int cap = (int)std::max<int64_t>(1, std::min<int64_t>(ctx / (2 * kSplitAlign), kMaxAutoSplits));
+        s = 1;
+        double best = -1.0;
+        for (int c = 1; c <= cap; ++c) {
+            const double x = (double)(groups * c) / kCUs;
+            const double e = x / std::ceil(x) * std::min(1.0, x / 2.0);
+            if (e > best + 1e-9) {
+                best = e;
+                s = c;
+            }
+        }
     }
     s = std::min(s, ctx);
-    const int len = (ctx + s - 1) / s;
+    int len = (ctx + s - 1) / s;
+    if (s > 1)
+        len = (len + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
     s = (ctx + len - 1) / len; // no empty split
     *split_len = len;
     return s;
@@ -155,7 +175,7 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
         return kvq::topk_ws_floats(pairs, ctx_len) * sizeof(float);
     const int hd = dims->h / dims->a;
     int len;
-    const int s = resolve_splits(pairs, hd, ctx_len, num_splits, &len);
+    const int s = resolve_splits(pairs, ctx_len, num_splits, &len);
     return kvq::decode_ws_floats(pairs, hd, s) * sizeof(float);
 }
 
@@ -180,7 +200,7 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
     kvq::DecodeShape sh;
     sh.unroll = unroll;
     sh.waves_per_pair = waves_per_pair;
-    sh.splits = resolve_splits(pairs, c.d, ctx_len, num_splits, &sh.split_len);
+    sh.splits = resolve_splits(pairs, ctx_len, num_splits, &sh.split_len);
     const size_t need = kvq::decode_ws_floats(pairs, c.d, sh.splits) * sizeof(float);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need))
         return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;

@@ -1098,7 +1098,6 @@ size_t decode_ws_floats(int pairs, int d, int splits)
     return splits > 1 ? (size_t)splits * (size_t)pairs * (size_t)(d + 2) : 0;
 }
 
-int decode_tokens_per_iter(int d, int unroll, int waves_per_pair) { return (64 / (d / 32)) * unroll * waves_per_pair; }
 
 size_t topk_ws_floats(int pairs, int T) { return (size_t)pairs * (size_t)T; }
 

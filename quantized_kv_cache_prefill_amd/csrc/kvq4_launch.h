@@ -39,9 +39,6 @@ int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *o
 // Workspace floats needed by launch_decode for `splits` > 1.
 size_t decode_ws_floats(int pairs, int d, int splits);
 
-// Tokens one workgroup iteration covers (for the split heuristic).
-int decode_tokens_per_iter(int d, int unroll, int waves_per_pair);
-
 // Top-k sparse decode attention: a streaming score pass into ws (one float
 // per (pair, token)), then one workgroup per (batch row, head) for the
 // selection and the gathered P.V.

@@ -347,3 +347,38 @@ def test_errors_enqueue_nothing():
     torch.cuda.synchronize()
     for t0, t1 in zip(before, cache.planes()):
         assert torch.equal(t0, t1)
+
+
+@pytest.mark.parametrize("T", [20, 300, 2048, 3000])
+def test_topk_exact_ties_pick_smallest_indices(T):
+    """Identical keys, or q = 0, make every score equal: the kept set must be exactly the
+    first k tokens (ties to the smaller index) and the output the mean of their V rows.
+    Covers the wave select (T <= 2048) and the workgroup select (T > 2048)."""
+    require_gpu()
+    b, a, d = 1, 3, 128
+    cache = kvq.QuantKVCache(b, a, a * d, T, 0, device=DEV, fill=0xFF)
+    k = W.random_fp16((b, 1, a, d), 2000 + T, DEV).expand(b, T, a, d).contiguous()   # identical keys
+    v = W.random_fp16((b, T, a, d), 2001 + T, DEV)
+    kvq.kv_quantize_prefill(cache, k, v)
+    hc = HostCache(b, a, d, T)
+    hc.prefill(f16_np(k), f16_np(v))
+    k_top = math.ceil(0.1 * T)
+    for q in (W.random_fp16((b, 1, a, d), 2002 + T, DEV), torch.zeros((b, 1, a, d), dtype=torch.float16, device=DEV)):
+        out, sel = kvq.decode_attention_q4_topk(cache, q, T, k_top, out=_nan_out(b, a, d))
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), np.broadcast_to(np.arange(k_top), (b, a, k_top)))
+        pairs = all_pairs(b, a)
+        ref = np.stack([oracle.attend_subset(np.ascontiguousarray(f16_np(q)[bi, 0, ai]), hc.head(bi, ai, T),
+                                             np.arange(k_top)) for bi, ai in pairs])
+        assert_close(_gpu_rows(out, pairs), ref, f"ties T={T}")
+
+
+def test_topk_deterministic():
+    """Run twice -> bit-identical outputs and selections."""
+    require_gpu()
+    b, a, d, T = 2, 8, 128, 1500
+    cache, hc, q = _small_cache(b, a, d, T, 0, 2100)
+    o1, s1 = kvq.decode_attention_q4_topk(cache, q, T, 150)
+    o2, s2 = kvq.decode_attention_q4_topk(cache, q, T, 150)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(s1, s2)
