@@ -5,8 +5,9 @@ One step is the whole hot path over one batch of the OPT-175B layer shape
 whose int4 caches stay resident in HBM):
 
   * prefill: kv_quantize_prefill of every layer's prompt K and V;
-  * decode:  for j = 1..32, for every layer: kv_append_quant at slot s+j-1,
-             then decode_attention_q4 over s+j tokens.
+  * decode:  for j = 1..32, for every layer: the new token's K/V quantised into
+             slot s+j-1 and attention over s+j tokens -- kv_append_quant then
+             decode_attention_q4 (or, with --fused, one kv_append_attend_q4 launch).
 
 value = algorithmic HBM bytes of the step / step time (GB/s).  Algorithmic
 bytes: quantise 2 B in + 0.5 B codes + 0.125 B metadata per element; decode
@@ -115,8 +116,11 @@ class Job:
         # algorithmic bytes of one step
         pairs = w.b * w.a
         self.b_prefill = 2 * self.L * bytes_quantize(w.b * w.a * w.s, w.d)
-        self.b_append = 2 * self.L * self.n * bytes_quantize(pairs, w.d)
+        self.b_append = 0 if args.fused else 2 * self.L * self.n * bytes_quantize(pairs, w.d)
+        self.fused = args.fused
         self.b_decode_per_launch = [bytes_decode(pairs, w.s + j, w.d) for j in range(1, self.n + 1)]
+        if self.fused:  # the timed launch also quantises and writes the new K/V rows
+            self.b_decode_per_launch = [x + 2 * bytes_quantize(pairs, w.d) for x in self.b_decode_per_launch]
         self.b_decode = self.L * sum(self.b_decode_per_launch)
         self.b_step = self.b_prefill + self.b_append + self.b_decode
 
@@ -128,11 +132,15 @@ class Job:
         for j in range(1, self.n + 1):
             for l in range(self.L):
                 q, kn, vn = self.dec[l][j - 1]
-                kvq.kv_append_quant(self.caches[l], kn, vn, w.s + j - 1)
+                if not self.fused:
+                    kvq.kv_append_quant(self.caches[l], kn, vn, w.s + j - 1)
                 if events is not None:
                     e0, e1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
                     e0.record(self.stream)
-                kvq.decode_attention_q4(self.caches[l], q, w.s + j, out=self.out[l])
+                if self.fused:
+                    kvq.kv_append_attend_q4(self.caches[l], q, kn, vn, w.s + j - 1, out=self.out[l])
+                else:
+                    kvq.decode_attention_q4(self.caches[l], q, w.s + j, out=self.out[l])
                 if events is not None:
                     e1.record(self.stream)
                     events.append((e0, e1, self.b_decode_per_launch[j - 1]))
@@ -307,6 +315,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=0, help="decode steps per job (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="append and attend in one kv_append_attend_q4 launch per layer-step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -346,7 +356,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": "k_decode<128,4,2> (decode_attention_q4)",
+                "kernel": ("k_decode<128,4,2> (kv_append_attend_q4: append + attention)" if job.fused
+                           else "k_decode<128,4,2> (decode_attention_q4)"),
                 "algorithmic_bytes_per_launch": int(avg_bytes),
                 "avg_launch_ms": round(avg_ms, 5), "launches_timed": len(events)}
 
@@ -357,7 +368,8 @@ def main():
         "config": {"workload": f"OPT-175B layer stack: b={w.b} a={w.a} d={w.d} h={w.h}, prompt {w.s}, "
                                f"{job.n} decode steps, {job.L} int4 caches resident",
                    "b": w.b, "a": w.a, "d": w.d, "h": w.h, "s": w.s, "n": job.n, "layers": job.L,
-                   "step": "prefill quantise all layers + n x (append + decode attention) all layers",
+                   "step": ("prefill quantise all layers + n x (append + decode attention) all layers"
+                            + (", append fused into the attention launch" if job.fused else ", two launches")),
                    "parallelism": "1 GPU"},
         "roofline": roofline,
         "decode_attention": {"gbs": round(achieved, 1), "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),

@@ -141,6 +141,17 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
                               int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
                               size_t ws_bytes, void *hip_stream);
 
+/* One decode step in one launch: kv_append_quant(cache, k_new, v_new, pos)
+ * followed by decode_attention_q4(cache, q, pos + 1, out, num_splits, ...),
+ * the blog's "解码阶段" order (concatenate the new token's K/V, then attend
+ * with its query).  0 <= pos < s+n; k_new, v_new, q, out fp16 [b][1][a][d];
+ * the workspace is kvq_workspace_bytes(dims, pos + 1, num_splits, 0).
+ * The cache planes and the output are bit-identical to the two separate
+ * calls. */
+int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k_f16, const void *v_f16,
+                        int32_t pos, void *out_f16, int32_t num_splits, void *ws, size_t ws_bytes,
+                        void *hip_stream);
+
 /* Sparse decode attention: for every (batch row, head) score all ctx_len
  * tokens, keep the k_top highest scores (ties to the smaller token index),
  * and take the softmax and P.V over the kept tokens only.

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "KvqError", "QuantKVCache", "kvq_cache_bytes", "kvq_workspace_bytes", "kv_quantize_prefill",
-    "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "decode_attention_q4_topk",
+    "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4",
+    "decode_attention_q4_topk",
     "library_path", "load_library", "GROUP",
 ]
 
@@ -31,7 +32,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq4.so")
 
 EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_append_quant", "kvq_workspace_bytes",
-            "decode_attention_q4", "decode_attention_q4_tuned", "decode_attention_q4_topk", "kvq_strerror")
+            "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4", "decode_attention_q4_topk",
+            "kvq_strerror")
 
 
 class KvqDims(ctypes.Structure):
@@ -81,6 +83,8 @@ def load_library() -> ctypes.CDLL:
     L.decode_attention_q4.restype = ctypes.c_int
     L.decode_attention_q4_tuned.argtypes = [PC, P, I32, P, I32, I32, I32, P, SZ, P]
     L.decode_attention_q4_tuned.restype = ctypes.c_int
+    L.kv_append_attend_q4.argtypes = [PC, P, P, P, I32, P, I32, P, SZ, P]
+    L.kv_append_attend_q4.restype = ctypes.c_int
     L.decode_attention_q4_topk.argtypes = [PC, P, I32, I32, P, P, P, SZ, P]
     L.decode_attention_q4_topk.restype = ctypes.c_int
     L.kvq_strerror.argtypes = [ctypes.c_int]
@@ -223,6 +227,22 @@ def decode_attention_q4_tuned(cache: QuantKVCache, q: torch.Tensor, ctx_len: int
     _check(load_library().decode_attention_q4_tuned(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
                                                     unroll, waves_per_pair, _ptr(ws), need, _stream(stream)),
            "decode_attention_q4_tuned")
+    return out
+
+
+def kv_append_attend_q4(cache: QuantKVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, pos: int,
+                        out: torch.Tensor | None = None, num_splits: int = 0, ws: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """One decode step in one launch: append (k_new, v_new) at slot `pos`, then attend over
+    slots 0..pos with q.  All fp16 [b, 1, a, d]."""
+    for t, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _act(t, (cache.b, 1, cache.a, cache.d), name)
+    if out is None:
+        out = torch.empty_like(q)
+    _act(out, q.shape, "out")
+    ws, need = _workspace(cache, pos + 1, num_splits, ws)
+    _check(load_library().kv_append_attend_q4(cache.struct_ref(), _ptr(q), _ptr(k_new), _ptr(v_new), pos, _ptr(out),
+                                              num_splits, _ptr(ws), need, _stream(stream)), "kv_append_attend_q4")
     return out
 
 

@@ -179,15 +179,21 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
     return kvq::decode_ws_floats(pairs, hd, s) * sizeof(float);
 }
 
-int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
-                              int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
-                              size_t ws_bytes, void *hip_stream)
+} // extern "C"
+
+namespace {
+
+int decode_common(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16, int32_t num_splits,
+                  int32_t unroll, int32_t waves_per_pair, void *ws, size_t ws_bytes, const void *k_new,
+                  const void *v_new, void *hip_stream)
 {
     kvq::CachePlanes c;
     int st = check_cache(cache, &c);
     if (st != KVQ_OK)
         return st;
     if ((st = check_act(q_f16)) != KVQ_OK || (st = check_act(out_f16)) != KVQ_OK)
+        return st;
+    if (k_new != nullptr && ((st = check_act(k_new)) != KVQ_OK || (st = check_act(v_new)) != KVQ_OK))
         return st;
     if (ctx_len < 1 || ctx_len > c.S)
         return KVQ_ERANGE;
@@ -204,15 +210,38 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
     const size_t need = kvq::decode_ws_floats(pairs, c.d, sh.splits) * sizeof(float);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need))
         return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
-    return status_of(kvq::launch_decode(c, pairs, q_f16, ctx_len, out_f16, sh, static_cast<float *>(ws),
-                                        static_cast<hipStream_t>(hip_stream)));
+    return status_of(kvq::launch_decode(c, pairs, q_f16, ctx_len, out_f16, sh, static_cast<float *>(ws), k_new,
+                                        v_new, static_cast<hipStream_t>(hip_stream)));
+}
+
+} // namespace
+
+extern "C" {
+
+int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                              int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
+                              size_t ws_bytes, void *hip_stream)
+{
+    return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, unroll, waves_per_pair, ws, ws_bytes, nullptr,
+                         nullptr, hip_stream);
 }
 
 int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
                         int32_t num_splits, void *ws, size_t ws_bytes, void *hip_stream)
 {
-    return decode_attention_q4_tuned(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll,
-                                     kDefaultWavesPerPair, ws, ws_bytes, hip_stream);
+    return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll, kDefaultWavesPerPair, ws,
+                         ws_bytes, nullptr, nullptr, hip_stream);
+}
+
+int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k_f16, const void *v_f16,
+                        int32_t pos, void *out_f16, int32_t num_splits, void *ws, size_t ws_bytes, void *hip_stream)
+{
+    if (k_f16 == nullptr || v_f16 == nullptr)
+        return KVQ_EINVAL;
+    if (cache != nullptr && check_dims(&cache->dims) == KVQ_OK && (pos < 0 || pos >= cache->dims.s + cache->dims.n))
+        return KVQ_ERANGE;
+    return decode_common(cache, q_f16, pos + 1, out_f16, num_splits, kDefaultUnroll, kDefaultWavesPerPair, ws,
+                         ws_bytes, k_f16, v_f16, hip_stream);
 }
 
 int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,

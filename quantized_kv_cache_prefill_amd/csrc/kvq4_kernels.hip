@@ -160,6 +160,59 @@ __device__ __forceinline__ float token_sum(float v)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ===========================================================================
+// The group codec for one lane's 8 consecutive fp16 values; 8 consecutive
+// lanes (an aligned 8-lane group) hold one 64-element group.  Every lane of
+// the wave must be active (DPP).  Binary32, one rounding per operation:
+// min/max over the group (exact; -0 -> +0), rng = max - min, scale = rng/15,
+// inv = 15/rng (correctly rounded divisions), code = clamp(rint_even((x -
+// min) * inv), 0, 15); a constant group gets scale 0 and codes 0.  word holds
+// the lane's 8 codes, element i at bits 4i..4i+3.
+// ===========================================================================
+__device__ __forceinline__ void quant_lane8(const uint4 x, uint32_t &word, float &mn_out, float &scale_out)
+{
+#pragma clang fp contract(off)
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = h2f_lo(w[j]);
+        f[2 * j + 1] = h2f_hi(w[j]);
+    }
+    float mn = f[0], mx = f[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, f[i]);
+        mx = fmaxf(mx, f[i]);
+    }
+    mn = fminf(mn, dpp<kQuadXor1>(mn));
+    mx = fmaxf(mx, dpp<kQuadXor1>(mx));
+    mn = fminf(mn, dpp<kQuadXor2>(mn));
+    mx = fmaxf(mx, dpp<kQuadXor2>(mx));
+    mn = fminf(mn, dpp<kHalfRowMirror>(mn));
+    mx = fmaxf(mx, dpp<kHalfRowMirror>(mx));
+    mn = mn + 0.0f; // -0 -> +0
+    mx = mx + 0.0f;
+    const float rng = mx - mn;
+    uint32_t codes = 0;
+    float scale = 0.0f;
+    if (rng != 0.0f) {
+        scale = rng / 15.0f; // correctly rounded (HIP default division)
+        const float inv = 15.0f / rng;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float t = f[i] - mn;
+            t = t * inv;
+            float r = __builtin_rintf(t); // ties to even
+            r = fminf(fmaxf(r, 0.0f), 15.0f);
+            codes |= (uint32_t)r << (4 * i);
+        }
+    }
+    word = codes;
+    mn_out = mn;
+    scale_out = scale;
+}
+
+// ===========================================================================
 // Quantise.  Each lane loads 8 fp16 values (16 bytes); 8 consecutive lanes
 // hold one 64-element group and reduce its min/max with three DPP steps.
 // Row r of the flattened work list is (pair, token) = (r / s_src, r % s_src),
@@ -173,7 +226,6 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
                                                   float *__restrict__ k_min, float *__restrict__ k_scale,
                                                   float *__restrict__ v_min, float *__restrict__ v_scale)
 {
-#pragma clang fp contract(off)
     constexpr int LPR = D / 8;   // lanes per token row
     constexpr int RPB = 256 / LPR;
     constexpr int G = D / 64;
@@ -202,42 +254,9 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
     }
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[2 * j] = h2f_lo(w[j]);
-            f[2 * j + 1] = h2f_hi(w[j]);
-        }
-        float mn = f[0], mx = f[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-            mn = fminf(mn, f[i]);
-            mx = fmaxf(mx, f[i]);
-        }
-        mn = fminf(mn, dpp<kQuadXor1>(mn));
-        mx = fmaxf(mx, dpp<kQuadXor1>(mx));
-        mn = fminf(mn, dpp<kQuadXor2>(mn));
-        mx = fmaxf(mx, dpp<kQuadXor2>(mx));
-        mn = fminf(mn, dpp<kHalfRowMirror>(mn));
-        mx = fmaxf(mx, dpp<kHalfRowMirror>(mx));
-        mn = mn + 0.0f; // -0 -> +0
-        mx = mx + 0.0f;
-        const float rng = mx - mn;
-        uint32_t word = 0;
-        float scale = 0.0f;
-        if (rng != 0.0f) {
-            scale = rng / 15.0f;          // correctly rounded (HIP default division)
-            const float inv = 15.0f / rng;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float t = f[i] - mn;
-                t = t * inv;
-                float r = __builtin_rintf(t); // ties to even
-                r = fminf(fmaxf(r, 0.0f), 15.0f);
-                word |= (uint32_t)r << (4 * i);
-            }
-        }
+        uint32_t word;
+        float mn, scale;
+        quant_lane8(x[u], word, mn, scale);
         // Nontemporal stores: cache rows are read back only by a later launch,
         // and ordinary stores left dirty lines whose write-back slowed the next
         // decode launch by ~5% (measured on MI355X).
@@ -256,6 +275,12 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
 // clamped to t_end-1 so they stay inside the written cache).  Updates the
 // lane's online-softmax state (m, l in log2 units; bsum collects the folded
 // min terms; acc the biased P.V sums).
+// One token row in the attention lane layout (see append_rows).
+struct NewRow {
+    uint4 kx, vx;
+    float km, ks, vm, vs;
+};
+
 // The streams of one (batch row, head): plane bases that are uniform across
 // the wave (scalar registers), and the lane's 32-bit offsets of its slice
 // inside a token row.  Loads then take the scalar-base + 32-bit-offset
@@ -290,9 +315,10 @@ __device__ __forceinline__ CacheRow cache_row(const uint8_t *kc, const uint8_t *
             vsc ? vsc + mb : nullptr, (uint32_t)part * 16u, (uint32_t)(part >> 1) * 4u};
 }
 
-template <int D, int UU>
+template <int D, int UU, bool NEWROW = false>
 __device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
-                                            float c2, float &m, float &l, float &bsum, float (&acc)[32])
+                                            float c2, float &m, float &l, float &bsum, float (&acc)[32],
+                                            const NewRow nr = NewRow{}, int t_new = -1)
 {
     constexpr int LPT = D / 32;
     constexpr int TPW = 64 / LPT;
@@ -312,6 +338,16 @@ __device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_en
         ks[u] = ld_stream(at_byte(cr.ksb, mo));
         vm[u] = ld_stream(at_byte(cr.vmb, mo));
         vs[u] = ld_stream(at_byte(cr.vsb, mo));
+        if constexpr (NEWROW) {
+            if (t == t_new) {
+                kx[u] = nr.kx;
+                vx[u] = nr.vx;
+                km[u] = nr.km;
+                ks[u] = nr.ks;
+                vm[u] = nr.vm;
+                vs[u] = nr.vs;
+            }
+        }
     }
     float z[UU];
     float mx = m;
@@ -342,6 +378,58 @@ __device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_en
     }
 }
 
+// Fused append.  The wave whose range ends at the new slot quantises the new
+// token's K and V rows of its (batch row, head) and stores them into slot
+// `pos` for later steps.  It does not wait for or read back those stores:
+// the row is also returned in the attention lane layout (lane `part` gets
+// code words 4*part..4*part+3 and the min/scale of group part/2) and is
+// substituted for slot `pos` in the wave's last iteration.  The values are
+// the stored ones, so the result is identical to a separate append.
+// The lane's 16 bytes of the new K row (lanes 0..D/8-1) or V row (lanes
+// D/8..2D/8-1); lanes past 2*D/8 repeat the V row.  Loaded at the start of the
+// tail wave so the load latency is hidden behind its main loop.
+template <int D>
+__device__ __forceinline__ uint4 load_new_row(const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new,
+                                              int64_t pair, int lane)
+{
+    constexpr int LPR = D / 8;
+    return ld_stream16((lane < LPR ? k_new : v_new) + pair * (D / 8) + lane % LPR);
+}
+
+template <int D>
+__device__ __forceinline__ NewRow append_rows(const uint4 x, int64_t pair, int64_t pos, int S, uint8_t *kc,
+                                              uint8_t *vc, float *kmin, float *ksc, float *vmin, float *vsc,
+                                              int lane)
+{
+    constexpr int LPR = D / 8;
+    constexpr int G = D / 64;
+    constexpr int LPT = D / 32;
+    const int which = min(lane / LPR, 1);
+    const int lir = lane % LPR;
+    uint32_t word;
+    float mn, scale;
+    quant_lane8(x, word, mn, scale);
+    if (lane < 2 * LPR) {
+        const int64_t slot = pair * S + pos;
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(which ? vc : kc) + slot * (D / 8) + lir);
+        if ((lir & 7) == 0) {
+            __builtin_nontemporal_store(mn, (which ? vmin : kmin) + slot * G + (lir >> 3));
+            __builtin_nontemporal_store(scale, (which ? vsc : ksc) + slot * G + (lir >> 3));
+        }
+    }
+    const int part = lane % LPT, g = part >> 1;
+    NewRow r;
+    r.kx = make_uint4(__shfl(word, 4 * part), __shfl(word, 4 * part + 1), __shfl(word, 4 * part + 2),
+                      __shfl(word, 4 * part + 3));
+    r.vx = make_uint4(__shfl(word, LPR + 4 * part), __shfl(word, LPR + 4 * part + 1),
+                      __shfl(word, LPR + 4 * part + 2), __shfl(word, LPR + 4 * part + 3));
+    r.km = __shfl(mn, 8 * g);
+    r.ks = __shfl(scale, 8 * g);
+    r.vm = __shfl(mn, LPR + 8 * g);
+    r.vs = __shfl(scale, LPR + 8 * g);
+    return r;
+}
+
 // ===========================================================================
 // Dense decode attention.
 //
@@ -360,12 +448,11 @@ __device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_en
 // mixed-precision FMA (V).  Scores are kept in log2 units (z = s*log2e/sqrt(d)).
 // ===========================================================================
 template <int D, int U, int WPP>
-__global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ kc, const uint8_t *__restrict__ vc,
-                                                const float *__restrict__ kmin, const float *__restrict__ ksc,
-                                                const float *__restrict__ vmin, const float *__restrict__ vsc,
-                                                const uint4 *__restrict__ q, uint4 *__restrict__ out,
+__global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, float *kmin, float *ksc, float *vmin,
+                                                float *vsc, const uint4 *__restrict__ q, uint4 *__restrict__ out,
                                                 float *__restrict__ ws, int pairs, int S, int T, int splits,
-                                                int split_len, float c2)
+                                                int split_len, float c2, const uint4 *__restrict__ k_new,
+                                                const uint4 *__restrict__ v_new)
 {
     constexpr int LPT = D / 32;
     constexpr int TPW = 64 / LPT;
@@ -394,6 +481,12 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ kc, 
     const int t_end = min(t1, w_begin + per_wave);
     const int n_full = (t_end - w_begin) / TPI;            // iterations with all U rows valid
     const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW; // single-row tail iterations
+    // Fused append (k_new != null): the wave whose range ends at the new slot
+    // T-1 quantises and stores it, and uses the register copy in its last row.
+    const bool tail_wave = k_new != nullptr && pair_ok && t_end == T && w_begin < t_end; // wave-uniform
+    uint4 new_raw = make_uint4(0, 0, 0, 0);
+    if (tail_wave)
+        new_raw = load_new_row<D>(k_new, v_new, pc, lane);
     const QSlice qs = load_q_slice(q + pc * (D / 8) + part * 4);
     const uint32_t mg = magic64_vgpr();
 
@@ -406,10 +499,24 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ kc, 
         acc[i] = 0.0f;
 
     int tb = w_begin + lt;
-    for (int it = 0; it < n_full; ++it, tb += TPI)
-        decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
-    for (int it = 0; it < n_rest; ++it, tb += TPW)
-        decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
+    if (!tail_wave) {
+        for (int it = 0; it < n_full; ++it, tb += TPI)
+            decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
+        for (int it = 0; it < n_rest; ++it, tb += TPW)
+            decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
+    } else {
+        // every row but the last TPW-row chunk as usual, then that chunk with
+        // the new row substituted for slot T-1
+        const int last = w_begin + (t_end - 1 - w_begin) / TPW * TPW;
+        const int nf = (last - w_begin) / TPI;
+        const int nr1 = (last - w_begin - nf * TPI) / TPW;
+        for (int it = 0; it < nf; ++it, tb += TPI)
+            decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
+        for (int it = 0; it < nr1; ++it, tb += TPW)
+            decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
+        const NewRow nr = append_rows<D>(new_raw, pc, T - 1, S, kc, vc, kmin, ksc, vmin, vsc, lane);
+        decode_iter<D, 1, true>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc, nr, T - 1);
+    }
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         acc[i] += bsum;
@@ -1004,14 +1111,15 @@ int launch_quantize_d(const CachePlanes &c, const void *k, const void *v, int b,
 
 template <int D, int U, int WPP>
 int launch_decode_k(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
-                    float *ws, hipStream_t st)
+                    float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     constexpr int PPB = 4 / WPP;
     const float c2 = 1.4426950408889634f / sqrtf((float)D);
     const int64_t blocks = (int64_t)((pairs + PPB - 1) / PPB) * sh.splits;
     hipLaunchKernelGGL((k_decode<D, U, WPP>), dim3((unsigned)blocks), dim3(256), 0, st, c.k_codes, c.v_codes,
                        c.k_min, c.k_scale, c.v_min, c.v_scale, static_cast<const uint4 *>(q),
-                       static_cast<uint4 *>(out), ws, pairs, c.S, T, sh.splits, sh.split_len, c2);
+                       static_cast<uint4 *>(out), ws, pairs, c.S, T, sh.splits, sh.split_len, c2,
+                       static_cast<const uint4 *>(k_new), static_cast<const uint4 *>(v_new));
     int e = (int)hipGetLastError();
     if (e != 0 || sh.splits == 1)
         return e;
@@ -1022,23 +1130,23 @@ int launch_decode_k(const CachePlanes &c, int pairs, const void *q, int T, void 
 
 template <int D, int U>
 int launch_decode_u(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
-                    float *ws, hipStream_t st)
+                    float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     switch (sh.waves_per_pair) {
-    case 1: return launch_decode_k<D, U, 1>(c, pairs, q, T, out, sh, ws, st);
-    case 2: return launch_decode_k<D, U, 2>(c, pairs, q, T, out, sh, ws, st);
-    default: return launch_decode_k<D, U, 4>(c, pairs, q, T, out, sh, ws, st);
+    case 1: return launch_decode_k<D, U, 1>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 2: return launch_decode_k<D, U, 2>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    default: return launch_decode_k<D, U, 4>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
     }
 }
 
 template <int D>
 int launch_decode_d(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
-                    float *ws, hipStream_t st)
+                    float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     switch (sh.unroll) {
-    case 1: return launch_decode_u<D, 1>(c, pairs, q, T, out, sh, ws, st);
-    case 2: return launch_decode_u<D, 2>(c, pairs, q, T, out, sh, ws, st);
-    default: return launch_decode_u<D, 4>(c, pairs, q, T, out, sh, ws, st);
+    case 1: return launch_decode_u<D, 1>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 2: return launch_decode_u<D, 2>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    default: return launch_decode_u<D, 4>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
     }
 }
 
@@ -1084,12 +1192,12 @@ int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, i
 }
 
 int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
-                  float *ws, hipStream_t st)
+                  float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     switch (c.d) {
-    case 64: return launch_decode_d<64>(c, pairs, q, T, out, sh, ws, st);
-    case 128: return launch_decode_d<128>(c, pairs, q, T, out, sh, ws, st);
-    default: return launch_decode_d<256>(c, pairs, q, T, out, sh, ws, st);
+    case 64: return launch_decode_d<64>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 128: return launch_decode_d<128>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    default: return launch_decode_d<256>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
     }
 }
 

@@ -26,7 +26,8 @@ int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, i
 
 // Dense decode attention.  splits ranges of split_len tokens each; when
 // splits > 1 the partial (max, sum, unnormalised output) go to ws and the
-// reduce pass writes out.
+// reduce pass writes out.  With k_new/v_new non-null ([b][1][a][d] fp16),
+// the same launch first quantises them into slot T-1 (fused append).
 struct DecodeShape {
     int unroll;          // tokens per lane per iteration: 1, 2, 4
     int waves_per_pair;  // 1, 2, 4
@@ -34,7 +35,7 @@ struct DecodeShape {
     int split_len;
 };
 int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
-                  float *ws, hipStream_t st);
+                  float *ws, const void *k_new, const void *v_new, hipStream_t st);
 
 // Workspace floats needed by launch_decode for `splits` > 1.
 size_t decode_ws_floats(int pairs, int d, int splits);

@@ -141,6 +141,20 @@ def test_workspace_sizing_and_enospace(L):
     assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2048, 205, FAKE, None, None, 0, st) == KVQ_ENOSPACE
 
 
+def test_append_attend_validation(L):
+    st = ctypes.c_void_p(0)
+    c = cache()  # S = 20
+    assert L.kv_append_attend_q4(None, FAKE, FAKE, FAKE, 0, FAKE, 0, None, 0, st) == KVQ_EINVAL
+    assert L.kv_append_attend_q4(ctypes.byref(c), FAKE, None, FAKE, 0, FAKE, 0, None, 0, st) == KVQ_EINVAL
+    assert L.kv_append_attend_q4(ctypes.byref(c), FAKE, FAKE, FAKE + 2, 0, FAKE, 0, None, 0, st) == KVQ_EINVAL
+    assert L.kv_append_attend_q4(ctypes.byref(c), FAKE, FAKE, FAKE, -1, FAKE, 0, None, 0, st) == KVQ_ERANGE
+    assert L.kv_append_attend_q4(ctypes.byref(c), FAKE, FAKE, FAKE, 20, FAKE, 0, None, 0, st) == KVQ_ERANGE
+    assert L.kv_append_attend_q4(ctypes.byref(cache(dims(group=32))), FAKE, FAKE, FAKE, 0, FAKE, 0, None, 0,
+                                 st) == KVQ_EUNSUPPORTED
+    d = dims(b=1, a=1, h=128, s=4000, n=96)
+    assert L.kv_append_attend_q4(ctypes.byref(cache(d)), FAKE, FAKE, FAKE, 4095, FAKE, 7, None, 0, st) == KVQ_ENOSPACE
+
+
 def test_strerror(L):
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert len(L.kvq_strerror(s)) > 0

@@ -382,3 +382,63 @@ def test_topk_deterministic():
     o2, s2 = kvq.decode_attention_q4_topk(cache, q, T, 150)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(s1, s2)
+
+
+# ----------------------------------------------------------------- fused decode step
+@pytest.mark.parametrize("d,b,a,s,pos,splits", [
+    (128, 3, 5, 40, 40, 0), (128, 2, 3, 600, 600, 0), (128, 2, 3, 600, 640, 3), (64, 2, 2, 16, 16, 0),
+    (256, 2, 3, 100, 150, 2), (128, 1, 2, 200, 0, 0), (128, 4, 4, 256, 256, 2), (128, 1, 1, 16384, 16384, 0),
+])
+def test_fused_step_bit_identical_to_separate_calls(d, b, a, s, pos, splits):
+    """kv_append_attend_q4 == kv_append_quant + decode_attention_q4(ctx = pos + 1), bit for bit,
+    for the cache planes and the output; and within tolerance of the oracle.  Covers the new
+    slot at the start, at a wave boundary, at a split boundary and in split mode."""
+    require_gpu()
+    n = max(1, pos - s + 1)
+    S = s + n
+    seed = 3000 + d + pos
+    k = W.random_fp16((b, S, a, d), seed, DEV)
+    v = W.random_fp16((b, S, a, d), seed + 1, DEV)
+    kn = W.random_fp16((b, 1, a, d), seed + 2, DEV)
+    vn = W.random_fp16((b, 1, a, d), seed + 3, DEV)
+    q = W.random_fp16((b, 1, a, d), seed + 4, DEV)
+    c1 = kvq.QuantKVCache(b, a, a * d, s, n, device=DEV, fill=0xFF)
+    c2 = kvq.QuantKVCache(b, a, a * d, s, n, device=DEV, fill=0xFF)
+    for c in (c1, c2):
+        kvq.kv_quantize_prefill(c, k, v)
+    kvq.kv_append_quant(c1, kn, vn, pos)
+    o1 = kvq.decode_attention_q4(c1, q, pos + 1, out=_nan_out(b, a, d), num_splits=splits)
+    o2 = kvq.kv_append_attend_q4(c2, q, kn, vn, pos, out=_nan_out(b, a, d), num_splits=splits)
+    torch.cuda.synchronize()
+    for t1, t2 in zip(c1.planes(), c2.planes()):
+        assert torch.equal(t1, t2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    hc = HostCache(b, a, d, S)
+    hc.prefill(f16_np(k), f16_np(v))
+    hc.append(f16_np(kn), f16_np(vn), pos)
+    pairs = all_pairs(b, a)
+    ref = oracle_attend_pairs(hc, f16_np(q), pos + 1, pairs)
+    assert_close(_gpu_rows(o2, pairs), ref, f"fused d={d} pos={pos}")
+
+
+def test_fused_decode_loop_opt_6_7b_shape():
+    """The OPT-6.7B layer (b=32, a=32, d=128), 32 fused decode steps after a 512-token prompt:
+    every appended slot bit-exact, outputs of sampled pairs within tolerance."""
+    require_gpu()
+    w = W.OPT_6_7B
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=DEV, fill=0xFF)
+    k, v = W.prefill_kv(w, 1, DEV)
+    kvq.kv_quantize_prefill(cache, k, v)
+    hc = HostCache(w.b, w.a, w.d, w.S)
+    pairs = sample_pairs(w.b, w.a, 48, seed=61)
+    hc.prefill(f16_np(k), f16_np(v), pairs)
+    for j in range(1, w.n + 1):
+        pos = w.s + j - 1
+        q, kn, vn = W.decode_inputs(w, 1, j, DEV)
+        out = kvq.kv_append_attend_q4(cache, q, kn, vn, pos, out=_nan_out(w.b, w.a, w.d))
+        torch.cuda.synchronize()
+        hc.append(f16_np(kn), f16_np(vn), pos)
+        _check_slot(cache, hc, pos, "fused opt-6.7b")
+        if j in (1, 2, 16, 32):
+            ref = oracle_attend_pairs(hc, f16_np(q), pos + 1, pairs)
+            assert_close(_gpu_rows(out, pairs), ref, f"fused opt-6.7b step {j}")
