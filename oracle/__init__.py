@@ -10,7 +10,8 @@ and marshals numpy arrays into it.  What each function computes and which
 page passage it follows is stated in the C source:
 
 * codec -- "FlexGen研究学术报告", section 三.2(C): group-wise asymmetric
-  4-bit quantisation, 64 contiguous elements per group; attention uses the
+  4-bit quantisation, 64 contiguous elements per group, with binary32 or
+  binary16 (``*_m16``) min/scale planes; attention uses the
   dequantised values min + code*scale exactly (the report's FP16 form is
   available as ``dequant_rows_f16``);
 * dense attention -- the FlexGen blog's decode-phase equation (section
@@ -54,6 +55,8 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_f32_to_f16.restype = ctypes.c_uint16
     L.oracle_quantize_group.argtypes = [P, P, P, P]
     L.oracle_quantize_rows.argtypes = [I, I, P, P, P, P]
+    L.oracle_quantize_group_m16.argtypes = [P, P, P, P]
+    L.oracle_quantize_rows_m16.argtypes = [I, I, P, P, P, P]
     L.oracle_dequant_rows.argtypes = [I, I, P, P, P, P]
     L.oracle_dequant_rows_f16.argtypes = [I, I, P, P, P, P]
     L.oracle_scores.argtypes = [I, I, P, P, P, P, P]
@@ -61,7 +64,8 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_attend_subset.argtypes = [I, I, P, P, P, P, P, P, P, P, P]
     L.oracle_select_topk.argtypes = [I, P, I, P]
     L.oracle_attend_topk.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P]
-    for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_dequant_rows", "oracle_dequant_rows_f16",
+    for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_quantize_group_m16", "oracle_quantize_rows_m16",
+              "oracle_dequant_rows", "oracle_dequant_rows_f16",
               "oracle_scores",
               "oracle_attend", "oracle_attend_subset", "oracle_select_topk", "oracle_attend_topk"):
         getattr(L, f).restype = None
@@ -169,6 +173,31 @@ def quantize_rows(x):
     scales = np.zeros(lead + (d // GROUP,), np.float32)
     lib().oracle_quantize_rows(n, d, _ptr(x), _ptr(codes), _ptr(mins), _ptr(scales))
     return codes, mins, scales
+
+
+def quantize_group_m16(x64):
+    """One group with binary16 metadata -> (codes uint8[32], min float16, scale float16)."""
+    x = _f16bits(x64).reshape(-1)
+    assert x.size == GROUP
+    codes = np.zeros(GROUP // 2, np.uint8)
+    mn = np.zeros(1, np.uint16)
+    sc = np.zeros(1, np.uint16)
+    lib().oracle_quantize_group_m16(_ptr(x), _ptr(codes), _ptr(mn), _ptr(sc))
+    return codes, mn.view(np.float16)[0], sc.view(np.float16)[0]
+
+
+def quantize_rows_m16(x):
+    """Like quantize_rows with binary16 metadata: mins/scales float16 [..., d/64]."""
+    x = _f16bits(x)
+    d = x.shape[-1]
+    assert d % GROUP == 0
+    lead = x.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    codes = np.zeros(lead + (d // 2,), np.uint8)
+    mins = np.zeros(lead + (d // GROUP,), np.uint16)
+    scales = np.zeros(lead + (d // GROUP,), np.uint16)
+    lib().oracle_quantize_rows_m16(n, d, _ptr(x), _ptr(codes), _ptr(mins), _ptr(scales))
+    return codes, mins.view(np.float16), scales.view(np.float16)
 
 
 def _dequant_args(codes, mins, scales):

@@ -42,6 +42,9 @@
  *     min + c*scale, code = round_half_even((x-min)*(15/(max-min))),
  *     clamped to 0..15;
  *   - a constant group (max == min) stores scale 0 and codes 0;
+ *   - metadata planes in binary32 (oracle_quantize_group) or binary16
+ *     (oracle_quantize_group_m16: min exact, scale rounded to nearest, codes
+ *     taken against the stored scale);
  *   - a stored min/max of -0 is canonicalised to +0;
  *   - two codes per byte, the even element in the low nibble;
  *   - attention scale 1/sqrt(d), d = head_dim = h/a (the survey's d_k);
@@ -117,10 +120,9 @@ uint16_t oracle_f32_to_f16(float f)
  *   else scale = rng / 15, inv = 15 / rng (correctly rounded divisions),
  *        code = clamp(rint_half_even((x - mn) * inv), 0, 15);
  *   byte j = code[2j] | code[2j+1] << 4.                                   */
-void oracle_quantize_group(const uint16_t *x, uint8_t *codes, float *out_min, float *out_scale)
+/* Widen a group to binary32 and find its min and max, -0 stored as +0. */
+static void group_minmax(const uint16_t *x, float *f, float *out_mn, float *out_mx)
 {
-    float f[ORACLE_GROUP];
-    int c[ORACLE_GROUP];
     for (int i = 0; i < ORACLE_GROUP; ++i)
         f[i] = oracle_f16_to_f32(x[i]);
     float mn = f[0], mx = f[0];
@@ -130,8 +132,22 @@ void oracle_quantize_group(const uint16_t *x, uint8_t *codes, float *out_min, fl
         if (f[i] > mx)
             mx = f[i];
     }
-    mn = mn + 0.0f;
-    mx = mx + 0.0f;
+    *out_mn = mn + 0.0f;
+    *out_mx = mx + 0.0f;
+}
+
+static void pack_codes(const int *c, uint8_t *codes)
+{
+    for (int j = 0; j < ORACLE_GROUP / 2; ++j)
+        codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+}
+
+void oracle_quantize_group(const uint16_t *x, uint8_t *codes, float *out_min, float *out_scale)
+{
+    float f[ORACLE_GROUP];
+    int c[ORACLE_GROUP];
+    float mn, mx;
+    group_minmax(x, f, &mn, &mx);
     float rng = mx - mn;
     float scale;
     if (rng == 0.0f) {
@@ -152,10 +168,52 @@ void oracle_quantize_group(const uint16_t *x, uint8_t *codes, float *out_min, fl
             c[i] = (int)r;
         }
     }
-    for (int j = 0; j < ORACLE_GROUP / 2; ++j)
-        codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+    pack_codes(c, codes);
     *out_min = mn;
     *out_scale = scale;
+}
+
+/* The same codec with binary16 min and scale planes (half the metadata
+ * bytes).  The pages fix no metadata type; this variant stores:
+ *   min   = the group minimum, which is one of the fp16 inputs, so exact;
+ *   scale = the binary32 quotient rng/15 rounded to the nearest binary16
+ *           value, ties to even;
+ * and takes the codes against the stored pair, so that min + code*scale is
+ * the nearest of the 16 levels it can reconstruct:
+ *   inv = 1/scale (binary32, correctly rounded),
+ *   code = clamp(rint_half_even((x - min) * inv), 0, 15).
+ * A group whose stored scale is 0 (a constant group, or a range below
+ * 15 * 2^-25 whose scale underflows binary16) gets codes 0.                */
+void oracle_quantize_group_m16(const uint16_t *x, uint8_t *codes, uint16_t *out_min, uint16_t *out_scale)
+{
+    float f[ORACLE_GROUP];
+    int c[ORACLE_GROUP];
+    float mn, mx;
+    group_minmax(x, f, &mn, &mx);
+    float rng = mx - mn;
+    uint16_t s16 = 0;
+    if (rng != 0.0f)
+        s16 = oracle_f32_to_f16(rng / 15.0f);
+    float scale = oracle_f16_to_f32(s16);
+    if (scale == 0.0f) {
+        for (int i = 0; i < ORACLE_GROUP; ++i)
+            c[i] = 0;
+    } else {
+        float inv = 1.0f / scale;
+        for (int i = 0; i < ORACLE_GROUP; ++i) {
+            float t = f[i] - mn;
+            t = t * inv;
+            float r = rintf(t);
+            if (r < 0.0f)
+                r = 0.0f;
+            if (r > 15.0f)
+                r = 15.0f;
+            c[i] = (int)r;
+        }
+    }
+    pack_codes(c, codes);
+    *out_min = oracle_f32_to_f16(mn);
+    *out_scale = s16;
 }
 
 /* Quantise one token row of d fp16 values (d a multiple of 64): group g
@@ -173,6 +231,18 @@ void oracle_quantize_rows(int nrows, int d, const uint16_t *x, uint8_t *codes, f
     for (int r = 0; r < nrows; ++r)
         oracle_quantize_row(d, x + (size_t)r * d, codes + (size_t)r * (d / 2), mins + (size_t)r * G,
                             scales + (size_t)r * G);
+}
+
+/* Rows with binary16 metadata: mins[d/64], scales[d/64] as binary16 bits. */
+void oracle_quantize_rows_m16(int nrows, int d, const uint16_t *x, uint8_t *codes, uint16_t *mins,
+                              uint16_t *scales)
+{
+    int G = d / ORACLE_GROUP;
+    for (int r = 0; r < nrows; ++r)
+        for (int g = 0; g < G; ++g)
+            oracle_quantize_group_m16(x + (size_t)r * d + g * ORACLE_GROUP,
+                                      codes + (size_t)r * (d / 2) + g * (ORACLE_GROUP / 2), mins + (size_t)r * G + g,
+                                      scales + (size_t)r * G + g);
 }
 
 /* Code of element i of a row (low nibble = even element). */

@@ -12,7 +12,8 @@ mistake and requires each copy to fail at least one pin.
 Passages pinned:
 * the codec -- "FlexGen研究学术报告", section 三.2(C) (group-wise asymmetric
   4-bit, 64 contiguous elements; the dequantised value min + code*scale, and
-  the report's FP16 form of it);
+  the report's FP16 form of it), with binary32 and with binary16 min/scale
+  planes;
 * dense decode attention -- the FlexGen blog, section "解码阶段", with the
   1/sqrt(d_k) scale of eq. (2) in the efficient-inference survey notes;
 * top-10% sparse attention -- the report's section 三.2(C).
@@ -43,10 +44,10 @@ def _expand(tokens):
     return out
 
 
-def load_codec_examples():
-    """Parse tests/golden/codec_examples.txt into a list of dicts."""
+def load_codec_examples(name: str = "codec_examples.txt"):
+    """Parse a codec fixture under tests/golden/ into a list of dicts."""
     ex, cur = [], None
-    with open(os.path.join(GOLDEN, "codec_examples.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -59,6 +60,8 @@ def load_codec_examples():
                 cur["x"] = np.array([float(v) for v in _expand(rest)], np.float16)
             elif key in ("min", "scale"):
                 cur[key] = float(rest[0])
+            elif key == "scale_bits":
+                cur[key] = int(rest[0], 16)
             elif key == "codes":
                 cur["codes"] = np.array([int(v) for v in _expand(rest)])
             elif key == "bytes":
@@ -245,6 +248,79 @@ def pin_codec_rows_are_groupwise():
                 c1, m1, s1 = oracle.quantize_group(x[i, j, 64 * g:64 * g + 64])
                 assert np.array_equal(codes[i, j, 32 * g:32 * g + 32], c1)
                 assert mins[i, j, g] == m1 and scales[i, j, g] == s1
+
+
+# ------------------------------------------------ codec, binary16 metadata
+def pin_codec_m16_worked_examples():
+    """Hand-derived examples in tests/golden/codec_m16_examples.txt (scale rounded to
+    binary16, codes against the stored scale, underflow to 0, subnormal-scale clamp)."""
+    for ex in load_codec_examples("codec_m16_examples.txt"):
+        codes, mn, sc = oracle.quantize_group_m16(ex["x"])
+        got = unpack(codes[None])[0]
+        assert np.array_equal(got, ex["codes"]), (ex["name"], got, ex["codes"])
+        assert mn.view(np.uint16) == np.float16(ex["min"]).view(np.uint16), (ex["name"], mn)
+        assert int(sc.view(np.uint16)) == ex["scale_bits"], (ex["name"], hex(int(sc.view(np.uint16))))
+        assert float(sc) == ex["scale"], (ex["name"], sc)
+        if "bytes" in ex:
+            assert np.array_equal(codes, ex["bytes"]), (ex["name"], codes)
+
+
+def pin_codec_m16_stored_pair_is_library_rounding():
+    """The stored min is the group minimum (exact, +0 for a zero minimum) and the stored
+    scale is numpy's IEEE binary16 rounding of the binary32 quotient (max - min)/15."""
+    for x in _groups(17, 120):
+        codes, mn, sc = oracle.quantize_group_m16(x)
+        x32 = x.astype(np.float32)
+        lo, hi = x32.min() + np.float32(0), x32.max() + np.float32(0)
+        assert mn.view(np.uint16) == np.float16(lo).view(np.uint16)
+        rng = np.float32(hi - lo)
+        ref = np.float16(np.float32(rng / np.float32(15))) if rng != 0 else np.float16(0)
+        assert sc.view(np.uint16) == ref.view(np.uint16), (sc, ref)
+
+
+def pin_codec_m16_nearest_level_bruteforce():
+    """Each code is the nearest of the 16 levels min + c*scale of the STORED binary16 pair
+    (exact rational distances; values within 1e-5 of a midpoint may take either
+    neighbour); a stored scale of 0 gives codes 0."""
+    r = np.random.default_rng(18)
+    groups = _groups(19, 80)
+    for i in range(40):     # tiny ranges: subnormal scales, and (range < 7.5 * 2^-24) scales that underflow to 0
+        g = np.zeros(64)
+        g[r.integers(0, 64, 4)] = r.integers(1, 40 if i % 2 else 8, 4) * 2.0 ** -24
+        groups.append(g.astype(np.float16))
+    for x in groups:
+        codes, mn, sc = oracle.quantize_group_m16(x)
+        c = unpack(codes[None])[0]
+        xs = _exact(x)
+        s16 = Fraction(float(sc))
+        assert Fraction(float(mn)) == min(xs)
+        if s16 == 0:
+            assert not c.any()
+            continue
+        for xi, ci in zip(xs, c):
+            pos = (xi - min(xs)) / s16
+            dist = [abs(pos - k) for k in range(16)]
+            best = min(dist)
+            assert dist[ci] <= best + Fraction(1, 100000), (float(pos), ci)
+            if abs(pos - math.floor(pos) - Fraction(1, 2)) > Fraction(1, 100000):
+                assert dist[ci] == best, (float(pos), ci)
+
+
+def pin_codec_m16_error_bound():
+    """|x - (min + c*scale)| <= scale/2 for the stored scale, plus what the clamp at code 15
+    leaves when the binary16 scale rounded down (max - (min + 15*scale)); with a stored
+    scale of 0 the error is at most the group's range."""
+    for x in _groups(20, 80):
+        codes, mn, sc = oracle.quantize_group_m16(x)
+        c = unpack(codes[None])[0]
+        xs = x.astype(np.float64)
+        xhat = float(mn) + c * float(sc)
+        rng = xs.max() - xs.min()
+        if float(sc) == 0:
+            assert np.all(np.abs(xs - xhat) <= rng)
+            continue
+        over = max(0.0, rng - 15 * float(sc))
+        assert np.all(np.abs(xs - xhat) <= float(sc) / 2 * (1 + 1e-5) + over + abs(xs).max() * 2.0 ** -22)
 
 
 # ----------------------------------------------------------------- attention

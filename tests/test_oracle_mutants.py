@@ -17,10 +17,18 @@ from tests import oracle_pins
 
 MUTANTS = [
     ("round_half_away", "float r = rintf(t);", "float r = roundf(t);"),
+    ("m16_codes_against_binary32_scale", "        float inv = 1.0f / scale;\n",
+     "        float inv = 15.0f / rng;\n"),
+    ("m16_scale_truncated", "s16 = oracle_f32_to_f16(rng / 15.0f);",
+     "s16 = oracle_f32_to_f16(rng / 15.0f);\n    if (oracle_f16_to_f32(s16) > rng / 15.0f)\n        s16 -= 1;"),
+    ("m16_no_underflow_case", "    if (scale == 0.0f) {\n        for", "    if (rng == 0.0f) {\n        for"),
+    ("m16_min_rounded", "    *out_min = oracle_f32_to_f16(mn);", "    *out_min = oracle_f32_to_f16(mn * 1.0005f);"),
+    ("m16_codes_truncated", "            float r = rintf(t);\n            if (r < 0.0f)\n                r = 0.0f;\n            if (r > 15.0f)\n                r = 15.0f;\n            c[i] = (int)r;\n        }\n    }\n    pack_codes(c, codes);\n    *out_min = oracle_f32_to_f16(mn);",
+     "            float r = floorf(t);\n            if (r < 0.0f)\n                r = 0.0f;\n            if (r > 15.0f)\n                r = 15.0f;\n            c[i] = (int)r;\n        }\n    }\n    pack_codes(c, codes);\n    *out_min = oracle_f32_to_f16(mn);"),
     ("truncate_codes", "float r = rintf(t);", "float r = floorf(t);"),
     ("scale_over_16", "scale = rng / 15.0f;", "scale = rng / 16.0f;"),
     ("inv_over_16", "float inv = 15.0f / rng;", "float inv = 16.0f / rng;"),
-    ("no_signed_zero_fix", "    mn = mn + 0.0f;\n", "\n"),
+    ("no_signed_zero_fix", "    *out_mn = mn + 0.0f;\n", "    *out_mn = mn;\n"),
     ("nibbles_swapped", "codes[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));",
      "codes[j] = (uint8_t)((c[2 * j] << 4) | c[2 * j + 1]);"),
     ("dequant_drops_min", "* (double)row_scales[g] + (double)row_mins[g];", "* (double)row_scales[g];"),
