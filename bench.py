@@ -46,21 +46,24 @@ def log(msg):
 
 
 # ------------------------------------------------------------ algorithmic bytes
-def bytes_quantize(rows: int, d: int) -> int:
-    """fp16 in (2 B/elem) + codes (0.5 B/elem) + fp32 min and scale per 64 elements."""
-    return rows * d * 2 + rows * d // 2 + rows * (d // 64) * 8
+def bytes_quantize(rows: int, d: int, mb: int = 4) -> int:
+    """fp16 in (2 B/elem) + codes (0.5 B/elem) + min and scale (mb bytes each) per 64 elements."""
+    return rows * d * 2 + rows * d // 2 + rows * (d // 64) * 2 * mb
 
 
-def bytes_decode(pairs: int, T: int, d: int) -> int:
-    """K and V codes + fp32 min/scale for T tokens, plus q and out (fp16)."""
-    per_token = d + 4 * 4 * (d // 64)          # 2 * d/2 code bytes + 4 fp32 per group
+def bytes_decode(pairs: int, T: int, d: int, mb: int = 4) -> int:
+    """K and V codes + min/scale (mb bytes each) for T tokens, plus q and out (fp16)."""
+    per_token = d + 4 * mb * (d // 64)         # 2 * d/2 code bytes + 4 metadata values per group
     return pairs * (T * per_token + 2 * d * 2)
 
 
-def bytes_topk(pairs: int, T: int, k: int, d: int) -> int:
+def bytes_topk(pairs: int, T: int, k: int, d: int, mb: int = 4) -> int:
     """All K (codes + metadata), the k kept V rows, q, out and the kept indices."""
-    half = d // 2 + 2 * 4 * (d // 64)
+    half = d // 2 + 2 * mb * (d // 64)
     return pairs * ((T + k) * half + 2 * d * 2 + 4 * k)
+
+
+META_BYTES = {"f32": 4, "f16": 2}
 
 
 def kernel_source_hash() -> str:
@@ -95,10 +98,12 @@ class Job:
         w = self.w = W.OPT_175B
         self.L = args.layers or w.layers
         self.n = args.decode_steps or w.n
+        self.meta = args.meta
+        mb = META_BYTES[self.meta]
         dev = self.dev = "cuda"
         torch.cuda.set_device(0)
-        log(f"[bench] allocating {self.L} int4 caches of b={w.b} a={w.a} d={w.d} S={w.S}")
-        self.caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=dev) for _ in range(self.L)]
+        log(f"[bench] allocating {self.L} int4 caches of b={w.b} a={w.a} d={w.d} S={w.S}, {self.meta} min/scale")
+        self.caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=dev, meta=self.meta) for _ in range(self.L)]
         # prompt K/V: a few distinct seeded buffers used in rotation (one layer's prompt is 3.6 GB)
         self.n_prompt = min(4, self.L)
         self.prompts = [W.prefill_kv(w, l, dev) for l in range(self.n_prompt)]
@@ -115,12 +120,12 @@ class Job:
         torch.cuda.synchronize()
         # algorithmic bytes of one step
         pairs = w.b * w.a
-        self.b_prefill = 2 * self.L * bytes_quantize(w.b * w.a * w.s, w.d)
-        self.b_append = 0 if args.fused else 2 * self.L * self.n * bytes_quantize(pairs, w.d)
+        self.b_prefill = 2 * self.L * bytes_quantize(w.b * w.a * w.s, w.d, mb)
+        self.b_append = 0 if args.fused else 2 * self.L * self.n * bytes_quantize(pairs, w.d, mb)
         self.fused = args.fused
-        self.b_decode_per_launch = [bytes_decode(pairs, w.s + j, w.d) for j in range(1, self.n + 1)]
+        self.b_decode_per_launch = [bytes_decode(pairs, w.s + j, w.d, mb) for j in range(1, self.n + 1)]
         if self.fused:  # the timed launch also quantises and writes the new K/V rows
-            self.b_decode_per_launch = [x + 2 * bytes_quantize(pairs, w.d) for x in self.b_decode_per_launch]
+            self.b_decode_per_launch = [x + 2 * bytes_quantize(pairs, w.d, mb) for x in self.b_decode_per_launch]
         self.b_decode = self.L * sum(self.b_decode_per_launch)
         self.b_step = self.b_prefill + self.b_append + self.b_decode
 
@@ -227,6 +232,46 @@ def time_split_context(T: int = 65536, copies: int = 3, reps: int = 5):
     return res
 
 
+def time_meta_f16(copies: int = 6, reps: int = 8):
+    """Dense decode attention on the OPT-175B layer (b=144, a=96, d=128, context 544) with
+    binary16 min/scale planes (144 B per (batch row, head, token)) beside the same call on
+    binary32 planes (160 B).  `copies` caches of each kind are used in rotation so the
+    Infinity Cache cannot serve a repeat; medians of per-launch HIP events."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    w = W.OPT_175B
+    T = w.S
+    k, v = W.prefill_kv(w, 0, "cuda", s_len=T)
+    q, _, _ = W.decode_inputs(w, 0, 1, "cuda")
+    out = torch.empty_like(q)
+    st = torch.cuda.current_stream()
+    res = {"workload": f"OPT-175B layer: b={w.b} a={w.a} d={w.d} context {T}, {copies} caches in rotation"}
+    for meta in ("f32", "f16"):
+        caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda", meta=meta) for _ in range(copies)]
+        for c in caches:
+            kvq.kv_quantize_prefill(c, k, v)
+        times = []
+        for r in range((reps + 1) * copies):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            kvq.decode_attention_q4(caches[r % copies], q, T, out=out)
+            e1.record(st)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(x.elapsed_time(y) for x, y in times[copies:])
+        med = ms[len(ms) // 2]
+        nb = bytes_decode(w.b * w.a, T, w.d, META_BYTES[meta])
+        res[meta] = {"ms_per_call_median": round(med, 4), "algorithmic_bytes": nb,
+                     "gbs": round(nb / med / 1e6, 1), "frac_of_hbm_peak": round(nb / med / 1e6 / HBM_PEAK_GBS, 4),
+                     "layer_tokens_per_s": round(w.b / (med / 1e3), 1)}
+        del caches
+    del k, v
+    res["f16_speedup"] = round(res["f32"]["ms_per_call_median"] / res["f16"]["ms_per_call_median"], 4)
+    return res
+
+
 def hbm_copy_ceiling():
     """Practical HBM ceiling for mixed read/write streams: a plain 4 GiB device copy
     (torch), read + write bytes / time."""
@@ -315,6 +360,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=0, help="decode steps per job (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--no-meta16", action="store_true", help="skip the binary16-metadata leg")
+    ap.add_argument("--meta", choices=("f32", "f16"), default="f32",
+                    help="min/scale plane type of the timed stack (default binary32)")
     ap.add_argument("--fused", action="store_true",
                     help="append and attend in one kv_append_attend_q4 launch per layer-step")
     args = ap.parse_args()
@@ -352,12 +400,12 @@ def main():
     decode_ms_per_step = sum(dec_ms) / args.steps
     value = job.b_step / (ms_step / 1e3) / 1e9
 
-    traffic = stored_traffic()
+    traffic = stored_traffic() if job.meta == "f32" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": ("k_decode<128,4,2> (kv_append_attend_q4: append + attention)" if job.fused
-                           else "k_decode<128,4,2> (decode_attention_q4)"),
+                "kernel": (("k_decode<128,4,2> (kv_append_attend_q4: append + attention)" if job.fused
+                            else "k_decode<128,4,2> (decode_attention_q4)") + f", {job.meta} min/scale planes"),
                 "algorithmic_bytes_per_launch": int(avg_bytes),
                 "avg_launch_ms": round(avg_ms, 5), "launches_timed": len(events)}
 
@@ -368,6 +416,7 @@ def main():
         "config": {"workload": f"OPT-175B layer stack: b={w.b} a={w.a} d={w.d} h={w.h}, prompt {w.s}, "
                                f"{job.n} decode steps, {job.L} int4 caches resident",
                    "b": w.b, "a": w.a, "d": w.d, "h": w.h, "s": w.s, "n": job.n, "layers": job.L,
+                   "meta": job.meta,
                    "step": ("prefill quantise all layers + n x (append + decode attention) all layers"
                             + (", append fused into the attention launch" if job.fused else ", two launches")),
                    "parallelism": "1 GPU"},
@@ -385,6 +434,10 @@ def main():
         res["split_context"] = time_split_context()
     del job
     torch.cuda.empty_cache()
+    if not args.no_meta16:
+        log("[bench] binary16 metadata leg")
+        res["meta_f16"] = time_meta_f16()
+        torch.cuda.empty_cache()
     res["hbm_copy_ceiling_gbs"] = hbm_copy_ceiling()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -29,12 +29,20 @@
  *    per operation; a constant group stores scale 0 and codes 0; a min of -0
  *    is stored as +0;
  *  - two codes per byte, the even element in the low nibble;
- *  - per-group min and scale kept as binary32 planes beside the codes.
+ *  - per-group min and scale kept as planes beside the codes, binary32
+ *    (KVQ_META_F32) or binary16 (KVQ_META_F16).  With binary16 planes the
+ *    min is stored exactly (it is one of the fp16 inputs), the scale is the
+ *    binary32 quotient (max-min)/15 rounded to the nearest binary16 value
+ *    (ties to even), and the codes are taken against that stored scale:
+ *    code = round_half_even((x-min)*fl32(1/scale)) clamped to 0..15; a
+ *    stored scale of 0 (constant group, or a scale that underflows binary16)
+ *    gives codes 0.  Binary16 planes cut the cache from 160 to 144 bytes per
+ *    (batch row, head, token) at d = 128.
  *
  * Device layout of one layer's cache (all planes caller-allocated):
  *    S = s + n token slots per (batch row, head);  G = d / 64
  *    k_codes, v_codes : uint8  [b][a][S][d/2]
- *    k_min, k_scale, v_min, v_scale : float32 [b][a][S][G]
+ *    k_min, k_scale, v_min, v_scale : float32 or float16 [b][a][S][G]
  *  Slot t of (batch row bi, head ai) is row (bi*a + ai)*S + t.
  *  Activations passed in: fp16 (IEEE binary16), row-major, 16-byte aligned:
  *    prompt K/V      [b][s_len][a][d]
@@ -67,13 +75,13 @@ enum {
     KVQ_OK = 0,
     KVQ_EINVAL = -1,        /* null or misaligned pointer, non-positive size, h % a != 0, d % 64 != 0 */
     KVQ_ERANGE = -2,        /* s_len, pos, ctx_len, k_top or num_splits outside its range            */
-    KVQ_EUNSUPPORTED = -3,  /* group != 64, metadata type not F32, d not 64/128/256, context too long */
+    KVQ_EUNSUPPORTED = -3,  /* group != 64, unknown metadata type, d not 64/128/256, context too long  */
     KVQ_ENOSPACE = -4,      /* workspace smaller than kvq_workspace_bytes() asks for                 */
     KVQ_ELAUNCH = -5        /* the HIP runtime refused a launch                                      */
 };
 
-/* Metadata (min/scale) plane type.  Only F32 is implemented. */
-enum { KVQ_META_F32 = 0 };
+/* Metadata (min/scale) plane type. */
+enum { KVQ_META_F32 = 0, KVQ_META_F16 = 1 };
 
 #define KVQ_GROUP 64            /* elements per quantisation group                          */
 #define KVQ_MAX_HEAD_DIM 256    /* d = h/a must be 64, 128 or 256                            */
@@ -86,7 +94,7 @@ enum { KVQ_META_F32 = 0 };
 typedef struct kvq_dims {
     int32_t b, a, h, s, n;
     int32_t group;      /* must be KVQ_GROUP */
-    int32_t meta_dtype; /* must be KVQ_META_F32 */
+    int32_t meta_dtype; /* KVQ_META_F32 or KVQ_META_F16 */
 } kvq_dims;
 
 /* One layer's quantised cache: device pointers in the layout above. */
@@ -97,7 +105,8 @@ typedef struct kvq_cache {
 } kvq_cache;
 
 /* Bytes of one code plane (k_codes or v_codes: b*a*S*d/2) and of one metadata
- * plane (each of k_min, k_scale, v_min, v_scale: b*a*S*(d/64)*4).  Either
+ * plane (each of k_min, k_scale, v_min, v_scale: b*a*S*(d/64)*4, or *2 for
+ * KVQ_META_F16).  Either
  * output pointer may be NULL.  Host only; returns a status.
  * With precision 0.5 byte per element this is the blog's KV-cache size
  * 2*precision*layers*h*seq_len*batch (section "KV Cache") for one layer,

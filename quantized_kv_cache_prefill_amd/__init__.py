@@ -25,6 +25,8 @@ __all__ = [
 
 GROUP = 64
 META_F32 = 0
+META_F16 = 1
+_META = {"f32": (META_F32, torch.float32), "f16": (META_F16, torch.float16)}
 KVQ_TOPK_MAX_CTX = 8192
 KVQ_MAX_SPLITS = 256
 
@@ -115,21 +117,25 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def make_dims(b: int, a: int, h: int, s: int, n: int) -> KvqDims:
-    return KvqDims(b, a, h, s, n, GROUP, META_F32)
+def make_dims(b: int, a: int, h: int, s: int, n: int, meta: str = "f32") -> KvqDims:
+    return KvqDims(b, a, h, s, n, GROUP, _META[meta][0])
 
 
 class QuantKVCache:
     """One layer's int4 KV cache in device memory (planes owned by torch).
 
     k_codes, v_codes : uint8   [b, a, S, d/2]   (two codes per byte, even element low nibble)
-    k_min, k_scale, v_min, v_scale : float32 [b, a, S, d/64]
+    k_min, k_scale, v_min, v_scale : float32 (meta="f32") or float16 (meta="f16") [b, a, S, d/64]
     with S = s + n slots, d = h / a.
     """
 
-    def __init__(self, b: int, a: int, h: int, s: int, n: int, device="cuda", fill: int | None = None):
+    def __init__(self, b: int, a: int, h: int, s: int, n: int, device="cuda", fill: int | None = None,
+                 meta: str = "f32"):
         if h % a != 0:
             raise ValueError("h must be a multiple of a")
+        if meta not in _META:
+            raise ValueError("meta must be 'f32' or 'f16'")
+        self.meta = meta
         self.b, self.a, self.h, self.s, self.n = b, a, h, s, n
         self.d = h // a
         self.S = s + n
@@ -137,9 +143,9 @@ class QuantKVCache:
         alloc = torch.empty if fill is None else (lambda *sh, **kw: torch.full(sh, fill, **kw))
         self.k_codes = alloc(b, a, self.S, self.d // 2, dtype=torch.uint8, device=device)
         self.v_codes = alloc(b, a, self.S, self.d // 2, dtype=torch.uint8, device=device)
-        meta = [alloc(b, a, self.S, G, dtype=torch.float32, device=device) for _ in range(4)]
-        self.k_min, self.k_scale, self.v_min, self.v_scale = meta
-        self._struct = KvqCache(make_dims(b, a, h, s, n), self.k_codes.data_ptr(), self.v_codes.data_ptr(),
+        planes = [alloc(b, a, self.S, G, dtype=_META[meta][1], device=device) for _ in range(4)]
+        self.k_min, self.k_scale, self.v_min, self.v_scale = planes
+        self._struct = KvqCache(make_dims(b, a, h, s, n, meta), self.k_codes.data_ptr(), self.v_codes.data_ptr(),
                                 self.k_min.data_ptr(), self.k_scale.data_ptr(), self.v_min.data_ptr(),
                                 self.v_scale.data_ptr())
 
@@ -166,10 +172,10 @@ def _act(t: torch.Tensor, shape, name: str):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def kvq_cache_bytes(b: int, a: int, h: int, s: int, n: int) -> tuple[int, int]:
+def kvq_cache_bytes(b: int, a: int, h: int, s: int, n: int, meta: str = "f32") -> tuple[int, int]:
     """(bytes of one code plane, bytes of one metadata plane)."""
     cb, mb = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(load_library().kvq_cache_bytes(ctypes.byref(make_dims(b, a, h, s, n)), ctypes.byref(cb),
+    _check(load_library().kvq_cache_bytes(ctypes.byref(make_dims(b, a, h, s, n, meta)), ctypes.byref(cb),
                                           ctypes.byref(mb)), "kvq_cache_bytes")
     return cb.value, mb.value
 

@@ -29,7 +29,7 @@ int check_dims(const kvq_dims *d)
     const int hd = d->h / d->a;
     if (hd % KVQ_GROUP != 0)
         return KVQ_EINVAL;
-    if (d->group != KVQ_GROUP || d->meta_dtype != KVQ_META_F32)
+    if (d->group != KVQ_GROUP || (d->meta_dtype != KVQ_META_F32 && d->meta_dtype != KVQ_META_F16))
         return KVQ_EUNSUPPORTED;
     if (hd != 64 && hd != 128 && hd != 256)
         return KVQ_EUNSUPPORTED;
@@ -53,13 +53,14 @@ int check_cache(const kvq_cache *c, kvq::CachePlanes *planes)
             return KVQ_EINVAL;
     planes->k_codes = c->k_codes;
     planes->v_codes = c->v_codes;
-    planes->k_min = static_cast<float *>(c->k_min);
-    planes->k_scale = static_cast<float *>(c->k_scale);
-    planes->v_min = static_cast<float *>(c->v_min);
-    planes->v_scale = static_cast<float *>(c->v_scale);
+    planes->k_min = c->k_min;
+    planes->k_scale = c->k_scale;
+    planes->v_min = c->v_min;
+    planes->v_scale = c->v_scale;
     planes->a = c->dims.a;
     planes->d = c->dims.h / c->dims.a;
     planes->S = c->dims.s + c->dims.n;
+    planes->meta_f16 = c->dims.meta_dtype == KVQ_META_F16;
     return KVQ_OK;
 }
 
@@ -130,7 +131,7 @@ int kvq_cache_bytes(const kvq_dims *dims, size_t *codes_bytes_per_plane, size_t 
     if (codes_bytes_per_plane)
         *codes_bytes_per_plane = slots * hd / 2;
     if (meta_bytes_per_plane)
-        *meta_bytes_per_plane = slots * (hd / KVQ_GROUP) * sizeof(float);
+        *meta_bytes_per_plane = slots * (hd / KVQ_GROUP) * (dims->meta_dtype == KVQ_META_F16 ? 2 : 4);
     return KVQ_OK;
 }
 

@@ -56,6 +56,10 @@ __device__ __forceinline__ uint4 ld_stream16(const void *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ float ld_stream(const float *p) { return __builtin_nontemporal_load(p); }
+// A min or scale of either metadata type (binary32 or binary16), widened to
+// binary32 (exact).
+__device__ __forceinline__ float ld_meta(const float *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float ld_meta(const _Float16 *p) { return (float)__builtin_nontemporal_load(p); }
 
 // ---------------------------------------------------------------------------
 // Nibble unpack.  A 32-bit word of codes holds elements e0..e7 (nibble k at
@@ -163,11 +167,18 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // The group codec for one lane's 8 consecutive fp16 values; 8 consecutive
 // lanes (an aligned 8-lane group) hold one 64-element group.  Every lane of
 // the wave must be active (DPP).  Binary32, one rounding per operation:
-// min/max over the group (exact; -0 -> +0), rng = max - min, scale = rng/15,
-// inv = 15/rng (correctly rounded divisions), code = clamp(rint_even((x -
-// min) * inv), 0, 15); a constant group gets scale 0 and codes 0.  word holds
-// the lane's 8 codes, element i at bits 4i..4i+3.
+// min/max over the group (exact; -0 -> +0), rng = max - min, then
+//  * binary32 metadata (Meta = float): scale = rng/15, inv = 15/rng (correctly
+//    rounded divisions);
+//  * binary16 metadata (Meta = _Float16): scale = rng/15 rounded to the nearest
+//    binary16 value (ties to even), inv = 1/scale, so the codes are taken
+//    against the stored scale; the min is an fp16 input, stored exactly;
+// code = clamp(rint_even((x - min) * inv), 0, 15); a stored scale of 0
+// (constant group, or a binary16 scale that underflows) gives codes 0.
+// word holds the lane's 8 codes, element i at bits 4i..4i+3; mn_out and
+// scale_out are the stored values, widened to binary32.
 // ===========================================================================
+template <typename Meta>
 __device__ __forceinline__ void quant_lane8(const uint4 x, uint32_t &word, float &mn_out, float &scale_out)
 {
 #pragma clang fp contract(off)
@@ -194,10 +205,19 @@ __device__ __forceinline__ void quant_lane8(const uint4 x, uint32_t &word, float
     mx = mx + 0.0f;
     const float rng = mx - mn;
     uint32_t codes = 0;
-    float scale = 0.0f;
-    if (rng != 0.0f) {
-        scale = rng / 15.0f; // correctly rounded (HIP default division)
-        const float inv = 15.0f / rng;
+    float scale = 0.0f, inv = 0.0f;
+    if constexpr (sizeof(Meta) == 4) {
+        if (rng != 0.0f) {
+            scale = rng / 15.0f; // correctly rounded (HIP default division)
+            inv = 15.0f / rng;
+        }
+    } else {
+        if (rng != 0.0f)
+            scale = (float)(_Float16)(rng / 15.0f); // binary16, nearest, ties to even
+        if (scale != 0.0f)
+            inv = 1.0f / scale;
+    }
+    if (scale != 0.0f) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float t = f[i] - mn;
@@ -219,12 +239,12 @@ __device__ __forceinline__ void quant_lane8(const uint4 x, uint32_t &word, float
 // so lanes with consecutive rows write consecutive cache slots: the 16-byte
 // reads are full 256-byte rows and the code/metadata writes are contiguous.
 // ===========================================================================
-template <int D, int R>
+template <int D, int R, typename Meta>
 __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_src, const uint4 *__restrict__ v_src,
                                                   int64_t rows, int s_src, int a, int S, int t_dst0,
                                                   uint32_t *__restrict__ k_codes, uint32_t *__restrict__ v_codes,
-                                                  float *__restrict__ k_min, float *__restrict__ k_scale,
-                                                  float *__restrict__ v_min, float *__restrict__ v_scale)
+                                                  Meta *__restrict__ k_min, Meta *__restrict__ k_scale,
+                                                  Meta *__restrict__ v_min, Meta *__restrict__ v_scale)
 {
     constexpr int LPR = D / 8;   // lanes per token row
     constexpr int RPB = 256 / LPR;
@@ -232,8 +252,8 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
     const bool is_v = blockIdx.y != 0;
     const uint4 *__restrict__ src = is_v ? v_src : k_src;
     uint32_t *__restrict__ codes = is_v ? v_codes : k_codes;
-    float *__restrict__ mins = is_v ? v_min : k_min;
-    float *__restrict__ scales = is_v ? v_scale : k_scale;
+    Meta *__restrict__ mins = is_v ? v_min : k_min;
+    Meta *__restrict__ scales = is_v ? v_scale : k_scale;
     const int lir = threadIdx.x % LPR;
     const int64_t row0 = (int64_t)blockIdx.x * (RPB * R) + threadIdx.x / LPR;
 
@@ -256,15 +276,15 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
     for (int u = 0; u < R; ++u) {
         uint32_t word;
         float mn, scale;
-        quant_lane8(x[u], word, mn, scale);
+        quant_lane8<Meta>(x[u], word, mn, scale);
         // Nontemporal stores: cache rows are read back only by a later launch,
         // and ordinary stores left dirty lines whose write-back slowed the next
         // decode launch by ~5% (measured on MI355X).
         if (ok[u]) {
             __builtin_nontemporal_store(word, codes + slot[u] * (D / 8) + lir);
             if ((lir & 7) == 0) {
-                __builtin_nontemporal_store(mn, mins + slot[u] * G + (lir >> 3));
-                __builtin_nontemporal_store(scale, scales + slot[u] * G + (lir >> 3));
+                __builtin_nontemporal_store((Meta)mn, mins + slot[u] * G + (lir >> 3));
+                __builtin_nontemporal_store((Meta)scale, scales + slot[u] * G + (lir >> 3));
             }
         }
     }
@@ -285,15 +305,16 @@ struct NewRow {
 // the wave (scalar registers), and the lane's 32-bit offsets of its slice
 // inside a token row.  Loads then take the scalar-base + 32-bit-offset
 // address form instead of a per-lane 64-bit pointer (saves ~2 VALU per load).
+template <typename Meta>
 struct CacheRow {
     const uint8_t *__restrict__ kb;
     const uint8_t *__restrict__ vb;
-    const float *__restrict__ kmb;
-    const float *__restrict__ ksb;
-    const float *__restrict__ vmb;
-    const float *__restrict__ vsb;
+    const Meta *__restrict__ kmb;
+    const Meta *__restrict__ ksb;
+    const Meta *__restrict__ vmb;
+    const Meta *__restrict__ vsb;
     uint32_t code_off; // part * 16 bytes
-    uint32_t meta_off; // 4 * group index g, bytes
+    uint32_t meta_off; // sizeof(Meta) * group index g, bytes
 };
 
 // Element at a 32-bit byte offset from a wave-uniform base.
@@ -303,20 +324,19 @@ __device__ __forceinline__ const T *at_byte(const T *base, uint32_t off)
     return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
 }
 
-template <int D>
-__device__ __forceinline__ CacheRow cache_row(const uint8_t *kc, const uint8_t *vc, const float *kmin,
-                                              const float *ksc, const float *vmin, const float *vsc, int pair,
-                                              int S, int part)
+template <int D, typename Meta>
+__device__ __forceinline__ CacheRow<Meta> cache_row(const uint8_t *kc, const uint8_t *vc, const Meta *kmin, const Meta *ksc,
+                                                 const Meta *vmin, const Meta *vsc, int pair, int S, int part)
 {
     constexpr int G = D / 64;
     const int64_t p = __builtin_amdgcn_readfirstlane(pair); // wave-uniform by construction
     const int64_t cb = p * S * (D / 2), mb = p * S * G;
     return {kc + cb, vc ? vc + cb : nullptr, kmin + mb, ksc + mb, vmin ? vmin + mb : nullptr,
-            vsc ? vsc + mb : nullptr, (uint32_t)part * 16u, (uint32_t)(part >> 1) * 4u};
+            vsc ? vsc + mb : nullptr, (uint32_t)part * 16u, (uint32_t)(part >> 1) * (uint32_t)sizeof(Meta)};
 }
 
-template <int D, int UU, bool NEWROW = false>
-__device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
+template <int D, int UU, bool NEWROW = false, typename Meta>
+__device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
                                             float c2, float &m, float &l, float &bsum, float (&acc)[32],
                                             const NewRow nr = NewRow{}, int t_new = -1)
 {
@@ -331,13 +351,13 @@ __device__ __forceinline__ void decode_iter(const CacheRow &cr, int tb, int t_en
         const int t = tb + u * TPW;
         valid[u] = t < t_end;
         const uint32_t tcl = (uint32_t)(valid[u] ? t : t_end - 1);
-        const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (4 * G) + cr.meta_off;
+        const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (uint32_t)(sizeof(Meta) * G) + cr.meta_off;
         kx[u] = ld_stream16(cr.kb + co);
         vx[u] = ld_stream16(cr.vb + co);
-        km[u] = ld_stream(at_byte(cr.kmb, mo));
-        ks[u] = ld_stream(at_byte(cr.ksb, mo));
-        vm[u] = ld_stream(at_byte(cr.vmb, mo));
-        vs[u] = ld_stream(at_byte(cr.vsb, mo));
+        km[u] = ld_meta(at_byte(cr.kmb, mo));
+        ks[u] = ld_meta(at_byte(cr.ksb, mo));
+        vm[u] = ld_meta(at_byte(cr.vmb, mo));
+        vs[u] = ld_meta(at_byte(cr.vsb, mo));
         if constexpr (NEWROW) {
             if (t == t_new) {
                 kx[u] = nr.kx;
@@ -396,10 +416,9 @@ __device__ __forceinline__ uint4 load_new_row(const uint4 *__restrict__ k_new, c
     return ld_stream16((lane < LPR ? k_new : v_new) + pair * (D / 8) + lane % LPR);
 }
 
-template <int D>
+template <int D, typename Meta>
 __device__ __forceinline__ NewRow append_rows(const uint4 x, int64_t pair, int64_t pos, int S, uint8_t *kc,
-                                              uint8_t *vc, float *kmin, float *ksc, float *vmin, float *vsc,
-                                              int lane)
+                                              uint8_t *vc, Meta *kmin, Meta *ksc, Meta *vmin, Meta *vsc, int lane)
 {
     constexpr int LPR = D / 8;
     constexpr int G = D / 64;
@@ -408,13 +427,13 @@ __device__ __forceinline__ NewRow append_rows(const uint4 x, int64_t pair, int64
     const int lir = lane % LPR;
     uint32_t word;
     float mn, scale;
-    quant_lane8(x, word, mn, scale);
+    quant_lane8<Meta>(x, word, mn, scale);
     if (lane < 2 * LPR) {
         const int64_t slot = pair * S + pos;
         __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(which ? vc : kc) + slot * (D / 8) + lir);
         if ((lir & 7) == 0) {
-            __builtin_nontemporal_store(mn, (which ? vmin : kmin) + slot * G + (lir >> 3));
-            __builtin_nontemporal_store(scale, (which ? vsc : ksc) + slot * G + (lir >> 3));
+            __builtin_nontemporal_store((Meta)mn, (which ? vmin : kmin) + slot * G + (lir >> 3));
+            __builtin_nontemporal_store((Meta)scale, (which ? vsc : ksc) + slot * G + (lir >> 3));
         }
     }
     const int part = lane % LPT, g = part >> 1;
@@ -447,9 +466,9 @@ __device__ __forceinline__ NewRow append_rows(const uint4 x, int64_t pair, int64
 // so the per-element work is the nibble unpack plus one dot2 (K) or one
 // mixed-precision FMA (V).  Scores are kept in log2 units (z = s*log2e/sqrt(d)).
 // ===========================================================================
-template <int D, int U, int WPP>
-__global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, float *kmin, float *ksc, float *vmin,
-                                                float *vsc, const uint4 *__restrict__ q, uint4 *__restrict__ out,
+template <int D, int U, int WPP, typename Meta>
+__global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, Meta *kmin, Meta *ksc, Meta *vmin, Meta *vsc,
+                                                const uint4 *__restrict__ q, uint4 *__restrict__ out,
                                                 float *__restrict__ ws, int pairs, int S, int T, int splits,
                                                 int split_len, float c2, const uint4 *__restrict__ k_new,
                                                 const uint4 *__restrict__ v_new)
@@ -490,7 +509,7 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, float 
     const QSlice qs = load_q_slice(q + pc * (D / 8) + part * 4);
     const uint32_t mg = magic64_vgpr();
 
-    const CacheRow cr = cache_row<D>(kc, vc, kmin, ksc, vmin, vsc, (int)pc, S, part);
+    const CacheRow<Meta> cr = cache_row<D, Meta>(kc, vc, kmin, ksc, vmin, vsc, (int)pc, S, part);
 
     float m = -INFINITY, l = 0.0f, bsum = 0.0f;
     float acc[32];
@@ -514,7 +533,7 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, float 
             decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
         for (int it = 0; it < nr1; ++it, tb += TPW)
             decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
-        const NewRow nr = append_rows<D>(new_raw, pc, T - 1, S, kc, vc, kmin, ksc, vmin, vsc, lane);
+        const NewRow nr = append_rows<D, Meta>(new_raw, pc, T - 1, S, kc, vc, kmin, ksc, vmin, vsc, lane);
         decode_iter<D, 1, true>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc, nr, T - 1);
     }
 #pragma unroll
@@ -699,8 +718,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp4)
     return base + incl - v;
 }
 
-template <int D, int UU>
-__device__ __forceinline__ void score_iter(const CacheRow &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
+template <int D, int UU, typename Meta>
+__device__ __forceinline__ void score_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
                                            float c2, bool writer, float *__restrict__ srow)
 {
     constexpr int LPT = D / 32;
@@ -712,10 +731,10 @@ __device__ __forceinline__ void score_iter(const CacheRow &cr, int tb, int t_end
     for (int u = 0; u < UU; ++u) {
         const int t = tb + u * TPW;
         const uint32_t tcl = (uint32_t)(t < t_end ? t : t_end - 1);
-        const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (4 * G) + cr.meta_off;
+        const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (uint32_t)(sizeof(Meta) * G) + cr.meta_off;
         kx[u] = ld_stream16(cr.kb + co);
-        km[u] = ld_stream(at_byte(cr.kmb, mo));
-        ks[u] = ld_stream(at_byte(cr.ksb, mo));
+        km[u] = ld_meta(at_byte(cr.kmb, mo));
+        ks[u] = ld_meta(at_byte(cr.ksb, mo));
     }
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
@@ -729,9 +748,9 @@ __device__ __forceinline__ void score_iter(const CacheRow &cr, int tb, int t_end
 }
 
 // One wave per (pair, chunk of `chunk` tokens); four waves per workgroup.
-template <int D, int U>
-__global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__ kc, const float *__restrict__ kmin,
-                                                     const float *__restrict__ ksc, const uint4 *__restrict__ q,
+template <int D, int U, typename Meta>
+__global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__ kc, const Meta *__restrict__ kmin,
+                                                     const Meta *__restrict__ ksc, const uint4 *__restrict__ q,
                                                      float *__restrict__ scores, int pairs, int S, int T,
                                                      int chunk, int n_chunks, float c2)
 {
@@ -751,7 +770,7 @@ __global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__
     const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW;
     const QSlice qs = load_q_slice(q + pair * (D / 8) + part * 4);
     const uint32_t mg = magic64_vgpr();
-    const CacheRow cr = cache_row<D>(kc, nullptr, kmin, ksc, nullptr, nullptr, (int)pair, S, part);
+    const CacheRow<Meta> cr = cache_row<D, Meta>(kc, nullptr, kmin, ksc, nullptr, nullptr, (int)pair, S, part);
     float *__restrict__ srow = scores + pair * T;
     const bool writer = part == 0;
     int tb = w_begin + lt;
@@ -761,9 +780,9 @@ __global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__
         score_iter<D, 1>(cr, tb, t_end, qs, mg, c2, writer, srow);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__ vc, const float *__restrict__ vmin,
-                                                     const float *__restrict__ vsc, const float *__restrict__ scores,
+template <int D, typename Meta>
+__global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__ vc, const Meta *__restrict__ vmin,
+                                                     const Meta *__restrict__ vsc, const float *__restrict__ scores,
                                                      _Float16 *__restrict__ out, int32_t *__restrict__ sel_out,
                                                      int S, int T, int k_top)
 {
@@ -879,8 +898,8 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
     // (4) softmax over the kept scores and P.V over their V rows, UG rows per
     // lane in flight
     const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
-    const float *__restrict__ vmb = vmin + pair * S * G + g;
-    const float *__restrict__ vsb = vsc + pair * S * G + g;
+    const Meta *__restrict__ vmb = vmin + pair * S * G + g;
+    const Meta *__restrict__ vsb = vsc + pair * S * G + g;
     const uint32_t mg = magic64_vgpr();
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
@@ -896,8 +915,8 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
             const bool valid = j < k_top;
             const int64_t t = sel[valid ? j : k_top - 1];
             vx[u] = ld_stream16(vb + t * (D / 2));
-            vm[u] = ld_stream(vmb + t * G);
-            vs[u] = ld_stream(vsb + t * G);
+            vm[u] = ld_meta(vmb + t * G);
+            vs[u] = ld_meta(vsb + t * G);
             p[u] = valid ? exp2_fast(sc[t] - M) : 0.0f;
         }
 #pragma unroll
@@ -942,10 +961,10 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
 // are then compacted in ascending order with ballots and mbcnt, ties to the
 // smaller index.  Each kept token's index and softmax weight go to LDS, and
 // the wave gathers the kept V rows.
-template <int D>
+template <int D, typename Meta>
 __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict__ vc,
-                                                       const float *__restrict__ vmin,
-                                                       const float *__restrict__ vsc,
+                                                       const Meta *__restrict__ vmin,
+                                                       const Meta *__restrict__ vsc,
                                                        const float *__restrict__ scores, uint4 *__restrict__ out,
                                                        int32_t *__restrict__ sel_out, int pairs, int S, int T,
                                                        int k_top, int region_bytes)
@@ -1029,8 +1048,8 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
     // (4) P.V over the kept rows
     const int part = lane % LPT, lt = lane / LPT, g = part >> 1;
     const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
-    const float *__restrict__ vmb = vmin + pair * S * G + g;
-    const float *__restrict__ vsb = vsc + pair * S * G + g;
+    const Meta *__restrict__ vmb = vmin + pair * S * G + g;
+    const Meta *__restrict__ vsb = vsc + pair * S * G + g;
     const uint32_t mg = magic64_vgpr();
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
@@ -1047,8 +1066,8 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
             const int jc = valid ? j : k_top - 1;
             const int64_t t = sel_t[jc];
             vx[u] = ld_stream16(vb + t * (D / 2));
-            vm[u] = ld_stream(vmb + t * G);
-            vs[u] = ld_stream(vsb + t * G);
+            vm[u] = ld_meta(vmb + t * G);
+            vs[u] = ld_meta(vsb + t * G);
             p[u] = valid ? sel_p[jc] : 0.0f;
         }
 #pragma unroll
@@ -1088,7 +1107,13 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename Meta>
+Meta *meta(void *p)
+{
+    return static_cast<Meta *>(p);
+}
+
+template <int D, typename Meta>
 int launch_quantize_d(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
                       hipStream_t st)
 {
@@ -1101,23 +1126,24 @@ int launch_quantize_d(const CachePlanes &c, const void *k, const void *v, int b,
     const auto *ks = static_cast<const uint4 *>(k);
     const auto *vs = static_cast<const uint4 *>(v);
     if (R == 1)
-        hipLaunchKernelGGL((k_quantize<D, 1>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc, vc,
-                           c.k_min, c.k_scale, c.v_min, c.v_scale);
+        hipLaunchKernelGGL((k_quantize<D, 1, Meta>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc,
+                           vc, meta<Meta>(c.k_min), meta<Meta>(c.k_scale), meta<Meta>(c.v_min), meta<Meta>(c.v_scale));
     else
-        hipLaunchKernelGGL((k_quantize<D, 4>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc, vc,
-                           c.k_min, c.k_scale, c.v_min, c.v_scale);
+        hipLaunchKernelGGL((k_quantize<D, 4, Meta>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc,
+                           vc, meta<Meta>(c.k_min), meta<Meta>(c.k_scale), meta<Meta>(c.v_min), meta<Meta>(c.v_scale));
     return (int)hipGetLastError();
 }
 
-template <int D, int U, int WPP>
+template <int D, int U, int WPP, typename Meta>
 int launch_decode_k(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
                     float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     constexpr int PPB = 4 / WPP;
     const float c2 = 1.4426950408889634f / sqrtf((float)D);
     const int64_t blocks = (int64_t)((pairs + PPB - 1) / PPB) * sh.splits;
-    hipLaunchKernelGGL((k_decode<D, U, WPP>), dim3((unsigned)blocks), dim3(256), 0, st, c.k_codes, c.v_codes,
-                       c.k_min, c.k_scale, c.v_min, c.v_scale, static_cast<const uint4 *>(q),
+    hipLaunchKernelGGL((k_decode<D, U, WPP, Meta>), dim3((unsigned)blocks), dim3(256), 0, st, c.k_codes, c.v_codes,
+                       meta<Meta>(c.k_min), meta<Meta>(c.k_scale), meta<Meta>(c.v_min), meta<Meta>(c.v_scale),
+                       static_cast<const uint4 *>(q),
                        static_cast<uint4 *>(out), ws, pairs, c.S, T, sh.splits, sh.split_len, c2,
                        static_cast<const uint4 *>(k_new), static_cast<const uint4 *>(v_new));
     int e = (int)hipGetLastError();
@@ -1128,31 +1154,31 @@ int launch_decode_k(const CachePlanes &c, int pairs, const void *q, int T, void 
     return (int)hipGetLastError();
 }
 
-template <int D, int U>
+template <int D, int U, typename Meta>
 int launch_decode_u(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
                     float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     switch (sh.waves_per_pair) {
-    case 1: return launch_decode_k<D, U, 1>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    case 2: return launch_decode_k<D, U, 2>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    default: return launch_decode_k<D, U, 4>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 1: return launch_decode_k<D, U, 1, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 2: return launch_decode_k<D, U, 2, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    default: return launch_decode_k<D, U, 4, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
     }
 }
 
-template <int D>
+template <int D, typename Meta>
 int launch_decode_d(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
                     float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
     switch (sh.unroll) {
-    case 1: return launch_decode_u<D, 1>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    case 2: return launch_decode_u<D, 2>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    default: return launch_decode_u<D, 4>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 1: return launch_decode_u<D, 1, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 2: return launch_decode_u<D, 2, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    default: return launch_decode_u<D, 4, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
     }
 }
 
 constexpr int kTopkWaveMaxCtx = 2048; // k_topk_select_w holds 32 keys per lane
 
-template <int D>
+template <int D, typename Meta>
 int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
                   float *ws, hipStream_t st)
 {
@@ -1161,22 +1187,55 @@ int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_t
     const int chunk = std::min(128, (T + TPW - 1) / TPW * TPW);
     const int n_chunks = (T + chunk - 1) / chunk;
     const int64_t waves = (int64_t)pairs * n_chunks;
-    hipLaunchKernelGGL((k_topk_scores<D, 2>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, c.k_codes,
-                       c.k_min, c.k_scale, static_cast<const uint4 *>(q), ws, pairs, c.S, T, chunk, n_chunks, c2);
+    hipLaunchKernelGGL((k_topk_scores<D, 2, Meta>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, c.k_codes,
+                       meta<Meta>(c.k_min), meta<Meta>(c.k_scale), static_cast<const uint4 *>(q), ws, pairs, c.S, T, chunk, n_chunks, c2);
     int e = (int)hipGetLastError();
     if (e != 0)
         return e;
     if (T <= kTopkWaveMaxCtx) {
         const int region = (int)(((size_t)k_top * (sizeof(float) + sizeof(uint16_t)) + 15) / 16 * 16);
-        hipLaunchKernelGGL((k_topk_select_w<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), (size_t)4 * region, st,
-                           c.v_codes, c.v_min, c.v_scale, ws, static_cast<uint4 *>(out), sel, pairs, c.S, T, k_top,
+        hipLaunchKernelGGL((k_topk_select_w<D, Meta>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), (size_t)4 * region,
+                           st, c.v_codes, meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<uint4 *>(out), sel, pairs, c.S, T, k_top,
                            region);
     } else {
         const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
-        hipLaunchKernelGGL((k_topk_select<D>), dim3((unsigned)pairs), dim3(256), lds, st, c.v_codes, c.v_min,
-                           c.v_scale, ws, static_cast<_Float16 *>(out), sel, c.S, T, k_top);
+        hipLaunchKernelGGL((k_topk_select<D, Meta>), dim3((unsigned)pairs), dim3(256), lds, st, c.v_codes,
+                           meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<_Float16 *>(out), sel, c.S, T, k_top);
     }
     return (int)hipGetLastError();
+}
+
+template <typename Meta>
+int launch_quantize_m(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
+                      hipStream_t st)
+{
+    switch (c.d) {
+    case 64: return launch_quantize_d<64, Meta>(c, k, v, b, s_src, t_dst0, st);
+    case 128: return launch_quantize_d<128, Meta>(c, k, v, b, s_src, t_dst0, st);
+    default: return launch_quantize_d<256, Meta>(c, k, v, b, s_src, t_dst0, st);
+    }
+}
+
+template <typename Meta>
+int launch_decode_m(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
+                    float *ws, const void *k_new, const void *v_new, hipStream_t st)
+{
+    switch (c.d) {
+    case 64: return launch_decode_d<64, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    case 128: return launch_decode_d<128, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    default: return launch_decode_d<256, Meta>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+    }
+}
+
+template <typename Meta>
+int launch_topk_m(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
+                  float *ws, hipStream_t st)
+{
+    switch (c.d) {
+    case 64: return launch_topk_d<64, Meta>(c, pairs, q, T, k_top, out, sel, ws, st);
+    case 128: return launch_topk_d<128, Meta>(c, pairs, q, T, k_top, out, sel, ws, st);
+    default: return launch_topk_d<256, Meta>(c, pairs, q, T, k_top, out, sel, ws, st);
+    }
 }
 
 } // namespace
@@ -1184,21 +1243,15 @@ int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_t
 int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
                     hipStream_t st)
 {
-    switch (c.d) {
-    case 64: return launch_quantize_d<64>(c, k, v, b, s_src, t_dst0, st);
-    case 128: return launch_quantize_d<128>(c, k, v, b, s_src, t_dst0, st);
-    default: return launch_quantize_d<256>(c, k, v, b, s_src, t_dst0, st);
-    }
+    return c.meta_f16 ? launch_quantize_m<_Float16>(c, k, v, b, s_src, t_dst0, st)
+                      : launch_quantize_m<float>(c, k, v, b, s_src, t_dst0, st);
 }
 
 int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *out, const DecodeShape &sh,
                   float *ws, const void *k_new, const void *v_new, hipStream_t st)
 {
-    switch (c.d) {
-    case 64: return launch_decode_d<64>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    case 128: return launch_decode_d<128>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    default: return launch_decode_d<256>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
-    }
+    return c.meta_f16 ? launch_decode_m<_Float16>(c, pairs, q, T, out, sh, ws, k_new, v_new, st)
+                      : launch_decode_m<float>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
 }
 
 size_t decode_ws_floats(int pairs, int d, int splits)
@@ -1212,11 +1265,8 @@ size_t topk_ws_floats(int pairs, int T) { return (size_t)pairs * (size_t)T; }
 int launch_topk(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
                 float *ws, hipStream_t st)
 {
-    switch (c.d) {
-    case 64: return launch_topk_d<64>(c, pairs, q, T, k_top, out, sel, ws, st);
-    case 128: return launch_topk_d<128>(c, pairs, q, T, k_top, out, sel, ws, st);
-    default: return launch_topk_d<256>(c, pairs, q, T, k_top, out, sel, ws, st);
-    }
+    return c.meta_f16 ? launch_topk_m<_Float16>(c, pairs, q, T, k_top, out, sel, ws, st)
+                      : launch_topk_m<float>(c, pairs, q, T, k_top, out, sel, ws, st);
 }
 
 } // namespace kvq

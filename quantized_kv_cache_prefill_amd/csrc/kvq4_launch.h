@@ -12,10 +12,11 @@ namespace kvq {
 
 struct CachePlanes {
     uint8_t *k_codes, *v_codes;
-    float *k_min, *k_scale, *v_min, *v_scale;
-    int a;       // heads
-    int d;       // head_dim (64, 128 or 256)
-    int S;       // token slots per (batch row, head)
+    void *k_min, *k_scale, *v_min, *v_scale; // binary32, or binary16 when meta_f16
+    int a;         // heads
+    int d;         // head_dim (64, 128 or 256)
+    int S;         // token slots per (batch row, head)
+    bool meta_f16; // metadata planes hold binary16 values
 };
 
 // Quantise b*a*s_src token rows of fp16 K and V ([b][s_src][a][d]) into

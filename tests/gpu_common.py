@@ -31,16 +31,20 @@ def f16_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().numpy().view(np.uint16)
 
 
-def oracle_planes_from_prompt(k: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+QUANTIZE = {"f32": oracle.quantize_rows, "f16": oracle.quantize_rows_m16}
+META_NP = {"f32": np.float32, "f16": np.float16}
+
+
+def oracle_planes_from_prompt(k: np.ndarray, meta: str = "f32") -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Prompt rows [b][s][a][d] (fp16 bits) -> oracle planes in cache order [b][a][s][...]."""
-    codes, mins, scales = oracle.quantize_rows(k)
+    codes, mins, scales = QUANTIZE[meta](k)
     return (np.ascontiguousarray(codes.transpose(0, 2, 1, 3)), np.ascontiguousarray(mins.transpose(0, 2, 1, 3)),
             np.ascontiguousarray(scales.transpose(0, 2, 1, 3)))
 
 
-def oracle_row(x: np.ndarray):
+def oracle_row(x: np.ndarray, meta: str = "f32"):
     """New-token rows [b][1][a][d] -> oracle planes [b][a][...] of that slot."""
-    codes, mins, scales = oracle.quantize_rows(x[:, 0])
+    codes, mins, scales = QUANTIZE[meta](x[:, 0])
     return codes, mins, scales
 
 
@@ -48,43 +52,51 @@ def assert_bits_equal(gpu: torch.Tensor, ref: np.ndarray, what: str):
     g = gpu.detach().cpu().contiguous().numpy()
     if g.dtype == np.float32:
         g = g.view(np.uint32)
+        assert np.asarray(ref).dtype == np.float32, (what, np.asarray(ref).dtype)
         ref = np.ascontiguousarray(ref, np.float32).view(np.uint32)
+    elif g.dtype == np.float16:
+        g = g.view(np.uint16)
+        assert np.asarray(ref).dtype == np.float16, (what, np.asarray(ref).dtype)
+        ref = np.ascontiguousarray(ref, np.float16).view(np.uint16)
     assert g.shape == ref.shape, (what, g.shape, ref.shape)
     bad = np.argwhere(g != ref)
     assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:3].tolist()}: gpu {g[tuple(bad[0])]} ref {ref[tuple(bad[0])]}"
 
 
 class HostCache:
-    """The oracle's own copy of a layer's planes, [b][a][S][...], filled from inputs."""
+    """The oracle's own copy of a layer's planes, [b][a][S][...], filled from inputs.
+    meta = "f32" or "f16": the metadata type, quantised by the matching oracle codec."""
 
-    def __init__(self, b, a, d, S):
+    def __init__(self, b, a, d, S, meta: str = "f32"):
         G = d // 64
+        self.meta = meta
+        mt = META_NP[meta]
         self.kc = np.zeros((b, a, S, d // 2), np.uint8)
         self.vc = np.zeros((b, a, S, d // 2), np.uint8)
-        self.kmin = np.zeros((b, a, S, G), np.float32)
-        self.ksc = np.zeros((b, a, S, G), np.float32)
-        self.vmin = np.zeros((b, a, S, G), np.float32)
-        self.vsc = np.zeros((b, a, S, G), np.float32)
+        self.kmin = np.zeros((b, a, S, G), mt)
+        self.ksc = np.zeros((b, a, S, G), mt)
+        self.vmin = np.zeros((b, a, S, G), mt)
+        self.vsc = np.zeros((b, a, S, G), mt)
 
     def prefill(self, k: np.ndarray, v: np.ndarray, pairs=None):
         """k, v: [b][s][a][d] fp16 bits.  pairs: optional list of (bi, ai) to quantise only."""
         s = k.shape[1]
         if pairs is None:
-            kc, km, ks = oracle_planes_from_prompt(k)
-            vc, vm, vs = oracle_planes_from_prompt(v)
+            kc, km, ks = oracle_planes_from_prompt(k, self.meta)
+            vc, vm, vs = oracle_planes_from_prompt(v, self.meta)
             self.kc[:, :, :s], self.kmin[:, :, :s], self.ksc[:, :, :s] = kc, km, ks
             self.vc[:, :, :s], self.vmin[:, :, :s], self.vsc[:, :, :s] = vc, vm, vs
         else:
             for bi, ai in pairs:
-                c, m, sc = oracle.quantize_rows(np.ascontiguousarray(k[bi, :, ai]))
+                c, m, sc = QUANTIZE[self.meta](np.ascontiguousarray(k[bi, :, ai]))
                 self.kc[bi, ai, :s], self.kmin[bi, ai, :s], self.ksc[bi, ai, :s] = c, m, sc
-                c, m, sc = oracle.quantize_rows(np.ascontiguousarray(v[bi, :, ai]))
+                c, m, sc = QUANTIZE[self.meta](np.ascontiguousarray(v[bi, :, ai]))
                 self.vc[bi, ai, :s], self.vmin[bi, ai, :s], self.vsc[bi, ai, :s] = c, m, sc
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray, pos: int):
-        c, m, s = oracle_row(k_new)
+        c, m, s = oracle_row(k_new, self.meta)
         self.kc[:, :, pos], self.kmin[:, :, pos], self.ksc[:, :, pos] = c, m, s
-        c, m, s = oracle_row(v_new)
+        c, m, s = oracle_row(v_new, self.meta)
         self.vc[:, :, pos], self.vmin[:, :, pos], self.vsc[:, :, pos] = c, m, s
 
     def head(self, bi, ai, T):

@@ -62,11 +62,19 @@ def test_cache_bytes_closed_form(L):
         cb, mb = kvq.kvq_cache_bytes(b, a, h, s, n)
         assert 2 * cb == 2 * 0.5 * h * (s + n) * b
         assert mb == b * (s + n) * (h // 64) * 4
+        cb16, mb16 = kvq.kvq_cache_bytes(b, a, h, s, n, meta="f16")
+        assert cb16 == cb and mb16 == b * (s + n) * (h // 64) * 2
+    # OPT-175B layer at d = 128: 160 bytes per (batch row, head, token) with binary32 planes, 144 with binary16
+    cb, mb = kvq.kvq_cache_bytes(144, 96, 12288, 512, 32)
+    cb16, mb16 = kvq.kvq_cache_bytes(144, 96, 12288, 512, 32, meta="f16")
+    slots = 144 * 96 * 544
+    assert (2 * cb + 4 * mb) == 160 * slots and (2 * cb16 + 4 * mb16) == 144 * slots
 
 
 @pytest.mark.parametrize("mut,status", [
     (dict(b=0), KVQ_EINVAL), (dict(a=0), KVQ_EINVAL), (dict(h=100), KVQ_EINVAL), (dict(s=0), KVQ_EINVAL),
-    (dict(h=2 * 96), KVQ_EINVAL), (dict(group=32), KVQ_EUNSUPPORTED), (dict(meta=1), KVQ_EUNSUPPORTED),
+    (dict(h=2 * 96), KVQ_EINVAL), (dict(group=32), KVQ_EUNSUPPORTED), (dict(meta=2), KVQ_EUNSUPPORTED),
+    (dict(meta=-1), KVQ_EUNSUPPORTED),
     (dict(h=2 * 192), KVQ_EUNSUPPORTED), (dict(h=2 * 512), KVQ_EUNSUPPORTED), (dict(n=-1), KVQ_EINVAL),
 ])
 def test_bad_dims(L, mut, status):

@@ -57,17 +57,18 @@ def _check_prefill_pairs(cache, hc, s, pairs, what):
             assert_bits_equal(g[bi, ai, :s], r[bi, ai, :s], f"{what} {name} pair ({bi},{ai})")
 
 
-def run_decode_workload(w: W.Workload, full_planes: bool, attend_pairs_full_steps, sample_n: int):
+def run_decode_workload(w: W.Workload, full_planes: bool, attend_pairs_full_steps, sample_n: int,
+                        meta: str = "f32"):
     """Prefill + n decode steps of one layer at full shape, checked against the oracle."""
     require_gpu()
-    log(f"[{w.name}] b={w.b} a={w.a} d={w.d} s={w.s} n={w.n}: prefill")
-    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=DEV, fill=0xFF)
+    log(f"[{w.name}] b={w.b} a={w.a} d={w.d} s={w.s} n={w.n} meta={meta}: prefill")
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=DEV, fill=0xFF, meta=meta)
     k, v = W.prefill_kv(w, 0, DEV)
     kvq.kv_quantize_prefill(cache, k, v)
     torch.cuda.synchronize()
     kh, vh = f16_np(k), f16_np(v)
     del k, v
-    hc = HostCache(w.b, w.a, w.d, w.S)
+    hc = HostCache(w.b, w.a, w.d, w.S, meta)
     pairs_s = sample_pairs(w.b, w.a, sample_n, seed=w.idx)
     if full_planes:
         hc.prefill(kh, vh)
@@ -93,8 +94,8 @@ def run_decode_workload(w: W.Workload, full_planes: bool, attend_pairs_full_step
         else:
             continue
         ref = oracle_attend_pairs(hc, f16_np(q), T, pairs)
-        err = assert_close(_gpu_rows(out, pairs), ref, f"{w.name} step {j} (T={T})")
-        log(f"[{w.name}] step {j} T={T}: {len(pairs)} pairs ok, max abs err {err:.2e}")
+        err = assert_close(_gpu_rows(out, pairs), ref, f"{w.name} meta={meta} step {j} (T={T})")
+        log(f"[{w.name}] meta={meta} step {j} T={T}: {len(pairs)} pairs ok, max abs err {err:.2e}")
     return cache, hc
 
 
@@ -177,12 +178,12 @@ def test_sparse_top10_layer_sampled():
     assert same >= len(pairs) * 0.9
 
 
-def _small_cache(b, a, d, s, n, seed, std=1.0, fill=0xFF):
-    cache = kvq.QuantKVCache(b, a, a * d, s, n, device=DEV, fill=fill)
+def _small_cache(b, a, d, s, n, seed, std=1.0, fill=0xFF, meta="f32"):
+    cache = kvq.QuantKVCache(b, a, a * d, s, n, device=DEV, fill=fill, meta=meta)
     k = W.random_fp16((b, s + n, a, d), seed, DEV, std)
     v = W.random_fp16((b, s + n, a, d), seed + 1, DEV, std)
     kvq.kv_quantize_prefill(cache, k, v)
-    hc = HostCache(b, a, d, s + n)
+    hc = HostCache(b, a, d, s + n, meta)
     hc.prefill(f16_np(k), f16_np(v))
     q = W.random_fp16((b, 1, a, d), seed + 2, DEV, std)
     return cache, hc, q
