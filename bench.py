@@ -236,7 +236,8 @@ def time_meta_f16(copies: int = 6, reps: int = 8):
     """Dense decode attention on the OPT-175B layer (b=144, a=96, d=128, context 544) with
     binary16 min/scale planes (144 B per (batch row, head, token)) beside the same call on
     binary32 planes (160 B).  `copies` caches of each kind are used in rotation so the
-    Infinity Cache cannot serve a repeat; medians of per-launch HIP events."""
+    Infinity Cache cannot serve a repeat, and the two kinds' launches alternate so that
+    both see the same conditions; medians of per-launch HIP events."""
     import torch
 
     import quantized_kv_cache_prefill_amd as kvq
@@ -247,27 +248,32 @@ def time_meta_f16(copies: int = 6, reps: int = 8):
     q, _, _ = W.decode_inputs(w, 0, 1, "cuda")
     out = torch.empty_like(q)
     st = torch.cuda.current_stream()
-    res = {"workload": f"OPT-175B layer: b={w.b} a={w.a} d={w.d} context {T}, {copies} caches in rotation"}
-    for meta in ("f32", "f16"):
-        caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda", meta=meta) for _ in range(copies)]
-        for c in caches:
+    metas = ("f32", "f16")
+    caches = {m: [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda", meta=m) for _ in range(copies)]
+              for m in metas}
+    for m in metas:
+        for c in caches[m]:
             kvq.kv_quantize_prefill(c, k, v)
-        times = []
-        for r in range((reps + 1) * copies):
+    del k, v
+    times = {m: [] for m in metas}
+    for r in range((reps + 1) * copies):
+        for m in metas:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
-            kvq.decode_attention_q4(caches[r % copies], q, T, out=out)
+            kvq.decode_attention_q4(caches[m][r % copies], q, T, out=out)
             e1.record(st)
-            times.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = sorted(x.elapsed_time(y) for x, y in times[copies:])
+            times[m].append((e0, e1))
+    torch.cuda.synchronize()
+    res = {"workload": f"OPT-175B layer: b={w.b} a={w.a} d={w.d} context {T}, {copies} caches per kind in rotation, "
+                       f"launches of the two kinds alternating"}
+    for m in metas:
+        ms = sorted(x.elapsed_time(y) for x, y in times[m][copies:])
         med = ms[len(ms) // 2]
-        nb = bytes_decode(w.b * w.a, T, w.d, META_BYTES[meta])
-        res[meta] = {"ms_per_call_median": round(med, 4), "algorithmic_bytes": nb,
-                     "gbs": round(nb / med / 1e6, 1), "frac_of_hbm_peak": round(nb / med / 1e6 / HBM_PEAK_GBS, 4),
-                     "layer_tokens_per_s": round(w.b / (med / 1e3), 1)}
-        del caches
-    del k, v
+        nb = bytes_decode(w.b * w.a, T, w.d, META_BYTES[m])
+        res[m] = {"ms_per_call_median": round(med, 4), "algorithmic_bytes": nb,
+                  "gbs": round(nb / med / 1e6, 1), "frac_of_hbm_peak": round(nb / med / 1e6 / HBM_PEAK_GBS, 4),
+                  "layer_tokens_per_s": round(w.b / (med / 1e3), 1)}
+    del caches
     res["f16_speedup"] = round(res["f32"]["ms_per_call_median"] / res["f16"]["ms_per_call_median"], 4)
     return res
 
@@ -343,11 +349,27 @@ def cpu_baseline(budget_s: float = 12.0):
     per_pair_bytes = (2 * bytes_quantize(w.s, w.d) + w.n * 2 * bytes_quantize(1, w.d)
                       + sum(bytes_decode(1, w.s + j, w.d) for j in range(1, w.n + 1)))
     gbs = n_pairs * per_pair_bytes / wall / 1e9
+    # one thread: the same per-pair job, a few pairs in sequence
+    n1 = 3
+    t1 = sum(one_pair(int(sd)) for sd in r.integers(0, 2**31, n1))
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": (f"{n_pairs} of the {w.b * w.a} (batch row, head) pairs of one OPT-175B layer: "
                        f"prompt quantise (512 tokens) + 32 x (append + dense attention, context 513..544); "
                        f"{wall:.1f} s wall on {cores} threads"),
-            "layer_tokens_per_s": round(n_pairs / w.a * w.n / wall, 3)}
+            "layer_tokens_per_s": round(n_pairs / w.a * w.n / wall, 3),
+            "single_thread_gbs": round(n1 * per_pair_bytes / t1 / 1e9, 4),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # --------------------------------------------------------------------- main
@@ -398,6 +420,7 @@ def main():
     avg_bytes = sum(dec_bytes) / len(dec_bytes)
     achieved = avg_bytes / avg_ms / 1e6
     decode_ms_per_step = sum(dec_ms) / args.steps
+    srt = sorted(dec_ms)
     value = job.b_step / (ms_step / 1e3) / 1e9
 
     traffic = stored_traffic() if job.meta == "f32" else None
@@ -423,7 +446,11 @@ def main():
         "roofline": roofline,
         "decode_attention": {"gbs": round(achieved, 1), "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
                              "layer_tokens_per_s": round(w.b / (avg_ms / 1e3), 1),
-                             "stack_tokens_per_s": round(w.b * job.n / (decode_ms_per_step / 1e3), 1)},
+                             "stack_tokens_per_s": round(w.b * job.n / (decode_ms_per_step / 1e3), 1),
+                             "launch_ms": {"min": round(srt[0], 5), "median": round(srt[len(srt) // 2], 5),
+                                           "p90": round(srt[int(0.9 * (len(srt) - 1))], 5),
+                                           "max": round(srt[-1], 5), "mean": round(avg_ms, 5),
+                                           "launches": len(srt)}},
         "step_bytes": {"prefill": job.b_prefill, "append": job.b_append, "decode": job.b_decode},
     }
     log(f"[bench] step {ms_step:.1f} ms, decode kernel {achieved:.0f} GB/s")

@@ -63,28 +63,38 @@ __device__ __forceinline__ float ld_meta(const _Float16 *p) { return (float)__bu
 
 // ---------------------------------------------------------------------------
 // Nibble unpack.  A 32-bit word of codes holds elements e0..e7 (nibble k at
-// bits 4k..4k+3, even element in the low nibble of each byte).  Moving one
-// nibble of each 16-bit half to bits 4..7 and OR-ing the fp16 pattern of 64.0
-// yields the exact fp16 value 64 + code in that half (the fraction's bits
-// 4..7 weigh 1 at exponent 6).  The four pairs come out as (e0,e4), (e1,e5),
-// (e2,e6), (e3,e7): one shift + one and-or per pair, no conversion.
+// bits 4k..4k+3, even element in the low nibble of each byte).  Each 16-bit
+// half holds two codes in its low byte (bits 0..3 and 4..7); one shift by 8
+// brings the two codes of its high byte down.  Masking then gives the pairs
+// (e0,e4), (e1,e5) from the word and (e2,e6), (e3,e7) from the shifted word,
+// one instruction each, in two forms:
+//  * keys, for v_dot2_f32_f16 (which flushes binary16 subnormals): OR-ing the
+//    binary16 pattern of 1024 onto a nibble at bits 0..3 gives exactly
+//    1024 + c (the fraction's bit 0 weighs 1 at exponent 10), OR-ing 64 onto a
+//    nibble at bits 4..7 gives 64 + c (bit 4 weighs 1 at exponent 6);
+//  * values, for the mixed-precision FMA (which keeps binary16 subnormals):
+//    the masked halves alone are the subnormals c * 2^-24 (bits 0..3) and
+//    c * 2^-20 (bits 4..7), with no bias to remove.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kNibMask = 0x00F000F0u;
-constexpr float kBias = 64.0f;
+constexpr uint32_t kLoNib = 0x000F000Fu;
+constexpr uint32_t kHiNib = 0x00F000F0u;
+constexpr float kBiasLo = 1024.0f; // keys: bias of e0, e2, e4, e6
+constexpr float kBiasHi = 64.0f;   // keys: bias of e1, e3, e5, e7
+constexpr float kTwo24 = 16777216.0f;
 
-// The OR constant is held in a VGPR (opaque to the compiler) so each pair
+// The OR constants are held in VGPRs (opaque to the compiler) so each key pair
 // compiles to a single v_and_or_b32 with the mask in an SGPR: GFX9's VOP3
 // takes no literal and at most one scalar operand.
-__device__ __forceinline__ uint32_t magic64_vgpr()
+struct Magic {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ Magic magic_vgprs()
 {
-    uint32_t v;
-    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(v));
-    return v;
+    Magic m;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.lo));
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(m.hi));
+    return m;
 }
-__device__ __forceinline__ uint32_t pair0(uint32_t x, uint32_t mg) { return ((x << 4) & kNibMask) | mg; }
-__device__ __forceinline__ uint32_t pair1(uint32_t x, uint32_t mg) { return (x & kNibMask) | mg; }
-__device__ __forceinline__ uint32_t pair2(uint32_t x, uint32_t mg) { return ((x >> 4) & kNibMask) | mg; }
-__device__ __forceinline__ uint32_t pair3(uint32_t x, uint32_t mg) { return ((x >> 8) & kNibMask) | mg; }
 
 __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c)
 {
@@ -92,16 +102,17 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c)
 }
 
 // One lane's 32-element slice of q, regrouped into the unpack's pair order,
-// plus the slice's sum (for the bias and the group min).
+// plus its sum (for the group min) and the key bias sum_i q_i * bias_i.
 struct QSlice {
     uint32_t qp[16];
     float qsum;
+    float qbias;
 };
 
 __device__ __forceinline__ QSlice load_q_slice(const uint4 *__restrict__ qrow)
 {
     QSlice s;
-    s.qsum = 0.0f;
+    float even = 0.0f, odd = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const uint4 v = qrow[w]; // elements 8w..8w+7: x=(e0,e1) y=(e2,e3) z=(e4,e5) w=(e6,e7)
@@ -109,42 +120,48 @@ __device__ __forceinline__ QSlice load_q_slice(const uint4 *__restrict__ qrow)
         s.qp[4 * w + 1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
         s.qp[4 * w + 2] = (v.y & 0xFFFFu) | (v.w << 16);
         s.qp[4 * w + 3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
-        s.qsum += h2f_lo(v.x) + h2f_hi(v.x) + h2f_lo(v.y) + h2f_hi(v.y) + h2f_lo(v.z) + h2f_hi(v.z) + h2f_lo(v.w) +
-                  h2f_hi(v.w);
+        even += h2f_lo(v.x) + h2f_lo(v.y) + h2f_lo(v.z) + h2f_lo(v.w);
+        odd += h2f_hi(v.x) + h2f_hi(v.y) + h2f_hi(v.z) + h2f_hi(v.w);
     }
+    s.qsum = even + odd;
+    s.qbias = kBiasLo * even + kBiasHi * odd;
     return s;
 }
 
-// sum_i q_i * (64 + c_i) over the lane's 32 elements.
-__device__ __forceinline__ float dot_biased(const QSlice &q, const uint4 kx, uint32_t mg)
+// sum_i q_i * (bias_i + c_i) over the lane's 32 elements (key form).
+__device__ __forceinline__ float dot_keys(const QSlice &q, const uint4 kx, const Magic mg)
 {
     const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        acc = fdot2(q.qp[4 * j + 0], pair0(w[j], mg), acc);
-        acc = fdot2(q.qp[4 * j + 1], pair1(w[j], mg), acc);
-        acc = fdot2(q.qp[4 * j + 2], pair2(w[j], mg), acc);
-        acc = fdot2(q.qp[4 * j + 3], pair3(w[j], mg), acc);
+        const uint32_t y = w[j] >> 8;
+        acc = fdot2(q.qp[4 * j + 0], (w[j] & kLoNib) | mg.lo, acc);
+        acc = fdot2(q.qp[4 * j + 1], (w[j] & kHiNib) | mg.hi, acc);
+        acc = fdot2(q.qp[4 * j + 2], (y & kLoNib) | mg.lo, acc);
+        acc = fdot2(q.qp[4 * j + 3], (y & kHiNib) | mg.hi, acc);
     }
     return acc;
 }
 
-// acc[i] += ps * (64 + c_i) for the lane's 32 elements (natural order).
-__device__ __forceinline__ void axpy_biased(float (&acc)[32], float ps, const uint4 vx, uint32_t mg)
+// acc[i] += ps * c_i for the lane's 32 elements (natural order), value form;
+// ps_lo = ps * 2^24.
+__device__ __forceinline__ void axpy_values(float (&acc)[32], float ps_lo, const uint4 vx)
 {
+    const float ps_hi = ps_lo * 0.0625f;
     const uint32_t w[4] = {vx.x, vx.y, vx.z, vx.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t p0 = pair0(w[j], mg), p1 = pair1(w[j], mg), p2 = pair2(w[j], mg), p3 = pair3(w[j], mg);
-        acc[8 * j + 0] = __builtin_fmaf(ps, h2f_lo(p0), acc[8 * j + 0]);
-        acc[8 * j + 4] = __builtin_fmaf(ps, h2f_hi(p0), acc[8 * j + 4]);
-        acc[8 * j + 1] = __builtin_fmaf(ps, h2f_lo(p1), acc[8 * j + 1]);
-        acc[8 * j + 5] = __builtin_fmaf(ps, h2f_hi(p1), acc[8 * j + 5]);
-        acc[8 * j + 2] = __builtin_fmaf(ps, h2f_lo(p2), acc[8 * j + 2]);
-        acc[8 * j + 6] = __builtin_fmaf(ps, h2f_hi(p2), acc[8 * j + 6]);
-        acc[8 * j + 3] = __builtin_fmaf(ps, h2f_lo(p3), acc[8 * j + 3]);
-        acc[8 * j + 7] = __builtin_fmaf(ps, h2f_hi(p3), acc[8 * j + 7]);
+        const uint32_t y = w[j] >> 8;
+        const uint32_t p0 = w[j] & kLoNib, p1 = w[j] & kHiNib, p2 = y & kLoNib, p3 = y & kHiNib;
+        acc[8 * j + 0] = __builtin_fmaf(ps_lo, h2f_lo(p0), acc[8 * j + 0]);
+        acc[8 * j + 4] = __builtin_fmaf(ps_lo, h2f_hi(p0), acc[8 * j + 4]);
+        acc[8 * j + 1] = __builtin_fmaf(ps_hi, h2f_lo(p1), acc[8 * j + 1]);
+        acc[8 * j + 5] = __builtin_fmaf(ps_hi, h2f_hi(p1), acc[8 * j + 5]);
+        acc[8 * j + 2] = __builtin_fmaf(ps_lo, h2f_lo(p2), acc[8 * j + 2]);
+        acc[8 * j + 6] = __builtin_fmaf(ps_lo, h2f_hi(p2), acc[8 * j + 6]);
+        acc[8 * j + 3] = __builtin_fmaf(ps_hi, h2f_lo(p3), acc[8 * j + 3]);
+        acc[8 * j + 7] = __builtin_fmaf(ps_hi, h2f_hi(p3), acc[8 * j + 7]);
     }
 }
 
@@ -336,7 +353,7 @@ __device__ __forceinline__ CacheRow<Meta> cache_row(const uint8_t *kc, const uin
 }
 
 template <int D, int UU, bool NEWROW = false, typename Meta>
-__device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
+__device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, const Magic mg,
                                             float c2, float &m, float &l, float &bsum, float (&acc)[32],
                                             const NewRow nr = NewRow{}, int t_new = -1)
 {
@@ -373,8 +390,8 @@ __device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, in
     float mx = m;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-        const float dq = dot_biased(qs, kx[u], mg);
-        float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
+        const float dq = dot_keys(qs, kx[u], mg) - qs.qbias;
+        float sp = __builtin_fmaf(ks[u], dq, km[u] * qs.qsum);
         sp = token_sum<LPT>(sp);
         z[u] = valid[u] ? sp * c2 : -INFINITY;
         mx = fmaxf(mx, z[u]);
@@ -393,8 +410,8 @@ __device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, in
     for (int u = 0; u < UU; ++u) {
         const float p = exp2_fast(z[u] - mref);
         l += p;
-        bsum = __builtin_fmaf(p, __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
-        axpy_biased(acc, p * vs[u], vx[u], mg);
+        bsum = __builtin_fmaf(p, vm[u], bsum);
+        axpy_values(acc, p * (vs[u] * kTwo24), vx[u]);
     }
 }
 
@@ -507,7 +524,7 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, Meta *
     if (tail_wave)
         new_raw = load_new_row<D>(k_new, v_new, pc, lane);
     const QSlice qs = load_q_slice(q + pc * (D / 8) + part * 4);
-    const uint32_t mg = magic64_vgpr();
+    const Magic mg = magic_vgprs();
 
     const CacheRow<Meta> cr = cache_row<D, Meta>(kc, vc, kmin, ksc, vmin, vsc, (int)pc, S, part);
 
@@ -719,7 +736,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp4)
 }
 
 template <int D, int UU, typename Meta>
-__device__ __forceinline__ void score_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, uint32_t mg,
+__device__ __forceinline__ void score_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, const Magic mg,
                                            float c2, bool writer, float *__restrict__ srow)
 {
     constexpr int LPT = D / 32;
@@ -738,8 +755,8 @@ __device__ __forceinline__ void score_iter(const CacheRow<Meta> &cr, int tb, int
     }
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-        const float dq = dot_biased(qs, kx[u], mg);
-        float sp = __builtin_fmaf(ks[u], dq, __builtin_fmaf(-kBias, ks[u], km[u]) * qs.qsum);
+        const float dq = dot_keys(qs, kx[u], mg) - qs.qbias;
+        float sp = __builtin_fmaf(ks[u], dq, km[u] * qs.qsum);
         sp = token_sum<LPT>(sp);
         const int t = tb + u * TPW;
         if (writer && t < t_end)
@@ -769,7 +786,7 @@ __global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__
     const int n_full = (t_end - w_begin) / TPI;
     const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW;
     const QSlice qs = load_q_slice(q + pair * (D / 8) + part * 4);
-    const uint32_t mg = magic64_vgpr();
+    const Magic mg = magic_vgprs();
     const CacheRow<Meta> cr = cache_row<D, Meta>(kc, nullptr, kmin, ksc, nullptr, nullptr, (int)pair, S, part);
     float *__restrict__ srow = scores + pair * T;
     const bool writer = part == 0;
@@ -900,7 +917,6 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
     const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
     const Meta *__restrict__ vmb = vmin + pair * S * G + g;
     const Meta *__restrict__ vsb = vsc + pair * S * G + g;
-    const uint32_t mg = magic64_vgpr();
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
 #pragma unroll
@@ -922,8 +938,8 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
 #pragma unroll
         for (int u = 0; u < UG; ++u) {
             l += p[u];
-            bsum = __builtin_fmaf(p[u], __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
-            axpy_biased(acc, p[u] * vs[u], vx[u], mg);
+            bsum = __builtin_fmaf(p[u], vm[u], bsum);
+            axpy_values(acc, p[u] * (vs[u] * kTwo24), vx[u]);
         }
     }
 #pragma unroll
@@ -1050,7 +1066,6 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
     const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
     const Meta *__restrict__ vmb = vmin + pair * S * G + g;
     const Meta *__restrict__ vsb = vsc + pair * S * G + g;
-    const uint32_t mg = magic64_vgpr();
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
 #pragma unroll
@@ -1073,8 +1088,8 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
 #pragma unroll
         for (int u = 0; u < UG; ++u) {
             l += p[u];
-            bsum = __builtin_fmaf(p[u], __builtin_fmaf(-kBias, vs[u], vm[u]), bsum);
-            axpy_biased(acc, p[u] * vs[u], vx[u], mg);
+            bsum = __builtin_fmaf(p[u], vm[u], bsum);
+            axpy_values(acc, p[u] * (vs[u] * kTwo24), vx[u]);
         }
     }
 #pragma unroll
