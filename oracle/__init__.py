@@ -56,6 +56,10 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_quantize_group.argtypes = [P, P, P, P]
     L.oracle_quantize_rows.argtypes = [I, I, P, P, P, P]
     L.oracle_quantize_group_m16.argtypes = [P, P, P, P]
+    L.oracle_w_dequant.argtypes = [I, ctypes.c_uint16, ctypes.c_uint16]
+    L.oracle_w_dequant.restype = ctypes.c_uint16
+    L.oracle_gemm_w4a16.argtypes = [I, I, I, P, P, P, P, P]
+    L.oracle_gemm_w4a16.restype = None
     L.oracle_quantize_rows_m16.argtypes = [I, I, P, P, P, P]
     L.oracle_dequant_rows.argtypes = [I, I, P, P, P, P]
     L.oracle_dequant_rows_f16.argtypes = [I, I, P, P, P, P]
@@ -290,3 +294,32 @@ def attend_topk(q, hc: HeadCache, k: int, T: int | None = None):
     sel = np.zeros(k, np.int32)
     lib().oracle_attend_topk(hc.d, T, k, _ptr(q), *hc.kargs(), *hc.vargs(), _ptr(out), _ptr(sel))
     return out, sel
+
+
+# ------------------------------------------------------------ int4 weights
+def w_dequant(code: int, min16, scale16) -> np.float16:
+    """FP16 form of one dequantised weight: binary16 nearest to min + code*scale."""
+    mb = int(np.float16(min16).view(np.uint16))
+    sb = int(np.float16(scale16).view(np.uint16))
+    return np.uint16(lib().oracle_w_dequant(int(code), mb, sb)).view(np.float16)
+
+
+def quantize_weight(w):
+    """W fp16 [N][K] -> (codes uint8 [N][K/2], mins float16 [N][K/64], scales float16 [N][K/64])."""
+    return quantize_rows_m16(w)
+
+
+def gemm_w4a16(x, codes, mins, scales) -> np.ndarray:
+    """y = x W^T (binary64) with W^ the FP16 form of the dequantised int4 weights.
+    x fp16 [M][K]; codes [N][K/2]; mins/scales float16 [N][K/64]."""
+    x = _f16bits(x)
+    M, K = x.shape
+    codes = np.ascontiguousarray(codes, np.uint8)
+    N = codes.shape[0]
+    assert codes.shape == (N, K // 2)
+    mins = _f16bits(np.ascontiguousarray(mins, np.float16))
+    scales = _f16bits(np.ascontiguousarray(scales, np.float16))
+    assert mins.shape == (N, K // GROUP) and scales.shape == (N, K // GROUP)
+    y = np.zeros((M, N), np.float64)
+    lib().oracle_gemm_w4a16(M, N, K, _ptr(x), _ptr(codes), _ptr(mins), _ptr(scales), _ptr(y))
+    return y

@@ -426,3 +426,65 @@ void oracle_attend_topk(int d, int T, int k, const uint16_t *q, const uint8_t *k
     free(idx);
     free(s);
 }
+
+/* ------------------------------------------------------------------------
+ * Group-wise int4 weights ([FG-report] 三.2(C): the weights are compressed
+ * with the same group-wise asymmetric 4-bit code as the KV cache and
+ * dequantised to FP16 before compute).  A weight matrix W [N][K] (output
+ * row n, input column k; the [FG-blog] 解码阶段 projections t W_Q, t W_K,
+ * t W_V and t_out W_O) is quantised row by row with the binary16-metadata
+ * codec (oracle_quantize_rows_m16): groups of 64 contiguous k.
+ * --------------------------------------------------------------------- */
+
+/* The FP16 form of a dequantised weight: the binary16 value nearest to
+ * min + code*scale (ties to even), the sum taken exactly.  With binary16 min
+ * and scale every term is an integer multiple of 2^-24, so the sum is an
+ * exact 64-bit integer count of 2^-24 units.                               */
+uint16_t oracle_w_dequant(int code, uint16_t min16, uint16_t scale16)
+{
+    double mn = (double)oracle_f16_to_f32(min16), sc = (double)oracle_f16_to_f32(scale16);
+    int64_t units = (int64_t)llround(ldexp(mn, 24)) + (int64_t)code * (int64_t)llround(ldexp(sc, 24));
+    int neg = units < 0;
+    uint64_t a = (uint64_t)(neg ? -units : units);
+    if (a == 0)
+        return 0; /* +0 */
+    /* binary16 spacing at a * 2^-24: 2^(e-10) for 2^e <= value < 2^(e+1), at least 2^-24 */
+    int e = 63 - __builtin_clzll(a) - 24;
+    int qshift = (e - 10 > -24 ? e - 10 : -24) + 24; /* spacing in units, log2 */
+    uint64_t q = (uint64_t)1 << qshift;
+    uint64_t lo = a / q * q, rem = a - lo;
+    uint64_t r = lo;
+    if (rem * 2 > q || (rem * 2 == q && ((lo / q) & 1)))
+        r = lo + q;
+    double v = ldexp((double)r, -24); /* exact: r is representable in binary16 (or overflows it) */
+    if (v > 65504.0)
+        return neg ? 0xfc00u : 0x7c00u;
+    uint16_t h = oracle_f32_to_f16((float)v); /* exact, v is a binary16 value */
+    return neg ? (uint16_t)(h | 0x8000u) : h;
+}
+
+/* y[m][n] = sum_k x[m][k] * W^[n][k] (binary64, k ascending), W^ the FP16
+ * form of the dequantised weights: the linear layer y = x W^T of a decode
+ * projection.  x fp16 [M][K]; codes [N][K/2]; mins, scales binary16
+ * [N][K/64].                                                               */
+void oracle_gemm_w4a16(int M, int N, int K, const uint16_t *x, const uint8_t *codes, const uint16_t *mins,
+                       const uint16_t *scales, double *y)
+{
+    int G = K / ORACLE_GROUP;
+    double *wrow = (double *)malloc(sizeof(double) * (size_t)K);
+    for (int n = 0; n < N; ++n) {
+        for (int k = 0; k < K; ++k) {
+            int g = k / ORACLE_GROUP;
+            int c = oracle_code_at(codes + (size_t)n * (K / 2), k);
+            wrow[k] = (double)oracle_f16_to_f32(
+                oracle_w_dequant(c, mins[(size_t)n * G + g], scales[(size_t)n * G + g]));
+        }
+        for (int m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += (double)oracle_f16_to_f32(x[(size_t)m * K + k]) * wrow[k];
+            y[(size_t)m * N + n] = acc;
+        }
+    }
+    free(wrow);
+}

@@ -16,7 +16,10 @@ Passages pinned:
   planes;
 * dense decode attention -- the FlexGen blog, section "解码阶段", with the
   1/sqrt(d_k) scale of eq. (2) in the efficient-inference survey notes;
-* top-10% sparse attention -- the report's section 三.2(C).
+* top-10% sparse attention -- the report's section 三.2(C);
+* int4 weights of the decode projections -- the same report section (weights
+  compressed with the same code, dequantised to FP16 before compute) and the
+  blog's "解码阶段" projections.
 """
 from __future__ import annotations
 
@@ -321,6 +324,82 @@ def pin_codec_m16_error_bound():
             continue
         over = max(0.0, rng - 15 * float(sc))
         assert np.all(np.abs(xs - xhat) <= float(sc) / 2 * (1 + 1e-5) + over + abs(xs).max() * 2.0 ** -22)
+
+
+# ------------------------------------------------------------- int4 weights
+def _load_w_examples():
+    out = []
+    with open(os.path.join(GOLDEN, "w_dequant_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                c, mn, sc, exp = line.split()
+                out.append((int(c), float(mn), float(sc), float(exp)))
+    return out
+
+
+def pin_w_dequant_worked_examples():
+    """Hand-derived FP16 forms of dequantised weights (tests/golden/w_dequant_examples.txt):
+    ties to even at both signs, exact cases, a subnormal scale, overflow to inf."""
+    for c, mn, sc, exp in _load_w_examples():
+        got = oracle.w_dequant(c, mn, sc)
+        assert np.float16(mn) == mn and np.float16(sc) == sc
+        assert got.view(np.uint16) == np.float16(exp).view(np.uint16), (c, mn, sc, got, exp)
+
+
+def pin_w_dequant_is_library_rounding():
+    """For weights quantised by the binary16-metadata codec, the dequantised value equals
+    numpy's IEEE binary16 rounding of min + code*scale taken in binary64 (exact here: the
+    terms' binary exponents differ by less than 30)."""
+    r = np.random.default_rng(33)
+    W = (r.standard_normal((40, 256)) * np.exp(r.uniform(-6, 6, (40, 1)))).astype(np.float16)
+    codes, mins, scales = oracle.quantize_weight(W)
+    c = unpack(codes)
+    for n in range(0, 40, 3):
+        for k in range(0, 256, 7):
+            g = k // 64
+            m64, s64 = float(mins[n, g]), float(scales[n, g])
+            ref = np.float16(m64 + c[n, k] * s64)
+            got = oracle.w_dequant(int(c[n, k]), mins[n, g], scales[n, g])
+            assert got.view(np.uint16) == ref.view(np.uint16), (n, k, got, ref)
+
+
+def _w_hat_numpy(codes, mins, scales):
+    c = unpack(codes).astype(np.float64)
+    g = np.repeat(np.arange(c.shape[1] // 64), 64)
+    return (mins.astype(np.float64)[:, g] + c * scales.astype(np.float64)[:, g]).astype(np.float16)
+
+
+def pin_w_gemm_matches_library_matmul():
+    """y = x W^T equals numpy's float64 matmul with the dequantised binary16 weights
+    (dequantised here by numpy's own conversion)."""
+    r = np.random.default_rng(34)
+    for M, N, K in [(1, 5, 64), (3, 16, 192), (9, 7, 512)]:
+        W = r.standard_normal((N, K)).astype(np.float16)
+        x = r.standard_normal((M, K)).astype(np.float16)
+        codes, mins, scales = oracle.quantize_weight(W)
+        ref = x.astype(np.float64) @ _w_hat_numpy(codes, mins, scales).astype(np.float64).T
+        got = oracle.gemm_w4a16(x, codes, mins, scales)
+        assert np.allclose(got, ref, rtol=1e-13, atol=1e-12), np.abs(got - ref).max()
+
+
+def pin_w_gemm_one_hot_and_fractions():
+    """x = e_k picks column k of W^ exactly; a tiny case equals the exact rational sum."""
+    r = np.random.default_rng(35)
+    N, K = 6, 128
+    W = r.standard_normal((N, K)).astype(np.float16)
+    codes, mins, scales = oracle.quantize_weight(W)
+    What = _w_hat_numpy(codes, mins, scales)
+    for k in (0, 63, 64, 127):
+        x = np.zeros((1, K), np.float16)
+        x[0, k] = 1.0
+        assert np.array_equal(oracle.gemm_w4a16(x, codes, mins, scales)[0], What[:, k].astype(np.float64))
+    x = r.standard_normal((2, K)).astype(np.float16)
+    y = oracle.gemm_w4a16(x, codes, mins, scales)
+    for m in range(2):
+        for n in range(N):
+            exact = sum(Fraction(float(x[m, k])) * Fraction(float(What[n, k])) for k in range(K))
+            assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 60)
 
 
 # ----------------------------------------------------------------- attention

@@ -25,6 +25,14 @@ MUTANTS = [
     ("m16_min_rounded", "    *out_min = oracle_f32_to_f16(mn);", "    *out_min = oracle_f32_to_f16(mn * 1.0005f);"),
     ("m16_codes_truncated", "            float r = rintf(t);\n            if (r < 0.0f)\n                r = 0.0f;\n            if (r > 15.0f)\n                r = 15.0f;\n            c[i] = (int)r;\n        }\n    }\n    pack_codes(c, codes);\n    *out_min = oracle_f32_to_f16(mn);",
      "            float r = floorf(t);\n            if (r < 0.0f)\n                r = 0.0f;\n            if (r > 15.0f)\n                r = 15.0f;\n            c[i] = (int)r;\n        }\n    }\n    pack_codes(c, codes);\n    *out_min = oracle_f32_to_f16(mn);"),
+    ("w_dequant_drops_min", "int64_t units = (int64_t)llround(ldexp(mn, 24)) + (int64_t)code",
+     "int64_t units = (int64_t)code"),
+    ("w_dequant_rounds_down", "if (rem * 2 > q || (rem * 2 == q && ((lo / q) & 1)))", "if (0)"),
+    ("w_dequant_ties_up", "if (rem * 2 > q || (rem * 2 == q && ((lo / q) & 1)))", "if (rem * 2 >= q)"),
+    ("w_gemm_neighbour_group", "            int g = k / ORACLE_GROUP;\n            int c = oracle_code_at",
+     "            int g = (k / ORACLE_GROUP + 1) % G;\n            int c = oracle_code_at"),
+    ("w_gemm_x_reversed", "(double)oracle_f16_to_f32(x[(size_t)m * K + k])",
+     "(double)oracle_f16_to_f32(x[(size_t)m * K + (K - 1 - k)])"),
     ("truncate_codes", "float r = rintf(t);", "float r = floorf(t);"),
     ("scale_over_16", "scale = rng / 15.0f;", "scale = rng / 16.0f;"),
     ("inv_over_16", "float inv = 15.0f / rng;", "float inv = 16.0f / rng;"),
