@@ -278,6 +278,53 @@ def time_meta_f16(copies: int = 6, reps: int = 8):
     return res
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def time_projections(copies: int = 3, reps: int = 8):
+    """The decode projections of one OPT-175B layer with int4 weights (gemm_w4a16): the
+    fused Q/K/V projection (N = 3h = 36864, K = h = 12288) and the output projection
+    (N = K = 12288), M = 144 tokens (the effective batch).  Synthetic weights N(0, 0.02^2),
+    activations N(0, 1); `copies` weight sets in rotation so the Infinity Cache cannot
+    serve a repeat; medians of per-launch HIP events."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    M, h = 144, 12288
+    st = torch.cuda.current_stream()
+    res = {"workload": f"OPT-175B decode projections, M={M} tokens, int4 weights (group 64, binary16 min/scale), "
+                       f"{copies} weight sets in rotation"}
+    for label, N in (("qkv", 3 * h), ("out", h)):
+        sets = []
+        for c in range(copies):
+            w = W.random_fp16((N, h), 9000 + 10 * c + (N == h), "cuda", 0.02)
+            sets.append(kvq.kvq_w4_quantize(w))
+            del w
+        x = W.random_fp16((M, h), 9100, "cuda")
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        need = kvq.kvq_gemm_w4_workspace_bytes(M, N, h)
+        ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
+        times = []
+        for r in range((reps + 1) * copies):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            kvq.gemm_w4a16(x, *sets[r % copies], y=y, ws=ws)
+            e1.record(st)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in times[copies:])
+        med = ms[len(ms) // 2]
+        flops = 2 * M * N * h
+        wbytes = N * h // 2 + 2 * 2 * N * (h // 64)
+        res[label] = {"N": N, "K": h, "ms_per_call_median": round(med, 4),
+                      "tflops": round(flops / med / 1e9, 1),
+                      "frac_of_mfma_f16_peak": round(flops / med / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                      "weight_gbs": round(wbytes / med / 1e6, 1), "split_workspace_bytes": need}
+        del sets
+    return res
+
+
 def hbm_copy_ceiling():
     """Practical HBM ceiling for mixed read/write streams: a plain 4 GiB device copy
     (torch), read + write bytes / time."""
@@ -383,6 +430,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--no-meta16", action="store_true", help="skip the binary16-metadata leg")
+    ap.add_argument("--no-proj", action="store_true", help="skip the int4-weight projection leg")
     ap.add_argument("--meta", choices=("f32", "f16"), default="f32",
                     help="min/scale plane type of the timed stack (default binary32)")
     ap.add_argument("--fused", action="store_true",
@@ -464,6 +512,10 @@ def main():
     if not args.no_meta16:
         log("[bench] binary16 metadata leg")
         res["meta_f16"] = time_meta_f16()
+        torch.cuda.empty_cache()
+    if not args.no_proj:
+        log("[bench] int4-weight projection leg")
+        res["projections_w4"] = time_projections()
         torch.cuda.empty_cache()
     res["hbm_copy_ceiling_gbs"] = hbm_copy_ceiling()
     if not args.no_cpu_baseline:

@@ -172,6 +172,44 @@ int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k
 int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
                              void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Decode projections with int4 weights.  "FlexGen研究学术报告" section 三.2(C)
+ * compresses the weights with the same group-wise asymmetric 4-bit code as
+ * the KV cache and dequantises them to FP16 before compute; the FlexGen
+ * blog's "解码阶段" applies them as t W_Q, t W_K, t W_V (and t_out W_O).
+ * A weight W is given as in a linear layer, [N][K] fp16 (output row n,
+ * input column k), and quantised row by row in groups of 64 contiguous k
+ * with binary16 min/scale (the KVQ_META_F16 codec above).  The planes are
+ * tiled so that each 64-row x 128-k block is contiguous:
+ *    codes        : uint8   [N/64][K/128][64][64]  (row n%64, byte (k%128)/2,
+ *                                                  even k in the low nibble)
+ *    mins, scales : float16 [N/64][K/128][64][2]   (row n%64, group (k%128)/64)
+ * The dequantised weight is the binary16 value nearest to min + code*scale
+ * (sum exact, ties to even); y = x W^T accumulates in binary32 on the matrix
+ * cores.  Requirements: N % 64 == 0, K % 128 == 0, N*K/64 < 2^30,
+ * M*K < 2^31 (x is addressed with 32-bit byte offsets); every
+ * pointer a 16-byte aligned device pointer owned by the caller.
+ * ---------------------------------------------------------------------- */
+
+/* Quantise W (fp16 [N][K]) into codes, mins and scales. */
+int kvq_w4_quantize(const void *w_f16, int32_t N, int32_t K, uint8_t *codes, void *mins_f16, void *scales_f16,
+                    void *hip_stream);
+
+/* Workspace bytes gemm_w4a16 needs: binary32 partial sums [splits][M][N]
+ * when the K range is split across workgroups (num_splits 0 = automatic,
+ * chosen from M, N, K only), else 0. */
+size_t kvq_gemm_w4_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t num_splits);
+
+/* y (fp16 [M][N]) = x (fp16 [M][K]) times the transposed dequantised W, with
+ * M >= 1 rows (the effective batch of one decode step).  num_splits: 0 =
+ * automatic, else 1 <= num_splits <= K/128 ranges of K (KVQ_ERANGE
+ * otherwise).  ws: device workspace of ws_bytes >=
+ * kvq_gemm_w4_workspace_bytes(M, N, K, num_splits) (may be NULL when that is
+ * 0). */
+int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t *codes, const void *mins_f16,
+               const void *scales_f16, void *y_f16, int32_t num_splits, void *ws, size_t ws_bytes,
+               void *hip_stream);
+
 /* Static text for a status code. */
 const char *kvq_strerror(int status);
 

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "KvqError", "QuantKVCache", "kvq_cache_bytes", "kvq_workspace_bytes", "kv_quantize_prefill",
     "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4",
-    "decode_attention_q4_topk",
+    "decode_attention_q4_topk", "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16",
     "library_path", "load_library", "GROUP",
 ]
 
@@ -35,7 +35,7 @@ _LIB_PATH = os.path.join(_HERE, "libkvq4.so")
 
 EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_append_quant", "kvq_workspace_bytes",
             "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4", "decode_attention_q4_topk",
-            "kvq_strerror")
+            "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kvq_strerror")
 
 
 class KvqDims(ctypes.Structure):
@@ -89,6 +89,12 @@ def load_library() -> ctypes.CDLL:
     L.kv_append_attend_q4.restype = ctypes.c_int
     L.decode_attention_q4_topk.argtypes = [PC, P, I32, I32, P, P, P, SZ, P]
     L.decode_attention_q4_topk.restype = ctypes.c_int
+    L.kvq_w4_quantize.argtypes = [P, I32, I32, P, P, P, P]
+    L.kvq_w4_quantize.restype = ctypes.c_int
+    L.kvq_gemm_w4_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    L.kvq_gemm_w4_workspace_bytes.restype = SZ
+    L.gemm_w4a16.argtypes = [P, I32, I32, I32, P, P, P, P, I32, P, SZ, P]
+    L.gemm_w4a16.restype = ctypes.c_int
     L.kvq_strerror.argtypes = [ctypes.c_int]
     L.kvq_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -274,3 +280,58 @@ def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int,
                                                    _ptr(sel_idx), _ptr(ws), need, _stream(stream)),
            "decode_attention_q4_topk")
     return out, sel_idx
+
+
+# ------------------------------------------------------------ int4 weights
+def _t16(t: torch.Tensor, shape, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float16 CUDA tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def kvq_w4_quantize(w: torch.Tensor, stream=None):
+    """W fp16 [N, K] -> device planes in the tiled layout gemm_w4a16 streams:
+    codes uint8 [N/64, K/128, 64, 64], mins and scales fp16 [N/64, K/128, 64, 2]
+    (tile (nt, kt): rows 64nt.., k 128kt..; row r, k-byte j; row r, group h)."""
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    N, K = w.shape
+    _t16(w, (N, K), "w")
+    if N % 64 or K % 128:
+        raise ValueError("N must be a multiple of 64 and K of 128")
+    codes = torch.empty((N // 64, K // 128, 64, 64), dtype=torch.uint8, device=w.device)
+    mins = torch.empty((N // 64, K // 128, 64, 2), dtype=torch.float16, device=w.device)
+    scales = torch.empty_like(mins)
+    _check(load_library().kvq_w4_quantize(_ptr(w), N, K, _ptr(codes), _ptr(mins), _ptr(scales), _stream(stream)),
+           "kvq_w4_quantize")
+    return codes, mins, scales
+
+
+def kvq_gemm_w4_workspace_bytes(M: int, N: int, K: int, num_splits: int = 0) -> int:
+    return load_library().kvq_gemm_w4_workspace_bytes(M, N, K, num_splits)
+
+
+def gemm_w4a16(x: torch.Tensor, codes: torch.Tensor, mins: torch.Tensor, scales: torch.Tensor,
+               y: torch.Tensor | None = None, num_splits: int = 0, ws: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """y = x W^T with int4 weights in the tiled layout of kvq_w4_quantize: x fp16 [M, K] -> y fp16 [M, N]."""
+    if x.dim() != 2 or codes.dim() != 4:
+        raise ValueError("x must be [M, K] and codes [N/64, K/128, 64, 64]")
+    M, K = x.shape
+    N = codes.shape[0] * 64
+    _t16(x, (M, K), "x")
+    if (codes.dtype != torch.uint8 or not codes.is_contiguous()
+            or tuple(codes.shape) != (N // 64, K // 128, 64, 64)):
+        raise ValueError("codes must be a contiguous uint8 tensor [N/64, K/128, 64, 64]")
+    _t16(mins, (N // 64, K // 128, 64, 2), "mins")
+    _t16(scales, (N // 64, K // 128, 64, 2), "scales")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _t16(y, (M, N), "y")
+    need = kvq_gemm_w4_workspace_bytes(M, N, K, num_splits)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need // 4, dtype=torch.float32, device=x.device)
+    _check(load_library().gemm_w4a16(_ptr(x), M, N, K, _ptr(codes), _ptr(mins), _ptr(scales), _ptr(y), num_splits,
+                                     _ptr(ws), need, _stream(stream)), "gemm_w4a16")
+    return y

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq4.so")
-SOURCES = [os.path.join(CSRC, "kvq4_kernels.hip"), os.path.join(CSRC, "kvq4_api.cpp")]
+SOURCES = [os.path.join(CSRC, "kvq4_kernels.hip"), os.path.join(CSRC, "kvq4_gemm.hip"),
+           os.path.join(CSRC, "kvq4_api.cpp")]
 HEADERS = [os.path.join(CSRC, "kvq4_launch.h"), os.path.join(INCLUDE, "kvq4.h")]
 
 ARCH = "gfx950"

@@ -117,6 +117,39 @@ int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
     return s;
 }
 
+// Split of the K range for gemm_w4a16: as many splits as keep the workgroups
+// within one resident round (256 CUs x the workgroups one CU holds at that
+// row-block count: 4 at one block of 16 rows, 2 at two or three, else 1,
+// set by registers and LDS), with at least 4 chunks of 128 k per split.
+// Depends on (M, N, K) only.
+constexpr int kGemmChunk = 128;
+constexpr int kGemmCols = 256;
+
+bool gemm_dims_ok(int M, int N, int K)
+{
+    return M >= 1 && N >= 64 && N % 64 == 0 && K >= kGemmChunk && K % kGemmChunk == 0 &&
+           (int64_t)N * (K / 64) < ((int64_t)1 << 30) && (int64_t)M * K < ((int64_t)1 << 31) &&
+           (int64_t)M * N < ((int64_t)1 << 40);
+}
+
+int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
+{
+    const int chunks = K / kGemmChunk;
+    int s = num_splits;
+    if (s <= 0) {
+        const int mb = kvq::gemm_row_blocks(M);
+        const int rows = 16 * mb;
+        const int per_cu = mb == 1 ? 4 : mb <= 3 ? 2 : 1;
+        const int64_t tiles = (int64_t)((N + kGemmCols - 1) / kGemmCols) * ((M + rows - 1) / rows);
+        s = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)kCUs * per_cu / std::max<int64_t>(tiles, 1),
+                                                        chunks / 4));
+    }
+    s = std::min(s, chunks);
+    const int cps = (chunks + s - 1) / s;
+    *chunks_per_split = cps;
+    return (chunks + cps - 1) / cps; // no empty split
+}
+
 } // namespace
 
 extern "C" {
@@ -268,6 +301,51 @@ int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t 
         return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
     return status_of(kvq::launch_topk(c, pairs, q_f16, ctx_len, k_top, out_f16, sel_idx, static_cast<float *>(ws),
                                       static_cast<hipStream_t>(hip_stream)));
+}
+
+int kvq_w4_quantize(const void *w_f16, int32_t N, int32_t K, uint8_t *codes, void *mins_f16, void *scales_f16,
+                    void *hip_stream)
+{
+    if (!gemm_dims_ok(1, N, K))
+        return KVQ_EINVAL;
+    const void *ptrs[4] = {w_f16, codes, mins_f16, scales_f16};
+    for (const void *p : ptrs)
+        if (check_act(p) != KVQ_OK)
+            return KVQ_EINVAL;
+    return status_of(kvq::launch_quantize_weight(w_f16, N, K, codes, mins_f16, scales_f16,
+                                                 static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t kvq_gemm_w4_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t num_splits)
+{
+    if (!gemm_dims_ok(M, N, K) || num_splits < 0 || num_splits > K / kGemmChunk)
+        return 0;
+    int cps;
+    const int s = gemm_splits(M, N, K, num_splits, &cps);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t *codes, const void *mins_f16,
+               const void *scales_f16, void *y_f16, int32_t num_splits, void *ws, size_t ws_bytes,
+               void *hip_stream)
+{
+    if (!gemm_dims_ok(M, N, K))
+        return KVQ_EINVAL;
+    const void *ptrs[5] = {x_f16, codes, mins_f16, scales_f16, y_f16};
+    for (const void *p : ptrs)
+        if (check_act(p) != KVQ_OK)
+            return KVQ_EINVAL;
+    if (num_splits < 0 || num_splits > K / kGemmChunk)
+        return KVQ_ERANGE;
+    int cps;
+    const int s = gemm_splits(M, N, K, num_splits, &cps);
+    const size_t need = s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return KVQ_ENOSPACE;
+    if (need > 0 && !aligned16(ws))
+        return KVQ_EINVAL;
+    kvq::GemmArgs g{x_f16, codes, mins_f16, scales_f16, y_f16, static_cast<float *>(ws), M, N, K, s, cps};
+    return status_of(kvq::launch_gemm_w4(g, static_cast<hipStream_t>(hip_stream)));
 }
 
 const char *kvq_strerror(int status)

@@ -1253,7 +1253,53 @@ int launch_topk_m(const CachePlanes &c, int pairs, const void *q, int T, int k_t
     }
 }
 
+// Quantise a weight matrix W [N][K] (fp16, row-major): group gi = n*(K/64) + g
+// of 64 contiguous k is read by 8 lanes, coded with the binary16-metadata
+// codec, and stored in the tiled layout the projection kernel streams: tile
+// (n/64, g/2) of 4 KB codes, row n%64 at byte 64*(n%64), half g%2 at byte 32;
+// min and scale at tile*128 + 2*(n%64) + g%2.
+__global__ __launch_bounds__(256) void k_quantize_w(const uint4 *__restrict__ w, int64_t groups, int gk,
+                                                    uint32_t *__restrict__ codes, _Float16 *__restrict__ mins,
+                                                    _Float16 *__restrict__ scales)
+{
+    constexpr int R = 4;
+    const int lir = threadIdx.x & 7;
+    const int64_t g0 = (int64_t)blockIdx.x * (32 * R) + (threadIdx.x >> 3);
+    uint4 x[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        const int64_t gi = min(g0 + 32 * u, groups - 1);
+        x[u] = ld_stream16(w + gi * 8 + lir);
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        uint32_t word;
+        float mn, sc;
+        quant_lane8<_Float16>(x[u], word, mn, sc);
+        const int64_t gi = g0 + 32 * u;
+        if (gi < groups) {
+            const int64_t n = gi / gk, g = gi - n * gk;
+            const int64_t slot = ((n >> 6) * (gk >> 1) + (g >> 1)) * 128 + (n & 63) * 2 + (g & 1);
+            __builtin_nontemporal_store(word, codes + slot * 8 + lir);
+            if (lir == 0) {
+                __builtin_nontemporal_store((_Float16)mn, mins + slot);
+                __builtin_nontemporal_store((_Float16)sc, scales + slot);
+            }
+        }
+    }
+}
+
 } // namespace
+
+int launch_quantize_weight(const void *w, int N, int K, uint8_t *codes, void *mins, void *scales, hipStream_t st)
+{
+    const int64_t groups = (int64_t)N * (K / 64);
+    const int64_t per_block = 32 * 4;
+    hipLaunchKernelGGL(k_quantize_w, dim3((unsigned)((groups + per_block - 1) / per_block)), dim3(256), 0, st,
+                       static_cast<const uint4 *>(w), groups, K / 64, reinterpret_cast<uint32_t *>(codes),
+                       static_cast<_Float16 *>(mins), static_cast<_Float16 *>(scales));
+    return (int)hipGetLastError();
+}
 
 int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
                     hipStream_t st)

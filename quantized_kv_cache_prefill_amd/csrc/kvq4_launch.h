@@ -50,4 +50,24 @@ int launch_topk(const CachePlanes &c, int pairs, const void *q, int T, int k_top
 // Workspace floats needed by launch_topk.
 size_t topk_ws_floats(int pairs, int T);
 
+// y = x W^T with int4 weights (binary16 min/scale planes).  x fp16 [M][K],
+// codes [N][K/2], mins/scales binary16 [N][K/64], y fp16 [M][N].  K % 128 == 0,
+// N % 64 == 0.  splits > 1: binary32 partials in ws ([splits][M][N]) and a
+// reduce pass.
+struct GemmArgs {
+    const void *x;
+    const uint8_t *codes;
+    const void *mins, *scales;
+    void *y;
+    float *ws;
+    int M, N, K;
+    int splits, chunks_per_split;
+};
+int launch_gemm_w4(const GemmArgs &g, hipStream_t st);
+int gemm_row_blocks(int M);
+
+// Quantise W fp16 [N][K] with the binary16-metadata codec: codes [N][K/2],
+// mins/scales binary16 [N][K/64].
+int launch_quantize_weight(const void *w, int N, int K, uint8_t *codes, void *mins, void *scales, hipStream_t st);
+
 }  // namespace kvq

@@ -166,3 +166,31 @@ def test_append_attend_validation(L):
 def test_strerror(L):
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert len(L.kvq_strerror(s)) > 0
+
+
+def test_gemm_w4_validation_and_workspace(L):
+    st = ctypes.c_void_p(0)
+    # shapes: N % 64, K % 128, M >= 1
+    for (M, N, K) in [(0, 64, 128), (1, 63, 128), (1, 64, 64), (1, 100, 128), (4, 64, 192)]:
+        assert L.gemm_w4a16(FAKE, M, N, K, FAKE, FAKE, FAKE, FAKE, 0, None, 0, st) == KVQ_EINVAL
+        assert L.kvq_gemm_w4_workspace_bytes(M, N, K, 0) == 0
+    assert L.kvq_w4_quantize(FAKE, 64, 96, FAKE, FAKE, FAKE, st) == KVQ_EINVAL
+    assert L.kvq_w4_quantize(None, 64, 128, FAKE, FAKE, FAKE, st) == KVQ_EINVAL
+    assert L.kvq_w4_quantize(FAKE, 64, 128, FAKE, FAKE + 2, FAKE, st) == KVQ_EINVAL
+    assert L.gemm_w4a16(None, 1, 64, 128, FAKE, FAKE, FAKE, FAKE, 0, None, 0, st) == KVQ_EINVAL
+    assert L.gemm_w4a16(FAKE, 1, 64, 128, FAKE, FAKE, FAKE, FAKE + 8, 0, None, 0, st) == KVQ_EINVAL
+    # num_splits range: 0 (auto) .. K/128
+    assert L.gemm_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, FAKE, FAKE, 3, FAKE, 1 << 20, st) == KVQ_ERANGE
+    assert L.gemm_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 1 << 20, st) == KVQ_ERANGE
+    # explicit splits: splits x M x N binary32 partials
+    assert L.kvq_gemm_w4_workspace_bytes(144, 256, 1024, 1) == 0
+    assert L.kvq_gemm_w4_workspace_bytes(144, 256, 1024, 4) == 4 * 144 * 256 * 4
+    assert L.gemm_w4a16(FAKE, 144, 256, 1024, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4 * 144 * 256 * 4 - 4,
+                        st) == KVQ_ENOSPACE
+    assert L.gemm_w4a16(FAKE, 144, 256, 1024, FAKE, FAKE, FAKE, FAKE, 4, None, 0, st) == KVQ_ENOSPACE
+    # automatic: the OPT-175B decode projection (M=144, N=K=12288) splits K over the 48 column tiles
+    auto = L.kvq_gemm_w4_workspace_bytes(144, 12288, 12288, 0)
+    assert auto > 0 and auto % (144 * 12288 * 4) == 0
+    # a split count that leaves an empty split is reduced: 96 chunks in 7 splits -> 14 per split, 7 splits
+    assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 7) == 7 * 64 * 4
+    assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 95) == 48 * 64 * 4  # ceil(96/95)=2 chunks each -> 48 splits
