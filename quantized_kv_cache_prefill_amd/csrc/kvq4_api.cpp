@@ -118,9 +118,9 @@ int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
 }
 
 // Split of the K range for gemm_w4a16: as many splits as keep the workgroups
-// within one resident round (256 CUs x the workgroups one CU holds at that
-// row-block count: 4 at one block of 16 rows, 2 at two or three, else 1,
-// set by registers and LDS), with at least 4 chunks of 128 k per split.
+// within one resident round (256 CUs x the eight-wave workgroups one CU holds
+// at that row-block count: 2 at one block of 16 rows, else 1, set by
+// registers), with at least 4 chunks of 128 k per split.
 // Depends on (M, N, K) only.
 constexpr int kGemmChunk = 128;
 constexpr int kGemmCols = 256;
@@ -139,7 +139,7 @@ int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
     if (s <= 0) {
         const int mb = kvq::gemm_row_blocks(M);
         const int rows = 16 * mb;
-        const int per_cu = mb == 1 ? 4 : mb <= 3 ? 2 : 1;
+        const int per_cu = mb == 1 ? 2 : 1;
         const int64_t tiles = (int64_t)((N + kGemmCols - 1) / kGemmCols) * ((M + rows - 1) / rows);
         s = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)kCUs * per_cu / std::max<int64_t>(tiles, 1),
                                                         chunks / 4));

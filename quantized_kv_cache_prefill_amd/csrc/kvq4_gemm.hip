@@ -16,11 +16,11 @@
 //
 // Shape of the work (OPT-175B decode: M = 144 tokens, N = K = 12288): the
 // weight stream (N*K/2 bytes) and the matrix-core time are of the same order,
-// so the kernel keeps both busy: each wave owns a 16*MB x 64 output tile
-// (MB <= 9 row blocks of 16, four column blocks of 16) and a range of K; the
-// four waves of a workgroup cover 256 columns and share each 128-wide chunk
-// of x through LDS (double-buffered), while every wave streams and
-// dequantises its own 64 weight rows.  Ranges of K are split across
+// so the kernel keeps both busy: a workgroup owns a 16*MB x 256 output tile
+// (MB <= 9 row blocks of 16) and a range of K; its eight waves (two per SIMD)
+// each take 64 columns and half of the row blocks, share each 128-wide chunk
+// of x through LDS (double-buffered), and stream and dequantise their own 64
+// weight rows.  Ranges of K are split across
 // workgroups when the column tiles alone cannot fill the 256 CUs; the split
 // partials (binary32) are summed by a second kernel.
 #include <hip/hip_runtime.h>
@@ -40,6 +40,7 @@ constexpr int kChunk = 128;          // k per pipeline step
 constexpr int kPitch = kChunk + 8;   // LDS row pitch of the x chunk, halves (breaks bank aliasing)
 constexpr int kColsPerWave = 64;     // four 16-column blocks
 constexpr int kColsPerGroup = 4 * kColsPerWave;
+constexpr int kThreads = 512;        // 8 waves: 4 column groups x 2 row halves
 
 __device__ __forceinline__ uint4 ld_nt16(const void *p)
 {
@@ -132,12 +133,12 @@ __device__ __forceinline__ WChunk load_w_chunk(const uint8_t *__restrict__ codes
 }
 
 // Rows m0 .. m0+16*MB-1 of x[:, kc .. kc+127], in 16*MB*16 pieces of 8
-// halves; thread t holds pieces t, t+256, ...  Loaded into registers first
+// halves; thread t holds pieces t, t+512, ...  Loaded into registers first
 // and written to LDS later, so the loads are in flight during the matrix work.
 template <int MB>
 struct XStage {
     static constexpr int PIECES = 16 * MB * (kChunk / 8);
-    static constexpr int PER_THREAD = (PIECES + 255) / 256;
+    static constexpr int PER_THREAD = (PIECES + kThreads - 1) / kThreads;
     uint4 v[PER_THREAD];
 };
 
@@ -158,14 +159,14 @@ __device__ __forceinline__ XOffsets<MB> x_offsets(int M, int K, int m0)
     o.ok = 0;
 #pragma unroll
     for (int i = 0; i < XStage<MB>::PER_THREAD; ++i) {
-        const int p = threadIdx.x + 256 * i;
+        const int p = threadIdx.x + kThreads * i;
         const int row = (p >> 4) % (16 * MB), kp = p & 15;
         const int rc = min(m0 + row, M - 1);
         o.off[i] = (uint32_t)(((int64_t)rc * K + 8 * kp) * 2);
         if (p < XStage<MB>::PIECES && m0 + row < M)
             o.ok |= 1u << i;
     }
-    o.partial = m0 + 16 * MB > M || XStage<MB>::PIECES % 256 != 0;
+    o.partial = m0 + 16 * MB > M || XStage<MB>::PIECES % kThreads != 0;
     return o;
 }
 
@@ -193,86 +194,83 @@ __device__ __forceinline__ void store_x(const XStage<MB> &xs, _Float16 *__restri
 {
 #pragma unroll
     for (int i = 0; i < XStage<MB>::PER_THREAD; ++i) {
-        const int p = threadIdx.x + 256 * i;
+        const int p = threadIdx.x + kThreads * i;
         if (p < XStage<MB>::PIECES)
             *reinterpret_cast<uint4 *>(sx + (p >> 4) * kPitch + 8 * (p & 15)) = interleave_halves(xs.v[i]);
     }
 }
 
 // One 128-k chunk of one wave: dequantise its weights k-step by k-step and
-// accumulate the MB x 4 blocks from the x chunk in LDS.
-template <int MB>
-__device__ __forceinline__ void mma_chunk(const WChunk &cur, const _Float16 *__restrict__ sxb, int lane,
-                                          f4 (&acc)[MB][4])
+// accumulate its MBW x 4 blocks (row blocks rb0 .. rb0+MBW-1 of the x chunk in
+// LDS).
+template <int MBW>
+__device__ __forceinline__ void mma_chunk(const WChunk &cur, const _Float16 *__restrict__ sxb, int rb0, int lane,
+                                          f4 (&acc)[MBW > 0 ? MBW : 1][4])
 {
-    const Magic16 mg = magic16();
-    h2 sc[4], mn[4];
+    if constexpr (MBW > 0) {
+        const Magic16 mg = magic16();
+        h2 sc[4], mn[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        sc[b] = __builtin_bit_cast(h2, (cur.sc[b] & 0xFFFFu) * 0x00010001u);
-        mn[b] = __builtin_bit_cast(h2, (cur.mn[b] & 0xFFFFu) * 0x00010001u);
-    }
-    auto word = [&](int b, int j) -> uint32_t {
-        return j == 0 ? cur.code[b].x : j == 1 ? cur.code[b].y : j == 2 ? cur.code[b].z : cur.code[b].w;
-    };
+        for (int b = 0; b < 4; ++b) {
+            sc[b] = __builtin_bit_cast(h2, (cur.sc[b] & 0xFFFFu) * 0x00010001u);
+            mn[b] = __builtin_bit_cast(h2, (cur.mn[b] & 0xFFFFu) * 0x00010001u);
+        }
+        auto word = [&](int b, int j) -> uint32_t {
+            return j == 0 ? cur.code[b].x : j == 1 ? cur.code[b].y : j == 2 ? cur.code[b].z : cur.code[b].w;
+        };
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        h8 bw[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            bw[b] = dequant8(word(b, j), sc[b], mn[b], mg);
-        // all of this k-step's x reads are issued before its products
-        h8 a[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            a[mb] = *reinterpret_cast<const h8 *>(sxb + (mb * 16 + (lane & 15)) * kPitch + 32 * (lane >> 4) + 8 * j);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int j = 0; j < 4; ++j) {
+            h8 bw[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], bw[b], acc[mb][b], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);     // the k-step's LDS reads,
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB, 0); // then its products
+                bw[b] = dequant8(word(b, j), sc[b], mn[b], mg);
+            // all of this k-step's x reads are issued before its products
+            h8 a[MBW];
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+                a[mb] = *reinterpret_cast<const h8 *>(sxb + ((rb0 + mb) * 16 + (lane & 15)) * kPitch +
+                                                      32 * (lane >> 4) + 8 * j);
+#pragma unroll
+            for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], bw[b], acc[mb][b], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);     // the k-step's LDS reads,
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * MBW, 0); // then its products
+        }
     }
     // keep the caller's LDS writes of the next x chunk (and their wait on its
     // global loads) after this chunk's products
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// grid.x: column groups of 256 (fastest), grid.y: K splits, grid.z: row tiles
-// of 16*MB.  splits == 1: y written as fp16; else binary32 partials to
-// ws[split][M][N].  The next chunk's weights and x are loaded into registers
-// while the current chunk is multiplied; x then goes to the other LDS buffer.
-template <int MB>
-__global__ __launch_bounds__(256) void k_gemm_w4(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
-                                                 const uint16_t *__restrict__ mins,
-                                                 const uint16_t *__restrict__ scales, _Float16 *__restrict__ y,
-                                                 float *__restrict__ ws, int M, int N, int K, int chunks_per_split)
+// The K loop and the stores of one wave: its 64 columns starting at n0 and
+// its MBW row blocks starting at block rb0 of the tile (the tile's MB blocks
+// are staged in LDS by all waves).  Every wave runs the same sequence of
+// barriers whatever its MBW.
+template <int MB, int MBW>
+__device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+                                          const uint16_t *__restrict__ mins, const uint16_t *__restrict__ scales,
+                                          _Float16 *__restrict__ y, float *__restrict__ ws, int M, int N, int K,
+                                          int m0, int64_t n0, int rb0, int split, int splits, int c_begin, int c_end,
+                                          _Float16 (*sx)[16 * MB * kPitch])
 {
-    __shared__ __attribute__((aligned(16))) _Float16 sx[2][16 * MB * kPitch];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + wave * kColsPerWave;
+    const int lane = threadIdx.x & 63;
     const bool wave_ok = n0 < N; // N % 64 == 0: a wave's columns are all in range or all out
-    const int split = blockIdx.y, splits = gridDim.y;
-    const int m0 = blockIdx.z * 16 * MB;
-    const int n_chunks = K / kChunk;
-    const int c_begin = split * chunks_per_split;
-    const int c_end = min(n_chunks, c_begin + chunks_per_split);
-
-    f4 acc[MB][4];
+    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0..63 and store nothing
+    f4 acc[MBW > 0 ? MBW : 1][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < (MBW > 0 ? MBW : 1); ++mb)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             acc[mb][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0..63 and store nothing
-    auto wload = [&](int c) { return load_w_chunk(codes, mins, scales, nsafe, K, c, lane); };
     XStage<MB> xs;
     const XOffsets<MB> xo = x_offsets<MB>(M, K, m0);
     WChunk cur{};
     if (c_begin < c_end) {
-        cur = wload(c_begin);
+        if constexpr (MBW > 0)
+            cur = load_w_chunk(codes, mins, scales, nsafe, K, c_begin, lane);
         load_x<MB>(x, c_begin * kChunk, xo, xs);
         store_x<MB>(xs, sx[0]);
     }
@@ -282,36 +280,70 @@ __global__ __launch_bounds__(256) void k_gemm_w4(const uint16_t *__restrict__ x,
         const bool more = c + 1 < c_end; // uniform
         WChunk nxt{};
         if (more) {
-            nxt = wload(c + 1);
+            if constexpr (MBW > 0)
+                nxt = load_w_chunk(codes, mins, scales, nsafe, K, c + 1, lane);
             load_x<MB>(x, (c + 1) * kChunk, xo, xs);
         }
-        mma_chunk<MB>(cur, sx[buf], lane, acc);
+        mma_chunk<MBW>(cur, sx[buf], rb0, lane, acc);
         if (more)
             store_x<MB>(xs, sx[buf ^ 1]);
         cur = nxt;
         __syncthreads();
     }
 
-    if (!wave_ok)
-        return;
-    // D layout: lane l holds rows 4*(l/16) .. +3 of column l%16 of each 16x16 block
+    if constexpr (MBW > 0) {
+        if (!wave_ok)
+            return;
+        // D layout: lane l holds rows 4*(l/16) .. +3 of column l%16 of each 16x16 block
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t n = n0 + b * 16 + (lane & 15);
+            for (int b = 0; b < 4; ++b) {
+                const int64_t n = n0 + b * 16 + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + mb * 16 + 4 * (lane >> 4) + r;
-                if (m < M) {
-                    if (splits == 1)
-                        y[(int64_t)m * N + n] = (_Float16)acc[mb][b][r];
-                    else
-                        ws[((int64_t)split * M + m) * N + n] = acc[mb][b][r];
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + (rb0 + mb) * 16 + 4 * (lane >> 4) + r;
+                    if (m < M) {
+                        if (splits == 1)
+                            y[(int64_t)m * N + n] = (_Float16)acc[mb][b][r];
+                        else
+                            ws[((int64_t)split * M + m) * N + n] = acc[mb][b][r];
+                    }
                 }
             }
         }
     }
+}
+
+// grid.x: column groups of 256 (fastest), grid.y: K splits, grid.z: row tiles
+// of 16*MB.  Eight waves: wave w takes columns 64*(w%4) of the group and the
+// upper (w < 4: ceil(MB/2) blocks) or lower (w >= 4) row blocks, so two waves
+// share each SIMD and one's dequantisation overlaps the other's matrix work;
+// the pair streams the same weight tile (the second read is an L2 hit).
+// splits == 1: y written as fp16; else binary32 partials to ws[split][M][N].
+// The next chunk's weights and x are loaded into registers while the current
+// chunk is multiplied; x then goes to the other LDS buffer.
+template <int MB>
+__global__ __launch_bounds__(kThreads) void k_gemm_w4(const uint16_t *__restrict__ x,
+                                                      const uint8_t *__restrict__ codes,
+                                                      const uint16_t *__restrict__ mins,
+                                                      const uint16_t *__restrict__ scales,
+                                                      _Float16 *__restrict__ y, float *__restrict__ ws, int M,
+                                                      int N, int K, int chunks_per_split)
+{
+    constexpr int MH = (MB + 1) / 2;
+    __shared__ __attribute__((aligned(16))) _Float16 sx[2][16 * MB * kPitch];
+    const int wave = threadIdx.x >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + (wave & 3) * kColsPerWave;
+    const int split = blockIdx.y, splits = gridDim.y;
+    const int m0 = blockIdx.z * 16 * MB;
+    const int c_begin = split * chunks_per_split;
+    const int c_end = min(K / kChunk, c_begin + chunks_per_split);
+    if (wave < 4)
+        gemm_wave<MB, MH>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, 0, split, splits, c_begin, c_end, sx);
+    else
+        gemm_wave<MB, MB - MH>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, MH, split, splits, c_begin, c_end,
+                               sx);
 }
 
 // y[m][n] = fp16(sum over splits of ws[s][m][n]), 4 outputs per thread.
@@ -340,7 +372,7 @@ int launch_gemm_mb(const GemmArgs &g, hipStream_t st)
 {
     const dim3 grid((unsigned)((g.N + kColsPerGroup - 1) / kColsPerGroup), (unsigned)g.splits,
                     (unsigned)((g.M + 16 * MB - 1) / (16 * MB)));
-    hipLaunchKernelGGL((k_gemm_w4<MB>), grid, dim3(256), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
+    hipLaunchKernelGGL((k_gemm_w4<MB>), grid, dim3(kThreads), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
                        static_cast<const uint16_t *>(g.mins), static_cast<const uint16_t *>(g.scales),
                        static_cast<_Float16 *>(g.y), g.ws, g.M, g.N, g.K, g.chunks_per_split);
     int e = (int)hipGetLastError();
