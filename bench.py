@@ -325,6 +325,61 @@ def time_projections(copies: int = 3, reps: int = 8):
     return res
 
 
+def time_host_attention(reps: int = 5):
+    """Decode attention delegated to the CPU (decode_attention_q4_host) on one OPT-6.7B layer
+    (b=32, a=32, d=128, context 544) with the int4 cache in host memory, on the host's cores,
+    beside the two GPU alternatives for a cache that lives in host memory: copy its planes to
+    HBM over PCIe (pinned, one transfer) and attend there, or keep a resident copy in HBM
+    (decode_attention_q4 alone).  Medians over `reps` calls."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    w = W.OPT_6_7B
+    T = w.s + w.n
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    k, v = W.prefill_kv(w, 0, "cpu", s_len=T)
+    q = W.decode_inputs(w, 0, 1, "cpu")[0]
+    hc = kvq.QuantKVCache(w.b, w.a, w.h, T, 0, device="cpu", meta="f32")
+    kvq.kv_quantize_prefill_host(hc, k, v, n_threads=threads)
+    out = torch.empty_like(q)
+    host_ms = []
+    for _ in range(reps + 1):
+        t0 = time.perf_counter()
+        kvq.decode_attention_q4_host(hc, q, T, out=out, n_threads=threads)
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+    host_ms = sorted(host_ms[1:])
+    pinned = [p.pin_memory() for p in hc.planes()]
+    gc = kvq.QuantKVCache(w.b, w.a, w.h, T, 0, device="cuda", meta="f32")
+    qd = q.cuda()
+    st = torch.cuda.current_stream()
+    copy_ms, attend_ms = [], []
+    for _ in range(reps + 1):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(st)
+        for dst, src in zip(gc.planes(), pinned):
+            dst.copy_(src, non_blocking=True)
+        e1.record(st)
+        kvq.decode_attention_q4(gc, qd, T)
+        e2.record(st)
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+        attend_ms.append(e1.elapsed_time(e2))
+    copy_ms, attend_ms = sorted(copy_ms[1:]), sorted(attend_ms[1:])
+    nb = bytes_decode(w.b * w.a, T, w.d)
+    plane_bytes = sum(p.numel() * p.element_size() for p in pinned)
+    hm, cm, am = host_ms[len(host_ms) // 2], copy_ms[len(copy_ms) // 2], attend_ms[len(attend_ms) // 2]
+    return {"workload": f"OPT-6.7B layer: b={w.b} a={w.a} d={w.d} context {T}, binary32 min/scale planes",
+            "threads": threads, "avx512": kvq.kvq_host_simd(), "cpu_model": cpu_model(),
+            "algorithmic_bytes": nb, "cache_plane_bytes": plane_bytes,
+            "host_attention": {"ms_per_call_median": round(hm, 3), "gbs": round(nb / hm / 1e6, 2),
+                               "layer_tokens_per_s": round(w.b / (hm / 1e3), 1)},
+            "copy_to_hbm_then_gpu": {"copy_ms_median": round(cm, 3), "attend_ms_median": round(am, 4),
+                                     "pcie_gbs": round(plane_bytes / cm / 1e6, 2),
+                                     "layer_tokens_per_s": round(w.b / ((cm + am) / 1e3), 1)},
+            "gpu_resident": {"ms_per_call_median": round(am, 4), "gbs": round(nb / am / 1e6, 1)}}
+
+
 def hbm_copy_ceiling():
     """Practical HBM ceiling for mixed read/write streams: a plain 4 GiB device copy
     (torch), read + write bytes / time."""
@@ -431,6 +486,7 @@ def main():
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--no-meta16", action="store_true", help="skip the binary16-metadata leg")
     ap.add_argument("--no-proj", action="store_true", help="skip the int4-weight projection leg")
+    ap.add_argument("--no-host", action="store_true", help="skip the CPU-delegated attention leg")
     ap.add_argument("--meta", choices=("f32", "f16"), default="f32",
                     help="min/scale plane type of the timed stack (default binary32)")
     ap.add_argument("--fused", action="store_true",
@@ -516,6 +572,10 @@ def main():
     if not args.no_proj:
         log("[bench] int4-weight projection leg")
         res["projections_w4"] = time_projections()
+        torch.cuda.empty_cache()
+    if not args.no_host:
+        log("[bench] CPU-delegated attention leg")
+        res["host_attention"] = time_host_attention()
         torch.cuda.empty_cache()
     res["hbm_copy_ceiling_gbs"] = hbm_copy_ceiling()
     if not args.no_cpu_baseline:

@@ -210,6 +210,32 @@ int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t
                const void *scales_f16, void *y_f16, int32_t num_splits, void *ws, size_t ws_bytes,
                void *hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Host path: the cache kept in CPU memory and the decode attention run on
+ * the CPU, the placement "FlexGen研究学术报告" section 三.2(A) describes
+ * (attention delegated to the CPU so the KV cache never crosses PCIe).  Same
+ * operations, layout, codec and results as the GPU calls above, but every
+ * pointer (the kvq_cache planes included) is HOST memory; the work is split
+ * over (batch row, head) pairs on n_threads threads (0 = all cores) and the
+ * call returns when it is done.  The codec and the attention use AVX-512
+ * when the CPU has it (kvq_host_simd() returns 1), scalar loops otherwise;
+ * both codecs give the same bits as the GPU's.  kvq_host_use_simd(0)
+ * selects the scalar loops everywhere (process-wide, for comparison and
+ * tests; not to be changed while another thread is inside a host call) and
+ * kvq_host_use_simd(1) restores the default.  Errors: as the GPU calls
+ * (KVQ_EINVAL for NULL pointers or bad dimensions, KVQ_ERANGE for s_len,
+ * pos or ctx_len outside the cache); a cache plane that is device memory is
+ * the caller's error and is not detected.
+ * ---------------------------------------------------------------------- */
+int kv_quantize_prefill_host(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t s_len,
+                             int32_t n_threads);
+int kv_append_quant_host(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos,
+                         int32_t n_threads);
+int decode_attention_q4_host(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                             int32_t n_threads);
+int kvq_host_simd(void);
+void kvq_host_use_simd(int enable);
+
 /* Static text for a status code. */
 const char *kvq_strerror(int status);
 

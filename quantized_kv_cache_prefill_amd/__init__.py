@@ -20,6 +20,8 @@ __all__ = [
     "KvqError", "QuantKVCache", "kvq_cache_bytes", "kvq_workspace_bytes", "kv_quantize_prefill",
     "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4",
     "decode_attention_q4_topk", "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16",
+    "kv_quantize_prefill_host", "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd",
+    "kvq_host_use_simd",
     "library_path", "load_library", "GROUP",
 ]
 
@@ -35,7 +37,8 @@ _LIB_PATH = os.path.join(_HERE, "libkvq4.so")
 
 EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_append_quant", "kvq_workspace_bytes",
             "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4", "decode_attention_q4_topk",
-            "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kvq_strerror")
+            "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kv_quantize_prefill_host",
+            "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd", "kvq_host_use_simd", "kvq_strerror")
 
 
 class KvqDims(ctypes.Structure):
@@ -95,6 +98,16 @@ def load_library() -> ctypes.CDLL:
     L.kvq_gemm_w4_workspace_bytes.restype = SZ
     L.gemm_w4a16.argtypes = [P, I32, I32, I32, P, P, P, P, I32, P, SZ, P]
     L.gemm_w4a16.restype = ctypes.c_int
+    L.kv_quantize_prefill_host.argtypes = [PC, P, P, I32, I32]
+    L.kv_quantize_prefill_host.restype = ctypes.c_int
+    L.kv_append_quant_host.argtypes = [PC, P, P, I32, I32]
+    L.kv_append_quant_host.restype = ctypes.c_int
+    L.decode_attention_q4_host.argtypes = [PC, P, I32, P, I32]
+    L.decode_attention_q4_host.restype = ctypes.c_int
+    L.kvq_host_simd.argtypes = []
+    L.kvq_host_simd.restype = ctypes.c_int
+    L.kvq_host_use_simd.argtypes = [ctypes.c_int]
+    L.kvq_host_use_simd.restype = None
     L.kvq_strerror.argtypes = [ctypes.c_int]
     L.kvq_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -335,3 +348,56 @@ def gemm_w4a16(x: torch.Tensor, codes: torch.Tensor, mins: torch.Tensor, scales:
     _check(load_library().gemm_w4a16(_ptr(x), M, N, K, _ptr(codes), _ptr(mins), _ptr(scales), _ptr(y), num_splits,
                                      _ptr(ws), need, _stream(stream)), "gemm_w4a16")
     return y
+
+
+# ------------------------------------------------------------------ host path
+def _host(t: torch.Tensor, shape, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float16 CPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _host_cache(cache: QuantKVCache):
+    if cache.k_codes.is_cuda:
+        raise TypeError("the host calls need a cache in CPU memory (QuantKVCache(..., device='cpu'))")
+
+
+def kv_quantize_prefill_host(cache: QuantKVCache, k: torch.Tensor, v: torch.Tensor, n_threads: int = 0):
+    """kv_quantize_prefill on the CPU: cache and fp16 [b, s_len, a, d] inputs in host memory."""
+    _host_cache(cache)
+    s_len = k.shape[1] if k.dim() == 4 else -1
+    _host(k, (cache.b, s_len, cache.a, cache.d), "k")
+    _host(v, (cache.b, s_len, cache.a, cache.d), "v")
+    _check(load_library().kv_quantize_prefill_host(cache.struct_ref(), _ptr(k), _ptr(v), s_len, n_threads),
+           "kv_quantize_prefill_host")
+
+
+def kv_append_quant_host(cache: QuantKVCache, k_new: torch.Tensor, v_new: torch.Tensor, pos: int,
+                         n_threads: int = 0):
+    _host_cache(cache)
+    _host(k_new, (cache.b, 1, cache.a, cache.d), "k_new")
+    _host(v_new, (cache.b, 1, cache.a, cache.d), "v_new")
+    _check(load_library().kv_append_quant_host(cache.struct_ref(), _ptr(k_new), _ptr(v_new), pos, n_threads),
+           "kv_append_quant_host")
+
+
+def decode_attention_q4_host(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, out: torch.Tensor | None = None,
+                             n_threads: int = 0) -> torch.Tensor:
+    """decode_attention_q4 on the CPU over a host-resident cache; q, out fp16 [b, 1, a, d] in host memory."""
+    _host_cache(cache)
+    _host(q, (cache.b, 1, cache.a, cache.d), "q")
+    if out is None:
+        out = torch.empty_like(q)
+    _host(out, q.shape, "out")
+    _check(load_library().decode_attention_q4_host(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), n_threads),
+           "decode_attention_q4_host")
+    return out
+
+
+def kvq_host_simd() -> bool:
+    return bool(load_library().kvq_host_simd())
+
+
+def kvq_host_use_simd(enable: bool):
+    load_library().kvq_host_use_simd(1 if enable else 0)

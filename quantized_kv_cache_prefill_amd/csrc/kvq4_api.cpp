@@ -348,6 +348,54 @@ int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t
     return status_of(kvq::launch_gemm_w4(g, static_cast<hipStream_t>(hip_stream)));
 }
 
+int kv_quantize_prefill_host(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t s_len,
+                             int32_t n_threads)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if (k_f16 == nullptr || v_f16 == nullptr || n_threads < 0)
+        return KVQ_EINVAL;
+    if (s_len < 1 || s_len > c.S)
+        return KVQ_ERANGE;
+    return kvq::host_quantize(c, k_f16, v_f16, cache->dims.b, s_len, 0, n_threads) == 0 ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+int kv_append_quant_host(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos,
+                         int32_t n_threads)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if (k_f16 == nullptr || v_f16 == nullptr || n_threads < 0)
+        return KVQ_EINVAL;
+    if (pos < 0 || pos >= c.S)
+        return KVQ_ERANGE;
+    return kvq::host_quantize(c, k_f16, v_f16, cache->dims.b, 1, pos, n_threads) == 0 ? KVQ_OK : KVQ_ELAUNCH;
+}
+
+int decode_attention_q4_host(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                             int32_t n_threads)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if (q_f16 == nullptr || out_f16 == nullptr || n_threads < 0)
+        return KVQ_EINVAL;
+    if (ctx_len < 1 || ctx_len > c.S)
+        return KVQ_ERANGE;
+    return kvq::host_attend(c, cache->dims.b * cache->dims.a, q_f16, ctx_len, out_f16, n_threads) == 0
+               ? KVQ_OK
+               : KVQ_ELAUNCH;
+}
+
+int kvq_host_simd() { return kvq::host_has_avx512(); }
+
+void kvq_host_use_simd(int enable) { kvq::host_set_simd(enable); }
+
 const char *kvq_strerror(int status)
 {
     switch (status) {

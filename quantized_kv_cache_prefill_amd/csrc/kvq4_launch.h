@@ -70,4 +70,11 @@ int gemm_row_blocks(int M);
 // mins/scales binary16 [N][K/64].
 int launch_quantize_weight(const void *w, int N, int K, uint8_t *codes, void *mins, void *scales, hipStream_t st);
 
+// Host (CPU) path: the same planes and activations in host memory; work
+// split over (batch row, head) pairs on n_threads threads (0 = all cores).
+int host_quantize(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0, int n_threads);
+int host_attend(const CachePlanes &c, int pairs, const void *q, int T, void *out, int n_threads);
+int host_has_avx512();
+void host_set_simd(int enable);
+
 }  // namespace kvq

@@ -20,7 +20,7 @@ FAKE = 0x10000  # aligned, non-null; never dereferenced because validation fails
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|void|size_t|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
                                  text, flags=re.M)))
 
 
