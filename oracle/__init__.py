@@ -18,7 +18,9 @@ page passage it follows is stated in the C source:
   "解码阶段") with the 1/sqrt(d_k) scale of the efficient-inference survey's
   eq. (2);
 * top-k sparse attention -- the same report section's top-10% sparse
-  attention.
+  attention;
+* prefill attention -- the blog's prefill-phase equation (section
+  "预填充阶段"), causal, over the fp16 K and V.
 """
 from __future__ import annotations
 
@@ -68,6 +70,7 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_attend_subset.argtypes = [I, I, P, P, P, P, P, P, P, P, P]
     L.oracle_select_topk.argtypes = [I, P, I, P]
     L.oracle_attend_topk.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P]
+    L.oracle_prefill_attend.argtypes = [I, I, I, P, P, P, P]
     for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_quantize_group_m16", "oracle_quantize_rows_m16",
               "oracle_dequant_rows", "oracle_dequant_rows_f16",
               "oracle_scores",
@@ -294,6 +297,18 @@ def attend_topk(q, hc: HeadCache, k: int, T: int | None = None):
     sel = np.zeros(k, np.int32)
     lib().oracle_attend_topk(hc.d, T, k, _ptr(q), *hc.kargs(), *hc.vargs(), _ptr(out), _ptr(sel))
     return out, sel
+
+
+def prefill_attend(q, k, v) -> np.ndarray:
+    """Causal prefill attention of one (batch row, head) over its prompt, fp16 inputs
+    [s][d] (or [s][...][d] views with the head's rows strided, e.g. x[bi, :, ai]); fp64 [s][d]."""
+    q, k, v = (_f16bits(np.asarray(x)) for x in (q, k, v))
+    s, d = q.shape
+    assert k.shape == (s, d) and v.shape == (s, d)
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    out = np.zeros((s, d), np.float64)
+    lib().oracle_prefill_attend(d, s, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out))
+    return out
 
 
 # ------------------------------------------------------------ int4 weights

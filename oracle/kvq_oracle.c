@@ -13,7 +13,8 @@
  *  [FG-blog]   "FlexGen: High-Throughput Generative Inference of Large
  *              Language Models with a Single GPU [ICML'23]" (qingweiji blog),
  *              sections "P/D阶段计算 / 解码阶段" (decode-phase KV update and
- *              attention) and "KV Cache" (the [b, s, a, h/a] cache shape).
+ *              attention), "预填充阶段" (prefill attention) and "KV Cache"
+ *              (the [b, s, a, h/a] cache shape).
  *  [FG-report] "FlexGen研究学术报告" (fmread), section 三.2(C) "近似方法的应用":
  *              group-wise asymmetric 4-bit quantisation, 64 contiguous
  *              elements per group, tensors dequantised to FP16 before
@@ -50,7 +51,9 @@
  *   - attention scale 1/sqrt(d), d = head_dim = h/a (the survey's d_k);
  *   - top-k ranks tokens by score (softmax is monotone), larger score
  *     first, ties to the smaller token index; the softmax is renormalised
- *     over the kept tokens.
+ *     over the kept tokens;
+ *   - prefill attention is causal and runs over the fp16 K and V (the
+ *     quantised copy is what the cache keeps for the decode steps).
  */
 #include <math.h>
 #include <stdint.h>
@@ -425,6 +428,50 @@ void oracle_attend_topk(int d, int T, int k, const uint16_t *q, const uint8_t *k
         memcpy(sel, idx, sizeof(int32_t) * (size_t)k);
     free(idx);
     free(s);
+}
+
+/* ------------------------------------------------------------------------
+ * Prefill attention for one (batch row, head) over the prompt ([FG-blog]
+ * 预填充阶段: x_out = softmax(x_Q x_K^T / sqrt(.)) x_V, stopping before W_O
+ * and the residual; scale 1/sqrt(d) per [Survey] eq. (2)).
+ * Readings: causal -- prompt token i attends to tokens 0..i, the tokens a
+ * decode step at position i would see ([FG-blog]: each generated token
+ * depends on the tokens before it), so prefill row i equals that decode
+ * step's attention; and over the fp16 K and V as the projections produced
+ * them (the quantised copy is what the cache keeps for the decode steps).
+ * q, k, v: fp16 bits, row t at + t*stride elements (stride >= d lets the
+ * caller pass one head of a [s][a][d] batch row); out: binary64 [s][d].
+ * --------------------------------------------------------------------- */
+void oracle_prefill_attend(int d, int s, int stride, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           double *out)
+{
+    double c = 1.0 / sqrt((double)d);
+    double *p = (double *)malloc(sizeof(double) * (size_t)(s > 0 ? s : 1));
+    for (int i = 0; i < s; ++i) {
+        const uint16_t *qi = q + (size_t)i * stride;
+        double m = -INFINITY;
+        for (int t = 0; t <= i; ++t) {
+            const uint16_t *kt = k + (size_t)t * stride;
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e)
+                acc += (double)oracle_f16_to_f32(qi[e]) * (double)oracle_f16_to_f32(kt[e]);
+            p[t] = acc * c;
+            if (p[t] > m)
+                m = p[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t <= i; ++t) {
+            p[t] = exp(p[t] - m);
+            l += p[t];
+        }
+        for (int e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int t = 0; t <= i; ++t)
+                acc += p[t] * (double)oracle_f16_to_f32(v[(size_t)t * stride + e]);
+            out[(size_t)i * d + e] = acc / l;
+        }
+    }
+    free(p);
 }
 
 /* ------------------------------------------------------------------------

@@ -19,7 +19,9 @@ Passages pinned:
 * top-10% sparse attention -- the report's section 三.2(C);
 * int4 weights of the decode projections -- the same report section (weights
   compressed with the same code, dequantised to FP16 before compute) and the
-  blog's "解码阶段" projections.
+  blog's "解码阶段" projections;
+* prefill attention -- the blog's "预填充阶段" equation, causal, over the fp16
+  K and V.
 """
 from __future__ import annotations
 
@@ -525,6 +527,75 @@ def pin_topk_matches_masked_library_sdpa():
         ref = _sdpa(q.astype(np.float64), Kh, Vh, mask)
         assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
         assert np.allclose(oracle.attend_subset(q, hc, sel), ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ prefill attention
+def _prompt(seed: int, s: int, d: int, std=1.0):
+    r = np.random.default_rng(seed)
+    return tuple((r.standard_normal((s, d)) * std).astype(np.float16) for _ in range(3))
+
+
+def _causal_sdpa(Q, K, V):
+    """torch's attention routine in float64 on the CPU with its causal mask."""
+    t = [torch.from_numpy(np.ascontiguousarray(x, np.float64)).reshape(1, 1, *x.shape) for x in (Q, K, V)]
+    return torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True).reshape(Q.shape).numpy()
+
+
+def pin_prefill_matches_library_causal_sdpa():
+    """Prefill attention equals torch's float64 scaled_dot_product_attention with
+    is_causal=True on the fp16 Q, K, V (pins the mask, the 1/sqrt(d) scale, the softmax
+    and P.V), including a strided head of a [s][a][d] batch row."""
+    for seed, s, d, std in [(1001, 1, 64, 1.0), (1002, 7, 64, 1.0), (1003, 65, 128, 0.5), (1004, 130, 128, 3.0),
+                            (1005, 20, 256, 1.0), (1006, 64, 64, 8.0)]:
+        Q, K, V = _prompt(seed, s, d, std)
+        got = oracle.prefill_attend(Q, K, V)
+        ref = _causal_sdpa(Q, K, V)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), np.abs(got - ref).max()
+    r = np.random.default_rng(1007)
+    X = [(r.standard_normal((40, 3, 64))).astype(np.float16) for _ in range(3)]
+    got = oracle.prefill_attend(X[0][:, 1], X[1][:, 1], X[2][:, 1])
+    assert np.allclose(got, _causal_sdpa(X[0][:, 1], X[1][:, 1], X[2][:, 1]), rtol=1e-12, atol=1e-12)
+
+
+def pin_prefill_rows_are_decode_steps():
+    """With K and V the codec reproduces exactly (every group holds the levels
+    min + c*scale for c = 0..15 with scale a power of two), prefill row i equals the
+    pinned decode attention of q_i over the cache of tokens 0..i."""
+    r = np.random.default_rng(1011)
+    s, d = 37, 128
+    def lossless():
+        c = r.integers(0, 16, (s, d))
+        c[:, 0::64], c[:, 1::64] = 0, 15                      # every group spans all 16 levels
+        off = np.repeat(r.integers(-8, 8, (s, d // 64)), 64, axis=1)
+        return ((c + off) * 0.25).astype(np.float16)
+    K, V = lossless(), lossless()
+    Q = r.standard_normal((s, d)).astype(np.float16)
+    kc, kmin, ksc = oracle.quantize_rows(K)
+    vc, vmin, vsc = oracle.quantize_rows(V)
+    assert np.array_equal(oracle.dequant_rows(kc, kmin, ksc), K.astype(np.float64))
+    assert np.array_equal(oracle.dequant_rows(vc, vmin, vsc), V.astype(np.float64))
+    hc = oracle.HeadCache(kc, kmin, ksc, vc, vmin, vsc)
+    got = oracle.prefill_attend(Q, K, V)
+    for i in range(s):
+        assert np.allclose(got[i], oracle.attend(Q[i], hc, i + 1), rtol=1e-12, atol=1e-12), i
+
+
+def pin_prefill_closed_forms():
+    """Row 0 is v_0 exactly; identical keys (or a zero query) give row i = the mean of
+    v_0..v_i; two tokens give row 1 = (v0 + e^D v1)/(1 + e^D), D = (q1.k1 - q1.k0)/sqrt(d)."""
+    Q, K, V = _prompt(1021, 50, 128, 1.5)
+    Vd = V.astype(np.float64)
+    got = oracle.prefill_attend(Q, K, V)
+    assert np.array_equal(got[0], Vd[0])
+    prefix_mean = np.cumsum(Vd, axis=0) / np.arange(1, 51)[:, None]
+    Ksame = np.repeat(K[:1], 50, axis=0)
+    assert np.allclose(oracle.prefill_attend(Q, Ksame, V), prefix_mean, rtol=0, atol=1e-12)
+    Qzero = np.zeros_like(Q)
+    assert np.allclose(oracle.prefill_attend(Qzero, K, V), prefix_mean, rtol=0, atol=1e-12)
+    q1 = Q[1].astype(np.float64)
+    D = (q1 @ K[1].astype(np.float64) - q1 @ K[0].astype(np.float64)) / math.sqrt(128)
+    ref = (Vd[0] + math.exp(D) * Vd[1]) / (1 + math.exp(D))
+    assert np.allclose(got[1], ref, rtol=1e-12, atol=1e-13)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -57,6 +57,14 @@ MUTANTS = [
     ("softmax_without_exp", "        s[t] = exp(s[t] - m);", "        s[t] = s[t] - m + 1.0;"),
     ("subset_v_index", "            int t = idx[j];", "            int t = j;"),
     ("topk_ties_to_larger", "if (best < 0 || scores[t] > scores[best])", "if (best < 0 || scores[t] >= scores[best])"),
+    ("prefill_not_causal", "        for (int t = 0; t <= i; ++t) {\n            const uint16_t *kt",
+     "        for (int t = 0; t < s; ++t) {\n            const uint16_t *kt"),
+    ("prefill_excludes_self", "        for (int t = 0; t <= i; ++t) {\n            const uint16_t *kt",
+     "        for (int t = 0; t < i; ++t) {\n            const uint16_t *kt"),
+    ("prefill_scale_1_over_d", "    double c = 1.0 / sqrt((double)d);\n    double *p", "    double c = 1.0 / (double)d;\n    double *p"),
+    ("prefill_v_from_k", "acc += p[t] * (double)oracle_f16_to_f32(v[", "acc += p[t] * (double)oracle_f16_to_f32(k["),
+    ("prefill_query_row_0", "const uint16_t *qi = q + (size_t)i * stride;", "const uint16_t *qi = q;"),
+    ("prefill_no_normalisation", "            out[(size_t)i * d + e] = acc / l;", "            out[(size_t)i * d + e] = acc;"),
     ("topk_smallest", "if (best < 0 || scores[t] > scores[best])", "if (best < 0 || scores[t] < scores[best])"),
 ]
 
