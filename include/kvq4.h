@@ -118,6 +118,20 @@ int kvq_cache_bytes(const kvq_dims *dims, size_t *codes_bytes_per_plane, size_t 
 int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t s_len,
                         void *hip_stream);
 
+/* Prompt phase with its attention, in one launch: writes exactly the planes
+ * kv_quantize_prefill writes (slots 0..s_len-1, bit for bit) and
+ * out = softmax(q k^T / sqrt(d)) v over the prompt, causal (row i over
+ * tokens 0..i), for every (batch row, head).  The FlexGen blog's
+ * "预填充阶段" gives x_out = softmax(x_Q x_K^T/sqrt(.)) x_V (before W_O and
+ * the residual); causal because the decode step at position i sees tokens
+ * 0..i; the attention reads the fp16 K and V (the int4 copy is for the
+ * decode steps).  q, k, v, out: fp16 [b][s_len][a][d], device, 16-byte
+ * aligned; out must not overlap q, k or v.  1 <= s_len <= s+n (KVQ_ERANGE).
+ * Accumulates in binary32 on the matrix cores; the probabilities enter the
+ * P.V product as binary16. */
+int kv_quantize_prefill_attend(const kvq_cache *cache, const void *q_f16, const void *k_f16, const void *v_f16,
+                               int32_t s_len, void *out_f16, void *hip_stream);
+
 /* Decode phase, KV update: quantise the new token's K and V (fp16
  * [b][1][a][d]) into slot `pos` of every (batch row, head), 0 <= pos < s+n.
  * Decode step j (1-based) appends at pos = s+j-1 and then attends over

@@ -35,7 +35,7 @@ KVQ_MAX_SPLITS = 256
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq4.so")
 
-EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_append_quant", "kvq_workspace_bytes",
+EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_quantize_prefill_attend", "kv_append_quant", "kvq_workspace_bytes",
             "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4", "decode_attention_q4_topk",
             "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kv_quantize_prefill_host",
             "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd", "kvq_host_use_simd", "kvq_strerror")
@@ -80,6 +80,8 @@ def load_library() -> ctypes.CDLL:
     L.kvq_cache_bytes.restype = ctypes.c_int
     L.kv_quantize_prefill.argtypes = [PC, P, P, I32, P]
     L.kv_quantize_prefill.restype = ctypes.c_int
+    L.kv_quantize_prefill_attend.argtypes = [PC, P, P, P, I32, P, P]
+    L.kv_quantize_prefill_attend.restype = ctypes.c_int
     L.kv_append_quant.argtypes = [PC, P, P, I32, P]
     L.kv_append_quant.restype = ctypes.c_int
     L.kvq_workspace_bytes.argtypes = [PD, I32, I32, I32]
@@ -210,6 +212,22 @@ def kv_quantize_prefill(cache: QuantKVCache, k: torch.Tensor, v: torch.Tensor, s
     _act(v, (cache.b, s_len, cache.a, cache.d), "v")
     _check(load_library().kv_quantize_prefill(cache.struct_ref(), _ptr(k), _ptr(v), s_len, _stream(stream)),
            "kv_quantize_prefill")
+
+
+def kv_quantize_prefill_attend(cache: QuantKVCache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One launch: the planes of kv_quantize_prefill for slots 0..s_len-1 and the causal
+    prefill attention softmax(q k^T / sqrt(d)) v over the fp16 prompt; q, k, v, out fp16
+    [b, s_len, a, d]."""
+    s_len = k.shape[1] if k.dim() == 4 else -1
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _act(t, (cache.b, s_len, cache.a, cache.d), name)
+    if out is None:
+        out = torch.empty_like(q)
+    _act(out, q.shape, "out")
+    _check(load_library().kv_quantize_prefill_attend(cache.struct_ref(), _ptr(q), _ptr(k), _ptr(v), s_len, _ptr(out),
+                                                     _stream(stream)), "kv_quantize_prefill_attend")
+    return out
 
 
 def kv_append_quant(cache: QuantKVCache, k_new: torch.Tensor, v_new: torch.Tensor, pos: int, stream=None):

@@ -15,8 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq4.so")
 SOURCES = [os.path.join(CSRC, "kvq4_kernels.hip"), os.path.join(CSRC, "kvq4_gemm.hip"),
+           os.path.join(CSRC, "kvq4_prefill.hip"),
            os.path.join(CSRC, "kvq4_host.cpp"), os.path.join(CSRC, "kvq4_api.cpp")]
-HEADERS = [os.path.join(CSRC, "kvq4_launch.h"), os.path.join(INCLUDE, "kvq4.h")]
+HEADERS = [os.path.join(CSRC, "kvq4_launch.h"), os.path.join(CSRC, "kvq4_device.h"), os.path.join(INCLUDE, "kvq4.h")]
 
 ARCH = "gfx950"
 

@@ -183,6 +183,22 @@ int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v
                                           static_cast<hipStream_t>(hip_stream)));
 }
 
+int kv_quantize_prefill_attend(const kvq_cache *cache, const void *q_f16, const void *k_f16, const void *v_f16,
+                               int32_t s_len, void *out_f16, void *hip_stream)
+{
+    kvq::CachePlanes c;
+    int st = check_cache(cache, &c);
+    if (st != KVQ_OK)
+        return st;
+    if ((st = check_act(q_f16)) != KVQ_OK || (st = check_act(k_f16)) != KVQ_OK || (st = check_act(v_f16)) != KVQ_OK ||
+        (st = check_act(out_f16)) != KVQ_OK)
+        return st;
+    if (s_len < 1 || s_len > c.S)
+        return KVQ_ERANGE;
+    return status_of(kvq::launch_prefill(c, cache->dims.b, q_f16, k_f16, v_f16, s_len, out_f16,
+                                         static_cast<hipStream_t>(hip_stream)));
+}
+
 int kv_append_quant(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos, void *hip_stream)
 {
     kvq::CachePlanes c;

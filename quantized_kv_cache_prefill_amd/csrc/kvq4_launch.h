@@ -25,6 +25,12 @@ struct CachePlanes {
 int launch_quantize(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
                     hipStream_t st);
 
+// Causal prefill attention over the prompt (fp16 q, k, v and out, each
+// [b][s_len][a][d]) fused with the prompt's quantisation into slots
+// 0..s_len-1 of the cache (the same planes launch_quantize writes).
+int launch_prefill(const CachePlanes &c, int b, const void *q, const void *k, const void *v, int s_len, void *out,
+                   hipStream_t st);
+
 // Dense decode attention.  splits ranges of split_len tokens each; when
 // splits > 1 the partial (max, sum, unnormalised output) go to ws and the
 // reduce pass writes out.  With k_new/v_new non-null ([b][1][a][d] fp16),

@@ -163,6 +163,25 @@ def test_append_attend_validation(L):
     assert L.kv_append_attend_q4(ctypes.byref(cache(d)), FAKE, FAKE, FAKE, 4095, FAKE, 7, None, 0, st) == KVQ_ENOSPACE
 
 
+def test_prefill_attend_validation(L):
+    """kv_quantize_prefill_attend: bad dims, NULL or misaligned q/k/v/out, s_len outside
+    1..S are rejected on the host before any launch."""
+    st = ctypes.c_void_p(0)
+    c = cache()  # S = 20
+    f = L.kv_quantize_prefill_attend
+    assert f(None, FAKE, FAKE, FAKE, 4, FAKE, st) == KVQ_EINVAL
+    for i in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[i] = 0
+        assert f(ctypes.byref(c), *ptrs[:3], 4, ptrs[3], st) == KVQ_EINVAL
+        ptrs[i] = FAKE + 2
+        assert f(ctypes.byref(c), *ptrs[:3], 4, ptrs[3], st) == KVQ_EINVAL
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, 0, FAKE, st) == KVQ_ERANGE
+    assert f(ctypes.byref(c), FAKE, FAKE, FAKE, 21, FAKE, st) == KVQ_ERANGE
+    bad = cache(dims(h=96 * 3))  # head_dim 3 is not a multiple of 64
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, 4, FAKE, st) != KVQ_OK
+
+
 def test_strerror(L):
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert len(L.kvq_strerror(s)) > 0

@@ -1,0 +1,146 @@
+"""GPU parity of the fused prefill (kv_quantize_prefill_attend) against the oracle.
+
+Planes: bit-exact with the oracle's codec (binary32 and binary16 metadata) and
+bit-identical to kv_quantize_prefill's; slots past the prompt untouched.
+Attention: the oracle's binary64 causal prefill attention over the same fp16
+Q, K, V, element-wise within 2e-3 + 1e-2 |oracle|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_kv_cache_prefill_amd as kvq
+import workloads as W
+from tests.gpu_common import QUANTIZE, HostCache, _pool, assert_close, f16_np, log, require_gpu
+from tests.test_parity_gpu import _check_prefill_full, _check_prefill_pairs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle_rows(qh, kh, vh, pairs):
+    """Oracle prefill attention of the given (bi, ai) pairs: [len(pairs)][s][d] (fp64)."""
+    with _pool() as ex:
+        return np.stack(list(ex.map(lambda p: oracle.prefill_attend(qh[p[0], :, p[1]], kh[p[0], :, p[1]],
+                                                                    vh[p[0], :, p[1]]), pairs)))
+
+
+def _gpu_pairs(out: torch.Tensor, pairs):
+    o = out.float()
+    return np.stack([o[bi, :, ai].cpu().numpy() for bi, ai in pairs])
+
+
+def _run_small(b, a, d, s_len, S, seed, meta="f32", std=1.0):
+    q = W.random_fp16((b, s_len, a, d), seed, DEV, std)
+    k = W.random_fp16((b, s_len, a, d), seed + 1, DEV, std)
+    v = W.random_fp16((b, s_len, a, d), seed + 2, DEV, std)
+    cache = kvq.QuantKVCache(b, a, a * d, S, 0, device=DEV, fill=0xFF, meta=meta)
+    out = torch.full_like(q, float("nan"))
+    kvq.kv_quantize_prefill_attend(cache, q, k, v, out=out)
+    torch.cuda.synchronize()
+    return q, k, v, cache, out
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("s_len", [1, 17, 64, 65, 127, 128, 129, 300])
+def test_prefill_small_full(d, s_len):
+    """Every plane and every output: one and several query tiles, ragged last key and
+    query tiles, the diagonal tiles, d = 64, 128, 256."""
+    require_gpu()
+    b, a = 2, 3
+    q, k, v, cache, out = _run_small(b, a, d, s_len, s_len + 5, 7000 + d + s_len)
+    hc = HostCache(b, a, d, s_len + 5)
+    hc.prefill(f16_np(k), f16_np(v))
+    _check_prefill_full(cache, hc, s_len, f"prefill d={d} s={s_len}")
+    pairs = [(bi, ai) for bi in range(b) for ai in range(a)]
+    ref = _oracle_rows(f16_np(q), f16_np(k), f16_np(v), pairs)
+    err = assert_close(_gpu_pairs(out, pairs), ref, f"prefill attention d={d} s={s_len}")
+    log(f"prefill d={d} s={s_len}: max abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+def test_prefill_planes_equal_separate_quantiser_and_tail_untouched(meta):
+    """The fused launch writes the same bytes as kv_quantize_prefill, and nothing past the
+    prompt (slots s_len..S-1 keep their fill)."""
+    require_gpu()
+    b, a, d, s_len, S = 3, 4, 128, 333, 360
+    q, k, v, c1, out = _run_small(b, a, d, s_len, S, 7100, meta=meta)
+    c2 = kvq.QuantKVCache(b, a, a * d, S, 0, device=DEV, fill=0xFF, meta=meta)
+    c0 = kvq.QuantKVCache(b, a, a * d, S, 0, device=DEV, fill=0xFF, meta=meta)  # never written
+    kvq.kv_quantize_prefill(c2, k, v)
+    torch.cuda.synchronize()
+    for t1, t2, t0 in zip(c1.planes(), c2.planes(), c0.planes()):
+        assert torch.equal(t1.view(torch.uint8), t2.view(torch.uint8))
+        assert torch.equal(t1[:, :, s_len:].contiguous().view(torch.uint8),
+                           t0[:, :, s_len:].contiguous().view(torch.uint8))
+    hc = HostCache(b, a, d, S, meta)
+    hc.prefill(f16_np(k), f16_np(v))
+    _check_prefill_full(c1, hc, s_len, f"prefill planes meta={meta}")
+
+
+@pytest.mark.parametrize("std", [4.0, 12.0])
+def test_prefill_sharp_softmax(std):
+    """Large q and k (scores of hundreds): near one-hot softmax rows, where the running
+    max moves between key tiles."""
+    require_gpu()
+    b, a, d, s_len = 2, 2, 128, 200
+    q, k, v, cache, out = _run_small(b, a, d, s_len, s_len, 7200 + int(std), std=std)
+    pairs = [(bi, ai) for bi in range(b) for ai in range(a)]
+    ref = _oracle_rows(f16_np(q), f16_np(k), f16_np(v), pairs)
+    assert_close(_gpu_pairs(out, pairs), ref, f"prefill std={std}")
+
+
+def test_prefill_deterministic():
+    """Two launches give bit-identical outputs and planes."""
+    require_gpu()
+    b, a, d, s_len = 2, 3, 128, 257
+    q, k, v, c1, o1 = _run_small(b, a, d, s_len, s_len, 7300)
+    c2 = kvq.QuantKVCache(b, a, a * d, s_len, 0, device=DEV, fill=0, meta="f32")
+    o2 = kvq.kv_quantize_prefill_attend(c2, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for t1, t2 in zip(c1.planes(), c2.planes()):
+        assert torch.equal(t1.view(torch.uint8), t2.view(torch.uint8))
+
+
+def _layer_sampled(w: W.Workload, meta: str, n_pairs: int, seed: int):
+    require_gpu()
+    log(f"[{w.name} prefill] b={w.b} a={w.a} d={w.d} s={w.s} meta={meta}")
+    q = W.prefill_q(w, 0, DEV)
+    k, v = W.prefill_kv(w, 0, DEV)
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=DEV, fill=0xFF, meta=meta)
+    out = kvq.kv_quantize_prefill_attend(cache, q, k, v)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(seed)
+    idx = r.choice(w.b * w.a, size=n_pairs, replace=False)
+    pairs = sorted({(0, 0), (w.b - 1, w.a - 1)} | {(int(i) // w.a, int(i) % w.a) for i in idx})
+    hq = {p: q[p[0], :, p[1]].cpu().numpy() for p in pairs}
+    hk = {p: k[p[0], :, p[1]].cpu().numpy() for p in pairs}
+    hv = {p: v[p[0], :, p[1]].cpu().numpy() for p in pairs}
+    hc = HostCache(w.b, w.a, w.d, w.S, meta)  # oracle planes of the sampled pairs only
+    for bi, ai in pairs:
+        c, m, s = QUANTIZE[meta](hk[(bi, ai)].view(np.uint16))
+        hc.kc[bi, ai, :w.s], hc.kmin[bi, ai, :w.s], hc.ksc[bi, ai, :w.s] = c, m, s
+        c, m, s = QUANTIZE[meta](hv[(bi, ai)].view(np.uint16))
+        hc.vc[bi, ai, :w.s], hc.vmin[bi, ai, :w.s], hc.vsc[bi, ai, :w.s] = c, m, s
+    _check_prefill_pairs(cache, hc, w.s, pairs, f"{w.name} prefill")
+    with _pool() as ex:
+        ref = np.stack(list(ex.map(lambda p: oracle.prefill_attend(hq[p], hk[p], hv[p]), pairs)))
+    err = assert_close(_gpu_pairs(out, pairs), ref, f"{w.name} prefill attention")
+    log(f"[{w.name} prefill] {len(pairs)} pairs: planes bit-exact, attention max abs err {err:.2e}")
+
+
+@pytest.mark.timeout(600)
+def test_prefill_opt175b_layer_sampled():
+    """The OPT-175B layer (b=144, a=96, d=128, prompt 512) in the launch the benchmark
+    times: 64 seeded (batch row, head) pairs plus the first and last, all 512 rows."""
+    _layer_sampled(W.OPT_175B, "f32", 64, 91)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_opt30b_layer_sampled_m16():
+    """OPT-30B (b=256, a=56) with its outlier channels, binary16 planes: sampled pairs."""
+    _layer_sampled(W.OPT_30B, "f16", 48, 92)

@@ -13,7 +13,7 @@ the decode-phase notation of the FlexGen blog (b, a, h, s, n; section
 activation is a seeded normal draw.
 
 Layouts handed to the library:
-  prefill K/V      fp16 [b][s][a][d]   (the blog's [b, s, a, h/a] cache shape)
+  prefill Q/K/V    fp16 [b][s][a][d]   (the blog's [b, s, a, h/a] cache shape)
   q, k_new, v_new  fp16 [b][1][a][d]
 """
 from __future__ import annotations
@@ -114,6 +114,15 @@ def prefill_kv(w: Workload, layer: int, device, s_len: int | None = None, b: int
             x = _boost_positions(x, w, layer, device)
         out.append(x.half())
     return out[0], out[1]
+
+
+def prefill_q(w: Workload, layer: int, device, s_len: int | None = None, b: int | None = None) -> torch.Tensor:
+    """Prompt queries for the prefill attention, fp16 [b][s_len][a][d] (same distribution
+    and outlier channels as q of the decode steps)."""
+    s_len = w.s if s_len is None else s_len
+    b = w.b if b is None else b
+    x = _normal((b, s_len, w.a, w.d), seed_of(w, layer, 0, TID_Q), device, w.std)
+    return _apply_outliers(x, w).half()
 
 
 def _boost_positions(k: torch.Tensor, w: Workload, layer: int, device) -> torch.Tensor:
