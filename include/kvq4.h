@@ -126,7 +126,9 @@ int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v
  * the residual); causal because the decode step at position i sees tokens
  * 0..i; the attention reads the fp16 K and V (the int4 copy is for the
  * decode steps).  q, k, v, out: fp16 [b][s_len][a][d], device, 16-byte
- * aligned; out must not overlap q, k or v.  1 <= s_len <= s+n (KVQ_ERANGE).
+ * aligned; out must not overlap q, k or v.  1 <= s_len <= s+n (KVQ_ERANGE);
+ * (s_len + 128) * h * 2 bytes must be below 2^31 (KVQ_EUNSUPPORTED otherwise:
+ * one batch row of the prompt is addressed with 32-bit offsets).
  * Accumulates in binary32 on the matrix cores; the probabilities enter the
  * P.V product as binary16. */
 int kv_quantize_prefill_attend(const kvq_cache *cache, const void *q_f16, const void *k_f16, const void *v_f16,

@@ -195,6 +195,9 @@ int kv_quantize_prefill_attend(const kvq_cache *cache, const void *q_f16, const 
         return st;
     if (s_len < 1 || s_len > c.S)
         return KVQ_ERANGE;
+    // Byte offsets within one batch row's prompt (plus two tiles) must fit in 31 bits.
+    if (((int64_t)s_len + 128) * cache->dims.h * 2 > 0x7FFFFFFF)
+        return KVQ_EUNSUPPORTED;
     return status_of(kvq::launch_prefill(c, cache->dims.b, q_f16, k_f16, v_f16, s_len, out_f16,
                                          static_cast<hipStream_t>(hip_stream)));
 }

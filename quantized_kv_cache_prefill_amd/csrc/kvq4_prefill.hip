@@ -21,8 +21,10 @@
 // matrix core already in the operand layout of O^T = V^T P^T (the key index
 // a lane holds is the same in both): only an fp32 -> fp16 conversion sits
 // between the two products.  K and V tiles are staged through LDS
-// (double-buffered, one barrier per tile): K row-major, V transposed at the
-// write so that the V^T operand is two 8-byte reads.
+// (double-buffered, one barrier per tile), both row-major; the V^T operand is
+// read with gfx950's transposing LDS read (ds_read_b64_tr_b16: within each
+// 16-lane group, lane i's element e comes from element i%4 of the 8 bytes
+// lane 4e + i/4 addresses), so no transposed copy is ever written.
 //
 // The fusion.  Every 64-key tile is read by all the query tiles at or after
 // it; the workgroup whose queries cover that tile's positions (its diagonal)
@@ -32,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "kvq4_device.h"
 #include "kvq4_launch.h"
@@ -55,65 +59,63 @@ struct Shape {
     static constexpr int QT = D <= 128 ? 2 : 1; // 16-query column tiles per wave
     static constexpr int QW = 16 * QT;          // queries per wave
     static constexpr int QB = kWaves * QW;      // queries per workgroup (128, or 64 at d = 256)
-    static constexpr int KP = D + 8;            // K tile row pitch, halves (16-byte rows, offset banks)
-    static constexpr int VP = kKeys + 8;        // V^T tile row pitch, halves
+    static constexpr int KP = D + 8;            // K row pitch, halves: 16-byte reads of 16 rows hit distinct banks
+    static constexpr int VP = D + 16;           // V row pitch, halves: 8-byte reads of 8 rows hit distinct banks
     static constexpr int KS = D / 32;           // k-steps of q.k
     static constexpr int DT = D / 16;           // 16-row tiles of O^T
-    static constexpr int NK = kKeys * (D / 8) / kThreads;       // 16-byte K chunks per thread per tile
-    static constexpr int NV = (kKeys / 2) * (D / 8) / kThreads; // V key pairs per thread per tile
+    static constexpr int NK = kKeys * (D / 8) / kThreads; // 16-byte chunks per thread per tile, each of K and V
     static constexpr int LDS_K = kKeys * KP;    // halves per K buffer
-    static constexpr int LDS_V = D * VP;        // halves per V^T buffer
+    static constexpr int LDS_V = kKeys * VP;    // halves per V buffer
     static constexpr int LDS_HALVES = 2 * (LDS_K + LDS_V);
 };
 
 struct PrefillArgs {
-    const uint16_t *q, *k, *v; // fp16 [b][s_len][a][D]
-    uint16_t *out;             // fp16 [b][s_len][a][D]
+    const uint16_t *q, *k, *v; // fp16 [b_chunk][s_len][a][D], this launch's batch rows
+    uint16_t *out;             // fp16 [b_chunk][s_len][a][D]
     uint32_t *k_codes, *v_codes;
     void *k_min, *k_scale, *v_min, *v_scale;
+    int64_t pair0;  // cache (batch row, head) index of this launch's first pair
+    int bytes;      // bytes of each of q, k, v in this launch (< 2^31)
     int a, S, s_len;
     int n_qtiles;   // query tiles per (batch row, head)
     int64_t total;  // pairs * n_qtiles
     int64_t chunk;  // work items per XCD slice
     float c2;       // log2(e) / sqrt(D)
+    float slack;    // raw-score growth allowed before the accumulators are rescaled: 8 / c2
 };
 
-// The prompt rows one thread moves per tile: NK 16-byte K chunks
-// (key = id / (D/8), chunk c = id % (D/8), id = u*256 + tid) and NV pairs of
-// V chunks (keys 2p and 2p+1 at the same chunk c).  Eight consecutive lanes
-// hold the eight chunks of one 64-element group of one row, the layout the
-// group codec needs.
+// The prompt rows one thread moves per tile: NK 16-byte chunks each of K and
+// V (key = id / (D/8), chunk c = id % (D/8), id = u*256 + tid).  Eight
+// consecutive lanes hold the eight chunks of one 64-element group of one row,
+// the layout the group codec needs.
 template <int D>
 struct TileRegs {
     uint4 k[Shape<D>::NK];
-    uint4 v[2 * Shape<D>::NV];
+    uint4 v[Shape<D>::NK];
 };
 
-__device__ __forceinline__ const uint4 *row_ptr(const uint16_t *base, int64_t bi, int tok, int a, int ai, int s_len,
-                                                int D)
+// The prompt tensors are read through buffer resources: a 32-bit byte offset
+// per lane, fixed for the kernel, plus a scalar offset that steps by one key
+// tile; reads past the end of the tensor return zero.
+typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
 {
-    return reinterpret_cast<const uint4 *>(base + (((bi * s_len + tok) * a + ai) * (int64_t)D));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    const u32x4b v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int D>
-__device__ __forceinline__ void load_tile(const PrefillArgs &g, int64_t bi, int ai, int j, TileRegs<D> &r)
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const int *voff,
+                                          int soff, TileRegs<D> &r)
 {
-    using Sh = Shape<D>;
-    const int tid = threadIdx.x;
-    const int c = tid % (D / 8);
 #pragma unroll
-    for (int u = 0; u < Sh::NK; ++u) {
-        const int key = (u * kThreads + tid) / (D / 8);
-        const int tok = min(kKeys * j + key, g.s_len - 1);
-        r.k[u] = row_ptr(g.k, bi, tok, g.a, ai, g.s_len, D)[c];
-    }
-#pragma unroll
-    for (int u = 0; u < Sh::NV; ++u) {
-        const int p = (u * kThreads + tid) / (D / 8);
-        const int t0 = min(kKeys * j + 2 * p, g.s_len - 1);
-        const int t1 = min(kKeys * j + 2 * p + 1, g.s_len - 1);
-        r.v[2 * u] = row_ptr(g.v, bi, t0, g.a, ai, g.s_len, D)[c];
-        r.v[2 * u + 1] = row_ptr(g.v, bi, t1, g.a, ai, g.s_len, D)[c];
+    for (int u = 0; u < Shape<D>::NK; ++u) {
+        r.k[u] = ld_buf(rk, voff[u], soff);
+        r.v[u] = ld_buf(rv, voff[u], soff);
     }
 }
 
@@ -133,9 +135,8 @@ __device__ __forceinline__ void put_group(uint32_t *codes, Meta *mins, Meta *sca
     }
 }
 
-// Write one tile to LDS (K row-major; V transposed: the two keys of a pair
-// share one 32-bit word per element) and, on the diagonal, quantise its rows
-// into the cache.
+// Write one tile to LDS (K and V row-major) and, on the diagonal, quantise
+// its rows into the cache.
 template <int D, typename Meta>
 __device__ __forceinline__ void store_tile(const PrefillArgs &g, int64_t pair, int j, bool quantise,
                                            const TileRegs<D> &r, _Float16 *lk, _Float16 *lv)
@@ -147,20 +148,7 @@ __device__ __forceinline__ void store_tile(const PrefillArgs &g, int64_t pair, i
     for (int u = 0; u < Sh::NK; ++u) {
         const int key = (u * kThreads + tid) / (D / 8);
         *reinterpret_cast<uint4 *>(lk + key * Sh::KP + 8 * c) = r.k[u];
-    }
-#pragma unroll
-    for (int u = 0; u < Sh::NV; ++u) {
-        const int p = (u * kThreads + tid) / (D / 8);
-        const uint32_t a0[4] = {r.v[2 * u].x, r.v[2 * u].y, r.v[2 * u].z, r.v[2 * u].w};
-        const uint32_t a1[4] = {r.v[2 * u + 1].x, r.v[2 * u + 1].y, r.v[2 * u + 1].z, r.v[2 * u + 1].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // element 2e: low halves of both keys; element 2e+1: high halves
-            const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-            *reinterpret_cast<uint32_t *>(lv + (8 * c + 2 * e) * Sh::VP + 2 * p) = lo;
-            *reinterpret_cast<uint32_t *>(lv + (8 * c + 2 * e + 1) * Sh::VP + 2 * p) = hi;
-        }
+        *reinterpret_cast<uint4 *>(lv + key * Sh::VP + 8 * c) = r.v[u];
     }
     if (quantise) {
         const int64_t base = pair * g.S;
@@ -169,16 +157,18 @@ __device__ __forceinline__ void store_tile(const PrefillArgs &g, int64_t pair, i
             const int tok = kKeys * j + (u * kThreads + tid) / (D / 8);
             put_group<Meta>(g.k_codes, static_cast<Meta *>(g.k_min), static_cast<Meta *>(g.k_scale), base + tok, D,
                             c, r.k[u], tok < g.s_len);
-        }
-#pragma unroll
-        for (int u = 0; u < Sh::NV; ++u) {
-            const int tok = kKeys * j + 2 * ((u * kThreads + tid) / (D / 8));
             put_group<Meta>(g.v_codes, static_cast<Meta *>(g.v_min), static_cast<Meta *>(g.v_scale), base + tok, D,
-                            c, r.v[2 * u], tok < g.s_len);
-            put_group<Meta>(g.v_codes, static_cast<Meta *>(g.v_min), static_cast<Meta *>(g.v_scale), base + tok + 1,
-                            D, c, r.v[2 * u + 1], tok + 1 < g.s_len);
+                            c, r.v[u], tok < g.s_len);
         }
     }
+}
+
+// 8 bytes through the transposing LDS read.
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+__device__ __forceinline__ h4 ld_tr(const _Float16 *p)
+{
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p)));
 }
 
 template <int D, typename Meta>
@@ -195,10 +185,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
     const int64_t w = (int64_t)(blockIdx.x % 8) * g.chunk + blockIdx.x / 8;
     if (w >= g.total)
         return;
-    const int64_t pair = w / g.n_qtiles;
+    const int64_t lpair = w / g.n_qtiles; // pair within this launch
     const int qtile = g.n_qtiles - 1 - (int)(w % g.n_qtiles);
-    const int64_t bi = pair / g.a;
-    const int ai = (int)(pair % g.a);
+    const int bi = (int)(lpair / g.a);
+    const int ai = (int)(lpair % g.a);
+    const int64_t pair = g.pair0 + lpair;
     const int q0 = qtile * Sh::QB;
     const int q_last = min(q0 + Sh::QB, g.s_len) - 1;
     const int n_tiles = q_last / kKeys + 1;
@@ -209,16 +200,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
     const int l16 = lane % 16, g4 = lane / 16;
     const int qw0 = q0 + wave * Sh::QW; // first query of this wave
 
-    // Q^T operand: lane holds query qw0 + 16*qt + l16, d = 32*kd + 8*g4 .. +7.
+    const int row_bytes = g.a * D * 2;                 // one token row of all heads
+    const int head0 = (bi * g.s_len * g.a + ai) * D * 2; // token 0 of this (batch row, head)
+    const __amdgpu_buffer_rsrc_t rq = rsrc(g.q, g.bytes), rk = rsrc(g.k, g.bytes), rv = rsrc(g.v, g.bytes);
+
+    // Q^T operand: lane holds query qw0 + 16*qt + l16, d = 32*kd + 8*g4 .. +7 (queries
+    // past the prompt read the next rows or zeros; their outputs are not stored).
     h8 qb[KS][QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-        const int tok = min(qw0 + 16 * qt + l16, g.s_len - 1);
-        const uint4 *row = row_ptr(g.q, bi, tok, g.a, ai, g.s_len, D);
+        const int voff = head0 + (qw0 + 16 * qt + l16) * row_bytes + 16 * g4;
 #pragma unroll
         for (int kd = 0; kd < KS; ++kd)
-            qb[kd][qt] = __builtin_bit_cast(h8, ld_stream16(row + 4 * kd + g4));
+            qb[kd][qt] = __builtin_bit_cast(h8, ld_buf(rq, voff + 64 * kd, 0));
     }
+    // This thread's tile chunks: key (u*256 + tid) / (D/8) of the tile, chunk tid % (D/8).
+    int voff[Sh::NK];
+#pragma unroll
+    for (int u = 0; u < Sh::NK; ++u)
+        voff[u] = head0 + ((u * kThreads + (int)threadIdx.x) / (D / 8)) * row_bytes + 16 * ((int)threadIdx.x % (D / 8));
+    const int tile_bytes = kKeys * row_bytes;
 
     f4 o[DT][QT];
 #pragma unroll
@@ -234,68 +235,119 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
     }
 
     TileRegs<D> regs;
-    load_tile<D>(g, bi, ai, 0, regs);
+    load_tile<D>(rk, rv, voff, 0, regs);
     store_tile<D, Meta>(g, pair, 0, 0 >= j_diag, regs, lds, lds + Sh::LDS_K);
+    // The query operands are complete before the loop: without this the loop's
+    // products wait on the in-order load counter, i.e. on the next tile's loads.
+#pragma unroll
+    for (int kd = 0; kd < KS; ++kd)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            asm volatile("" : : "v"(qb[kd][qt]));
     __syncthreads();
 
     for (int j = 0; j < n_tiles; ++j) {
         const bool more = j + 1 < n_tiles;
         if (more)
-            load_tile<D>(g, bi, ai, j + 1, regs);
+            load_tile<D>(rk, rv, voff, (j + 1) * tile_bytes, regs);
         const _Float16 *lk = lds + (j & 1) * (Sh::LDS_K + Sh::LDS_V);
         const _Float16 *lv = lk + Sh::LDS_K;
         if (kKeys * j <= qw0 + Sh::QW - 1) { // some key of the tile is visible to some query of the wave
-            // S^T = K Q^T: st[c][qt] holds keys 16c + 4*g4 + r, query 16*qt + l16.
+            // S^T = K Q^T: st[c][qt] holds keys 16c + 4*g4 + r, query 16*qt + l16.  The K
+            // operands of step kd+1 are read from LDS while the products of step kd run.
             f4 st[4][QT];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
                     st[c][qt] = f4{0.f, 0.f, 0.f, 0.f};
+            // Steps (kd, c) in order; the K operand of step i+3 is read while the
+            // products of step i run (a ring of four operands).
+            constexpr int NS = KS * 4, LA = 3;
+            h8 ka[4];
 #pragma unroll
-            for (int kd = 0; kd < KS; ++kd) {
+            for (int i = 0; i < LA; ++i)
+                ka[i] = *reinterpret_cast<const h8 *>(lk + (16 * (i % 4) + l16) * Sh::KP + 32 * (i / 4) + 8 * g4);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const h8 ka = *reinterpret_cast<const h8 *>(lk + (16 * c + l16) * Sh::KP + 32 * kd + 8 * g4);
+            for (int i = 0; i < NS; ++i) {
+                const int kd = i / 4, c = i % 4;
+                if (i + LA < NS) {
+                    const int n = i + LA;
+                    ka[n % 4] = *reinterpret_cast<const h8 *>(lk + (16 * (n % 4) + l16) * Sh::KP + 32 * (n / 4) + 8 * g4);
+                }
 #pragma unroll
-                    for (int qt = 0; qt < QT; ++qt)
-                        st[c][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[kd][qt], st[c][qt], 0, 0, 0);
+                for (int qt = 0; qt < QT; ++qt)
+                    st[c][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i % 4], qb[kd][qt], st[c][qt], 0, 0, 0);
+                if (i + LA < NS) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a later step's LDS read,
+                    __builtin_amdgcn_sched_group_barrier(0x008, QT, 0); // then this step's products
                 }
             }
-            const bool masked = kKeys * j + kKeys - 1 > qw0;
-            h8 pb[2][QT];
+            // Online softmax on the raw scores (the scale c2 > 0 is applied inside the
+            // exponent), both query tiles side by side so their cross-lane steps overlap.
+            // Keys after a query are masked only in the diagonal tiles.
+            if (kKeys * j + kKeys - 1 > qw0) {
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    const int rel = qw0 + 16 * qt + l16 - kKeys * j - 4 * g4; // key offset limit
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (16 * c + r > rel)
+                                st[c][qt][r] = -INFINITY;
+                }
+            }
+            float mx[QT];
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                const int qtok = qw0 + 16 * qt + l16;
-                float mx = -INFINITY;
+                mx[qt] = st[0][qt][0];
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x = st[c][qt][r] * g.c2;
-                        if (masked && kKeys * j + 16 * c + 4 * g4 + r > qtok)
-                            x = -INFINITY;
-                        st[c][qt][r] = x;
-                        mx = fmaxf(mx, x);
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m[qt], mx);
-                const float alpha = exp2_fast(m[qt] - m_new);
-                m[qt] = m_new;
+                    for (int r = 0; r < 4; ++r)
+                        mx[qt] = fmaxf(mx[qt], st[c][qt][r]);
+            }
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 16));
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32));
+            // The reference m only moves when some query's max exceeds it by more than
+            // 8 (log2 units): probabilities up to 2^8 are exact enough in fp16 and the
+            // sum and accumulators are binary32, so the result is the same softmax with
+            // far fewer rescales of O.
+            bool grow = false;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                grow |= mx[qt] > m[qt] + g.slack;
+            if (__any(grow)) {
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    const float m_new = fmaxf(m[qt], mx[qt]);
+                    const float alpha = exp2_fast((m[qt] - m_new) * g.c2);
+                    m[qt] = m_new;
+                    l[qt] *= alpha;
+#pragma unroll
+                    for (int t = 0; t < DT; ++t)
+                        o[t][qt] *= alpha;
+                }
+            }
+            h8 pb[2][QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                const float mb = -m[qt] * g.c2;
                 float ls = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float p = exp2_fast(st[c][qt][r] - m_new);
+                        const float p = exp2_fast(__builtin_fmaf(st[c][qt][r], g.c2, mb));
                         st[c][qt][r] = p;
                         ls += p;
                     }
-                l[qt] = l[qt] * alpha + ls;
-#pragma unroll
-                for (int t = 0; t < DT; ++t)
-                    o[t][qt] *= alpha;
+                l[qt] += ls;
                 // P^T operand of key step ks: slots 0..3 from key tile 2ks, 4..7 from 2ks+1.
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
@@ -305,18 +357,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
                         pb[ks][qt][4 + r] = (_Float16)st[2 * ks + 1][qt][r];
                     }
             }
-            // O^T += V^T P^T: lane holds rows d = 16t + l16 of V^T at the same key slots.
+            // O^T += V^T P^T.  The A operand of row tile t, key step ks: lane (l16, g4) holds
+            // V[key][16t + l16] for keys 32ks + 4*g4 + (0..3) and 32ks + 16 + 4*g4 + (0..3).
+            // Transposing reads: lane (i, g4) addresses row 32ks + 4*g4 + i/4 (and +16),
+            // columns 16t + 4*(i%4) .. +3.
+            const _Float16 *vbase = lv + (4 * g4 + l16 / 4) * Sh::VP + 4 * (l16 % 4);
+            // Steps (t, ks) in order, the operand of step i+3 read during step i.
+            constexpr int NV = DT * 2;
+            h8 va[4];
+            auto ld_va = [&](int n) {
+                const int t = n / 2, ks = n % 2;
+                const h4 v0 = ld_tr(vbase + (32 * ks) * Sh::VP + 16 * t);
+                const h4 v1 = ld_tr(vbase + (32 * ks + 16) * Sh::VP + 16 * t);
+                return h8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            };
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
+            for (int i = 0; i < LA; ++i)
+                va[i] = ld_va(i);
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const _Float16 *vr = lv + (16 * t + l16) * Sh::VP + 32 * ks + 4 * g4;
-                    const h4 v0 = *reinterpret_cast<const h4 *>(vr);
-                    const h4 v1 = *reinterpret_cast<const h4 *>(vr + 16);
-                    const h8 va = h8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            for (int i = 0; i < NV; ++i) {
+                const int t = i / 2, ks = i % 2;
+                if (i + LA < NV)
+                    va[(i + LA) % 4] = ld_va(i + LA);
 #pragma unroll
-                    for (int qt = 0; qt < QT; ++qt)
-                        o[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[ks][qt], o[t][qt], 0, 0, 0);
+                for (int qt = 0; qt < QT; ++qt)
+                    o[t][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i % 4], pb[ks][qt], o[t][qt], 0, 0, 0);
+                if (i + LA < NV) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, QT, 0);
                 }
             }
         }
@@ -336,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
         const float inv = 1.0f / lt;
         const int qtok = qw0 + 16 * qt + l16;
         if (qtok < g.s_len) {
-            uint16_t *row = g.out + (((bi * g.s_len + qtok) * g.a + ai) * (int64_t)D);
+            uint16_t *row = g.out + (((int64_t)bi * g.s_len + qtok) * g.a + ai) * D;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 const h4 h = h4{(_Float16)(o[t][qt][0] * inv), (_Float16)(o[t][qt][1] * inv),
@@ -355,11 +423,15 @@ int launch_prefill_d(const CachePlanes &c, int b, const void *q, const void *k, 
                      hipStream_t st)
 {
     using Sh = Shape<D>;
+    // Batch rows per launch: every byte offset the kernel forms (up to a tile and
+    // a query tile past the last prompt row) stays below 2^31.
+    const int64_t row_bytes = (int64_t)c.a * D * 2;
+    const int64_t seq_bytes = (int64_t)s_len * row_bytes;
+    const int64_t room = 0x7FFFFFFF - 2 * (int64_t)kKeys * row_bytes;
+    if (seq_bytes > room)
+        return (int)hipErrorNotSupported;
+    const int b_step = (int)std::min<int64_t>(b, room / seq_bytes);
     PrefillArgs g;
-    g.q = static_cast<const uint16_t *>(q);
-    g.k = static_cast<const uint16_t *>(k);
-    g.v = static_cast<const uint16_t *>(v);
-    g.out = static_cast<uint16_t *>(out);
     g.k_codes = reinterpret_cast<uint32_t *>(c.k_codes);
     g.v_codes = reinterpret_cast<uint32_t *>(c.v_codes);
     g.k_min = c.k_min;
@@ -370,14 +442,28 @@ int launch_prefill_d(const CachePlanes &c, int b, const void *q, const void *k, 
     g.S = c.S;
     g.s_len = s_len;
     g.n_qtiles = (s_len + Sh::QB - 1) / Sh::QB;
-    g.total = (int64_t)b * c.a * g.n_qtiles;
-    g.chunk = (g.total + 7) / 8;
     g.c2 = kLog2e / sqrtf((float)D);
-    const int64_t grid = 8 * g.chunk;
-    if (grid > 0x7FFFFFFF)
-        return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_prefill<D, Meta>), dim3((unsigned)grid), dim3(kThreads), 0, st, g);
-    return (int)hipGetLastError();
+    g.slack = 8.0f / g.c2;
+    for (int b0 = 0; b0 < b; b0 += b_step) {
+        const int bc = std::min(b_step, b - b0);
+        const int64_t elem0 = (int64_t)b0 * s_len * c.a * D;
+        g.q = static_cast<const uint16_t *>(q) + elem0;
+        g.k = static_cast<const uint16_t *>(k) + elem0;
+        g.v = static_cast<const uint16_t *>(v) + elem0;
+        g.out = static_cast<uint16_t *>(out) + elem0;
+        g.pair0 = (int64_t)b0 * c.a;
+        g.bytes = (int)(bc * seq_bytes);
+        g.total = (int64_t)bc * c.a * g.n_qtiles;
+        g.chunk = (g.total + 7) / 8;
+        const int64_t grid = 8 * g.chunk;
+        if (grid > 0x7FFFFFFF)
+            return (int)hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((k_prefill<D, Meta>), dim3((unsigned)grid), dim3(kThreads), 0, st, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return (int)e;
+    }
+    return 0;
 }
 
 template <typename Meta>
