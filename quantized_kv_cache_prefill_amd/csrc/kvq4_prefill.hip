@@ -20,16 +20,19 @@
 // Each wave computes S^T = K Q^T, so that the probabilities come out of the
 // matrix core already in the operand layout of O^T = V^T P^T (the key index
 // a lane holds is the same in both): only an fp32 -> fp16 conversion sits
-// between the two products.  K and V tiles are staged through LDS
-// (double-buffered, one barrier per tile), both row-major; the V^T operand is
-// read with gfx950's transposing LDS read (ds_read_b64_tr_b16: within each
-// 16-lane group, lane i's element e comes from element i%4 of the 8 bytes
-// lane 4e + i/4 addresses), so no transposed copy is ever written.
+// between the two products.  K and V tiles go from HBM straight into LDS
+// (gfx950's buffer loads to LDS: no staging registers, no LDS write
+// instructions), double-buffered with one barrier per tile, both row-major
+// with the 16-byte chunks of each row XOR-swizzled so that the operand reads
+// hit distinct banks.  The V^T operand is read with the transposing LDS read
+// (ds_read_b64_tr_b16: within each 16-lane group, lane i's element e comes
+// from element i%4 of the 8 bytes lane 4e + i/4 addresses), so no transposed
+// copy is ever written.
 //
 // The fusion.  Every 64-key tile is read by all the query tiles at or after
 // it; the workgroup whose queries cover that tile's positions (its diagonal)
-// also runs the group codec on the fp16 rows it already holds in registers
-// and writes their codes, mins and scales.  So each K/V row is quantised
+// also runs the group codec on the fp16 rows it already holds in LDS and
+// writes their codes, mins and scales.  So each K/V row is quantised
 // exactly once and the prompt is read from HBM once for both jobs.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -59,13 +62,21 @@ struct Shape {
     static constexpr int QT = D <= 128 ? 2 : 1; // 16-query column tiles per wave
     static constexpr int QW = 16 * QT;          // queries per wave
     static constexpr int QB = kWaves * QW;      // queries per workgroup (128, or 64 at d = 256)
-    static constexpr int KP = D + 8;            // K row pitch, halves: 16-byte reads of 16 rows hit distinct banks
-    static constexpr int VP = D + 16;           // V row pitch, halves: 8-byte reads of 8 rows hit distinct banks
     static constexpr int KS = D / 32;           // k-steps of q.k
     static constexpr int DT = D / 16;           // 16-row tiles of O^T
     static constexpr int NK = kKeys * (D / 8) / kThreads; // 16-byte chunks per thread per tile, each of K and V
-    static constexpr int LDS_K = kKeys * KP;    // halves per K buffer
-    static constexpr int LDS_V = kKeys * VP;    // halves per V buffer
+    static constexpr int LDS_K = kKeys * D;     // halves per K buffer (row pitch D)
+    static constexpr int LDS_V = kKeys * D;     // halves per V buffer
+    // Chunk swizzles: chunk c of row r sits at chunk c ^ swz(r) of that row.
+    // RPW rows share one 256-byte bank window; NC chunks of a row are swizzled.
+    static constexpr int RPW = D >= 128 ? 1 : 16 / (D / 8);
+    static constexpr int NC = D / 8 < 16 ? D / 8 : 16;
+    // K: 16-byte reads of 16 consecutive rows at one chunk land in 16 distinct
+    // 16-byte bank groups.
+    static __device__ __forceinline__ int swz_k(int r) { return (r / RPW) % NC; }
+    // V: 8-byte transposing reads of 4 consecutive rows x 2 chunks land in 8
+    // distinct bank groups (even swizzle, so a chunk pair stays a pair).
+    static __device__ __forceinline__ int swz_v(int r) { return 2 * ((r / RPW) % (NC / 2)); }
     static constexpr int LDS_HALVES = 2 * (LDS_K + LDS_V);
 };
 
@@ -84,16 +95,6 @@ struct PrefillArgs {
     float slack;    // raw-score growth allowed before the accumulators are rescaled: 8 / c2
 };
 
-// The prompt rows one thread moves per tile: NK 16-byte chunks each of K and
-// V (key = id / (D/8), chunk c = id % (D/8), id = u*256 + tid).  Eight
-// consecutive lanes hold the eight chunks of one 64-element group of one row,
-// the layout the group codec needs.
-template <int D>
-struct TileRegs {
-    uint4 k[Shape<D>::NK];
-    uint4 v[Shape<D>::NK];
-};
-
 // The prompt tensors are read through buffer resources: a 32-bit byte offset
 // per lane, fixed for the kernel, plus a scalar offset that steps by one key
 // tile; reads past the end of the tensor return zero.
@@ -108,14 +109,20 @@ __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, int voff, int 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// One tile of K and V, HBM -> LDS.  Wave w's u-th load fills 1 KB block
+// B = 4u + w of each buffer: lane l writes chunk position 64B + l, i.e. row
+// (64B + l) / (D/8), swizzled chunk (64B + l) % (D/8); vk/vv hold the byte
+// offsets of the unswizzled chunks that belong there.
 template <int D>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const int *voff,
-                                          int soff, TileRegs<D> &r)
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const int *vk,
+                                           const int *vv, int soff, _Float16 *lk, _Float16 *lv, int wave)
 {
+    typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
     for (int u = 0; u < Shape<D>::NK; ++u) {
-        r.k[u] = ld_buf(rk, voff[u], soff);
-        r.v[u] = ld_buf(rv, voff[u], soff);
+        const int blk = 4 * u + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(lk + 512 * blk), 16, vk[u], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lv + 512 * blk), 16, vv[u], soff, 0, 0);
     }
 }
 
@@ -135,31 +142,27 @@ __device__ __forceinline__ void put_group(uint32_t *codes, Meta *mins, Meta *sca
     }
 }
 
-// Write one tile to LDS (K and V row-major) and, on the diagonal, quantise
-// its rows into the cache.
+// Quantise the rows of one tile (this workgroup's diagonal) into the cache,
+// reading them back from LDS: thread chunk (key (u*256 + tid) / (D/8), chunk
+// tid % (D/8)), eight consecutive lanes per 64-element group.
 template <int D, typename Meta>
-__device__ __forceinline__ void store_tile(const PrefillArgs &g, int64_t pair, int j, bool quantise,
-                                           const TileRegs<D> &r, _Float16 *lk, _Float16 *lv)
+__device__ __forceinline__ void quantise_tile(const PrefillArgs &g, int64_t pair, int j, const _Float16 *lk,
+                                              const _Float16 *lv)
 {
     using Sh = Shape<D>;
     const int tid = threadIdx.x;
     const int c = tid % (D / 8);
+    const int64_t base = pair * g.S;
 #pragma unroll
     for (int u = 0; u < Sh::NK; ++u) {
         const int key = (u * kThreads + tid) / (D / 8);
-        *reinterpret_cast<uint4 *>(lk + key * Sh::KP + 8 * c) = r.k[u];
-        *reinterpret_cast<uint4 *>(lv + key * Sh::VP + 8 * c) = r.v[u];
-    }
-    if (quantise) {
-        const int64_t base = pair * g.S;
-#pragma unroll
-        for (int u = 0; u < Sh::NK; ++u) {
-            const int tok = kKeys * j + (u * kThreads + tid) / (D / 8);
-            put_group<Meta>(g.k_codes, static_cast<Meta *>(g.k_min), static_cast<Meta *>(g.k_scale), base + tok, D,
-                            c, r.k[u], tok < g.s_len);
-            put_group<Meta>(g.v_codes, static_cast<Meta *>(g.v_min), static_cast<Meta *>(g.v_scale), base + tok, D,
-                            c, r.v[u], tok < g.s_len);
-        }
+        const int tok = kKeys * j + key;
+        const uint4 xk = *reinterpret_cast<const uint4 *>(lk + key * D + 8 * (c ^ Sh::swz_k(key)));
+        const uint4 xv = *reinterpret_cast<const uint4 *>(lv + key * D + 8 * (c ^ Sh::swz_v(key)));
+        put_group<Meta>(g.k_codes, static_cast<Meta *>(g.k_min), static_cast<Meta *>(g.k_scale), base + tok, D, c,
+                        xk, tok < g.s_len);
+        put_group<Meta>(g.v_codes, static_cast<Meta *>(g.v_min), static_cast<Meta *>(g.v_scale), base + tok, D, c,
+                        xv, tok < g.s_len);
     }
 }
 
@@ -214,11 +217,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
         for (int kd = 0; kd < KS; ++kd)
             qb[kd][qt] = __builtin_bit_cast(h8, ld_buf(rq, voff + 64 * kd, 0));
     }
-    // This thread's tile chunks: key (u*256 + tid) / (D/8) of the tile, chunk tid % (D/8).
-    int voff[Sh::NK];
+    // Byte offsets (tile 0) of the chunks this lane moves into LDS.
+    int vk[Sh::NK], vv[Sh::NK];
 #pragma unroll
-    for (int u = 0; u < Sh::NK; ++u)
-        voff[u] = head0 + ((u * kThreads + (int)threadIdx.x) / (D / 8)) * row_bytes + 16 * ((int)threadIdx.x % (D / 8));
+    for (int u = 0; u < Sh::NK; ++u) {
+        const int pos = 64 * (4 * u + wave) + lane;
+        const int r = pos / (D / 8), cs = pos % (D / 8);
+        vk[u] = head0 + r * row_bytes + 16 * (cs ^ Sh::swz_k(r));
+        vv[u] = head0 + r * row_bytes + 16 * (cs ^ Sh::swz_v(r));
+    }
     const int tile_bytes = kKeys * row_bytes;
 
     f4 o[DT][QT];
@@ -234,9 +241,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
         l[qt] = 0.f;
     }
 
-    TileRegs<D> regs;
-    load_tile<D>(rk, rv, voff, 0, regs);
-    store_tile<D, Meta>(g, pair, 0, 0 >= j_diag, regs, lds, lds + Sh::LDS_K);
+    issue_tile<D>(rk, rv, vk, vv, 0, lds, lds + Sh::LDS_K, wave);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // The query operands are complete before the loop: without this the loop's
     // products wait on the in-order load counter, i.e. on the next tile's loads.
 #pragma unroll
@@ -248,10 +254,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
 
     for (int j = 0; j < n_tiles; ++j) {
         const bool more = j + 1 < n_tiles;
-        if (more)
-            load_tile<D>(rk, rv, voff, (j + 1) * tile_bytes, regs);
+        if (more) { // into the other buffer, which every wave finished reading before the last barrier
+            _Float16 *nk = lds + ((j + 1) & 1) * (Sh::LDS_K + Sh::LDS_V);
+            issue_tile<D>(rk, rv, vk, vv, (j + 1) * tile_bytes, nk, nk + Sh::LDS_K, wave);
+        }
         const _Float16 *lk = lds + (j & 1) * (Sh::LDS_K + Sh::LDS_V);
         const _Float16 *lv = lk + Sh::LDS_K;
+        if (j >= j_diag)
+            quantise_tile<D, Meta>(g, pair, j, lk, lv);
         if (kKeys * j <= qw0 + Sh::QW - 1) { // some key of the tile is visible to some query of the wave
             // S^T = K Q^T: st[c][qt] holds keys 16c + 4*g4 + r, query 16*qt + l16.  The K
             // operands of step kd+1 are read from LDS while the products of step kd run.
@@ -264,17 +274,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
             // Steps (kd, c) in order; the K operand of step i+3 is read while the
             // products of step i run (a ring of four operands).
             constexpr int NS = KS * 4, LA = 3;
+            const int sk = Sh::swz_k(l16); // rows 16c + l16 all share it
+            auto ld_ka = [&](int n) {
+                return *reinterpret_cast<const h8 *>(lk + (16 * (n % 4) + l16) * D + 8 * ((4 * (n / 4) + g4) ^ sk));
+            };
             h8 ka[4];
 #pragma unroll
             for (int i = 0; i < LA; ++i)
-                ka[i] = *reinterpret_cast<const h8 *>(lk + (16 * (i % 4) + l16) * Sh::KP + 32 * (i / 4) + 8 * g4);
+                ka[i] = ld_ka(i);
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const int kd = i / 4, c = i % 4;
-                if (i + LA < NS) {
-                    const int n = i + LA;
-                    ka[n % 4] = *reinterpret_cast<const h8 *>(lk + (16 * (n % 4) + l16) * Sh::KP + 32 * (n / 4) + 8 * g4);
-                }
+                if (i + LA < NS)
+                    ka[(i + LA) % 4] = ld_ka(i + LA);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
                     st[c][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i % 4], qb[kd][qt], st[c][qt], 0, 0, 0);
@@ -360,15 +372,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
             // O^T += V^T P^T.  The A operand of row tile t, key step ks: lane (l16, g4) holds
             // V[key][16t + l16] for keys 32ks + 4*g4 + (0..3) and 32ks + 16 + 4*g4 + (0..3).
             // Transposing reads: lane (i, g4) addresses row 32ks + 4*g4 + i/4 (and +16),
-            // columns 16t + 4*(i%4) .. +3.
-            const _Float16 *vbase = lv + (4 * g4 + l16 / 4) * Sh::VP + 4 * (l16 % 4);
+            // columns 16t + 4*(i%4) .. +3, i.e. chunk 2t + (i%4)/2, half i%2 of it.
+            const int vrow = 4 * g4 + l16 / 4;
+            const int sv = Sh::swz_v(vrow); // the same for rows vrow + 16k
+            const _Float16 *vbase = lv + vrow * D + 4 * (l16 % 2);
             // Steps (t, ks) in order, the operand of step i+3 read during step i.
             constexpr int NV = DT * 2;
             h8 va[4];
             auto ld_va = [&](int n) {
                 const int t = n / 2, ks = n % 2;
-                const h4 v0 = ld_tr(vbase + (32 * ks) * Sh::VP + 16 * t);
-                const h4 v1 = ld_tr(vbase + (32 * ks + 16) * Sh::VP + 16 * t);
+                const int ch = 8 * ((2 * t + (l16 % 4) / 2) ^ sv);
+                const h4 v0 = ld_tr(vbase + (32 * ks) * D + ch);
+                const h4 v1 = ld_tr(vbase + (32 * ks + 16) * D + ch);
                 return h8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             };
 #pragma unroll
@@ -388,10 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
                 }
             }
         }
-        if (more) {
-            _Float16 *nk = lds + ((j + 1) & 1) * (Sh::LDS_K + Sh::LDS_V);
-            store_tile<D, Meta>(g, pair, j + 1, j + 1 >= j_diag, regs, nk, nk + Sh::LDS_K);
-        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); // the next tile has landed in LDS
         __syncthreads();
     }
 
