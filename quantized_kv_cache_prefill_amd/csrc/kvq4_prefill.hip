@@ -99,14 +99,15 @@ struct PrefillArgs {
 // per lane, fixed for the kernel, plus a scalar offset that steps by one key
 // tile; reads past the end of the tensor return zero.
 typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+// 16 bytes per lane, HBM -> LDS: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, _Float16 *dst, int voff, int soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff)
-{
-    const u32x4b v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // One tile of K and V, HBM -> LDS.  Wave w's u-th load fills 1 KB block
@@ -117,12 +118,11 @@ template <int D>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const int *vk,
                                            const int *vv, int soff, _Float16 *lk, _Float16 *lv, int wave)
 {
-    typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
     for (int u = 0; u < Shape<D>::NK; ++u) {
         const int blk = 4 * u + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(lk + 512 * blk), 16, vk[u], soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lv + 512 * blk), 16, vv[u], soff, 0, 0);
+        dma16(rk, lk + 512 * blk, vk[u], soff);
+        dma16(rv, lv + 512 * blk, vv[u], soff);
     }
 }
 
@@ -207,15 +207,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
     const int head0 = (bi * g.s_len * g.a + ai) * D * 2; // token 0 of this (batch row, head)
     const __amdgpu_buffer_rsrc_t rq = rsrc(g.q, g.bytes), rk = rsrc(g.k, g.bytes), rv = rsrc(g.v, g.bytes);
 
-    // Q^T operand: lane holds query qw0 + 16*qt + l16, d = 32*kd + 8*g4 .. +7 (queries
-    // past the prompt read the next rows or zeros; their outputs are not stored).
-    h8 qb[KS][QT];
+    // The workgroup's QB query rows go HBM -> LDS (the second tile buffer, free until
+    // the loop fills it) as whole rows, chunks swizzled as K's (queries past the
+    // prompt read the next rows or zeros; their outputs are not stored).
+    {
+        constexpr int NQ = Sh::QB * (D / 8) / kThreads;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        const int voff = head0 + (qw0 + 16 * qt + l16) * row_bytes + 16 * g4;
-#pragma unroll
-        for (int kd = 0; kd < KS; ++kd)
-            qb[kd][qt] = __builtin_bit_cast(h8, ld_buf(rq, voff + 64 * kd, 0));
+        for (int u = 0; u < NQ; ++u) {
+            const int blk = 4 * u + wave;
+            const int pos = 64 * blk + lane;
+            const int r = pos / (D / 8), cs = pos % (D / 8);
+            dma16(rq, lds + Sh::LDS_K + Sh::LDS_V + 512 * blk, head0 + (q0 + r) * row_bytes + 16 * (cs ^ Sh::swz_k(r)),
+                  0);
+        }
     }
     // Byte offsets (tile 0) of the chunks this lane moves into LDS.
     int vk[Sh::NK], vv[Sh::NK];
@@ -243,14 +247,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
 
     issue_tile<D>(rk, rv, vk, vv, 0, lds, lds + Sh::LDS_K, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // The query operands are complete before the loop: without this the loop's
-    // products wait on the in-order load counter, i.e. on the next tile's loads.
-#pragma unroll
-    for (int kd = 0; kd < KS; ++kd)
+    __syncthreads();
+    // Q^T operand: lane holds query qw0 + 16*qt + l16, d = 32*kd + 8*g4 .. +7.
+    h8 qb[KS][QT];
+    {
+        const _Float16 *lq = lds + Sh::LDS_K + Sh::LDS_V;
+        const int sq = Sh::swz_k(l16); // query rows 16m + l16 all share it
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-            asm volatile("" : : "v"(qb[kd][qt]));
-    __syncthreads();
+#pragma unroll
+            for (int kd = 0; kd < KS; ++kd)
+                qb[kd][qt] = *reinterpret_cast<const h8 *>(lq + (wave * Sh::QW + 16 * qt + l16) * D +
+                                                           8 * ((4 * kd + g4) ^ sq));
+    }
+    __syncthreads(); // the query rows are in registers before tile 1 overwrites them
 
     for (int j = 0; j < n_tiles; ++j) {
         const bool more = j + 1 < n_tiles;
@@ -407,26 +417,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
         __syncthreads();
     }
 
-    // O = O^T / l: lane holds d = 16t + 4*g4 .. +3 of query 16*qt + l16.
+    // O = O^T / l.  Lane holds d = 16t + 4*g4 .. +3 of query 16*qt + l16; the wave's
+    // rows are gathered in LDS (row pitch D + 8 halves) and written to HBM as whole
+    // rows, 16 bytes per lane.  Every wave passed the loop's last barrier, so the tile
+    // buffers are free.
+    constexpr int OP = D + 8;
+    _Float16 *lo = lds + wave * Sh::QW * OP;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         float lt = l[qt];
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
         const float inv = 1.0f / lt;
-        const int qtok = qw0 + 16 * qt + l16;
-        if (qtok < g.s_len) {
-            uint16_t *row = g.out + (((int64_t)bi * g.s_len + qtok) * g.a + ai) * D;
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const h4 h = h4{(_Float16)(o[t][qt][0] * inv), (_Float16)(o[t][qt][1] * inv),
-                                (_Float16)(o[t][qt][2] * inv), (_Float16)(o[t][qt][3] * inv)};
-                __builtin_nontemporal_store(__builtin_bit_cast(uint2, h).x,
-                                            reinterpret_cast<uint32_t *>(row + 16 * t + 4 * g4));
-                __builtin_nontemporal_store(__builtin_bit_cast(uint2, h).y,
-                                            reinterpret_cast<uint32_t *>(row + 16 * t + 4 * g4) + 1);
-            }
-        }
+        for (int t = 0; t < DT; ++t)
+            *reinterpret_cast<h4 *>(lo + (16 * qt + l16) * OP + 16 * t + 4 * g4) =
+                h4{(_Float16)(o[t][qt][0] * inv), (_Float16)(o[t][qt][1] * inv), (_Float16)(o[t][qt][2] * inv),
+                   (_Float16)(o[t][qt][3] * inv)};
+    }
+    constexpr int LPR = D / 8;          // lanes per row
+#pragma unroll
+    for (int i = 0; i < Sh::QW * LPR / 64; ++i) {
+        const int r = (64 * i + lane) / LPR, cc = (64 * i + lane) % LPR;
+        const int qtok = qw0 + r;
+        const uint4 x = *reinterpret_cast<const uint4 *>(lo + r * OP + 8 * cc);
+        if (qtok < g.s_len)
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4b, x),
+                                        reinterpret_cast<u32x4b *>(g.out + (((int64_t)bi * g.s_len + qtok) * g.a + ai) * D) + cc);
     }
 }
 
