@@ -52,6 +52,7 @@ __device__ __forceinline__ float ld_stream(const float *p) { return __builtin_no
 //    against the stored scale; the min is an fp16 input, stored exactly;
 // code = clamp(rint_even((x - min) * inv), 0, 15); a stored scale of 0
 // (constant group, or a binary16 scale that underflows) gives codes 0.
+// Inputs are finite fp16 values (the caller's contract).
 // word holds the lane's 8 codes, element i at bits 4i..4i+3; mn_out and
 // scale_out are the stored values, widened to binary32.
 // ===========================================================================
@@ -95,14 +96,24 @@ __device__ __forceinline__ void quant_lane8(const uint4 x, uint32_t &word, float
             inv = 1.0f / scale;
     }
     if (scale != 0.0f) {
+        // v_cvt_pk_u8_f32 rounds to nearest even, takes t <= 0 to 0 and inserts the
+        // byte: the codes of the even elements go to bytes of ev, the odd ones to od,
+        // and ev | od << 4 puts element i at bits 4i.  With binary32 metadata t never
+        // reaches 15.5 (t <= 15 (1 + 2^-24)^2), so no clamp is needed; with binary16
+        // metadata the stored scale can be below rng/15 and t is clamped at 15 first.
+        uint32_t ev = 0, od = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float t = f[i] - mn;
             t = t * inv;
-            float r = __builtin_rintf(t); // ties to even
-            r = fminf(fmaxf(r, 0.0f), 15.0f);
-            codes |= (uint32_t)r << (4 * i);
+            if constexpr (sizeof(Meta) != 4)
+                t = fminf(t, 15.0f);
+            if (i % 2 == 0)
+                ev = __builtin_amdgcn_cvt_pk_u8_f32(t, i / 2, ev);
+            else
+                od = __builtin_amdgcn_cvt_pk_u8_f32(t, i / 2, od);
         }
+        codes = ev | (od << 4);
     }
     word = codes;
     mn_out = mn;
