@@ -38,7 +38,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode attention int4-KV HBM GB/s (% of peak) + layer-tokens/s, OPT-175B shape"
 HBM_PEAK_GBS = 8000.0
 PROFILE_PMC = os.path.join(ROOT, "profiles", "k_decode_opt175b_pmc.md")
-KERNEL_SRC = os.path.join(ROOT, "quantized_kv_cache_prefill_amd", "csrc", "kvq4_kernels.hip")
+KERNEL_SRC = (os.path.join(ROOT, "quantized_kv_cache_prefill_amd", "csrc", "kvq4_kernels.hip"),
+              os.path.join(ROOT, "quantized_kv_cache_prefill_amd", "csrc", "kvq4_device.h"))
 
 
 def log(msg):
@@ -67,8 +68,12 @@ META_BYTES = {"f32": 4, "f16": 2}
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the decode kernel's source files (the kernels and their shared device header)."""
+    hsh = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()[:16]
 
 
 def stored_traffic():
@@ -325,6 +330,65 @@ def time_projections(copies: int = 3, reps: int = 8):
     return res
 
 
+def bytes_prefill(b: int, a: int, s: int, d: int, mb: int = 4) -> int:
+    """Algorithmic HBM bytes of kv_quantize_prefill_attend: q, k, v read once, out written
+    once (fp16 [b][s][a][d] each), plus the K and V planes of s slots (codes d/2 bytes,
+    min and scale (d/64) * mb bytes each, per (batch row, head, token))."""
+    rows = b * a * s
+    return 4 * rows * d * 2 + 2 * rows * (d // 2 + 2 * (d // 64) * mb)
+
+
+def flops_prefill(b: int, a: int, s: int, d: int) -> int:
+    """Causal prefill attention: query i meets keys 0..i; 2d flops for q.k and 2d for p.v."""
+    return 4 * d * b * a * (s * (s + 1) // 2)
+
+
+def time_prefill(reps: int = 6):
+    """The prompt phase of one OPT-175B layer (b=144, a=96, d=128, prompt 512): the fused
+    kv_quantize_prefill_attend (causal attention on the matrix cores + the cache planes)
+    against kv_quantize_prefill alone; two caches in rotation; medians of per-launch HIP
+    events."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    w = W.OPT_175B
+    st = torch.cuda.current_stream()
+    q = W.prefill_q(w, 0, "cuda")
+    k, v = W.prefill_kv(w, 0, "cuda")
+    out = torch.empty_like(q)
+    caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda") for _ in range(2)]
+
+    def med(fn):
+        ms = []
+        for r in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn(caches[r % 2])
+            e1.record(st)
+            ms.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ms[2:])
+        return t[len(t) // 2], t
+    fused, all_ms = med(lambda c: kvq.kv_quantize_prefill_attend(c, q, k, v, out=out))
+    quant, _ = med(lambda c: kvq.kv_quantize_prefill(c, k, v))
+    nb = bytes_prefill(w.b, w.a, w.s, w.d)
+    fl = flops_prefill(w.b, w.a, w.s, w.d)
+    gbs = nb / fused / 1e6
+    tfl = fl / fused / 1e9
+    return {"workload": f"OPT-175B layer prompt: b={w.b} a={w.a} d={w.d} prompt {w.s}, causal, binary32 min/scale",
+            "kernel": "k_prefill<128,f32> (kv_quantize_prefill_attend)",
+            "ms_per_call_median": round(fused, 4), "ms_per_call_min": round(all_ms[0], 4),
+            "algorithmic_bytes": nb, "flops": fl,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "hbm_floor_ms": round(nb / HBM_PEAK_GBS / 1e6, 4),
+                         "mfma_floor_ms": round(fl / MFMA_F16_PEAK_TFLOPS / 1e9, 4)},
+            "tflops": round(tfl, 1), "frac_of_mfma_f16_peak": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
+            "quantise_only_ms_median": round(quant, 4),
+            "prompt_tokens_per_s": round(w.b * w.s / (fused / 1e3), 1)}
+
+
 def time_host_attention(reps: int = 5):
     """Decode attention delegated to the CPU (decode_attention_q4_host) on one OPT-6.7B layer
     (b=32, a=32, d=128, context 544) with the int4 cache in host memory, on the host's cores,
@@ -487,6 +551,7 @@ def main():
     ap.add_argument("--no-meta16", action="store_true", help="skip the binary16-metadata leg")
     ap.add_argument("--no-proj", action="store_true", help="skip the int4-weight projection leg")
     ap.add_argument("--no-host", action="store_true", help="skip the CPU-delegated attention leg")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the fused prefill attention leg")
     ap.add_argument("--meta", choices=("f32", "f16"), default="f32",
                     help="min/scale plane type of the timed stack (default binary32)")
     ap.add_argument("--fused", action="store_true",
@@ -572,6 +637,10 @@ def main():
     if not args.no_proj:
         log("[bench] int4-weight projection leg")
         res["projections_w4"] = time_projections()
+        torch.cuda.empty_cache()
+    if not args.no_prefill:
+        log("[bench] fused prefill attention leg")
+        res["prefill_attention"] = time_prefill()
         torch.cuda.empty_cache()
     if not args.no_host:
         log("[bench] CPU-delegated attention leg")
