@@ -180,6 +180,9 @@ def test_prefill_attend_validation(L):
     assert f(ctypes.byref(c), FAKE, FAKE, FAKE, 21, FAKE, st) == KVQ_ERANGE
     bad = cache(dims(h=96 * 3))  # head_dim 3 is not a multiple of 64
     assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, 4, FAKE, st) != KVQ_OK
+    # one batch row of a 90,000-token prompt at h = 12288 exceeds 31-bit byte offsets
+    long = cache(dims(b=1, a=96, h=12288, s=90000, n=0))
+    assert f(ctypes.byref(long), FAKE, FAKE, FAKE, 90000, FAKE, st) == KVQ_EUNSUPPORTED
 
 
 def test_strerror(L):

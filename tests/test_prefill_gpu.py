@@ -106,6 +106,36 @@ def test_prefill_deterministic():
         assert torch.equal(t1.view(torch.uint8), t2.view(torch.uint8))
 
 
+@pytest.mark.timeout(600)
+def test_prefill_batch_split_across_launches():
+    """Long prompts split the batch into launches whose tensors stay below 2 GiB (here
+    b=48, a=96, d=128, s=2048: 42 batch rows per launch).  Sampled pairs from both
+    launches, including the first and last rows of each: planes bit-exact, attention
+    within the bar."""
+    require_gpu()
+    b, a, d, s_len = 48, 96, 128, 2048
+    log(f"[prefill split] b={b} a={a} d={d} s={s_len}")
+    q = W.random_fp16((b, s_len, a, d), 7400, DEV)
+    k = W.random_fp16((b, s_len, a, d), 7401, DEV)
+    v = W.random_fp16((b, s_len, a, d), 7402, DEV)
+    cache = kvq.QuantKVCache(b, a, a * d, s_len, 0, device=DEV, fill=0xFF)
+    out = kvq.kv_quantize_prefill_attend(cache, q, k, v)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (41, 95), (42, 0), (42, 17), (47, 95), (20, 50)]
+    hq = {p: q[p[0], :, p[1]].cpu().numpy() for p in pairs}
+    hk = {p: k[p[0], :, p[1]].cpu().numpy() for p in pairs}
+    hv = {p: v[p[0], :, p[1]].cpu().numpy() for p in pairs}
+    hc = HostCache(b, a, d, s_len)
+    for bi, ai in pairs:
+        hc.kc[bi, ai], hc.kmin[bi, ai], hc.ksc[bi, ai] = QUANTIZE["f32"](hk[(bi, ai)].view(np.uint16))
+        hc.vc[bi, ai], hc.vmin[bi, ai], hc.vsc[bi, ai] = QUANTIZE["f32"](hv[(bi, ai)].view(np.uint16))
+    _check_prefill_pairs(cache, hc, s_len, pairs, "prefill split")
+    with _pool() as ex:
+        ref = np.stack(list(ex.map(lambda p: oracle.prefill_attend(hq[p], hk[p], hv[p]), pairs)))
+    err = assert_close(_gpu_pairs(out, pairs), ref, "prefill split attention")
+    log(f"[prefill split] {len(pairs)} pairs ok, max abs err {err:.2e}")
+
+
 def _layer_sampled(w: W.Workload, meta: str, n_pairs: int, seed: int):
     require_gpu()
     log(f"[{w.name} prefill] b={w.b} a={w.a} d={w.d} s={w.s} meta={meta}")
