@@ -61,6 +61,21 @@ def test_prefill_small_full(d, s_len):
     log(f"prefill d={d} s={s_len}: max abs err {err:.2e}")
 
 
+@pytest.mark.parametrize("d,s_len", [(64, 129), (128, 65), (256, 300)])
+def test_prefill_small_full_m16(d, s_len):
+    """Binary16 min/scale planes: every plane bit-exact with the oracle's binary16 codec and
+    every output within the bar, at each head_dim."""
+    require_gpu()
+    b, a = 2, 3
+    q, k, v, cache, out = _run_small(b, a, d, s_len, s_len + 3, 7500 + d + s_len, meta="f16")
+    hc = HostCache(b, a, d, s_len + 3, "f16")
+    hc.prefill(f16_np(k), f16_np(v))
+    _check_prefill_full(cache, hc, s_len, f"prefill m16 d={d} s={s_len}")
+    pairs = [(bi, ai) for bi in range(b) for ai in range(a)]
+    ref = _oracle_rows(f16_np(q), f16_np(k), f16_np(v), pairs)
+    assert_close(_gpu_pairs(out, pairs), ref, f"prefill m16 attention d={d} s={s_len}")
+
+
 @pytest.mark.parametrize("meta", ["f32", "f16"])
 def test_prefill_planes_equal_separate_quantiser_and_tail_untouched(meta):
     """The fused launch writes the same bytes as kv_quantize_prefill, and nothing past the
