@@ -96,7 +96,13 @@ int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
         s = num_splits;
     } else {
         const int64_t groups = (pairs + kPairsPerGroup - 1) / kPairsPerGroup;
-        const int cap = (int)std::max<int64_t>(1, std::min<int64_t>(ctx / (2 * kSplitAlign), kMaxAutoSplits));
+        // With at least four workgroups per CU there is parallelism enough and the
+        // last round is a small part of the launch: a split would only add the
+        // partials' traffic and the reduce pass (measured on MI355X: 2 splits at
+        // 6,528 workgroups ran 25% slower than one).
+        const int cap = groups >= 4 * kCUs
+                            ? 1
+                            : (int)std::max<int64_t>(1, std::min<int64_t>(ctx / (2 * kSplitAlign), kMaxAutoSplits));
         s = 1;
         double best = -1.0;
         for (int c = 1; c <= cap; ++c) {

@@ -185,6 +185,16 @@ def test_prefill_attend_validation(L):
     assert f(ctypes.byref(long), FAKE, FAKE, FAKE, 90000, FAKE, st) == KVQ_EUNSUPPORTED
 
 
+def test_auto_splits_only_when_the_pairs_cannot_fill_the_card(L):
+    """Automatic split choice (read through the workspace size, 0 when one split): many
+    pairs -> one split whatever the round count; few pairs over a long context -> splits."""
+    for b in (128, 136, 144, 171, 256):
+        d = dims(b=b, a=96, h=12288, s=512, n=32)
+        assert L.kvq_workspace_bytes(ctypes.byref(d), 544, 0, 0) == 0, b
+    long = dims(b=1, a=96, h=12288, s=65536, n=0)
+    assert L.kvq_workspace_bytes(ctypes.byref(long), 65536, 0, 0) > 0
+
+
 def test_strerror(L):
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert len(L.kvq_strerror(s)) > 0
