@@ -875,102 +875,249 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
 }
 
 // Selection for contexts up to 2048 tokens: one wave per (batch row, head),
-// four pairs per workgroup, no workgroup barrier.  Lane l holds the keys of
-// tokens l, l+64, l+128, ... in registers.  The k_top-th largest key is found
-// bit by bit from the top (32 steps; each step counts the keys in the upper
-// half of the current bucket with one ballot per register); the kept tokens
-// are then compacted in ascending order with ballots and mbcnt, ties to the
-// smaller index.  Each kept token's index and softmax weight go to LDS, and
-// the wave gathers the kept V rows.
-template <int D, typename Meta>
-__global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict__ vc,
-                                                       const Meta *__restrict__ vmin,
-                                                       const Meta *__restrict__ vsc,
-                                                       const float *__restrict__ scores, uint4 *__restrict__ out,
-                                                       int32_t *__restrict__ sel_out, int pairs, int S, int T,
-                                                       int k_top, int region_bytes)
+// four pairs per workgroup, no workgroup barrier.  The scores are loaded
+// coalesced and transposed through LDS so that lane l holds the keys of the
+// KPL consecutive tokens KPL*l .. KPL*l+KPL-1 in registers (KPL = 16 for
+// contexts up to 1024, else 32); ascending token order is then lane-major
+// order.
+//
+// The threshold (the k_top-th largest key) is found in two levels.  A
+// 256-bin histogram of the scores over [min, max] (LDS atomics; the bin is a
+// monotone function of the score, so every key in a higher bin is larger)
+// gives the bin b* that holds the k_top-th largest key and the number A of
+// keys in higher bins.  The keys of bin b* (at most 64, one per lane) are then
+// searched bit by bit for their (k_top - A)-th largest: the largest v with at
+// least k_top - A of them >= v.  When bin b* holds more than 64 keys (scores
+// crowded into a narrow range), the same bit-by-bit search runs over all the
+// keys instead.  A search step that finds exactly the wanted count has found
+// the selection itself and stops early.
+//
+// One prefix sum over the lanes then places each lane's kept tokens (ties to
+// the smaller index); their indices and softmax weights go to LDS, and the
+// wave gathers the kept V rows, all of a round's loads in flight together.
+// v <- sum of v over the lanes congruent to this one modulo STEP (STEP a power
+// of two, 2..32): row rotations by STEP, 2 STEP, .. 8 inside each 16-lane row
+// (DPP, no LDS), then exchanges across rows.
+template <int STEP>
+__device__ __forceinline__ void lane_group_sum(float &v)
+{
+#pragma unroll
+    for (int off = STEP; off < 16; off <<= 1)
+        v += off == 1 ? dpp<0x121>(v) : off == 2 ? dpp<0x122>(v) : off == 4 ? dpp<0x124>(v) : dpp<0x128>(v);
+#pragma unroll
+    for (int off = STEP < 16 ? 16 : STEP; off < 64; off <<= 1)
+        v += __shfl_xor(v, off);
+}
+
+// Inverse of order_key.
+__device__ __forceinline__ float tr_key_to_z(uint32_t kb)
+{
+    return __builtin_bit_cast(float, (kb & 0x80000000u) ? (kb ^ 0x80000000u) : ~kb);
+}
+
+// 0 <= (z - zmin) * bscale <= 256 (1 + 2^-22) for zmin <= z <= zmax.
+__device__ __forceinline__ int key_bin(uint32_t kb, float zmin, float bscale)
+{
+    return (int)fminf((tr_key_to_z(kb) - zmin) * bscale, 255.0f);
+}
+
+__device__ __forceinline__ int wave_sum_small(int c) // 0 <= c < 64 in every lane
+{
+    int s = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit)
+        s += __popcll(__ballot((c >> bit) & 1)) << bit;
+    return s;
+}
+
+// The largest v such that at least `want` of the wave's keys (N per lane) are
+// >= v: the want-th largest key.  With EARLY, a candidate that has exactly
+// `want` keys >= it ends the search, returning that candidate minus one (the
+// keys > the result are then exactly the wanted ones); this is only valid
+// when the keys searched are all the keys.  Keys of 0 never count: every
+// candidate is >= 1.
+template <int N, bool EARLY>
+__device__ __forceinline__ uint32_t greedy_threshold(const uint32_t (&key)[N], int want)
+{
+    uint32_t thr = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = thr | (1u << b);
+        int cnt;
+        if constexpr (N == 1) {
+            cnt = __popcll(__ballot(key[0] >= cand));
+        } else {
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                c += key[i] >= cand;
+            cnt = wave_sum_small(c);
+        }
+        if (cnt >= want) {
+            thr = cand;
+            if (EARLY && cnt == want)
+                return cand - 1u;
+        }
+    }
+    return thr;
+}
+
+template <int D, int KPL, int UG, typename Meta>
+__global__ __launch_bounds__(256, 3) void k_topk_select_w(const uint8_t *__restrict__ vc,
+                                                          const Meta *__restrict__ vmin,
+                                                          const Meta *__restrict__ vsc,
+                                                          const float *__restrict__ scores, uint4 *__restrict__ out,
+                                                          int32_t *__restrict__ sel_out, int pairs, int S, int T,
+                                                          int k_top, int region_bytes)
 {
     constexpr int LPT = D / 32;
     constexpr int TPW = 64 / LPT;
     constexpr int G = D / 64;
-    constexpr int KPL = 32; // keys per lane: T <= 64 * KPL
-    constexpr int UG = 4;   // gathered rows per lane in flight
+    // KPL keys per lane (T <= 64 * KPL); UG gathered rows per lane in flight,
+    // TPW * UG rows per round
+    constexpr int ROW = KPL + 1; // LDS row of one lane's keys, padded against bank conflicts
     extern __shared__ __attribute__((aligned(16))) float sm_dyn[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
-    if (pair >= pairs)
+    const int pair_v = blockIdx.x * 4 + wave;
+    if (pair_v >= pairs)
         return;
+    const int64_t pair = __builtin_amdgcn_readfirstlane(pair_v);
     char *region = reinterpret_cast<char *>(sm_dyn) + (size_t)wave * region_bytes;
-    float *__restrict__ sel_p = reinterpret_cast<float *>(region);                      // [k_top] weights
-    uint16_t *__restrict__ sel_t = reinterpret_cast<uint16_t *>(region + 4 * (size_t)k_top); // [k_top] tokens
+    // Region use, in turn: the transposed scores [64][ROW]; the histogram [256]
+    // (+64 discard counters) and bin b*'s keys [64] (+64 discard slots); the
+    // kept tokens' scores relative to the maximum and their indices [k_top]
+    // (+64 discard slots each).
+    float *__restrict__ tr = reinterpret_cast<float *>(region);
+    int *__restrict__ hist = reinterpret_cast<int *>(region);
+    uint32_t *__restrict__ cand = reinterpret_cast<uint32_t *>(region + 4 * (256 + 64));
+    float *__restrict__ sel_z = reinterpret_cast<float *>(region);
+    uint16_t *__restrict__ sel_t = reinterpret_cast<uint16_t *>(region + 4 * (size_t)(k_top + 64));
 
-    // (1) keys in registers (0 for t >= T: below every finite score's key).
-    // Every load is issued unconditionally (clamped index) and its value used
-    // without a branch, so all KPL loads are in flight together.
+    // (1) scores: token lane + 64j is loaded by lane `lane` (coalesced; every
+    // load issued unconditionally with a clamped index) and stored at row
+    // t / KPL, column t % KPL; lane l then reads row l.  Keys of t >= T are 0,
+    // below every finite score's key.
     const float *__restrict__ srow = scores + pair * T;
-    uint32_t key[KPL];
-#pragma unroll
-    for (int j = 0; j < KPL; ++j)
-        key[j] = __builtin_bit_cast(uint32_t, ld_stream(srow + min(lane + 64 * j, T - 1)));
-    float zmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-        const float z = __builtin_bit_cast(float, key[j]);
-        const uint32_t keep = (lane + 64 * j < T) ? 0xFFFFFFFFu : 0u;
-        zmax = fmaxf(zmax, __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, z) & keep) |
-                                                         (0xFF800000u & ~keep))); // -inf when masked
-        key[j] = order_key(z) & keep;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        zmax = fmaxf(zmax, __shfl_xor(zmax, off));
-
-    // (2) exact key of the k_top-th largest score
-    uint32_t prefix = 0;
-    int remaining = k_top;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = prefix | (1u << b);
-        const uint32_t hmask = ~((1u << b) - 1u);
-        int cnt = 0;
+    {
+        float zl[KPL];
 #pragma unroll
         for (int j = 0; j < KPL; ++j)
-            cnt += __popcll(__ballot((key[j] & hmask) == cand));
-        if (cnt >= remaining)
-            prefix = cand;
-        else
-            remaining -= cnt;
-    }
-    const uint32_t thr = prefix;
-
-    // (3) compaction in ascending token order; softmax weights of the kept keys
-    int base = 0, eq_seen = 0;
+            zl[j] = ld_stream(at_byte(srow, 4u * (uint32_t)min(lane + 64 * j, T - 1)));
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-        const bool eq = key[j] == thr;
-        const uint64_t eqm = __ballot(eq);
-        const int eq_rank = eq_seen + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqm >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)eqm, 0u));
-        const bool keep = key[j] > thr || (eq && eq_rank < remaining);
-        const uint64_t km = __ballot(keep);
-        if (keep) {
-            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
-            const uint32_t kb = key[j];
-            const float z = __builtin_bit_cast(float, (kb & 0x80000000u) ? (kb ^ 0x80000000u) : ~kb);
-            sel_p[pos] = exp2_fast(z - zmax);
-            sel_t[pos] = (uint16_t)(lane + 64 * j);
+        for (int j = 0; j < KPL; ++j)
+            tr[(j * (64 / KPL) + lane / KPL) * ROW + lane % KPL] = zl[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint32_t key[KPL];
+    float zmax = -INFINITY, zmin = INFINITY;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const float z = tr[lane * ROW + i];
+        const bool valid = KPL * lane + i < T;
+        zmax = fmaxf(zmax, valid ? z : -INFINITY);
+        zmin = fminf(zmin, valid ? z : INFINITY);
+        key[i] = valid ? order_key(z) : 0u;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        zmax = fmaxf(zmax, __shfl_xor(zmax, off));
+        zmin = fminf(zmin, __shfl_xor(zmin, off));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier(); // the reads of tr are done before hist reuses the region
+
+    // (2) threshold.  Bins: bin(z) = (int)min((z - zmin) * bscale, 255), monotone
+    // in z; a zero (or unrepresentable) range gives one bin and the full search.
+    // No branch: the keys of t >= T count in their lane's own discard counter.
+    const float zrange = zmax - zmin;
+    const float bscale = (zrange > 1e-30f && zrange <= 3e38f) ? 256.0f / zrange : 0.0f;
+    reinterpret_cast<int4 *>(hist)[lane] = make_int4(0, 0, 0, 0); // the discard counters are never read
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint32_t bins[KPL / 4]; // four 8-bit bins per register
+#pragma unroll
+    for (int r = 0; r < KPL / 4; ++r)
+        bins[r] = 0u;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int bi = key_bin(key[i], zmin, bscale);
+        bins[i / 4] |= (uint32_t)bi << (8 * (i % 4));
+        atomicAdd(&hist[key[i] != 0u ? bi : 256 + lane], 1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // counts of the keys in bins >= b, from the top: lane l holds bins 4l..4l+3
+    const int4 h4 = reinterpret_cast<const int4 *>(hist)[lane];
+    const int lsum = h4.x + h4.y + h4.z + h4.w;
+    const int lincl = wave_incl_scan(lsum, lane);
+    const int above_lane = __shfl(lincl, 63) - lincl; // keys in bins of higher lanes
+    const int ge3 = above_lane + h4.w, ge2 = ge3 + h4.z, ge1 = ge2 + h4.y, ge0 = ge1 + h4.x;
+    // bin b* holds the k_top-th largest: ge(b*+1) < k_top <= ge(b*)
+    int my_bin = -1, my_above = 0, my_n = 0;
+    if (above_lane < k_top && k_top <= ge3) { my_bin = 4 * lane + 3; my_above = above_lane; my_n = h4.w; }
+    if (ge3 < k_top && k_top <= ge2) { my_bin = 4 * lane + 2; my_above = ge3; my_n = h4.z; }
+    if (ge2 < k_top && k_top <= ge1) { my_bin = 4 * lane + 1; my_above = ge2; my_n = h4.y; }
+    if (ge1 < k_top && k_top <= ge0) { my_bin = 4 * lane; my_above = ge1; my_n = h4.x; }
+    const uint64_t owner = __ballot(my_bin >= 0);
+    const int src = (int)__builtin_ctzll(owner);
+    const int bstar = __shfl(my_bin, src), n_star = __shfl(my_n, src), a_star = __shfl(my_above, src);
+    uint32_t thr;
+    if (n_star <= 64) {
+        // bin b*'s keys, one per lane; the others go to discard slots
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+            c += (key[i] != 0u) & ((int)((bins[i / 4] >> (8 * (i % 4))) & 255u) == bstar);
+        int p = wave_incl_scan(c, lane) - c;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const bool in = (key[i] != 0u) & ((int)((bins[i / 4] >> (8 * (i % 4))) & 255u) == bstar);
+            cand[in ? p : 64 + lane] = key[i];
+            p += in;
         }
-        base += __popcll(km);
-        eq_seen += __popcll(eqm);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t ck[1] = {lane < n_star ? cand[lane] : 0u};
+        thr = greedy_threshold<1, false>(ck, k_top - a_star); // an exact key: lower bins stay below
+    } else {
+        thr = greedy_threshold<KPL, true>(key, k_top);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier(); // hist and cand are read before sel_z/sel_t reuse the region
+
+    // (3) compaction in ascending token order: one prefix sum over the lanes of
+    // (keys > thr) and (keys == thr); the first `remaining` keys equal to thr
+    // (smallest indices) are kept.  Dropped keys write to discard slots.
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        gt += key[i] > thr;
+        eq += key[i] == thr;
+    }
+    const int packed = gt | (eq << 16);
+    const int incl = wave_incl_scan(packed, lane);
+    const int tot = __shfl(incl, 63);
+    const int excl = incl - packed;
+    const int remaining = k_top - (tot & 0xFFFF);
+    int eq_rank = excl >> 16;
+    int pos = (excl & 0xFFFF) + min(eq_rank, remaining);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const uint32_t kb = key[i];
+        const bool is_eq = kb == thr;
+        const bool keep = (kb > thr) | (is_eq & (eq_rank < remaining));
+        eq_rank += is_eq;
+        const int slot = keep ? pos : k_top + lane;
+        sel_z[slot] = tr_key_to_z(kb) - zmax;
+        sel_t[slot] = (uint16_t)(KPL * lane + i);
+        pos += keep;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
-    // (4) P.V over the kept rows
-    const int part = lane % LPT, lt = lane / LPT, g = part >> 1;
-    const uint8_t *__restrict__ vb = vc + pair * S * (D / 2) + part * 16;
-    const Meta *__restrict__ vmb = vmin + pair * S * G + g;
-    const Meta *__restrict__ vsb = vsc + pair * S * G + g;
+    // (4) P.V over the kept rows, UG rows per lane in flight
+    const int part = lane % LPT, lt = lane / LPT;
+    const CacheRow<Meta> cr = cache_row<D, Meta>(nullptr, vc, nullptr, nullptr, vmin, vsc, (int)pair, S, part);
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
 #pragma unroll
@@ -982,13 +1129,12 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
 #pragma unroll
         for (int u = 0; u < UG; ++u) {
             const int j = j0 + u * TPW + lt;
-            const bool valid = j < k_top;
-            const int jc = valid ? j : k_top - 1;
-            const int64_t t = sel_t[jc];
-            vx[u] = ld_stream16(vb + t * (D / 2));
-            vm[u] = ld_meta(vmb + t * G);
-            vs[u] = ld_meta(vsb + t * G);
-            p[u] = valid ? sel_p[jc] : 0.0f;
+            const int jc = min(j, k_top - 1);
+            const uint32_t t = sel_t[jc];
+            vx[u] = ld_stream16(cr.vb + (t * (D / 2) + cr.code_off));
+            vm[u] = ld_meta(at_byte(cr.vmb, t * (uint32_t)(sizeof(Meta) * G) + cr.meta_off));
+            vs[u] = ld_meta(at_byte(cr.vsb, t * (uint32_t)(sizeof(Meta) * G) + cr.meta_off));
+            p[u] = j < k_top ? exp2_fast(sel_z[jc]) : 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < UG; ++u) {
@@ -1000,13 +1146,12 @@ __global__ __launch_bounds__(256) void k_topk_select_w(const uint8_t *__restrict
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         acc[i] += bsum;
+    // sum over the token lanes (lanes of equal `part`): rotations inside each
+    // 16-lane row (DPP), then across rows
+    lane_group_sum<LPT>(l);
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-        l += __shfl_xor(l, off);
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            acc[i] += __shfl_xor(acc[i], off);
-    }
+    for (int i = 0; i < 32; ++i)
+        lane_group_sum<LPT>(acc[i]);
     if (lt == 0) {
         const float inv = 1.0f / l;
         uint32_t h[16];
@@ -1107,16 +1252,26 @@ int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_t
     const int chunk = std::min(128, (T + TPW - 1) / TPW * TPW);
     const int n_chunks = (T + chunk - 1) / chunk;
     const int64_t waves = (int64_t)pairs * n_chunks;
-    hipLaunchKernelGGL((k_topk_scores<D, 2, Meta>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, c.k_codes,
+    hipLaunchKernelGGL((k_topk_scores<D, 4, Meta>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, c.k_codes,
                        meta<Meta>(c.k_min), meta<Meta>(c.k_scale), static_cast<const uint4 *>(q), ws, pairs, c.S, T, chunk, n_chunks, c2);
     int e = (int)hipGetLastError();
     if (e != 0)
         return e;
     if (T <= kTopkWaveMaxCtx) {
-        const int region = (int)(((size_t)k_top * (sizeof(float) + sizeof(uint16_t)) + 15) / 16 * 16);
-        hipLaunchKernelGGL((k_topk_select_w<D, Meta>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), (size_t)4 * region,
-                           st, c.v_codes, meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<uint4 *>(out), sel, pairs, c.S, T, k_top,
-                           region);
+        // per wave: the transposed scores (64 rows of KPL + 1 floats), later the
+        // kept tokens' scores and indices with 64 discard slots each
+        const int kpl = T <= 1024 ? 16 : 32;
+        const size_t sel_bytes = (size_t)(k_top + 64) * (sizeof(float) + sizeof(uint16_t));
+        const int region = (int)((std::max(sel_bytes, (size_t)64 * (kpl + 1) * sizeof(float)) + 15) / 16 * 16);
+        const dim3 grid((unsigned)((pairs + 3) / 4));
+        if (kpl == 16)
+            hipLaunchKernelGGL((k_topk_select_w<D, 16, 4, Meta>), grid, dim3(256), (size_t)4 * region, st, c.v_codes,
+                               meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<uint4 *>(out), sel, pairs,
+                               c.S, T, k_top, region);
+        else
+            hipLaunchKernelGGL((k_topk_select_w<D, 32, 13, Meta>), grid, dim3(256), (size_t)4 * region, st, c.v_codes,
+                               meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<uint4 *>(out), sel, pairs,
+                               c.S, T, k_top, region);
     } else {
         const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
         hipLaunchKernelGGL((k_topk_select<D, Meta>), dim3((unsigned)pairs), dim3(256), lds, st, c.v_codes,

@@ -374,6 +374,66 @@ def test_topk_exact_ties_pick_smallest_indices(T):
         assert_close(_gpu_rows(out, pairs), ref, f"ties T={T}")
 
 
+def _topk_keys(case, b, a, d, T, seed):
+    """K rows for the exact-selection test: score distributions that put the k-th score in
+    a crowded range, among exact ties, or far from the rest."""
+    g = np.random.default_rng(seed)
+    if case == "normal":
+        k = g.standard_normal((b, T, a, d))
+    elif case == "outlier":          # one key 30x the rest: nearly every score in one bin
+        k = 0.05 * g.standard_normal((b, T, a, d))
+        k[:, T // 3] *= 600.0
+    elif case == "five_rows":        # five distinct rows: every score has many exact ties
+        rows = g.standard_normal((5, a, d))
+        k = rows[g.integers(0, 5, size=(b, T))]
+    elif case == "tie_block":        # 48 copies of one row among random rows
+        k = g.standard_normal((b, T, a, d))
+        pos = g.choice(T, size=min(48, T), replace=False)
+        k[:, pos] = g.standard_normal((1, 1, a, d))
+    else:                            # "wide": large scores of both signs
+        k = 300.0 * g.standard_normal((b, T, a, d))
+    return torch.from_numpy(k.astype(np.float16)).to(DEV)
+
+
+@pytest.mark.parametrize("T", [37, 300, 1024, 1025, 2048, 4000])
+@pytest.mark.parametrize("case", ["normal", "outlier", "five_rows", "tie_block", "wide"])
+def test_topk_selection_exact_on_own_scores(case, T):
+    """Exact check of the selection logic, free of any tolerance: the call leaves every
+    token's score in the workspace (fp32 [b][a][T]); the kept set must be exactly the k
+    largest of those scores, ties to the smaller index, in ascending order.  The k-th score
+    falls in a crowded range, among exact ties (also inside a 48-key tie block), or next to
+    an outlier; k runs from 1 to T.  T <= 1024 uses the wave select with 16 keys per lane, up to 2048 with 32, and 4000
+    the workgroup select."""
+    require_gpu()
+    b, a, d = 1, 3, 128
+    seed = 4100 + T + ["normal", "outlier", "five_rows", "tie_block", "wide"].index(case)
+    k = _topk_keys(case, b, a, d, T, seed)
+    v = W.random_fp16((b, T, a, d), seed + 1, DEV)
+    q = W.random_fp16((b, 1, a, d), seed + 2, DEV)
+    cache = kvq.QuantKVCache(b, a, a * d, T, 0, device=DEV, fill=0xFF)
+    kvq.kv_quantize_prefill(cache, k, v)
+    ws = torch.empty(kvq.kvq_workspace_bytes(cache, T, 0, T) // 4, dtype=torch.float32, device=DEV)
+    kvq.decode_attention_q4_topk(cache, q, T, 1, ws=ws)
+    torch.cuda.synchronize()
+    scores = ws[: b * a * T].view(b * a, T).cpu().numpy().copy()
+    k_set = {1, max(1, math.ceil(0.1 * T)), T // 2 or 1, max(1, T - 1), T}
+    if case == "tie_block":          # put the boundary inside the tie block of every pair
+        for p in range(b * a):
+            vals, counts = np.unique(scores[p], return_counts=True)
+            tie = vals[np.argmax(counts)]
+            k_set.add(int(np.sum(scores[p] > tie)) + int(counts.max()) // 2)
+    for k_top in sorted(k_set):
+        _, sel = kvq.decode_attention_q4_topk(cache, q, T, k_top, ws=ws)
+        torch.cuda.synchronize()
+        again = ws[: b * a * T].view(b * a, T).cpu().numpy()
+        assert np.array_equal(again.view(np.uint32), scores.view(np.uint32)), "scores changed between calls"
+        got = sel.view(b * a, k_top).cpu().numpy()
+        for p in range(b * a):
+            order = np.lexsort((np.arange(T), -scores[p]))
+            want = np.sort(order[:k_top])
+            assert np.array_equal(got[p], want), f"{case} T={T} k={k_top} pair {p}: selection differs"
+
+
 def test_topk_deterministic():
     """Run twice -> bit-identical outputs and selections."""
     require_gpu()
