@@ -184,7 +184,9 @@ int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k
  * k_top = ceil(0.1 * ctx_len).  sel_idx (device int32 [b][a][k_top], may be
  * NULL) receives the kept token indices in ascending order.  ws: device
  * workspace of ws_bytes >= kvq_workspace_bytes(dims, ctx_len, 0, k_top),
- * 16-byte aligned; it holds the scores between the two kernels. */
+ * 16-byte aligned; it holds the scores between the two kernels, and when the
+ * stream work is done it still holds them: fp32 [b][a][ctx_len], in log2
+ * units (q . k * log2(e) / sqrt(d)), the values the selection ranked. */
 int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
                              void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream);
 
