@@ -371,6 +371,39 @@ __device__ __forceinline__ NewRow append_rows(const uint4 x, int64_t pair, int64
     return r;
 }
 
+// The value of v held by another lane: for OFF < 16 the lane OFF places
+// earlier in the same 16-lane row (DPP row rotation, no LDS), else lane ^ OFF.
+template <int OFF>
+__device__ __forceinline__ float lane_peer(float v)
+{
+    if constexpr (OFF < 16)
+        return dpp<0x120 + OFF>(v); // row_ror:OFF
+    else
+        return __shfl_xor(v, OFF);
+}
+
+// Online-softmax states (m, l, acc) merged over the lanes congruent modulo
+// OFF0: at each step a lane merges its state with lane_peer's.  The merge
+// (max, rescale, add) is associative and commutative, so after the steps
+// OFF0, 2 OFF0, .. 32 every lane holds the merge of its whole class.
+template <int OFF>
+__device__ __forceinline__ void merge_token_lanes(float &m, float &l, float (&acc)[32])
+{
+    if constexpr (OFF < 64) {
+        const float mo = lane_peer<OFF>(m);
+        const float lo = lane_peer<OFF>(l);
+        const float M = fmaxf(m, mo);
+        const float Mr = (M == -INFINITY) ? 0.0f : M;
+        const float a1 = exp2_fast(m - Mr), a2 = exp2_fast(mo - Mr);
+        l = l * a1 + lo * a2;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            acc[i] = acc[i] * a1 + lane_peer<OFF>(acc[i]) * a2;
+        m = M;
+        merge_token_lanes<OFF * 2>(m, l, acc);
+    }
+}
+
 // ===========================================================================
 // Dense decode attention.
 //
@@ -463,19 +496,7 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, Meta *
         acc[i] += bsum;
 
     // Merge the TPW token lanes that share `part`.
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-        const float mo = __shfl_xor(m, off);
-        const float lo = __shfl_xor(l, off);
-        const float M = fmaxf(m, mo);
-        const float Mr = (M == -INFINITY) ? 0.0f : M;
-        const float a1 = exp2_fast(m - Mr), a2 = exp2_fast(mo - Mr);
-        l = l * a1 + lo * a2;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            acc[i] = acc[i] * a1 + __shfl_xor(acc[i], off) * a2;
-        m = M;
-    }
+    merge_token_lanes<LPT>(m, l, acc);
 
     if constexpr (WPP == 1) {
         if (!pair_ok || lt != 0)
