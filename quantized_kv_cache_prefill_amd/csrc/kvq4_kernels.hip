@@ -83,13 +83,27 @@ struct QSlice {
     float qbias;
 };
 
-__device__ __forceinline__ QSlice load_q_slice(const uint4 *__restrict__ qrow)
+// The lane's 32 query elements as loaded (4 x 16 bytes).
+struct QRaw {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ QRaw load_q_raw(const uint4 *__restrict__ qrow)
+{
+    QRaw r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        r.v[w] = qrow[w];
+    return r;
+}
+
+__device__ __forceinline__ QSlice q_slice(const QRaw &r)
 {
     QSlice s;
     float even = 0.0f, odd = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const uint4 v = qrow[w]; // elements 8w..8w+7: x=(e0,e1) y=(e2,e3) z=(e4,e5) w=(e6,e7)
+        const uint4 v = r.v[w]; // elements 8w..8w+7: x=(e0,e1) y=(e2,e3) z=(e4,e5) w=(e6,e7)
         s.qp[4 * w + 0] = (v.x & 0xFFFFu) | (v.z << 16);
         s.qp[4 * w + 1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
         s.qp[4 * w + 2] = (v.y & 0xFFFFu) | (v.w << 16);
@@ -257,48 +271,78 @@ __device__ __forceinline__ CacheRow<Meta> cache_row(const uint8_t *kc, const uin
             vsc ? vsc + mb : nullptr, (uint32_t)part * 16u, (uint32_t)(part >> 1) * (uint32_t)sizeof(Meta)};
 }
 
-template <int D, int UU, bool NEWROW = false, typename Meta>
-__device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, const Magic mg,
-                                            float c2, float &m, float &l, float &bsum, float (&acc)[32],
-                                            const NewRow nr = NewRow{}, int t_new = -1)
+// The cache rows of one iteration: UU token rows per lane (rows tb, tb + TPW,
+// ...), each with its K and V code words and min/scale.  Rows at or past
+// t_end load row t_end - 1 (in bounds) and are flagged invalid.
+template <int UU>
+struct KVRows {
+    uint4 kx[UU], vx[UU];
+    float km[UU], ks[UU], vm[UU], vs[UU];
+    bool valid[UU];
+};
+
+// The K half (KV = false: K codes and min/scale, and the valid flags) or the
+// V half (KV = true) of load_kv_rows.
+template <int D, int UU, bool KV, typename Meta>
+__device__ __forceinline__ void load_rows_half(const CacheRow<Meta> &cr, int tb, int t_end, KVRows<UU> &r)
 {
     constexpr int LPT = D / 32;
     constexpr int TPW = 64 / LPT;
     constexpr int G = D / 64;
-    uint4 kx[UU], vx[UU];
-    float km[UU], ks[UU], vm[UU], vs[UU];
-    bool valid[UU];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
         const int t = tb + u * TPW;
-        valid[u] = t < t_end;
-        const uint32_t tcl = (uint32_t)(valid[u] ? t : t_end - 1);
+        const bool valid = t < t_end;
+        const uint32_t tcl = (uint32_t)(valid ? t : t_end - 1);
         const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (uint32_t)(sizeof(Meta) * G) + cr.meta_off;
-        kx[u] = ld_stream16(cr.kb + co);
-        vx[u] = ld_stream16(cr.vb + co);
-        km[u] = ld_meta(at_byte(cr.kmb, mo));
-        ks[u] = ld_meta(at_byte(cr.ksb, mo));
-        vm[u] = ld_meta(at_byte(cr.vmb, mo));
-        vs[u] = ld_meta(at_byte(cr.vsb, mo));
-        if constexpr (NEWROW) {
-            if (t == t_new) {
-                kx[u] = nr.kx;
-                vx[u] = nr.vx;
-                km[u] = nr.km;
-                ks[u] = nr.ks;
-                vm[u] = nr.vm;
-                vs[u] = nr.vs;
-            }
+        if constexpr (!KV) {
+            r.valid[u] = valid;
+            r.kx[u] = ld_stream16(cr.kb + co);
+            r.km[u] = ld_meta(at_byte(cr.kmb, mo));
+            r.ks[u] = ld_meta(at_byte(cr.ksb, mo));
+        } else {
+            r.vx[u] = ld_stream16(cr.vb + co);
+            r.vm[u] = ld_meta(at_byte(cr.vmb, mo));
+            r.vs[u] = ld_meta(at_byte(cr.vsb, mo));
         }
     }
+}
+
+template <int D, int UU, typename Meta>
+__device__ __forceinline__ void load_kv_rows(const CacheRow<Meta> &cr, int tb, int t_end, KVRows<UU> &r)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int G = D / 64;
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const int t = tb + u * TPW;
+        r.valid[u] = t < t_end;
+        const uint32_t tcl = (uint32_t)(r.valid[u] ? t : t_end - 1);
+        const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (uint32_t)(sizeof(Meta) * G) + cr.meta_off;
+        r.kx[u] = ld_stream16(cr.kb + co);
+        r.vx[u] = ld_stream16(cr.vb + co);
+        r.km[u] = ld_meta(at_byte(cr.kmb, mo));
+        r.ks[u] = ld_meta(at_byte(cr.ksb, mo));
+        r.vm[u] = ld_meta(at_byte(cr.vmb, mo));
+        r.vs[u] = ld_meta(at_byte(cr.vsb, mo));
+    }
+}
+
+// Scores of the rows, online-softmax update of (m, l, bsum, acc).
+template <int D, int UU>
+__device__ __forceinline__ void attend_kv_rows(const KVRows<UU> &r, const QSlice &qs, const Magic mg, float c2,
+                                               float &m, float &l, float &bsum, float (&acc)[32])
+{
+    constexpr int LPT = D / 32;
     float z[UU];
     float mx = m;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-        const float dq = dot_keys(qs, kx[u], mg) - qs.qbias;
-        float sp = __builtin_fmaf(ks[u], dq, km[u] * qs.qsum);
+        const float dq = dot_keys(qs, r.kx[u], mg) - qs.qbias;
+        float sp = __builtin_fmaf(r.ks[u], dq, r.km[u] * qs.qsum);
         sp = token_sum<LPT>(sp);
-        z[u] = valid[u] ? sp * c2 : -INFINITY;
+        z[u] = r.valid[u] ? sp * c2 : -INFINITY;
         mx = fmaxf(mx, z[u]);
     }
     const float mref = (mx == -INFINITY) ? 0.0f : mx;
@@ -315,9 +359,33 @@ __device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, in
     for (int u = 0; u < UU; ++u) {
         const float p = exp2_fast(z[u] - mref);
         l += p;
-        bsum = __builtin_fmaf(p, vm[u], bsum);
-        axpy_values(acc, p * (vs[u] * kTwo24), vx[u]);
+        bsum = __builtin_fmaf(p, r.vm[u], bsum);
+        axpy_values(acc, p * (r.vs[u] * kTwo24), r.vx[u]);
     }
+}
+
+template <int D, int UU, bool NEWROW = false, typename Meta>
+__device__ __forceinline__ void decode_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, const Magic mg,
+                                            float c2, float &m, float &l, float &bsum, float (&acc)[32],
+                                            const NewRow nr = NewRow{}, int t_new = -1)
+{
+    constexpr int TPW = 64 / (D / 32);
+    KVRows<UU> r;
+    load_kv_rows<D, UU>(cr, tb, t_end, r);
+    if constexpr (NEWROW) {
+#pragma unroll
+        for (int u = 0; u < UU; ++u) {
+            if (tb + u * TPW == t_new) {
+                r.kx[u] = nr.kx;
+                r.vx[u] = nr.vx;
+                r.km[u] = nr.km;
+                r.ks[u] = nr.ks;
+                r.vm[u] = nr.vm;
+                r.vs[u] = nr.vs;
+            }
+        }
+    }
+    attend_kv_rows<D, UU>(r, qs, mg, c2, m, l, bsum, acc);
 }
 
 // Fused append.  The wave whose range ends at the new slot quantises the new
@@ -458,13 +526,26 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, Meta *
     // Fused append (k_new != null): the wave whose range ends at the new slot
     // T-1 quantises and stores it, and uses the register copy in its last row.
     const bool tail_wave = k_new != nullptr && pair_ok && t_end == T && w_begin < t_end; // wave-uniform
+    // The tail wave's rows: all but the last TPW-row chunk as usual, then that
+    // chunk with the new row substituted for slot T-1.
+    const int last = w_begin + (t_end - 1 - w_begin) / TPW * TPW;
+    const int nf = tail_wave ? (last - w_begin) / TPI : n_full; // full iterations
+    const CacheRow<Meta> cr = cache_row<D, Meta>(kc, vc, kmin, ksc, vmin, vsc, (int)pc, S, part);
     uint4 new_raw = make_uint4(0, 0, 0, 0);
     if (tail_wave)
         new_raw = load_new_row<D>(k_new, v_new, pc, lane);
-    const QSlice qs = load_q_slice(q + pc * (D / 8) + part * 4);
+    // The first iteration's K rows are requested right behind the query, so
+    // the wave's first memory round trip carries both; its V rows follow the
+    // query's processing and arrive during the scores.
+    const QRaw qraw = load_q_raw(q + pc * (D / 8) + part * 4);
+    int tb = w_begin + lt;
+    KVRows<U> first;
+    if (nf > 0)
+        load_rows_half<D, U, false>(cr, tb, t_end, first);
+    const QSlice qs = q_slice(qraw);
     const Magic mg = magic_vgprs();
-
-    const CacheRow<Meta> cr = cache_row<D, Meta>(kc, vc, kmin, ksc, vmin, vsc, (int)pc, S, part);
+    if (nf > 0)
+        load_rows_half<D, U, true>(cr, tb, t_end, first);
 
     float m = -INFINITY, l = 0.0f, bsum = 0.0f;
     float acc[32];
@@ -472,19 +553,18 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, Meta *
     for (int i = 0; i < 32; ++i)
         acc[i] = 0.0f;
 
-    int tb = w_begin + lt;
+    if (nf > 0) {
+        attend_kv_rows<D, U>(first, qs, mg, c2, m, l, bsum, acc);
+        tb += TPI;
+    }
     if (!tail_wave) {
-        for (int it = 0; it < n_full; ++it, tb += TPI)
+        for (int it = 1; it < n_full; ++it, tb += TPI)
             decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
         for (int it = 0; it < n_rest; ++it, tb += TPW)
             decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
     } else {
-        // every row but the last TPW-row chunk as usual, then that chunk with
-        // the new row substituted for slot T-1
-        const int last = w_begin + (t_end - 1 - w_begin) / TPW * TPW;
-        const int nf = (last - w_begin) / TPI;
         const int nr1 = (last - w_begin - nf * TPI) / TPW;
-        for (int it = 0; it < nf; ++it, tb += TPI)
+        for (int it = 1; it < nf; ++it, tb += TPI)
             decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
         for (int it = 0; it < nr1; ++it, tb += TPW)
             decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
@@ -661,33 +741,54 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp4)
     return base + incl - v;
 }
 
-template <int D, int UU, typename Meta>
-__device__ __forceinline__ void score_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, const Magic mg,
-                                           float c2, bool writer, float *__restrict__ srow)
-{
-    constexpr int LPT = D / 32;
-    constexpr int TPW = 64 / LPT;
-    constexpr int G = D / 64;
+// The K rows of one score iteration (UU token rows per lane), clamped and
+// flagged as in load_kv_rows.
+template <int UU>
+struct KRows {
     uint4 kx[UU];
     float km[UU], ks[UU];
+};
+
+template <int D, int UU, typename Meta>
+__device__ __forceinline__ void load_k_rows(const CacheRow<Meta> &cr, int tb, int t_end, KRows<UU> &r)
+{
+    constexpr int TPW = 64 / (D / 32);
+    constexpr int G = D / 64;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
         const int t = tb + u * TPW;
         const uint32_t tcl = (uint32_t)(t < t_end ? t : t_end - 1);
         const uint32_t co = tcl * (D / 2) + cr.code_off, mo = tcl * (uint32_t)(sizeof(Meta) * G) + cr.meta_off;
-        kx[u] = ld_stream16(cr.kb + co);
-        km[u] = ld_meta(at_byte(cr.kmb, mo));
-        ks[u] = ld_meta(at_byte(cr.ksb, mo));
+        r.kx[u] = ld_stream16(cr.kb + co);
+        r.km[u] = ld_meta(at_byte(cr.kmb, mo));
+        r.ks[u] = ld_meta(at_byte(cr.ksb, mo));
     }
+}
+
+template <int D, int UU>
+__device__ __forceinline__ void store_scores(const KRows<UU> &r, int tb, int t_end, const QSlice &qs, const Magic mg,
+                                             float c2, bool writer, float *__restrict__ srow)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-        const float dq = dot_keys(qs, kx[u], mg) - qs.qbias;
-        float sp = __builtin_fmaf(ks[u], dq, km[u] * qs.qsum);
+        const float dq = dot_keys(qs, r.kx[u], mg) - qs.qbias;
+        float sp = __builtin_fmaf(r.ks[u], dq, r.km[u] * qs.qsum);
         sp = token_sum<LPT>(sp);
         const int t = tb + u * TPW;
         if (writer && t < t_end)
             srow[t] = sp * c2;
     }
+}
+
+template <int D, int UU, typename Meta>
+__device__ __forceinline__ void score_iter(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs, const Magic mg,
+                                           float c2, bool writer, float *__restrict__ srow)
+{
+    KRows<UU> r;
+    load_k_rows<D, UU>(cr, tb, t_end, r);
+    store_scores<D, UU>(r, tb, t_end, qs, mg, c2, writer, srow);
 }
 
 // One wave per (pair, chunk of `chunk` tokens); four waves per workgroup.
@@ -711,13 +812,22 @@ __global__ __launch_bounds__(256) void k_topk_scores(const uint8_t *__restrict__
     const int t_end = min(T, w_begin + chunk);
     const int n_full = (t_end - w_begin) / TPI;
     const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW;
-    const QSlice qs = load_q_slice(q + pair * (D / 8) + part * 4);
-    const Magic mg = magic_vgprs();
     const CacheRow<Meta> cr = cache_row<D, Meta>(kc, nullptr, kmin, ksc, nullptr, nullptr, (int)pair, S, part);
     float *__restrict__ srow = scores + pair * T;
     const bool writer = part == 0;
     int tb = w_begin + lt;
-    for (int it = 0; it < n_full; ++it, tb += TPI)
+    // the first iteration's rows are requested right behind the query
+    const QRaw qraw = load_q_raw(q + pair * (D / 8) + part * 4);
+    KRows<U> first;
+    if (n_full > 0)
+        load_k_rows<D, U>(cr, tb, t_end, first);
+    const QSlice qs = q_slice(qraw);
+    const Magic mg = magic_vgprs();
+    if (n_full > 0) {
+        store_scores<D, U>(first, tb, t_end, qs, mg, c2, writer, srow);
+        tb += TPI;
+    }
+    for (int it = 1; it < n_full; ++it, tb += TPI)
         score_iter<D, U>(cr, tb, t_end, qs, mg, c2, writer, srow);
     for (int it = 0; it < n_rest; ++it, tb += TPW)
         score_iter<D, 1>(cr, tb, t_end, qs, mg, c2, writer, srow);
