@@ -70,11 +70,18 @@ int status_of(int hip_err) { return hip_err == 0 ? KVQ_OK : KVQ_ELAUNCH; }
 
 // Launch shape for the dense decode kernel.  Default: 4 token rows per lane
 // per iteration and 2 waves per (batch row, head), two pairs per 256-thread
-// workgroup -- the fastest shape of the measured sweep on the OPT-175B layer
-// (79% of HBM peak vs 70% for 4 waves per pair).
+// workgroup -- the fastest shape of the measured sweeps on the OPT-175B layer
+// (191.8 us against 197.1 us for 4 waves per pair at context 544).
 constexpr int kDefaultUnroll = 4;
 constexpr int kDefaultWavesPerPair = 2;
 constexpr int kPairsPerGroup = 4 / kDefaultWavesPerPair;
+// Automatic launch shape: an unsplit context of at least this many tokens is
+// shared by four waves per (batch row, head) instead of two (measured on
+// MI355X: b=32 a=96 T=2048 170.7 -> 159.7 us, b=64 a=32 T=2048 118.1 ->
+// 108.9 us, b=144 a=96 T=1024 level within 1.4%; with splits, or below 1536
+// tokens, two waves were level or faster).
+constexpr int kLongCtxFourWaves = 1536;
+constexpr int kAutoWavesPerPair = 0;
 
 // Automatic split count.  The split workgroups of all pairs should spread
 // evenly over MI355X's 256 CUs with at least two workgroups (8 waves) per CU:
@@ -258,14 +265,16 @@ int decode_common(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, vo
         return KVQ_ERANGE;
     if (num_splits < 0 || num_splits > KVQ_MAX_SPLITS)
         return KVQ_ERANGE;
-    if ((unroll != 1 && unroll != 2 && unroll != 4) || (waves_per_pair != 1 && waves_per_pair != 2 &&
-                                                         waves_per_pair != 4))
+    if ((unroll != 1 && unroll != 2 && unroll != 4) ||
+        (waves_per_pair != kAutoWavesPerPair && waves_per_pair != 1 && waves_per_pair != 2 && waves_per_pair != 4))
         return KVQ_EINVAL;
     const int pairs = cache->dims.b * cache->dims.a;
     kvq::DecodeShape sh;
     sh.unroll = unroll;
-    sh.waves_per_pair = waves_per_pair;
     sh.splits = resolve_splits(pairs, ctx_len, num_splits, &sh.split_len);
+    sh.waves_per_pair = waves_per_pair != kAutoWavesPerPair ? waves_per_pair
+                        : (sh.splits == 1 && ctx_len >= kLongCtxFourWaves) ? 4
+                                                                           : kDefaultWavesPerPair;
     const size_t need = kvq::decode_ws_floats(pairs, c.d, sh.splits) * sizeof(float);
     if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need))
         return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
@@ -281,6 +290,8 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
                               int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
                               size_t ws_bytes, void *hip_stream)
 {
+    if (waves_per_pair == kAutoWavesPerPair)
+        return KVQ_EINVAL; // the caller fixes the shape here
     return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, unroll, waves_per_pair, ws, ws_bytes, nullptr,
                          nullptr, hip_stream);
 }
@@ -288,7 +299,7 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
 int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
                         int32_t num_splits, void *ws, size_t ws_bytes, void *hip_stream)
 {
-    return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll, kDefaultWavesPerPair, ws,
+    return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll, kAutoWavesPerPair, ws,
                          ws_bytes, nullptr, nullptr, hip_stream);
 }
 
@@ -299,7 +310,7 @@ int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k
         return KVQ_EINVAL;
     if (cache != nullptr && check_dims(&cache->dims) == KVQ_OK && (pos < 0 || pos >= cache->dims.s + cache->dims.n))
         return KVQ_ERANGE;
-    return decode_common(cache, q_f16, pos + 1, out_f16, num_splits, kDefaultUnroll, kDefaultWavesPerPair, ws,
+    return decode_common(cache, q_f16, pos + 1, out_f16, num_splits, kDefaultUnroll, kAutoWavesPerPair, ws,
                          ws_bytes, k_f16, v_f16, hip_stream);
 }
 

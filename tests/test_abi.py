@@ -123,6 +123,7 @@ def test_ranges(L):
     assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4, FAKE, 257, None, 0, st) == KVQ_ERANGE
     assert L.decode_attention_q4_tuned(ctypes.byref(c), FAKE, 4, FAKE, 1, 3, 1, None, 0, st) == KVQ_EINVAL
     assert L.decode_attention_q4_tuned(ctypes.byref(c), FAKE, 4, FAKE, 1, 2, 8, None, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_tuned(ctypes.byref(c), FAKE, 4, FAKE, 1, 4, 0, None, 0, st) == KVQ_EINVAL
     assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 10, 0, FAKE, None, None, 0, st) == KVQ_ERANGE
     assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 10, 11, FAKE, None, None, 0, st) == KVQ_ERANGE
     big = cache(dims(s=9000, n=0))

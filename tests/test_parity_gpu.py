@@ -235,6 +235,34 @@ def test_dense_ragged_contexts(d, T):
     assert_close(_gpu_rows(out, pairs), ref, f"d={d} T={T}")
 
 
+def test_dense_long_unsplit_context_auto_shape():
+    """An unsplit context of >= 1536 tokens takes four waves per (batch row, head) by default:
+    the automatic call equals the explicit (unroll 4, 4 waves) launch bit for bit, the fused
+    append + attend equals the separate calls, and sampled pairs match the oracle."""
+    require_gpu()
+    b, a, d, s, n = 32, 64, 128, 1599, 1
+    T = s + n
+    cache, hc, q = _small_cache(b, a, d, s, n, 5100)
+    cache2 = kvq.QuantKVCache(b, a, a * d, s, n, device=DEV, fill=0xFF)
+    k = W.random_fp16((b, T, a, d), 5100, DEV)[:, :s].contiguous()   # the same prompt rows as `cache`
+    v = W.random_fp16((b, T, a, d), 5101, DEV)[:, :s].contiguous()
+    kvq.kv_quantize_prefill(cache2, k, v)
+    kn = W.random_fp16((b, 1, a, d), 5103, DEV)
+    vn = W.random_fp16((b, 1, a, d), 5104, DEV)
+    kvq.kv_append_quant(cache, kn, vn, s)
+    hc.append(f16_np(kn), f16_np(vn), s)
+    assert kvq.kvq_workspace_bytes(cache, T, 0, 0) == 0      # one split: the four-wave shape applies
+    auto = kvq.decode_attention_q4(cache, q, T, out=_nan_out(b, a, d))
+    fixed = kvq.decode_attention_q4_tuned(cache, q, T, unroll=4, waves_per_pair=4, out=_nan_out(b, a, d))
+    fused = kvq.kv_append_attend_q4(cache2, q, kn, vn, s, out=_nan_out(b, a, d))
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int16), fixed.view(torch.int16))
+    assert torch.equal(fused.view(torch.int16), auto.view(torch.int16))
+    pairs = sample_pairs(b, a, 24, seed=71)
+    ref = oracle_attend_pairs(hc, f16_np(q), T, pairs)
+    assert_close(_gpu_rows(auto, pairs), ref, f"auto shape T={T}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 64, 256])
 @pytest.mark.parametrize("unroll,wpp", [(1, 1), (2, 1), (4, 1), (1, 2), (2, 2), (4, 2), (1, 4), (2, 4), (4, 4)])
 def test_dense_launch_shapes_and_splits(splits, unroll, wpp):
