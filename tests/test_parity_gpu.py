@@ -462,6 +462,31 @@ def test_topk_selection_exact_on_own_scores(case, T):
             assert np.array_equal(got[p], want), f"{case} T={T} k={k_top} pair {p}: selection differs"
 
 
+@pytest.mark.parametrize("T", [37, 700, 1500, 2048, 3000])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_topk_head_dims(d, T):
+    """Sparse attention at every supported head_dim (2, 4 or 8 lanes per token row in the
+    score pass, the gather and the final lane sums), both wave-select key layouts (16 keys
+    per lane up to T = 1024, 32 up to 2048) and the workgroup select (T > 2048): the
+    selection is exactly the top k of the kernel's own scores, and the output matches the
+    oracle on the GPU's selection; k = 1, 10% and T."""
+    require_gpu()
+    b, a = 2, 3
+    cache, hc, q = _small_cache(b, a, d, T, 0, 5200 + d + T)
+    pairs = all_pairs(b, a)
+    qh = f16_np(q)
+    ws = torch.empty(kvq.kvq_workspace_bytes(cache, T, 0, T) // 4, dtype=torch.float32, device=DEV)
+    for k_top in sorted({1, math.ceil(0.1 * T), T}):
+        out, sel = kvq.decode_attention_q4_topk(cache, q, T, k_top, out=_nan_out(b, a, d), ws=ws)
+        torch.cuda.synchronize()
+        scores = ws[: b * a * T].view(b * a, T).cpu().numpy()
+        got = sel.view(b * a, k_top).cpu().numpy()
+        for p in range(b * a):
+            want = np.sort(np.lexsort((np.arange(T), -scores[p]))[:k_top])
+            assert np.array_equal(got[p], want), f"d={d} T={T} k={k_top} pair {p}: selection differs"
+        _topk_checks(hc, qh, T, k_top, pairs, _gpu_rows(out, pairs), sel.cpu().numpy(), f"topk d={d} T={T} k={k_top}")
+
+
 def test_topk_deterministic():
     """Run twice -> bit-identical outputs and selections."""
     require_gpu()
