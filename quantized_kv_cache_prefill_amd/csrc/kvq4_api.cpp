@@ -133,7 +133,9 @@ int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
 // Split of the K range for gemm_w4a16: as many splits as keep the workgroups
 // within one resident round (256 CUs x the eight-wave workgroups one CU holds
 // at that row-block count: 2 at one block of 16 rows, else 1, set by
-// registers), with at least 4 chunks of 128 k per split.
+// registers), with at least 4 chunks of 128 k per split; when that leaves one
+// split of an under-filled round, the split count that minimises (rounds x
+// each split's share of K) + a cost for the partials.
 // Depends on (M, N, K) only.
 constexpr int kGemmChunk = 128;
 constexpr int kGemmCols = 256;
@@ -145,6 +147,17 @@ bool gemm_dims_ok(int M, int N, int K)
            (int64_t)M * N < ((int64_t)1 << 40);
 }
 
+// Weight of the split partials in the automatic split choice: each extra
+// split writes and re-reads M*N binary32 partials, 16*M/K of the weight bytes.
+// Fitted to measured sweeps on MI355X (OPT-175B projections, K = 12288):
+// QKV (N = 36864) at M = 144 took 256 us with 1 split, 202 us with 3 and
+// 214 us with 5; at M = 32, 212 us with 1 split and 119-124 us with 3 to 7;
+// the output projection (N = 12288) was fastest with 5 at M = 144 and 32.
+// The choices it makes (3, 7, 7, 3 splits at M = 144, 64, 32, 16) ran within
+// ~1% of the fastest split count at each M.
+constexpr double kGemmPartialWeight = 0.2;
+constexpr int kGemmMaxAutoSplits = 16;
+
 int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
 {
     const int chunks = K / kGemmChunk;
@@ -153,9 +166,27 @@ int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
         const int mb = kvq::gemm_row_blocks(M);
         const int rows = 16 * mb;
         const int per_cu = mb == 1 ? 2 : 1;
+        const int64_t slots = (int64_t)kCUs * per_cu;
         const int64_t tiles = (int64_t)((N + kGemmCols - 1) / kGemmCols) * ((M + rows - 1) / rows);
-        s = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)kCUs * per_cu / std::max<int64_t>(tiles, 1),
-                                                        chunks / 4));
+        const int max_s = std::max(1, chunks / 4); // at least 4 chunks per split
+        // As many splits as one resident round holds ...
+        s = (int)std::max<int64_t>(1, std::min<int64_t>(slots / std::max<int64_t>(tiles, 1), max_s));
+        // ... unless that is one split of an under-filled round: then weigh the
+        // rounds each split count needs against its partials.
+        if (s == 1 && tiles < slots) {
+            const double rho = 16.0 * M / K;
+            double best = 1.0; // one split: one round, the whole K, no partials
+            for (int c = 2; c <= std::min(max_s, kGemmMaxAutoSplits); ++c) {
+                const int cps = (chunks + c - 1) / c;
+                const int se = (chunks + cps - 1) / cps; // splits actually made
+                const double rounds = std::ceil((double)(tiles * se) / (double)slots);
+                const double cost = rounds * cps / chunks + kGemmPartialWeight * rho * se;
+                if (cost < best - 1e-9) {
+                    best = cost;
+                    s = se;
+                }
+            }
+        }
     }
     s = std::min(s, chunks);
     const int cps = (chunks + s - 1) / s;
