@@ -18,8 +18,8 @@
 // weight stream (N*K/2 bytes) and the matrix-core time are of the same order,
 // so the kernel keeps both busy: a workgroup owns a 16*MB x 256 output tile
 // (MB <= 9 row blocks of 16) and a range of K; its eight waves (two per SIMD)
-// each take 64 columns and half of the row blocks, share each 128-wide chunk
-// of x through LDS (double-buffered), and stream and dequantise their own 64
+// each take 32 columns and all the row blocks, share each 128-wide chunk of x
+// through LDS (double-buffered), and stream and dequantise their own 32
 // weight rows.  Ranges of K are split across
 // workgroups when the column tiles alone cannot fill the 256 CUs; the split
 // partials (binary32) are summed by a second kernel.
@@ -40,7 +40,14 @@ constexpr int kChunk = 128;          // k per pipeline step
 constexpr int kPitch = kChunk + 8;   // LDS row pitch of the x chunk, halves (breaks bank aliasing)
 constexpr int kColsPerWave = 64;     // four 16-column blocks
 constexpr int kColsPerGroup = 4 * kColsPerWave;
-constexpr int kThreads = 512;        // 8 waves: 4 column groups x 2 row halves
+constexpr int kThreads = 512;        // 8 waves
+// Work of a wave: kGemmWaveColBlocks = 4: 64 columns and half of the row
+// blocks (8 waves = 4 column groups x 2 row halves); 2: 32 columns and all
+// the row blocks (8 waves side by side), each weight dequantised once.
+#ifndef KVQ_GEMM_WAVE_COL_BLOCKS
+#define KVQ_GEMM_WAVE_COL_BLOCKS 2
+#endif
+constexpr int kGemmWaveColBlocks = KVQ_GEMM_WAVE_COL_BLOCKS;
 
 __device__ __forceinline__ uint4 ld_nt16(const void *p)
 {
@@ -96,12 +103,13 @@ __device__ __forceinline__ h8 dequant8(uint32_t w, h2 sc, h2 mn, const Magic16 m
     return __builtin_bit_cast(h8, d);
 }
 
-// One wave's weights for one 128-k chunk: for each of its four column blocks,
-// lane l holds column (block*16 + l%16), k = 32*(l/16) .. +31 of the chunk
+// One wave's weights for one 128-k chunk: for each of its CB column blocks of
+// 16, lane l holds column (block*16 + l%16), k = 32*(l/16) .. +31 of the chunk
 // (16 code bytes) and that range's group min and scale.
+template <int CB>
 struct WChunk {
-    uint4 code[4];
-    uint32_t mn[4], sc[4]; // binary16 bits, low half
+    uint4 code[CB];
+    uint32_t mn[CB], sc[CB]; // binary16 bits, low half
 };
 
 // Element at a 32-bit byte offset from a wave-uniform base (the load then
@@ -112,19 +120,22 @@ __device__ __forceinline__ const T *at_byte(const T *base, uint32_t off)
     return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
 }
 
-// Chunk c of the wave's 64 rows starting at n0 (a multiple of 64): one 4 KB
-// tile, lane l reading 16 bytes of row 16b + l%16 at byte 16*(l/16).
-__device__ __forceinline__ WChunk load_w_chunk(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ mins,
-                                               const uint16_t *__restrict__ scales, int64_t n0, int K, int c,
-                                               int lane)
+// Chunk c of the wave's 16*CB rows starting at n0 (n0 % 64 + 16*CB <= 64):
+// part of one 4 KB tile, lane l reading 16 bytes of row n0%64 + 16b + l%16 at
+// byte 16*(l/16).
+template <int CB>
+__device__ __forceinline__ WChunk<CB> load_w_chunk(const uint8_t *__restrict__ codes,
+                                                   const uint16_t *__restrict__ mins,
+                                                   const uint16_t *__restrict__ scales, int64_t n0, int K, int c,
+                                                   int lane)
 {
     const int64_t tile = (n0 >> 6) * (K / kChunk) + c; // wave-uniform
     const uint8_t *ct = codes + tile * 4096;
     const uint16_t *mt = mins + tile * 128, *st = scales + tile * 128;
-    WChunk w;
+    WChunk<CB> w;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t r = b * 16 + (lane & 15);
+    for (int b = 0; b < CB; ++b) {
+        const uint32_t r = (uint32_t)(n0 & 63) + b * 16 + (lane & 15);
         w.code[b] = ld_nt16(ct + (r * 64 + 16 * (lane >> 4)));
         w.mn[b] = __builtin_nontemporal_load(at_byte(mt, 4 * r + 2 * (lane >> 5)));
         w.sc[b] = __builtin_nontemporal_load(at_byte(st, 4 * r + 2 * (lane >> 5)));
@@ -201,17 +212,17 @@ __device__ __forceinline__ void store_x(const XStage<MB> &xs, _Float16 *__restri
 }
 
 // One 128-k chunk of one wave: dequantise its weights k-step by k-step and
-// accumulate its MBW x 4 blocks (row blocks rb0 .. rb0+MBW-1 of the x chunk in
-// LDS).
-template <int MBW>
-__device__ __forceinline__ void mma_chunk(const WChunk &cur, const _Float16 *__restrict__ sxb, int rb0, int lane,
-                                          f4 (&acc)[MBW > 0 ? MBW : 1][4])
+// accumulate its MBW x CB blocks (row blocks rb0 .. rb0+MBW-1 of the x chunk
+// in LDS).
+template <int MBW, int CB>
+__device__ __forceinline__ void mma_chunk(const WChunk<CB> &cur, const _Float16 *__restrict__ sxb, int rb0, int lane,
+                                          f4 (&acc)[MBW > 0 ? MBW : 1][CB])
 {
     if constexpr (MBW > 0) {
         const Magic16 mg = magic16();
-        h2 sc[4], mn[4];
+        h2 sc[CB], mn[CB];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < CB; ++b) {
             sc[b] = __builtin_bit_cast(h2, (cur.sc[b] & 0xFFFFu) * 0x00010001u);
             mn[b] = __builtin_bit_cast(h2, (cur.mn[b] & 0xFFFFu) * 0x00010001u);
         }
@@ -220,9 +231,9 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const _Float16 *__r
         };
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            h8 bw[4];
+            h8 bw[CB];
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < CB; ++b)
                 bw[b] = dequant8(word(b, j), sc[b], mn[b], mg);
             // all of this k-step's x reads are issued before its products
             h8 a[MBW];
@@ -233,10 +244,10 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const _Float16 *__r
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < CB; ++b)
                     acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], bw[b], acc[mb][b], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);     // the k-step's LDS reads,
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * MBW, 0); // then its products
+            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);      // the k-step's LDS reads,
+            __builtin_amdgcn_sched_group_barrier(0x008, CB * MBW, 0); // then its products
         }
     }
     // keep the caller's LDS writes of the next x chunk (and their wait on its
@@ -244,11 +255,11 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const _Float16 *__r
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The K loop and the stores of one wave: its 64 columns starting at n0 and
+// The K loop and the stores of one wave: its 16*CB columns starting at n0 and
 // its MBW row blocks starting at block rb0 of the tile (the tile's MB blocks
 // are staged in LDS by all waves).  Every wave runs the same sequence of
 // barriers whatever its MBW.
-template <int MB, int MBW>
+template <int MB, int MBW, int CB>
 __device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
                                           const uint16_t *__restrict__ mins, const uint16_t *__restrict__ scales,
                                           _Float16 *__restrict__ y, float *__restrict__ ws, int M, int N, int K,
@@ -257,20 +268,20 @@ __device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const 
 {
     const int lane = threadIdx.x & 63;
     const bool wave_ok = n0 < N; // N % 64 == 0: a wave's columns are all in range or all out
-    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0..63 and store nothing
-    f4 acc[MBW > 0 ? MBW : 1][4];
+    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0.. and store nothing
+    f4 acc[MBW > 0 ? MBW : 1][CB];
 #pragma unroll
     for (int mb = 0; mb < (MBW > 0 ? MBW : 1); ++mb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < CB; ++b)
             acc[mb][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
     XStage<MB> xs;
     const XOffsets<MB> xo = x_offsets<MB>(M, K, m0);
-    WChunk cur{};
+    WChunk<CB> cur{};
     if (c_begin < c_end) {
         if constexpr (MBW > 0)
-            cur = load_w_chunk(codes, mins, scales, nsafe, K, c_begin, lane);
+            cur = load_w_chunk<CB>(codes, mins, scales, nsafe, K, c_begin, lane);
         load_x<MB>(x, c_begin * kChunk, xo, xs);
         store_x<MB>(xs, sx[0]);
     }
@@ -278,13 +289,13 @@ __device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const 
     for (int c = c_begin; c < c_end; ++c) {
         const int buf = (c - c_begin) & 1;
         const bool more = c + 1 < c_end; // uniform
-        WChunk nxt{};
+        WChunk<CB> nxt{};
         if (more) {
             if constexpr (MBW > 0)
-                nxt = load_w_chunk(codes, mins, scales, nsafe, K, c + 1, lane);
+                nxt = load_w_chunk<CB>(codes, mins, scales, nsafe, K, c + 1, lane);
             load_x<MB>(x, (c + 1) * kChunk, xo, xs);
         }
-        mma_chunk<MBW>(cur, sx[buf], rb0, lane, acc);
+        mma_chunk<MBW, CB>(cur, sx[buf], rb0, lane, acc);
         if (more)
             store_x<MB>(xs, sx[buf ^ 1]);
         cur = nxt;
@@ -298,7 +309,7 @@ __device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const 
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < CB; ++b) {
                 const int64_t n = n0 + b * 16 + (lane & 15);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -316,14 +327,19 @@ __device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const 
 }
 
 // grid.x: column groups of 256 (fastest), grid.y: K splits, grid.z: row tiles
-// of 16*MB.  Eight waves: wave w takes columns 64*(w%4) of the group and the
-// upper (w < 4: ceil(MB/2) blocks) or lower (w >= 4) row blocks, so two waves
-// share each SIMD and one's dequantisation overlaps the other's matrix work;
-// the pair streams the same weight tile (the second read is an L2 hit).
+// of 16*MB.  Eight waves, two per SIMD, so one's dequantisation overlaps the
+// other's matrix work.  CB = 2 (the default): wave w takes columns 32w of the
+// group and all MB row blocks, so every weight is dequantised once.  CB = 4:
+// wave w takes columns 64*(w%4) and the upper (w < 4: ceil(MB/2) blocks) or
+// lower (w >= 4) row blocks; the two waves of a column group stream and
+// dequantise the same weight tile.  Measured on the OPT-175B projections, CB = 2
+// against CB = 4: QKV at M = 144, 64, 32: 251.7 -> 229.7, 157.4 -> 104.9,
+// 123.7 -> 82.3 us; output at M = 64, 32: 59.8 -> 48.3, 58.0 -> 42.6 us
+// (bit-identical results).
 // splits == 1: y written as fp16; else binary32 partials to ws[split][M][N].
 // The next chunk's weights and x are loaded into registers while the current
 // chunk is multiplied; x then goes to the other LDS buffer.
-template <int MB>
+template <int MB, int CB>
 __global__ __launch_bounds__(kThreads) void k_gemm_w4(const uint16_t *__restrict__ x,
                                                       const uint8_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ mins,
@@ -334,16 +350,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4(const uint16_t *__restrict
     constexpr int MH = (MB + 1) / 2;
     __shared__ __attribute__((aligned(16))) _Float16 sx[2][16 * MB * kPitch];
     const int wave = threadIdx.x >> 6;
-    const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + (wave & 3) * kColsPerWave;
     const int split = blockIdx.y, splits = gridDim.y;
     const int m0 = blockIdx.z * 16 * MB;
     const int c_begin = split * chunks_per_split;
     const int c_end = min(K / kChunk, c_begin + chunks_per_split);
-    if (wave < 4)
-        gemm_wave<MB, MH>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, 0, split, splits, c_begin, c_end, sx);
-    else
-        gemm_wave<MB, MB - MH>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, MH, split, splits, c_begin, c_end,
-                               sx);
+    if constexpr (CB == 4) {
+        const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + (wave & 3) * kColsPerWave;
+        if (wave < 4)
+            gemm_wave<MB, MH, 4>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, 0, split, splits, c_begin, c_end,
+                                 sx);
+        else
+            gemm_wave<MB, MB - MH, 4>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, MH, split, splits, c_begin,
+                                      c_end, sx);
+    } else {
+        const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + wave * 16 * CB;
+        gemm_wave<MB, MB, CB>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, 0, split, splits, c_begin, c_end, sx);
+    }
 }
 
 // y[m][n] = fp16(sum over splits of ws[s][m][n]), 4 outputs per thread.
@@ -372,7 +394,7 @@ int launch_gemm_mb(const GemmArgs &g, hipStream_t st)
 {
     const dim3 grid((unsigned)((g.N + kColsPerGroup - 1) / kColsPerGroup), (unsigned)g.splits,
                     (unsigned)((g.M + 16 * MB - 1) / (16 * MB)));
-    hipLaunchKernelGGL((k_gemm_w4<MB>), grid, dim3(kThreads), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
+    hipLaunchKernelGGL((k_gemm_w4<MB, kGemmWaveColBlocks>), grid, dim3(kThreads), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
                        static_cast<const uint16_t *>(g.mins), static_cast<const uint16_t *>(g.scales),
                        static_cast<_Float16 *>(g.y), g.ws, g.M, g.N, g.K, g.chunks_per_split);
     int e = (int)hipGetLastError();
