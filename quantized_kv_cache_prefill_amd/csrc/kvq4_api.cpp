@@ -149,13 +149,11 @@ bool gemm_dims_ok(int M, int N, int K)
 
 // Weight of the split partials in the automatic split choice: each extra
 // split writes and re-reads M*N binary32 partials, 16*M/K of the weight bytes.
-// Fitted to measured sweeps on MI355X (OPT-175B projections, K = 12288):
-// QKV (N = 36864) at M = 144 took 256 us with 1 split, 202 us with 3 and
-// 214 us with 5; at M = 32, 212 us with 1 split and 119-124 us with 3 to 7;
-// the output projection (N = 12288) was fastest with 5 at M = 144 and 32.
-// The choices it makes (3, 7, 7, 3 splits at M = 144, 64, 32, 16) ran within
-// ~1% of the fastest split count at each M.
-constexpr double kGemmPartialWeight = 0.2;
+// Fitted to measured sweeps on MI355X (OPT-175B QKV projection, N = 36864,
+// K = 12288, 144 column tiles): at M = 144, 250 us with 1 split, 199 us with
+// 3, 205 us with 5; at M = 64, 141 / 92 / 100 us with 1 / 3 / 7; at M = 32,
+// 147 / 77 / 78 us with 1 / 3 / 7.  The weight 0.3 picks 3, 3 and 7 there.
+constexpr double kGemmPartialWeight = 0.3;
 constexpr int kGemmMaxAutoSplits = 16;
 
 int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
