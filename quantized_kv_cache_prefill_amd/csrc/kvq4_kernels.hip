@@ -778,7 +778,7 @@ __device__ __forceinline__ void store_scores(const KRows<UU> &r, int tb, int t_e
         sp = token_sum<LPT>(sp);
         const int t = tb + u * TPW;
         if (writer && t < t_end)
-            srow[t] = sp * c2;
+            __builtin_nontemporal_store(sp * c2, srow + t); // streamed out beside the key stream
     }
 }
 
