@@ -71,10 +71,13 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_select_topk.argtypes = [I, P, I, P]
     L.oracle_attend_topk.argtypes = [I, I, I, P, P, P, P, P, P, P, P, P]
     L.oracle_prefill_attend.argtypes = [I, I, I, P, P, P, P]
+    L.oracle_attend_rows.argtypes = [I, I, P, P, P, P]
+    L.oracle_prefill_attend_rows.argtypes = [I, I, I, P, P, P, I, P, P]
     for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_quantize_group_m16", "oracle_quantize_rows_m16",
               "oracle_dequant_rows", "oracle_dequant_rows_f16",
               "oracle_scores",
-              "oracle_attend", "oracle_attend_subset", "oracle_select_topk", "oracle_attend_topk"):
+              "oracle_attend", "oracle_attend_subset", "oracle_select_topk", "oracle_attend_topk",
+              "oracle_attend_rows", "oracle_prefill_attend", "oracle_prefill_attend_rows"):
         getattr(L, f).restype = None
     return L
 
@@ -299,6 +302,31 @@ def attend_topk(q, hc: HeadCache, k: int, T: int | None = None):
     return out, sel
 
 
+def attend_rows(q, khat, vhat) -> np.ndarray:
+    """Decode attention of one query over explicit dequantised rows khat, vhat [T][d]
+    (float64); fp64 result [d]."""
+    q = _f16bits(q).reshape(-1)
+    khat = np.ascontiguousarray(khat, np.float64)
+    vhat = np.ascontiguousarray(vhat, np.float64)
+    T, d = khat.shape
+    assert vhat.shape == (T, d) and q.size == d and T >= 1
+    out = np.zeros(d, np.float64)
+    lib().oracle_attend_rows(d, T, _ptr(q), _ptr(khat), _ptr(vhat), _ptr(out))
+    return out
+
+
+def attend_f16form(q, hc: HeadCache, T: int | None = None, idx=None) -> np.ndarray:
+    """Attention over the cache in the report's FP16 form ("dequantised to FP16 before
+    compute"): every dequantised K and V element rounded to binary16 (dequant_rows_f16),
+    then the softmax and P.V of attend.  idx (optional): attend over those tokens only
+    (the sparse variant on a given selection)."""
+    T = hc.T if T is None else T
+    rows = np.arange(T) if idx is None else np.ascontiguousarray(idx, np.int64)
+    k16 = dequant_rows_f16(hc.kc[rows], hc.kmin[rows], hc.ksc[rows]).astype(np.float64)
+    v16 = dequant_rows_f16(hc.vc[rows], hc.vmin[rows], hc.vsc[rows]).astype(np.float64)
+    return attend_rows(q, k16, v16)
+
+
 def prefill_attend(q, k, v) -> np.ndarray:
     """Causal prefill attention of one (batch row, head) over its prompt, fp16 inputs
     [s][d] (or [s][...][d] views with the head's rows strided, e.g. x[bi, :, ai]); fp64 [s][d]."""
@@ -308,6 +336,20 @@ def prefill_attend(q, k, v) -> np.ndarray:
     q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
     out = np.zeros((s, d), np.float64)
     lib().oracle_prefill_attend(d, s, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out))
+    return out
+
+
+def prefill_attend_rows(q, k, v, rows) -> np.ndarray:
+    """The causal prefill attention of one (batch row, head) at the query rows `rows` only
+    (each 0..s-1); fp64 [len(rows)][d].  Same inputs as prefill_attend."""
+    q, k, v = (_f16bits(np.asarray(x)) for x in (q, k, v))
+    s, d = q.shape
+    assert k.shape == (s, d) and v.shape == (s, d)
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    rows = np.ascontiguousarray(rows, np.int32)
+    assert rows.ndim == 1 and np.all((rows >= 0) & (rows < s))
+    out = np.zeros((rows.size, d), np.float64)
+    lib().oracle_prefill_attend_rows(d, s, d, _ptr(q), _ptr(k), _ptr(v), rows.size, _ptr(rows), _ptr(out))
     return out
 
 

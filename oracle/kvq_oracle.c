@@ -29,12 +29,13 @@
  * no fast-math), in the order listed at oracle_quantize_group.  Attention
  * runs in binary64 over the dequantised values min + code*scale taken
  * exactly (oracle_dequant_value).  The report's "dequantised to FP16 before
- * compute" describes the data type of FlexGen's own GPU compute; it is kept
- * as oracle_dequant_elem_f16 but not used by attention: with the OPT-30B
- * style outlier channels (queries and keys x8) the FP16 rounding of a
- * dequantised key alone moves a logit by ~1e-2, more than the tolerance the
- * GPU path is held to, so an FP16-rounded reference would measure rounding
- * noise rather than the method.
+ * compute" describes the data type of FlexGen's own GPU compute; that form
+ * is oracle_dequant_elem_f16, and oracle_attend_rows runs the same attention
+ * over it (the second reference the GPU output is compared with).  It is not
+ * the primary reference: with the OPT-30B style outlier channels (queries
+ * and keys x8) the FP16 rounding of a dequantised key alone moves a logit by
+ * ~1e-2, more than the tolerance the GPU path is held to, so there an
+ * FP16-rounded reference measures rounding noise rather than the method.
  *
  * Readings taken where the pages are silent (each one is listed in the
  * design notes with its reason):
@@ -430,6 +431,43 @@ void oracle_attend_topk(int d, int T, int k, const uint16_t *q, const uint8_t *k
     free(s);
 }
 
+/* Decode attention of one query over T dequantised rows given explicitly
+ * (binary64, row t of K^ at khat + t*d, of V^ at vhat + t*d): the same
+ * scores (scale 1/sqrt(d)), max-subtracted softmax and P.V as oracle_attend.
+ * With the rows in the FP16 form (oracle_dequant_rows_f16, widened exactly)
+ * this is attention over the cache "dequantised to FP16 before compute" as
+ * [FG-report] 三.2(C) writes it; with a chosen subset of rows it is the
+ * sparse variant over those rows.                                          */
+void oracle_attend_rows(int d, int T, const uint16_t *q, const double *khat, const double *vhat, double *out)
+{
+    double c = 1.0 / sqrt((double)d);
+    if (T < 1)
+        return;
+    double *p = (double *)malloc(sizeof(double) * (size_t)T);
+    for (int t = 0; t < T; ++t) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i)
+            acc += (double)oracle_f16_to_f32(q[i]) * khat[(size_t)t * d + i];
+        p[t] = acc * c;
+    }
+    double m = p[0];
+    for (int t = 1; t < T; ++t)
+        if (p[t] > m)
+            m = p[t];
+    double l = 0.0;
+    for (int t = 0; t < T; ++t) {
+        p[t] = exp(p[t] - m);
+        l += p[t];
+    }
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int t = 0; t < T; ++t)
+            acc += p[t] * vhat[(size_t)t * d + i];
+        out[i] = acc / l;
+    }
+    free(p);
+}
+
 /* ------------------------------------------------------------------------
  * Prefill attention for one (batch row, head) over the prompt ([FG-blog]
  * 预填充阶段: x_out = softmax(x_Q x_K^T / sqrt(.)) x_V, stopping before W_O
@@ -442,35 +480,56 @@ void oracle_attend_topk(int d, int T, int k, const uint16_t *q, const uint8_t *k
  * q, k, v: fp16 bits, row t at + t*stride elements (stride >= d lets the
  * caller pass one head of a [s][a][d] batch row); out: binary64 [s][d].
  * --------------------------------------------------------------------- */
+/* Row i of the causal prefill attention (0 <= i < s): query i over keys
+ * 0..i; p holds at least i + 1 doubles of scratch.                          */
+static void prefill_row(int d, int s, int i, int stride, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        double *p, double *out_row)
+{
+    if (i < 0 || i >= s)
+        return;
+    double c = 1.0 / sqrt((double)d);
+    const uint16_t *qi = q + (size_t)i * stride;
+    double m = -INFINITY;
+    for (int t = 0; t <= i; ++t) {
+        const uint16_t *kt = k + (size_t)t * stride;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e)
+            acc += (double)oracle_f16_to_f32(qi[e]) * (double)oracle_f16_to_f32(kt[e]);
+        p[t] = acc * c;
+        if (p[t] > m)
+            m = p[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t <= i; ++t) {
+        p[t] = exp(p[t] - m);
+        l += p[t];
+    }
+    for (int e = 0; e < d; ++e) {
+        double acc = 0.0;
+        for (int t = 0; t <= i; ++t)
+            acc += p[t] * (double)oracle_f16_to_f32(v[(size_t)t * stride + e]);
+        out_row[e] = acc / l;
+    }
+}
+
 void oracle_prefill_attend(int d, int s, int stride, const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            double *out)
 {
-    double c = 1.0 / sqrt((double)d);
     double *p = (double *)malloc(sizeof(double) * (size_t)(s > 0 ? s : 1));
-    for (int i = 0; i < s; ++i) {
-        const uint16_t *qi = q + (size_t)i * stride;
-        double m = -INFINITY;
-        for (int t = 0; t <= i; ++t) {
-            const uint16_t *kt = k + (size_t)t * stride;
-            double acc = 0.0;
-            for (int e = 0; e < d; ++e)
-                acc += (double)oracle_f16_to_f32(qi[e]) * (double)oracle_f16_to_f32(kt[e]);
-            p[t] = acc * c;
-            if (p[t] > m)
-                m = p[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t <= i; ++t) {
-            p[t] = exp(p[t] - m);
-            l += p[t];
-        }
-        for (int e = 0; e < d; ++e) {
-            double acc = 0.0;
-            for (int t = 0; t <= i; ++t)
-                acc += p[t] * (double)oracle_f16_to_f32(v[(size_t)t * stride + e]);
-            out[(size_t)i * d + e] = acc / l;
-        }
-    }
+    for (int i = 0; i < s; ++i)
+        prefill_row(d, s, i, stride, q, k, v, p, out + (size_t)i * d);
+    free(p);
+}
+
+/* The same attention for the query rows rows[0..nrows-1] only (each in
+ * 0..s-1): out[j][d] is row rows[j].  The cost of row i grows with i, so a
+ * few rows of every head cost far less than every row of a few heads.     */
+void oracle_prefill_attend_rows(int d, int s, int stride, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                int nrows, const int32_t *rows, double *out)
+{
+    double *p = (double *)malloc(sizeof(double) * (size_t)(s > 0 ? s : 1));
+    for (int j = 0; j < nrows; ++j)
+        prefill_row(d, s, rows[j], stride, q, k, v, p, out + (size_t)j * d);
     free(p);
 }
 

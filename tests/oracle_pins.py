@@ -255,6 +255,30 @@ def pin_codec_rows_are_groupwise():
                 assert mins[i, j, g] == m1 and scales[i, j, g] == s1
 
 
+def pin_codec_m16_rows_are_groupwise():
+    """With binary16 metadata too, a row of d = 64*G values is G independent groups of 64
+    contiguous head_dim elements: every group of a [3, 5, 256] tensor (rows of different
+    ranges, so neighbouring groups differ) equals the one-group codec on its own 64 values,
+    its 32 code bytes at byte 32g of the row and its min and scale at slot g."""
+    r = np.random.default_rng(25)
+    x = (r.standard_normal((3, 5, 256)) * r.uniform(0.1, 10, (3, 5, 1))
+         * np.repeat(r.uniform(0.2, 5, (3, 5, 4)), 64, axis=2)).astype(np.float16)
+    x[1, 2, 64:128] = 0.5                                   # one constant group mid-row
+    codes, mins, scales = oracle.quantize_rows_m16(x)
+    assert codes.shape == (3, 5, 128) and mins.shape == (3, 5, 4) and scales.shape == (3, 5, 4)
+    assert mins.dtype == np.float16 and scales.dtype == np.float16
+    for i in range(3):
+        for j in range(5):
+            for g in range(4):
+                c1, m1, s1 = oracle.quantize_group_m16(x[i, j, 64 * g:64 * g + 64])
+                assert np.array_equal(codes[i, j, 32 * g:32 * g + 32], c1), (i, j, g)
+                assert mins[i, j, g].view(np.uint16) == m1.view(np.uint16), (i, j, g)
+                assert scales[i, j, g].view(np.uint16) == s1.view(np.uint16), (i, j, g)
+    # the stored pair of each group is that group's own minimum and range (not a neighbour's)
+    xs = x.astype(np.float32).reshape(3, 5, 4, 64)
+    assert np.array_equal(mins.view(np.uint16), (xs.min(-1) + np.float32(0)).astype(np.float16).view(np.uint16))
+
+
 # ------------------------------------------------ codec, binary16 metadata
 def pin_codec_m16_worked_examples():
     """Hand-derived examples in tests/golden/codec_m16_examples.txt (scale rounded to
@@ -484,6 +508,33 @@ def pin_attention_two_token_closed_form():
     assert np.allclose(oracle.attend(q, hc), ref, rtol=1e-12, atol=1e-13)
 
 
+def pin_attention_fp16_form_matches_library_sdpa():
+    """Attention over the report's FP16 form of the cache (every dequantised element rounded
+    to binary16 before compute) equals torch's float64 scaled_dot_product_attention on the
+    FP16-form K and V; over a token subset it equals the same routine with the other keys
+    masked out; one token gives its FP16-form V row exactly; identical keys give the mean
+    of the FP16-form V rows."""
+    for seed, T, d, std in [(2101, 1, 64, 1.0), (2102, 9, 64, 1.0), (2103, 70, 128, 0.5), (2104, 129, 128, 3.0),
+                            (2105, 33, 256, 1.0)]:
+        q, K, V, hc, Kh, Vh = _rand_head(seed, T, d, std)
+        K16 = oracle.dequant_rows_f16(hc.kc, hc.kmin, hc.ksc).astype(np.float64)
+        V16 = oracle.dequant_rows_f16(hc.vc, hc.vmin, hc.vsc).astype(np.float64)
+        ref = _sdpa(q.astype(np.float64), K16, V16)
+        got = oracle.attend_f16form(q, hc)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), np.abs(got - ref).max()
+        assert np.array_equal(oracle.attend_f16form(q, hc, 1), V16[0])
+        if T >= 4:
+            sel = np.sort(np.random.default_rng(seed).choice(T, T // 3 + 1, replace=False))
+            mask = np.full(T, -np.inf)
+            mask[sel] = 0.0
+            ref = _sdpa(q.astype(np.float64), K16, V16, mask)
+            got = oracle.attend_f16form(q, hc, idx=sel)
+            assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), np.abs(got - ref).max()
+    q, K, V, hc, Kh, Vh = _rand_head(2106, 40, 128, 1.0, kfix=lambda K: np.repeat(K[:1], K.shape[0], 0))
+    V16 = oracle.dequant_rows_f16(hc.vc, hc.vmin, hc.vsc).astype(np.float64)
+    assert np.allclose(oracle.attend_f16form(q, hc), V16.mean(axis=0), rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------------------- top-k
 def pin_topk_selection_matches_library_sort():
     """Selection = first k of a stable library sort by (score descending, index ascending),
@@ -555,6 +606,17 @@ def pin_prefill_matches_library_causal_sdpa():
     X = [(r.standard_normal((40, 3, 64))).astype(np.float16) for _ in range(3)]
     got = oracle.prefill_attend(X[0][:, 1], X[1][:, 1], X[2][:, 1])
     assert np.allclose(got, _causal_sdpa(X[0][:, 1], X[1][:, 1], X[2][:, 1]), rtol=1e-12, atol=1e-12)
+
+
+def pin_prefill_selected_rows_match_library_causal_sdpa():
+    """The row-selected prefill attention returns, for each requested query row, that row of
+    torch's float64 causal scaled_dot_product_attention (rows in any order, repeated, first
+    and last)."""
+    Q, K, V = _prompt(1031, 150, 128, 1.0)
+    ref = _causal_sdpa(Q, K, V)
+    rows = np.array([149, 0, 63, 64, 64, 127, 128, 1, 100], np.int32)
+    got = oracle.prefill_attend_rows(Q, K, V, rows)
+    assert np.allclose(got, ref[rows], rtol=1e-12, atol=1e-12), np.abs(got - ref[rows]).max()
 
 
 def pin_prefill_rows_are_decode_steps():

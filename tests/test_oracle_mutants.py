@@ -48,6 +48,13 @@ MUTANTS = [
     ("min_misses_last_element", "for (int i = 1; i < ORACLE_GROUP; ++i) {\n        if (f[i] < mn)",
      "for (int i = 1; i < ORACLE_GROUP - 1; ++i) {\n        if (f[i] < mn)"),
     ("second_group_reads_first", "oracle_quantize_group(x + g * ORACLE_GROUP,", "oracle_quantize_group(x,"),
+    ("m16_rows_every_group_reads_group_0", "oracle_quantize_group_m16(x + (size_t)r * d + g * ORACLE_GROUP,",
+     "oracle_quantize_group_m16(x + (size_t)r * d,"),
+    ("m16_rows_min_to_group_0_slot", "mins + (size_t)r * G + g,\n", "mins + (size_t)r * G,\n"),
+    ("m16_rows_scale_to_group_0_slot", "                                      scales + (size_t)r * G + g);",
+     "                                      scales + (size_t)r * G);"),
+    ("m16_rows_codes_of_group_0", "codes + (size_t)r * (d / 2) + g * (ORACLE_GROUP / 2), mins",
+     "codes + (size_t)r * (d / 2), mins"),
     ("f16_round_down", "double r = nearbyint(a / quantum) * quantum;", "double r = floor(a / quantum) * quantum;"),
     ("f16_subnormal_scale", "v = ldexpf((float)frac, -24);", "v = ldexpf((float)frac, -25);"),
     ("score_scale_1_over_d", "double c = 1.0 / sqrt((double)d);\n    for (int t = 0; t < T; ++t)",
@@ -57,14 +64,22 @@ MUTANTS = [
     ("softmax_without_exp", "        s[t] = exp(s[t] - m);", "        s[t] = s[t] - m + 1.0;"),
     ("subset_v_index", "            int t = idx[j];", "            int t = j;"),
     ("topk_ties_to_larger", "if (best < 0 || scores[t] > scores[best])", "if (best < 0 || scores[t] >= scores[best])"),
-    ("prefill_not_causal", "        for (int t = 0; t <= i; ++t) {\n            const uint16_t *kt",
-     "        for (int t = 0; t < s; ++t) {\n            const uint16_t *kt"),
-    ("prefill_excludes_self", "        for (int t = 0; t <= i; ++t) {\n            const uint16_t *kt",
-     "        for (int t = 0; t < i; ++t) {\n            const uint16_t *kt"),
-    ("prefill_scale_1_over_d", "    double c = 1.0 / sqrt((double)d);\n    double *p", "    double c = 1.0 / (double)d;\n    double *p"),
+    ("prefill_not_causal", "    for (int t = 0; t <= i; ++t) {\n        const uint16_t *kt",
+     "    for (int t = 0; t < s; ++t) {\n        const uint16_t *kt"),
+    ("prefill_excludes_self", "    for (int t = 0; t <= i; ++t) {\n        const uint16_t *kt",
+     "    for (int t = 0; t < i; ++t) {\n        const uint16_t *kt"),
+    ("prefill_scale_1_over_d", "    double c = 1.0 / sqrt((double)d);\n    const uint16_t *qi",
+     "    double c = 1.0 / (double)d;\n    const uint16_t *qi"),
     ("prefill_v_from_k", "acc += p[t] * (double)oracle_f16_to_f32(v[", "acc += p[t] * (double)oracle_f16_to_f32(k["),
     ("prefill_query_row_0", "const uint16_t *qi = q + (size_t)i * stride;", "const uint16_t *qi = q;"),
-    ("prefill_no_normalisation", "            out[(size_t)i * d + e] = acc / l;", "            out[(size_t)i * d + e] = acc;"),
+    ("prefill_no_normalisation", "        out_row[e] = acc / l;", "        out_row[e] = acc;"),
+    ("prefill_rows_wrong_row", "        prefill_row(d, s, rows[j], stride", "        prefill_row(d, s, j, stride"),
+    ("rows_attend_scale_1_over_d", "    double c = 1.0 / sqrt((double)d);\n    if (T < 1)\n        return;\n    double *p",
+     "    double c = 1.0 / (double)d;\n    if (T < 1)\n        return;\n    double *p"),
+    ("rows_attend_no_exp", "        p[t] = exp(p[t] - m);\n        l += p[t];", "        p[t] = p[t] - m + 1.0;\n        l += p[t];"),
+    ("rows_attend_v_from_k", "acc += p[t] * vhat[(size_t)t * d + i];", "acc += p[t] * khat[(size_t)t * d + i];"),
+    ("rows_attend_no_normalisation", "        out[i] = acc / l;\n    }\n    free(p);\n}\n\n/* ----",
+     "        out[i] = acc;\n    }\n    free(p);\n}\n\n/* ----"),
     ("topk_smallest", "if (best < 0 || scores[t] > scores[best])", "if (best < 0 || scores[t] < scores[best])"),
 ]
 
