@@ -75,7 +75,8 @@ enum {
     KVQ_OK = 0,
     KVQ_EINVAL = -1,        /* null or misaligned pointer, non-positive size, h % a != 0, d % 64 != 0 */
     KVQ_ERANGE = -2,        /* s_len, pos, ctx_len, k_top or num_splits outside its range            */
-    KVQ_EUNSUPPORTED = -3,  /* group != 64, unknown metadata type, d not 64/128/256, context too long  */
+    KVQ_EUNSUPPORTED = -3,  /* group != 64, unknown metadata type, d not 64/128/256, context too long
+                               ((s+n)*d/2 >= 2^31 for any call; see also the prefill and top-k limits) */
     KVQ_ENOSPACE = -4,      /* workspace smaller than kvq_workspace_bytes() asks for                 */
     KVQ_ELAUNCH = -5        /* the HIP runtime refused a launch                                      */
 };
@@ -90,7 +91,14 @@ enum { KVQ_META_F32 = 0, KVQ_META_F16 = 1 };
 
 /* Problem dimensions in the pages' notation: b batch (the effective batch of
  * one launch), a heads, h hidden size (d = h/a per head), s prompt length,
- * n generated tokens; the cache holds S = s + n slots. */
+ * n generated tokens; the cache holds S = s + n slots ("P/D阶段计算" of the
+ * FlexGen blog names b, s, n, h; "KV Cache" the multi-head shape
+ * [b, s, a, h/a]).  Every call checks them: b, a, h, s > 0, n >= 0,
+ * h % a == 0 and d % 64 == 0 (KVQ_EINVAL); group == 64, d in {64, 128, 256}
+ * and a known meta_dtype (KVQ_EUNSUPPORTED); s + n <= 2^30 - 1 and
+ * b * a <= 2^29 - 1 (KVQ_ERANGE); and S * d/2 < 2^31, since the tokens of one
+ * (batch row, head) are addressed with 32-bit byte offsets (KVQ_EUNSUPPORTED:
+ * at most 2^24 slots at d = 256, 2^25 at d = 128, 2^26 at d = 64). */
 typedef struct kvq_dims {
     int32_t b, a, h, s, n;
     int32_t group;      /* must be KVQ_GROUP */
@@ -114,7 +122,10 @@ typedef struct kvq_cache {
 int kvq_cache_bytes(const kvq_dims *dims, size_t *codes_bytes_per_plane, size_t *meta_bytes_per_plane);
 
 /* Prompt phase: quantise the prompt's K and V (fp16 [b][s_len][a][d]) into
- * slots 0..s_len-1 of every (batch row, head).  1 <= s_len <= s+n. */
+ * slots 0..s_len-1 of every (batch row, head).  1 <= s_len <= s+n.
+ * Passage: the FlexGen blog, "预填充阶段" (the prompt's x_K, x_V of shape
+ * b x s x h become the cache), with "FlexGen研究学术报告" 三.2(C) (the cache is
+ * kept group-wise 4-bit, 64 contiguous elements per group). */
 int kv_quantize_prefill(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t s_len,
                         void *hip_stream);
 
@@ -137,7 +148,9 @@ int kv_quantize_prefill_attend(const kvq_cache *cache, const void *q_f16, const 
 /* Decode phase, KV update: quantise the new token's K and V (fp16
  * [b][1][a][d]) into slot `pos` of every (batch row, head), 0 <= pos < s+n.
  * Decode step j (1-based) appends at pos = s+j-1 and then attends over
- * ctx_len = s+j tokens. */
+ * ctx_len = s+j tokens.  Passage: the FlexGen blog, "解码阶段" (x_K <-
+ * Concat(x_K, t W_K) along the sequence axis, the same for x_V), coded as in
+ * "FlexGen研究学术报告" 三.2(C). */
 int kv_append_quant(const kvq_cache *cache, const void *k_f16, const void *v_f16, int32_t pos,
                     void *hip_stream);
 
@@ -151,6 +164,12 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
  * every (batch row, head):
  *     out = softmax(q . K^T / sqrt(d)) . V      (per head; no W_O, no residual)
  * with K, V the dequantised cache.  q and out are fp16 [b][1][a][d].
+ * Passage: the FlexGen blog, "解码阶段" (t_out = softmax(t_Q x_K^T/sqrt(.)) x_V
+ * before W_O), with the 1/sqrt(d_k) of eq. (2) in the efficient-inference
+ * survey notes and the cache dequantised per "FlexGen研究学术报告" 三.2(C).
+ * Query elements that are binary16 subnormals (|q_i| < 2^-14) are taken as
+ * 0: each score then differs from the exact one by at most
+ * 2^-14 * sum_i |k_i| / sqrt(d) over those elements.
  * num_splits: 0 = choose automatically; k > 0 splits each context into at
  * most k ranges (when k > 1, each a whole number of 128-token blocks) handled
  * by separate workgroups and merged by a second pass (log-sum-exp).  ws: device workspace of ws_bytes >= kvq_workspace_bytes()
@@ -179,7 +198,10 @@ int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k
 
 /* Sparse decode attention: for every (batch row, head) score all ctx_len
  * tokens, keep the k_top highest scores (ties to the smaller token index),
- * and take the softmax and P.V over the kept tokens only.
+ * and take the softmax and P.V over the kept tokens only.  Passage:
+ * "FlexGen研究学术报告" 三.2(C), top-10% sparse attention (only the KV entries
+ * with the highest attention values are loaded); scores as in
+ * decode_attention_q4, subnormal query elements taken as 0 as there.
  * 1 <= k_top <= ctx_len <= min(s+n, KVQ_TOPK_MAX_CTX); the pages' rule keeps
  * k_top = ceil(0.1 * ctx_len).  sel_idx (device int32 [b][a][k_top], may be
  * NULL) receives the kept token indices in ascending order.  ws: device

@@ -11,6 +11,7 @@ If ``libkvq4.so`` has not been built, importing works but every call raises
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -134,6 +135,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for the buffers a call creates itself (workspace, out, sel_idx):
+    on the stream its kernels run on, so that the caching allocator ties each block to that
+    stream and never hands it to work on another stream while the kernels may still use it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -222,8 +230,7 @@ def kv_quantize_prefill_attend(cache: QuantKVCache, q: torch.Tensor, k: torch.Te
     s_len = k.shape[1] if k.dim() == 4 else -1
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _act(t, (cache.b, s_len, cache.a, cache.d), name)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out, stream)
     _act(out, q.shape, "out")
     _check(load_library().kv_quantize_prefill_attend(cache.struct_ref(), _ptr(q), _ptr(k), _ptr(v), s_len, _ptr(out),
                                                      _stream(stream)), "kv_quantize_prefill_attend")
@@ -238,21 +245,28 @@ def kv_append_quant(cache: QuantKVCache, k_new: torch.Tensor, v_new: torch.Tenso
            "kv_append_quant")
 
 
-def _workspace(cache, ctx_len, num_splits, ws):
+def _workspace(cache, ctx_len, num_splits, ws, stream):
     need = kvq_workspace_bytes(cache, ctx_len, num_splits)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
-        ws = torch.empty(need // 4, dtype=torch.float32, device=cache.k_codes.device)
+        with _on(stream):
+            ws = torch.empty(need // 4, dtype=torch.float32, device=cache.k_codes.device)
     return ws, need
+
+
+def _out_like(q: torch.Tensor, out, stream):
+    if out is None:
+        with _on(stream):
+            out = torch.empty_like(q)
+    return out
 
 
 def decode_attention_q4(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, out: torch.Tensor | None = None,
                         num_splits: int = 0, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """softmax(q K^T / sqrt(d)) V over slots 0..ctx_len-1; q, out fp16 [b, 1, a, d]."""
     _act(q, (cache.b, 1, cache.a, cache.d), "q")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out, stream)
     _act(out, q.shape, "out")
-    ws, need = _workspace(cache, ctx_len, num_splits, ws)
+    ws, need = _workspace(cache, ctx_len, num_splits, ws, stream)
     _check(load_library().decode_attention_q4(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
                                               _ptr(ws), need, _stream(stream)), "decode_attention_q4")
     return out
@@ -263,10 +277,9 @@ def decode_attention_q4_tuned(cache: QuantKVCache, q: torch.Tensor, ctx_len: int
                               ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """decode_attention_q4 with an explicit kernel launch shape (unroll 1/2/4, waves per pair 1/2/4)."""
     _act(q, (cache.b, 1, cache.a, cache.d), "q")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out, stream)
     _act(out, q.shape, "out")
-    ws, need = _workspace(cache, ctx_len, num_splits, ws)
+    ws, need = _workspace(cache, ctx_len, num_splits, ws, stream)
     _check(load_library().decode_attention_q4_tuned(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
                                                     unroll, waves_per_pair, _ptr(ws), need, _stream(stream)),
            "decode_attention_q4_tuned")
@@ -280,10 +293,9 @@ def kv_append_attend_q4(cache: QuantKVCache, q: torch.Tensor, k_new: torch.Tenso
     slots 0..pos with q.  All fp16 [b, 1, a, d]."""
     for t, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
         _act(t, (cache.b, 1, cache.a, cache.d), name)
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out, stream)
     _act(out, q.shape, "out")
-    ws, need = _workspace(cache, pos + 1, num_splits, ws)
+    ws, need = _workspace(cache, pos + 1, num_splits, ws, stream)
     _check(load_library().kv_append_attend_q4(cache.struct_ref(), _ptr(q), _ptr(k_new), _ptr(v_new), pos, _ptr(out),
                                               num_splits, _ptr(ws), need, _stream(stream)), "kv_append_attend_q4")
     return out
@@ -294,11 +306,11 @@ def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int,
                              ws: torch.Tensor | None = None, stream=None):
     """Top-k sparse decode attention.  Returns (out fp16 [b,1,a,d], sel_idx int32 [b,a,k_top] or None)."""
     _act(q, (cache.b, 1, cache.a, cache.d), "q")
-    if out is None:
-        out = torch.empty_like(q)
+    out = _out_like(q, out, stream)
     _act(out, q.shape, "out")
     if sel_idx is True:
-        sel_idx = torch.empty((cache.b, cache.a, k_top), dtype=torch.int32, device=q.device)
+        with _on(stream):
+            sel_idx = torch.empty((cache.b, cache.a, k_top), dtype=torch.int32, device=q.device)
     elif sel_idx is False:
         sel_idx = None
     if sel_idx is not None and (sel_idx.dtype != torch.int32 or not sel_idx.is_contiguous()
@@ -306,7 +318,8 @@ def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int,
         raise ValueError("sel_idx must be a contiguous int32 tensor of b*a*k_top elements")
     need = kvq_workspace_bytes(cache, ctx_len, 0, k_top)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
-        ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        with _on(stream):
+            ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     _check(load_library().decode_attention_q4_topk(cache.struct_ref(), _ptr(q), ctx_len, k_top, _ptr(out),
                                                    _ptr(sel_idx), _ptr(ws), need, _stream(stream)),
            "decode_attention_q4_topk")
@@ -331,9 +344,10 @@ def kvq_w4_quantize(w: torch.Tensor, stream=None):
     _t16(w, (N, K), "w")
     if N % 64 or K % 128:
         raise ValueError("N must be a multiple of 64 and K of 128")
-    codes = torch.empty((N // 64, K // 128, 64, 64), dtype=torch.uint8, device=w.device)
-    mins = torch.empty((N // 64, K // 128, 64, 2), dtype=torch.float16, device=w.device)
-    scales = torch.empty_like(mins)
+    with _on(stream):
+        codes = torch.empty((N // 64, K // 128, 64, 64), dtype=torch.uint8, device=w.device)
+        mins = torch.empty((N // 64, K // 128, 64, 2), dtype=torch.float16, device=w.device)
+        scales = torch.empty_like(mins)
     _check(load_library().kvq_w4_quantize(_ptr(w), N, K, _ptr(codes), _ptr(mins), _ptr(scales), _stream(stream)),
            "kvq_w4_quantize")
     return codes, mins, scales
@@ -358,11 +372,13 @@ def gemm_w4a16(x: torch.Tensor, codes: torch.Tensor, mins: torch.Tensor, scales:
     _t16(mins, (N // 64, K // 128, 64, 2), "mins")
     _t16(scales, (N // 64, K // 128, 64, 2), "scales")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+        with _on(stream):
+            y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _t16(y, (M, N), "y")
     need = kvq_gemm_w4_workspace_bytes(M, N, K, num_splits)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
-        ws = torch.empty(need // 4, dtype=torch.float32, device=x.device)
+        with _on(stream):
+            ws = torch.empty(need // 4, dtype=torch.float32, device=x.device)
     _check(load_library().gemm_w4a16(_ptr(x), M, N, K, _ptr(codes), _ptr(mins), _ptr(scales), _ptr(y), num_splits,
                                      _ptr(ws), need, _stream(stream)), "gemm_w4a16")
     return y

@@ -37,6 +37,10 @@ int check_dims(const kvq_dims *d)
         return KVQ_ERANGE;
     if ((int64_t)d->b * d->a > INT32_MAX / 4)
         return KVQ_ERANGE;
+    // The attention kernels address the tokens of one (batch row, head) with
+    // 32-bit byte offsets into its code rows: S * d/2 must stay below 2^31.
+    if (((int64_t)d->s + d->n) * (hd / 2) >= ((int64_t)1 << 31))
+        return KVQ_EUNSUPPORTED;
     return KVQ_OK;
 }
 

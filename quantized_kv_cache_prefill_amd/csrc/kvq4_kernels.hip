@@ -44,16 +44,20 @@ __device__ __forceinline__ float ld_meta(const _Float16 *p) { return (float)__bu
 // one instruction each, in two forms:
 //  * keys, for v_dot2_f32_f16 (which flushes binary16 subnormals): OR-ing the
 //    binary16 pattern of 1024 onto a nibble at bits 0..3 gives exactly
-//    1024 + c (the fraction's bit 0 weighs 1 at exponent 10), OR-ing 64 onto a
-//    nibble at bits 4..7 gives 64 + c (bit 4 weighs 1 at exponent 6);
+//    1024 + c (the fraction's bit 0 weighs 1 at exponent 10), and one packed
+//    binary16 subtraction of 1024 leaves c itself (exact); OR-ing 64 onto a
+//    nibble at bits 4..7 gives 64 + c (bit 4 weighs 1 at exponent 6), kept
+//    biased.  The dot's binary32 partial sums then stay near 64 * sum q_odd
+//    + sum q_i c_i: keeping 1024 + c for the even elements made them about
+//    1024 * sum q_even, and with queries and keys of outlier channels (x8)
+//    their rounding alone moved a score by ~1e-3.
 //  * values, for the mixed-precision FMA (which keeps binary16 subnormals):
 //    the masked halves alone are the subnormals c * 2^-24 (bits 0..3) and
 //    c * 2^-20 (bits 4..7), with no bias to remove.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kLoNib = 0x000F000Fu;
 constexpr uint32_t kHiNib = 0x00F000F0u;
-constexpr float kBiasLo = 1024.0f; // keys: bias of e0, e2, e4, e6
-constexpr float kBiasHi = 64.0f;   // keys: bias of e1, e3, e5, e7
+constexpr float kBiasHi = 64.0f;   // keys: bias of e1, e3, e5, e7 (e0, e2, e4, e6 carry none)
 constexpr float kTwo24 = 16777216.0f;
 
 // The OR constants are held in VGPRs (opaque to the compiler) so each key pair
@@ -76,7 +80,13 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c)
 }
 
 // One lane's 32-element slice of q, regrouped into the unpack's pair order,
-// plus its sum (for the group min) and the key bias sum_i q_i * bias_i.
+// plus its sum (for the group min) and the key bias sum_i q_i * bias_i
+// (64 * the sum of the odd elements).
+// v_dot2_f32_f16 flushes binary16 subnormals, so a subnormal query element
+// (|q_i| < 2^-14) is taken as 0 in all three: the score then misses only
+// q_i * k_i for those elements (at most 2^-14 |k_i| each), instead of the
+// bias term q_i * (bias_i + c_i) * scale a flushed dot against an unflushed
+// bias sum would leave in every score.
 struct QSlice {
     uint32_t qp[16];
     float qsum;
@@ -97,13 +107,24 @@ __device__ __forceinline__ QRaw load_q_raw(const uint4 *__restrict__ qrow)
     return r;
 }
 
+// The two binary16 values of a word with every subnormal (exponent field 0)
+// replaced by +0.
+__device__ __forceinline__ uint32_t flush_f16_subnormals(uint32_t w)
+{
+    const uint32_t keep_lo = (w & 0x00007C00u) ? 0x0000FFFFu : 0u;
+    const uint32_t keep_hi = (w & 0x7C000000u) ? 0xFFFF0000u : 0u;
+    return w & (keep_lo | keep_hi);
+}
+
 __device__ __forceinline__ QSlice q_slice(const QRaw &r)
 {
     QSlice s;
     float even = 0.0f, odd = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const uint4 v = r.v[w]; // elements 8w..8w+7: x=(e0,e1) y=(e2,e3) z=(e4,e5) w=(e6,e7)
+        // elements 8w..8w+7: x=(e0,e1) y=(e2,e3) z=(e4,e5) w=(e6,e7)
+        const uint4 v = make_uint4(flush_f16_subnormals(r.v[w].x), flush_f16_subnormals(r.v[w].y),
+                                   flush_f16_subnormals(r.v[w].z), flush_f16_subnormals(r.v[w].w));
         s.qp[4 * w + 0] = (v.x & 0xFFFFu) | (v.z << 16);
         s.qp[4 * w + 1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
         s.qp[4 * w + 2] = (v.y & 0xFFFFu) | (v.w << 16);
@@ -112,21 +133,29 @@ __device__ __forceinline__ QSlice q_slice(const QRaw &r)
         odd += h2f_hi(v.x) + h2f_hi(v.y) + h2f_hi(v.z) + h2f_hi(v.w);
     }
     s.qsum = even + odd;
-    s.qbias = kBiasLo * even + kBiasHi * odd;
+    s.qbias = kBiasHi * odd;
     return s;
 }
 
-// sum_i q_i * (bias_i + c_i) over the lane's 32 elements (key form).
+// (1024 + c0, 1024 + c1) -> (c0, c1), exact, one packed binary16 subtraction.
+__device__ __forceinline__ uint32_t unbias1024(uint32_t k)
+{
+    const f16x2 m = {(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, k) - m);
+}
+
+// sum_i q_i * c_i over the lane's 32 elements: the dot against the key form
+// (c for the even elements, 64 + c for the odd ones) started at -qbias.
 __device__ __forceinline__ float dot_keys(const QSlice &q, const uint4 kx, const Magic mg)
 {
     const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
-    float acc = 0.0f;
+    float acc = -q.qbias;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t y = w[j] >> 8;
-        acc = fdot2(q.qp[4 * j + 0], (w[j] & kLoNib) | mg.lo, acc);
+        acc = fdot2(q.qp[4 * j + 0], unbias1024((w[j] & kLoNib) | mg.lo), acc);
         acc = fdot2(q.qp[4 * j + 1], (w[j] & kHiNib) | mg.hi, acc);
-        acc = fdot2(q.qp[4 * j + 2], (y & kLoNib) | mg.lo, acc);
+        acc = fdot2(q.qp[4 * j + 2], unbias1024((y & kLoNib) | mg.lo), acc);
         acc = fdot2(q.qp[4 * j + 3], (y & kHiNib) | mg.hi, acc);
     }
     return acc;
@@ -339,7 +368,7 @@ __device__ __forceinline__ void attend_kv_rows(const KVRows<UU> &r, const QSlice
     float mx = m;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-        const float dq = dot_keys(qs, r.kx[u], mg) - qs.qbias;
+        const float dq = dot_keys(qs, r.kx[u], mg);
         float sp = __builtin_fmaf(r.ks[u], dq, r.km[u] * qs.qsum);
         sp = token_sum<LPT>(sp);
         z[u] = r.valid[u] ? sp * c2 : -INFINITY;
@@ -781,7 +810,7 @@ __device__ __forceinline__ void store_scores(const KRows<UU> &r, int tb, int t_e
     float zs[UU];
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
-        const float dq = dot_keys(qs, r.kx[u], mg) - qs.qbias;
+        const float dq = dot_keys(qs, r.kx[u], mg);
         const float sp = __builtin_fmaf(r.ks[u], dq, r.km[u] * qs.qsum);
         zs[u] = token_sum<LPT>(sp) * c2;
     }

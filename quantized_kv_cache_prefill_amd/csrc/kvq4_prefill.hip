@@ -95,15 +95,19 @@ struct PrefillArgs {
     float slack;    // raw-score growth allowed before the accumulators are rescaled: 8 / c2
 };
 
-// The prompt tensors are read through buffer resources: a 32-bit byte offset
-// per lane, fixed for the kernel, plus a scalar offset that steps by one key
-// tile; reads past the end of the tensor return zero.
+// The prompt tensors are read through buffer resources whose size is the
+// launch's bytes of q, k or v.  Every offset, the key-tile step included, is
+// passed in the lane's 32-bit VGPR offset: the hardware range check covers
+// that offset (not the scalar offset), so a read at or past the end of the
+// tensor returns zeros instead of the memory behind it.  That happens for
+// the rows of the last key tile past the prompt in the launch's last batch
+// row; those keys are masked (p = 0), and zeros keep 0 * V finite.
 typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 // 16 bytes per lane, HBM -> LDS: lane l's bytes land at dst + 16 l.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, _Float16 *dst, int voff, int soff)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, _Float16 *dst, int voff)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, voff, 0, 0, 0);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
 {
@@ -113,16 +117,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
 // One tile of K and V, HBM -> LDS.  Wave w's u-th load fills 1 KB block
 // B = 4u + w of each buffer: lane l writes chunk position 64B + l, i.e. row
 // (64B + l) / (D/8), swizzled chunk (64B + l) % (D/8); vk/vv hold the byte
-// offsets of the unswizzled chunks that belong there.
+// offsets (tile 0) of the unswizzled chunks that belong there, `step` the
+// byte offset of this tile.
 template <int D>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const int *vk,
-                                           const int *vv, int soff, _Float16 *lk, _Float16 *lv, int wave)
+                                           const int *vv, int step, _Float16 *lk, _Float16 *lv, int wave)
 {
 #pragma unroll
     for (int u = 0; u < Shape<D>::NK; ++u) {
         const int blk = 4 * u + wave;
-        dma16(rk, lk + 512 * blk, vk[u], soff);
-        dma16(rv, lv + 512 * blk, vv[u], soff);
+        dma16(rk, lk + 512 * blk, vk[u] + step);
+        dma16(rv, lv + 512 * blk, vv[u] + step);
     }
 }
 
@@ -217,8 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
             const int blk = 4 * u + wave;
             const int pos = 64 * blk + lane;
             const int r = pos / (D / 8), cs = pos % (D / 8);
-            dma16(rq, lds + Sh::LDS_K + Sh::LDS_V + 512 * blk, head0 + (q0 + r) * row_bytes + 16 * (cs ^ Sh::swz_k(r)),
-                  0);
+            dma16(rq, lds + Sh::LDS_K + Sh::LDS_V + 512 * blk, head0 + (q0 + r) * row_bytes + 16 * (cs ^ Sh::swz_k(r)));
         }
     }
     // Byte offsets (tile 0) of the chunks this lane moves into LDS.

@@ -79,13 +79,17 @@ class HostCache:
         self.vsc = np.zeros((b, a, S, G), mt)
 
     def prefill(self, k: np.ndarray, v: np.ndarray, pairs=None):
-        """k, v: [b][s][a][d] fp16 bits.  pairs: optional list of (bi, ai) to quantise only."""
+        """k, v: [b][s][a][d] fp16 bits.  pairs: optional list of (bi, ai) to quantise only.
+        Without pairs every batch row is quantised, batch rows spread over a thread pool."""
         s = k.shape[1]
         if pairs is None:
-            kc, km, ks = oracle_planes_from_prompt(k, self.meta)
-            vc, vm, vs = oracle_planes_from_prompt(v, self.meta)
-            self.kc[:, :, :s], self.kmin[:, :, :s], self.ksc[:, :, :s] = kc, km, ks
-            self.vc[:, :, :s], self.vmin[:, :, :s], self.vsc[:, :, :s] = vc, vm, vs
+            def one(bi):
+                kc, km, ks = oracle_planes_from_prompt(k[bi:bi + 1], self.meta)
+                vc, vm, vs = oracle_planes_from_prompt(v[bi:bi + 1], self.meta)
+                self.kc[bi, :, :s], self.kmin[bi, :, :s], self.ksc[bi, :, :s] = kc[0], km[0], ks[0]
+                self.vc[bi, :, :s], self.vmin[bi, :, :s], self.vsc[bi, :, :s] = vc[0], vm[0], vs[0]
+            with _pool() as ex:
+                list(ex.map(one, range(k.shape[0])))
         else:
             for bi, ai in pairs:
                 c, m, sc = QUANTIZE[self.meta](np.ascontiguousarray(k[bi, :, ai]))
@@ -115,6 +119,20 @@ def oracle_attend_pairs(hc: HostCache, q: np.ndarray, T: int, pairs) -> np.ndarr
         outs = list(ex.map(lambda p: oracle.attend(np.ascontiguousarray(q[p[0], 0, p[1]]), hc.head(p[0], p[1], T), T),
                            pairs))
     return np.stack(outs)
+
+
+def oracle_attend_pairs_f16form(hc: HostCache, q: np.ndarray, T: int, pairs) -> np.ndarray:
+    """The same pairs against attention over the FP16 form of the dequantised cache (every
+    dequantised element rounded to binary16 before compute, as the report writes it)."""
+    with _pool() as ex:
+        outs = list(ex.map(lambda p: oracle.attend_f16form(np.ascontiguousarray(q[p[0], 0, p[1]]),
+                                                           hc.head(p[0], p[1], T), T), pairs))
+    return np.stack(outs)
+
+
+def tolerance_ratio(gpu_rows: np.ndarray, ref_rows: np.ndarray) -> float:
+    """max |gpu - ref| / (ATOL + RTOL |ref|): <= 1 is inside the bar."""
+    return float(np.max(np.abs(gpu_rows.astype(np.float64) - ref_rows) / (ATOL + RTOL * np.abs(ref_rows))))
 
 
 def assert_close(gpu_rows: np.ndarray, ref_rows: np.ndarray, what: str):

@@ -90,6 +90,39 @@ def test_bad_dims(L, mut, status):
     assert L.kvq_workspace_bytes(ctypes.byref(d), 4, 0, 0) == 0
 
 
+@pytest.mark.parametrize("h,a,S,ok", [
+    (256, 1, (1 << 24) - 1, True), (256, 1, 1 << 24, False),       # d = 256: S * 128 < 2^31
+    (128, 1, (1 << 25) - 1, True), (128, 1, 1 << 25, False),       # d = 128: S * 64 < 2^31
+    (64, 1, (1 << 26) - 1, True), (64, 1, 1 << 26, False),         # d = 64: S * 32 < 2^31
+    (12288, 96, 1 << 25, False), (12288, 96, 544, True),
+])
+def test_slot_offsets_fit_31_bits(L, h, a, S, ok):
+    """The attention kernels address one (batch row, head)'s code rows with 32-bit byte
+    offsets: a cache with S * d/2 >= 2^31 is refused by every call (KVQ_EUNSUPPORTED), before
+    anything is enqueued, for every call that takes a cache and for the sizing calls."""
+    d = dims(b=1, a=a, h=h, s=S - 1, n=1)
+    cb = ctypes.c_size_t()
+    want = KVQ_OK if ok else KVQ_EUNSUPPORTED
+    assert L.kvq_cache_bytes(ctypes.byref(d), ctypes.byref(cb), None) == want
+    if ok:
+        assert cb.value == S * (h // a) // 2 * a
+        return
+    c = cache(d)
+    st = ctypes.c_void_p(0)
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 4, 0, 0) == 0
+    assert L.kv_quantize_prefill(ctypes.byref(c), FAKE, FAKE, 4, st) == KVQ_EUNSUPPORTED
+    assert L.kv_quantize_prefill_attend(ctypes.byref(c), FAKE, FAKE, FAKE, 4, FAKE, st) == KVQ_EUNSUPPORTED
+    assert L.kv_append_quant(ctypes.byref(c), FAKE, FAKE, S - 1, st) == KVQ_EUNSUPPORTED
+    assert L.decode_attention_q4(ctypes.byref(c), FAKE, S, FAKE, 0, FAKE, 1 << 30, st) == KVQ_EUNSUPPORTED
+    assert L.decode_attention_q4_tuned(ctypes.byref(c), FAKE, S, FAKE, 0, 4, 2, FAKE, 1 << 30, st) == KVQ_EUNSUPPORTED
+    assert L.kv_append_attend_q4(ctypes.byref(c), FAKE, FAKE, FAKE, S - 1, FAKE, 0, FAKE, 1 << 30,
+                                 st) == KVQ_EUNSUPPORTED
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 4, 1, FAKE, None, FAKE, 1 << 30,
+                                      st) == KVQ_EUNSUPPORTED
+    assert L.kv_quantize_prefill_host(ctypes.byref(c), FAKE, FAKE, 4, 1) == KVQ_EUNSUPPORTED
+    assert L.decode_attention_q4_host(ctypes.byref(c), FAKE, 4, FAKE, 1) == KVQ_EUNSUPPORTED
+
+
 def test_null_and_misaligned_pointers(L):
     st = ctypes.c_void_p(0)
     assert L.kv_quantize_prefill(None, FAKE, FAKE, 4, st) == KVQ_EINVAL

@@ -39,7 +39,8 @@ def test_m16_opt_6_7b_layer_full():
 @pytest.mark.timeout(600)
 def test_m16_opt_30b_layer_sampled():
     """b=256, a=56, d=128 with 1% outlier channels x8: appended rows in full, sampled pairs."""
-    run_decode_workload(W.OPT_30B, full_planes=False, attend_pairs_full_steps=(), sample_n=96, meta=META)
+    run_decode_workload(W.OPT_30B, full_planes=False, attend_pairs_full_steps=(), sample_n=96, meta=META,
+                        f16form=False)
 
 
 @pytest.mark.timeout(600)

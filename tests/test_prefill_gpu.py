@@ -189,3 +189,104 @@ def test_prefill_opt175b_layer_sampled():
 def test_prefill_opt30b_layer_sampled_m16():
     """OPT-30B (b=256, a=56) with its outlier channels, binary16 planes: sampled pairs."""
     _layer_sampled(W.OPT_30B, "f16", 48, 92)
+
+
+def _padded(shape, seed, slack_rows, std=1.0):
+    """An fp16 tensor of `shape` at the front of a larger allocation whose remaining
+    slack_rows token rows (a*d halves each) hold 0xFFFF, a binary16 NaN: any read past the
+    tensor that reached the kernel's arithmetic would turn its outputs into NaN."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + slack_rows * shape[2] * shape[3],), -1, dtype=torch.int16, device=DEV)
+    x = buf[:n].view(torch.float16).view(shape)
+    x.copy_(W.random_fp16(shape, seed, DEV, std))
+    return x, buf
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("s_len", [100, 300])
+def test_prefill_reads_nothing_past_the_prompt(d, s_len):
+    """The last key tile of the last batch row reaches up to 63 token rows past the end of k
+    and v.  With q, k and v at the front of allocations whose next 128 rows are NaN, every
+    output stays finite and equals the oracle, and every plane is bit-exact: the rows past
+    the prompt are read as zeros, not as the memory behind the tensors."""
+    require_gpu()
+    b, a = 3, 4
+    shape = (b, s_len, a, d)
+    seed = 7600 + d + s_len
+    q, qb = _padded(shape, seed, 128)
+    k, kb = _padded(shape, seed + 1, 128)
+    v, vb = _padded(shape, seed + 2, 128)
+    cache = kvq.QuantKVCache(b, a, a * d, s_len, 0, device=DEV, fill=0xFF)
+    out = torch.full_like(q, float("nan"))
+    kvq.kv_quantize_prefill_attend(cache, q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    hc = HostCache(b, a, d, s_len)
+    hc.prefill(f16_np(k), f16_np(v))
+    _check_prefill_full(cache, hc, s_len, f"prefill padded d={d} s={s_len}")
+    pairs = [(bi, ai) for bi in range(b) for ai in range(a)]
+    ref = _oracle_rows(f16_np(q), f16_np(k), f16_np(v), pairs)
+    assert_close(_gpu_pairs(out, pairs), ref, f"prefill padded d={d} s={s_len}")
+
+
+@pytest.mark.parametrize("mode", ["all", "mixed"])
+def test_prefill_subnormal_queries(mode):
+    """Prompt queries holding binary16 subnormals (all of them, or about 10% mixed into
+    N(0,1)): outputs against the oracle, which widens them exactly."""
+    require_gpu()
+    b, a, d, s_len = 2, 3, 128, 200
+    r = np.random.default_rng(7700 + (mode == "all"))
+    if mode == "all":
+        qn = r.standard_normal((b, s_len, a, d)) * 1e-5
+    else:
+        qn = r.standard_normal((b, s_len, a, d))
+        m = r.random(qn.shape) < 0.1
+        qn[m] = r.standard_normal(int(m.sum())) * 2e-6
+    q = torch.from_numpy(qn.astype(np.float16)).to(DEV)
+    k = W.random_fp16((b, s_len, a, d), 7701, DEV)
+    v = W.random_fp16((b, s_len, a, d), 7702, DEV)
+    cache = kvq.QuantKVCache(b, a, a * d, s_len, 0, device=DEV, fill=0xFF)
+    out = kvq.kv_quantize_prefill_attend(cache, q, k, v)
+    torch.cuda.synchronize()
+    pairs = [(bi, ai) for bi in range(b) for ai in range(a)]
+    ref = _oracle_rows(f16_np(q), f16_np(k), f16_np(v), pairs)
+    assert_close(_gpu_pairs(out, pairs), ref, f"prefill subnormal q ({mode})")
+
+
+# query rows at the edges of the key tiles (64), the query tiles (128) and the prompt
+PREFILL_ROWS = np.array([0, 1, 62, 63, 64, 65, 127, 128, 129, 191, 255, 256, 300, 383, 384, 447, 510, 511], np.int32)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_opt175b_layer_all_pairs():
+    """The OPT-175B layer (b=144, a=96, d=128, prompt 512) in the launch the benchmark times:
+    all 13,824 (batch row, head) pairs at the query rows on every tile edge, against the
+    oracle's causal attention at those rows; every prompt plane bit-exact."""
+    require_gpu()
+    w = W.OPT_175B
+    log(f"[{w.name} prefill] b={w.b} a={w.a} d={w.d} s={w.s}: all pairs at {PREFILL_ROWS.size} rows")
+    q = W.prefill_q(w, 0, DEV)
+    k, v = W.prefill_kv(w, 0, DEV)
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=DEV, fill=0xFF)
+    out = kvq.kv_quantize_prefill_attend(cache, q, k, v)
+    torch.cuda.synchronize()
+    qh, kh, vh = f16_np(q), f16_np(k), f16_np(v)
+    del q, k, v
+    hc = HostCache(w.b, w.a, w.d, w.S)
+    hc.prefill(kh, vh)
+    _check_prefill_full(cache, hc, w.s, f"{w.name} prefill")
+    del hc
+    rows_t = torch.from_numpy(PREFILL_ROWS.astype(np.int64)).to(DEV)
+    got = out.index_select(1, rows_t).float().cpu().numpy()           # [b][rows][a][d]
+    del out
+    pairs = [(bi, ai) for bi in range(w.b) for ai in range(w.a)]
+
+    def one(p):
+        bi, ai = p
+        return oracle.prefill_attend_rows(qh[bi, :, ai], kh[bi, :, ai], vh[bi, :, ai], PREFILL_ROWS)
+    with _pool() as ex:
+        ref = np.stack(list(ex.map(one, pairs)))                        # [pairs][rows][d]
+    gpu = np.stack([got[bi, :, ai] for bi, ai in pairs])
+    err = assert_close(gpu, ref, f"{w.name} prefill attention, all pairs")
+    log(f"[{w.name} prefill] {len(pairs)} pairs x {PREFILL_ROWS.size} rows ok, planes bit-exact, "
+        f"max abs err {err:.2e}")
