@@ -185,6 +185,25 @@ int decode_attention_q4_tuned(const kvq_cache *cache, const void *q_f16, int32_t
                               int32_t num_splits, int32_t unroll, int32_t waves_per_pair, void *ws,
                               size_t ws_bytes, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * decode_attention_q4 with the split partials kept in a library-owned
+ * static device array of KVQ_NOALLOC_SCRATCH_BYTES instead of a caller
+ * workspace.  Same kernels, split choice and results as
+ * decode_attention_q4(cache, q, ctx_len, out, num_splits, ...), bit for bit.
+ * The call allocates and frees nothing; the array's device address is looked
+ * up on the first call on each device (hipGetSymbolAddress) and each GPU
+ * keeps its copy until the process ends.  KVQ_ENOSPACE (before anything is
+ * enqueued) when the launch needs more than KVQ_NOALLOC_SCRATCH_BYTES, i.e.
+ * kvq_workspace_bytes(dims, ctx_len, num_splits, 0) exceeds it: pass a
+ * smaller num_splits.  KVQ_ELAUNCH when the address cannot be obtained.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time (on different streams of one GPU) race and must be ordered by the
+ * caller; calls on one stream are ordered. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int decode_attention_q4_noalloc(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                                int32_t num_splits, void *hip_stream);
+
 /* One decode step in one launch: kv_append_quant(cache, k_new, v_new, pos)
  * followed by decode_attention_q4(cache, q, pos + 1, out, num_splits, ...),
  * the blog's "解码阶段" order (concatenate the new token's K/V, then attend

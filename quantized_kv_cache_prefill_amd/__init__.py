@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "KvqError", "QuantKVCache", "kvq_cache_bytes", "kvq_workspace_bytes", "kv_quantize_prefill",
     "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4",
-    "decode_attention_q4_topk", "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16",
+    "decode_attention_q4_topk", "decode_attention_q4_noalloc", "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16",
     "kv_quantize_prefill_host", "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd",
     "kvq_host_use_simd",
     "library_path", "load_library", "GROUP",
@@ -38,6 +38,7 @@ _LIB_PATH = os.path.join(_HERE, "libkvq4.so")
 
 EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_quantize_prefill_attend", "kv_append_quant", "kvq_workspace_bytes",
             "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4", "decode_attention_q4_topk",
+            "decode_attention_q4_noalloc",
             "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kv_quantize_prefill_host",
             "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd", "kvq_host_use_simd", "kvq_strerror")
 
@@ -93,6 +94,8 @@ def load_library() -> ctypes.CDLL:
     L.decode_attention_q4_tuned.restype = ctypes.c_int
     L.kv_append_attend_q4.argtypes = [PC, P, P, P, I32, P, I32, P, SZ, P]
     L.kv_append_attend_q4.restype = ctypes.c_int
+    L.decode_attention_q4_noalloc.argtypes = [PC, P, I32, P, I32, P]
+    L.decode_attention_q4_noalloc.restype = ctypes.c_int
     L.decode_attention_q4_topk.argtypes = [PC, P, I32, I32, P, P, P, SZ, P]
     L.decode_attention_q4_topk.restype = ctypes.c_int
     L.kvq_w4_quantize.argtypes = [P, I32, I32, P, P, P, P]
@@ -283,6 +286,22 @@ def decode_attention_q4_tuned(cache: QuantKVCache, q: torch.Tensor, ctx_len: int
     _check(load_library().decode_attention_q4_tuned(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
                                                     unroll, waves_per_pair, _ptr(ws), need, _stream(stream)),
            "decode_attention_q4_tuned")
+    return out
+
+
+KVQ_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_attention_q4_noalloc(cache: QuantKVCache, q: torch.Tensor, ctx_len: int, out: torch.Tensor,
+                                num_splits: int = 0, stream=None) -> torch.Tensor:
+    """decode_attention_q4 with its split partials in the library's static device workspace:
+    nothing is allocated, here or in the library; the caller passes `out`.  Raises KvqError
+    (KVQ_ENOSPACE) when the launch needs more than KVQ_NOALLOC_SCRATCH_BYTES of partials.
+    Calls that may overlap on one GPU race on that workspace."""
+    _act(q, (cache.b, 1, cache.a, cache.d), "q")
+    _act(out, q.shape, "out")
+    _check(load_library().decode_attention_q4_noalloc(cache.struct_ref(), _ptr(q), ctx_len, _ptr(out), num_splits,
+                                                      _stream(stream)), "decode_attention_q4_noalloc")
     return out
 
 

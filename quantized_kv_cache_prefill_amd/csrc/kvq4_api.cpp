@@ -282,9 +282,11 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
 
 namespace {
 
+// use_scratch: the split partials go to the library's static device
+// workspace (decode_attention_q4_noalloc) instead of the caller's ws.
 int decode_common(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16, int32_t num_splits,
                   int32_t unroll, int32_t waves_per_pair, void *ws, size_t ws_bytes, const void *k_new,
-                  const void *v_new, void *hip_stream)
+                  const void *v_new, void *hip_stream, bool use_scratch = false)
 {
     kvq::CachePlanes c;
     int st = check_cache(cache, &c);
@@ -309,8 +311,19 @@ int decode_common(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, vo
                         : (sh.splits == 1 && ctx_len >= kLongCtxFourWaves) ? 4
                                                                            : kDefaultWavesPerPair;
     const size_t need = kvq::decode_ws_floats(pairs, c.d, sh.splits) * sizeof(float);
-    if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need))
+    if (use_scratch) {
+        if (need > KVQ_NOALLOC_SCRATCH_BYTES)
+            return KVQ_ENOSPACE;
+        ws = nullptr;
+        if (need > 0) {
+            float *p = nullptr;
+            if (kvq::noalloc_scratch(static_cast<hipStream_t>(hip_stream), &p) != 0)
+                return KVQ_ELAUNCH;
+            ws = p;
+        }
+    } else if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) {
         return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
+    }
     return status_of(kvq::launch_decode(c, pairs, q_f16, ctx_len, out_f16, sh, static_cast<float *>(ws), k_new,
                                         v_new, static_cast<hipStream_t>(hip_stream)));
 }
@@ -334,6 +347,13 @@ int decode_attention_q4(const kvq_cache *cache, const void *q_f16, int32_t ctx_l
 {
     return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll, kAutoWavesPerPair, ws,
                          ws_bytes, nullptr, nullptr, hip_stream);
+}
+
+int decode_attention_q4_noalloc(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, void *out_f16,
+                                int32_t num_splits, void *hip_stream)
+{
+    return decode_common(cache, q_f16, ctx_len, out_f16, num_splits, kDefaultUnroll, kAutoWavesPerPair, nullptr, 0,
+                         nullptr, nullptr, hip_stream, true);
 }
 
 int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k_f16, const void *v_f16,

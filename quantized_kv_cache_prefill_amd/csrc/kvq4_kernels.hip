@@ -23,9 +23,20 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
+#include "kvq4.h"
 #include "kvq4_device.h"
 #include "kvq4_launch.h"
+
+// The workspace of decode_attention_q4_noalloc: the split partials (max, sum
+// and unnormalised output per split and (batch row, head)) live in this
+// library-owned device array instead of a caller buffer.  Each GPU the
+// library runs on holds its own copy (KVQ_NOALLOC_SCRATCH_BYTES) until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device address: host code uses only the per-device address that
+// noalloc_scratch() obtains from the runtime.
+static __device__ __align__(256) float scratch[KVQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace kvq {
 namespace {
@@ -1548,6 +1559,43 @@ int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *o
 {
     return c.meta_f16 ? launch_decode_m<_Float16>(c, pairs, q, T, out, sh, ws, k_new, v_new, st)
                       : launch_decode_m<float>(c, pairs, q, T, out, sh, ws, k_new, v_new, st);
+}
+
+// Device address of `scratch` on the device `st` belongs to (the current
+// device for the null stream), looked up once per device with that device
+// current and kept for the life of the process.  Returns a hipError_t.
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static float *g_scratch_ptr[kMaxScratchDevices] = {};
+
+int noalloc_scratch(hipStream_t st, float **ptr)
+{
+    int dev = -1;
+    hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return (int)e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return (int)e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return (int)e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess)
+            return (int)e;
+        if (e2 != hipSuccess)
+            return (int)e2;
+        if (p == nullptr)
+            return (int)hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return 0;
 }
 
 size_t decode_ws_floats(int pairs, int d, int splits)

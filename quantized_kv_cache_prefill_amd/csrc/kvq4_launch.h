@@ -47,6 +47,11 @@ int launch_decode(const CachePlanes &c, int pairs, const void *q, int T, void *o
 // Workspace floats needed by launch_decode for `splits` > 1.
 size_t decode_ws_floats(int pairs, int d, int splits);
 
+// Device address (on the device of stream st) of the library's static
+// workspace of KVQ_NOALLOC_SCRATCH_BYTES; looked up once per device, never
+// allocated.  Returns a hipError_t cast to int.
+int noalloc_scratch(hipStream_t st, float **ptr);
+
 // Top-k sparse decode attention: a streaming score pass into ws (one float
 // per (pair, token)), then one workgroup per (batch row, head) for the
 // selection and the gathered P.V.

@@ -268,3 +268,21 @@ def test_gemm_w4_validation_and_workspace(L):
     # a split count that leaves an empty split is reduced: 96 chunks in 7 splits -> 14 per split, 7 splits
     assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 7) == 7 * 64 * 4
     assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 95) == 48 * 64 * 4  # ceil(96/95)=2 chunks each -> 48 splits
+
+
+def test_noalloc_refusals_before_any_launch(L):
+    """decode_attention_q4_noalloc checks everything on the host first: bad dimensions and
+    ranges as decode_attention_q4 does, and a launch whose split partials exceed the static
+    workspace (KVQ_NOALLOC_SCRATCH_BYTES) is KVQ_ENOSPACE -- no device is touched."""
+    st = ctypes.c_void_p(0)
+    big = cache(dims(b=64, a=32, h=32 * 256, s=8192, n=0))
+    d = big.dims
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 8192, 256, 0) > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert L.decode_attention_q4_noalloc(ctypes.byref(big), FAKE, 8192, FAKE, 256, st) == KVQ_ENOSPACE
+    c = cache()
+    assert L.decode_attention_q4_noalloc(ctypes.byref(c), FAKE, 0, FAKE, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4_noalloc(ctypes.byref(c), FAKE, 21, FAKE, 0, st) == KVQ_ERANGE
+    assert L.decode_attention_q4_noalloc(ctypes.byref(c), FAKE, 4, FAKE, 257, st) == KVQ_ERANGE
+    assert L.decode_attention_q4_noalloc(ctypes.byref(c), None, 4, FAKE, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_noalloc(ctypes.byref(c), FAKE, 4, FAKE + 2, 0, st) == KVQ_EINVAL
+    assert L.decode_attention_q4_noalloc(None, FAKE, 4, FAKE, 0, st) == KVQ_EINVAL
