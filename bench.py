@@ -93,45 +93,38 @@ def stored_traffic():
 
 # ------------------------------------------------------------------- GPU job
 class Job:
-    def __init__(self, args):
+    """One layer stack of workload `w`: L int4 caches resident in HBM, the prompt of every
+    layer quantised, then n decode steps, each appending the new token's K/V and attending
+    over s+j tokens in every layer (append + decode_attention_q4, or the fused launch)."""
+
+    def __init__(self, w, L, n, meta="f32", fused=False):
         import torch
 
         import quantized_kv_cache_prefill_amd as kvq
         import workloads as W
 
         self.torch, self.kvq, self.W = torch, kvq, W
-        w = self.w = W.OPT_175B
-        self.L = args.layers or w.layers
-        self.n = args.decode_steps or w.n
-        self.meta = args.meta
-        mb = META_BYTES[self.meta]
+        self.w, self.L, self.n, self.meta, self.fused = w, L, n, meta, fused
+        mb = META_BYTES[meta]
         dev = self.dev = "cuda"
         torch.cuda.set_device(0)
-        log(f"[bench] allocating {self.L} int4 caches of b={w.b} a={w.a} d={w.d} S={w.S}, {self.meta} min/scale")
-        self.caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=dev, meta=self.meta) for _ in range(self.L)]
-        # prompt K/V: a few distinct seeded buffers used in rotation (one layer's prompt is 3.6 GB)
-        self.n_prompt = min(4, self.L)
+        log(f"[bench] {w.name}: allocating {L} int4 caches of b={w.b} a={w.a} d={w.d} S={w.S}, {meta} min/scale")
+        self.caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device=dev, meta=meta) for _ in range(L)]
+        # prompt K/V: a few distinct seeded buffers used in rotation (an OPT-175B layer's prompt is 3.6 GB)
+        self.n_prompt = min(4, L)
         self.prompts = [W.prefill_kv(w, l, dev) for l in range(self.n_prompt)]
-        # decode inputs for every (layer, step): q, k_new, v_new [b][1][a][d]
-        log(f"[bench] generating decode inputs for {self.L} layers x {self.n} steps")
-        self.dec = []
-        for l in range(self.L):
-            per = []
-            for j in range(1, self.n + 1):
-                per.append(W.decode_inputs(w, l, j, dev))
-            self.dec.append(per)
-        self.out = torch.empty((self.L, w.b, 1, w.a, w.d), dtype=torch.float16, device=dev)
+        log(f"[bench] {w.name}: generating decode inputs for {L} layers x {n} steps")
+        self.dec = [[W.decode_inputs(w, l, j, dev) for j in range(1, n + 1)] for l in range(L)]
+        self.out = torch.empty((L, w.b, 1, w.a, w.d), dtype=torch.float16, device=dev)
         self.stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
-        # algorithmic bytes of one step
         pairs = w.b * w.a
-        self.b_prefill = 2 * self.L * bytes_quantize(w.b * w.a * w.s, w.d, mb)
-        self.b_append = 0 if args.fused else 2 * self.L * self.n * bytes_quantize(pairs, w.d, mb)
-        self.fused = args.fused
-        self.b_decode_per_launch = [bytes_decode(pairs, w.s + j, w.d, mb) for j in range(1, self.n + 1)]
-        if self.fused:  # the timed launch also quantises and writes the new K/V rows
+        self.b_prefill = 2 * L * bytes_quantize(w.b * w.a * w.s, w.d, mb)
+        self.b_append = 0 if fused else 2 * L * n * bytes_quantize(pairs, w.d, mb)
+        self.b_decode_per_launch = [bytes_decode(pairs, w.s + j, w.d, mb) for j in range(1, n + 1)]
+        if fused:  # the timed launch also quantises and writes the new K/V rows
             self.b_decode_per_launch = [x + 2 * bytes_quantize(pairs, w.d, mb) for x in self.b_decode_per_launch]
-        self.b_decode = self.L * sum(self.b_decode_per_launch)
+        self.b_decode = L * sum(self.b_decode_per_launch)
         self.b_step = self.b_prefill + self.b_append + self.b_decode
 
     def step(self, events=None):
@@ -154,6 +147,125 @@ class Job:
                 if events is not None:
                     e1.record(self.stream)
                     events.append((e0, e1, self.b_decode_per_launch[j - 1]))
+
+    def run(self, steps, warmup):
+        """warmup untimed steps, then `steps` timed ones; returns (wall ms per step, decode events)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(events)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps, events
+
+    def summary(self, ms_step, events, steps):
+        w = self.w
+        dec_ms = [a.elapsed_time(b) for a, b, _ in events]
+        dec_bytes = [nb for _, _, nb in events]
+        avg_ms = sum(dec_ms) / len(dec_ms)
+        achieved = (sum(dec_bytes) / len(dec_bytes)) / avg_ms / 1e6
+        srt = sorted(dec_ms)
+        return {"ms_per_step": round(ms_step, 2), "step_gbs": round(self.b_step / (ms_step / 1e3) / 1e9, 1),
+                "decode_attention": {
+                    "gbs": round(achieved, 1), "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+                    "layer_tokens_per_s": round(w.b / (avg_ms / 1e3), 1),
+                    "stack_tokens_per_s": round(w.b * self.n / (sum(dec_ms) / steps / 1e3), 1),
+                    "launch_ms": {"min": round(srt[0], 5), "median": round(srt[len(srt) // 2], 5),
+                                  "p90": round(srt[int(0.9 * (len(srt) - 1))], 5), "max": round(srt[-1], 5),
+                                  "mean": round(avg_ms, 5), "launches": len(srt)}},
+                "avg_launch_ms": avg_ms, "achieved_gbs": achieved,
+                "algorithmic_bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes))}
+
+
+def time_stack(w, steps=2, warmup=1):
+    """The whole stack job of workload `w` (all its layers resident), as the headline job."""
+    import torch
+    job = Job(w, w.layers, w.n)
+    ms, ev = job.run(steps, warmup)
+    res = job.summary(ms, ev, steps)
+    res.pop("avg_launch_ms"), res.pop("achieved_gbs")
+    res["workload"] = (f"{w.name} layer stack: b={w.b} a={w.a} d={w.d} h={w.h}, prompt {w.s}, {w.n} decode steps, "
+                       f"{w.layers} int4 caches resident ({job.L * job.caches[0].nbytes() / 1e9:.1f} GB)")
+    res["steps"], res["warmup"] = steps, warmup
+    del job
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_cache_warm_layer(w, reps=60):
+    """One layer of workload `w` at its final context, attended `reps` times in a row: the
+    layer's cache (89 MB for OPT-6.7B) stays in the 256 MB Infinity Cache, so this is a
+    cache-warm rate, not an HBM one."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    T = w.S
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda")
+    k, v = W.prefill_kv(w, 0, "cuda", s_len=T)
+    kvq.kv_quantize_prefill(cache, k, v)
+    del k, v
+    q = W.decode_inputs(w, 0, 1, "cuda")[0]
+    out = torch.empty_like(q)
+    st = torch.cuda.current_stream()
+    ev = []
+    for _ in range(reps + 5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        kvq.decode_attention_q4(cache, q, T, out=out)
+        e1.record(st)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev[5:])
+    med = ms[len(ms) // 2]
+    nb = bytes_decode(w.b * w.a, T, w.d)
+    return {"workload": f"{w.name} single layer: b={w.b} a={w.a} d={w.d} context {T}, the same cache {reps} times "
+                        f"(cache-warm: it fits the Infinity Cache)",
+            "ms_per_call_median": round(med, 5), "algorithmic_bytes": nb, "gbs": round(nb / med / 1e6, 1),
+            "layer_tokens_per_s": round(w.b / (med / 1e3), 1)}
+
+
+def time_tiny_latency(reps=200):
+    """Latency of one decode layer-step on the tiny configuration (b=2, a=2, d=64, prompt 16,
+    context 17..20): append + attention (two launches), attention alone, and the fused launch;
+    medians of HIP events around each, launch overhead included."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    w = W.TINY
+    cache = kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda")
+    k, v = W.prefill_kv(w, 0, "cuda")
+    kvq.kv_quantize_prefill(cache, k, v)
+    inputs = [W.decode_inputs(w, 0, j, "cuda") for j in range(1, w.n + 1)]
+    out = torch.empty_like(inputs[0][0])
+    st = torch.cuda.current_stream()
+    res = {}
+    for label in ("append_then_attend", "attend_only", "fused"):
+        ev = []
+        for r in range(reps + 10):
+            j = r % w.n + 1
+            q, kn, vn = inputs[j - 1]
+            pos = w.s + j - 1
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            if label == "fused":
+                kvq.kv_append_attend_q4(cache, q, kn, vn, pos, out=out)
+            else:
+                if label == "append_then_attend":
+                    kvq.kv_append_quant(cache, kn, vn, pos)
+                kvq.decode_attention_q4(cache, q, pos + 1, out=out)
+            e1.record(st)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev[10:])
+        res[label] = {"us_median": round(us[len(us) // 2], 2), "us_min": round(us[0], 2)}
+    res["workload"] = f"tiny: b={w.b} a={w.a} d={w.d}, prompt {w.s}, contexts {w.s + 1}..{w.S}, one layer"
+    res["bytes_per_step"] = bytes_decode(w.b * w.a, w.S, w.d)
+    return res
 
 
 def time_topk(reps: int = 6, copies: int = 4):
@@ -464,67 +576,114 @@ def hbm_copy_ceiling():
     return round(2 * n / min(ms[1:]) / 1e6, 1)
 
 
+def hbm_read_ceiling(gib: int = 4, reps: int = 8):
+    """Read-only HBM ceiling measured in the same run: kvq_stream_read over a `gib` GiB buffer
+    (16-byte nontemporal loads, the cache streams' load form), best and median of `reps`."""
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    n = gib << 30
+    a = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros((n + 65535) // 65536, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    ev = []
+    for _ in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        kvq.kvq_stream_read(a, sink)
+        e1.record(st)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(x.elapsed_time(y) for x, y in ev[2:])
+    del a, sink
+    return {"bytes": n, "gbs_best": round(n / ms[0] / 1e6, 1), "gbs_median": round(n / ms[len(ms) // 2] / 1e6, 1),
+            "kernel": "k_stream_read (kvq_stream_read)"}
+
+
 # ------------------------------------------------------------- CPU baseline
-def cpu_baseline(budget_s: float = 12.0):
-    """The oracle on a sample of the same job: for a sample of (batch row, head) pairs of
-    one OPT-175B layer, quantise the 512-token prompt, then 32 decode steps of append +
-    dense attention.  Pairs are spread over a thread pool (ctypes releases the GIL)."""
+def _oracle_pair_seconds(w, seed):
+    """The oracle's work for one (batch row, head) of one layer of workload `w`: quantise the
+    s-token prompt, then n decode steps of append + attention (dense, or top-k with
+    k = ceil(topk_frac * T) for the sparse workload).  Returns (seconds, algorithmic bytes)."""
+    import numpy as np
+
+    import oracle
+    G = w.d // 64
+    rr = np.random.default_rng(seed)
+    K = (rr.standard_normal((w.S, w.d)) * w.std).astype(np.float16)
+    V = (rr.standard_normal((w.S, w.d)) * w.std).astype(np.float16)
+    Q = (rr.standard_normal((w.n, w.d)) * w.std).astype(np.float16)
+    t0 = time.perf_counter()
+    planes = []
+    for X in (K, V):
+        c, m, sc = (np.zeros((w.S, w.d // 2), np.uint8), np.zeros((w.S, G), np.float32),
+                    np.zeros((w.S, G), np.float32))
+        c[:w.s], m[:w.s], sc[:w.s] = oracle.quantize_rows(X[:w.s])
+        planes.append((c, m, sc))
+    nbytes = 2 * bytes_quantize(w.s, w.d)
+    for j in range(1, w.n + 1):
+        pos = w.s + j - 1
+        for X, (c, m, sc) in zip((K, V), planes):
+            c[pos:pos + 1], m[pos:pos + 1], sc[pos:pos + 1] = oracle.quantize_rows(X[pos:pos + 1])
+        hc = oracle.HeadCache(*planes[0], *planes[1])
+        nbytes += 2 * bytes_quantize(1, w.d)
+        if w.topk_frac > 0:
+            oracle.attend_topk(Q[j - 1], hc, w.k_top(pos + 1), pos + 1)
+            nbytes += bytes_topk(1, pos + 1, w.k_top(pos + 1), w.d)
+        else:
+            oracle.attend(Q[j - 1], hc, pos + 1)
+            nbytes += bytes_decode(1, pos + 1, w.d)
+    return time.perf_counter() - t0, nbytes
+
+
+def oracle_layer_rate(w, cores, budget_s, seed0=1234):
+    """The oracle on a bounded sample of (batch row, head) pairs of one layer of `w`, spread
+    over `cores` threads (ctypes releases the GIL): GB/s over the same algorithmic bytes as
+    the GPU, and the layer-tokens/s the sampled rate implies."""
     import concurrent.futures as cf
 
     import numpy as np
 
     import oracle
+    oracle.lib()
+    r = np.random.default_rng(seed0 + w.idx)
+    pairs_total = w.b * w.a
+    with cf.ThreadPoolExecutor(cores) as ex:
+        # one untimed round (first calls), then one pair per thread timed to size the sample
+        list(ex.map(lambda sd: _oracle_pair_seconds(w, int(sd)), r.integers(0, 2**31, min(cores, pairs_total))))
+        tb = time.perf_counter()
+        list(ex.map(lambda sd: _oracle_pair_seconds(w, int(sd)), r.integers(0, 2**31, min(cores, pairs_total))))
+        batch = time.perf_counter() - tb
+        n_pairs = int(min(pairs_total, max(1, budget_s / max(batch, 1e-3)) * cores))
+        t0 = time.perf_counter()
+        res = list(ex.map(lambda sd: _oracle_pair_seconds(w, int(sd)), r.integers(0, 2**31, n_pairs)))
+        wall = time.perf_counter() - t0
+    nbytes = sum(b for _, b in res)
+    return {"gbs": round(nbytes / wall / 1e9, 4), "pairs": n_pairs, "of_pairs": pairs_total, "wall_s": round(wall, 2),
+            "layer_tokens_per_s": round(n_pairs / w.a * w.n / wall, 3),
+            "sample": (f"{n_pairs} of the {pairs_total} (batch row, head) pairs of one {w.name} layer: prompt quantise "
+                       f"({w.s} tokens) + {w.n} x (append + {'top-k' if w.topk_frac > 0 else 'dense'} attention)")}
+
+
+def cpu_baseline(budget_s: float = 12.0, per_config_budget_s: float = 3.0):
+    """The oracle on a sample of the headline job (OPT-175B layer, `budget_s` of work) and on
+    a sample of one layer of every other configuration (`per_config_budget_s` each)."""
     import workloads as W
 
-    w = W.OPT_175B
-    r = np.random.default_rng(1234)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    oracle.lib()
-
-    G = w.d // 64
-
-    def one_pair(seed):
-        rr = np.random.default_rng(seed)
-        K = rr.standard_normal((w.S, w.d)).astype(np.float16)
-        V = rr.standard_normal((w.S, w.d)).astype(np.float16)
-        Q = rr.standard_normal((w.n, w.d)).astype(np.float16)
-        t0 = time.perf_counter()
-        planes = []
-        for X in (K, V):
-            c, m, s = (np.zeros((w.S, w.d // 2), np.uint8), np.zeros((w.S, G), np.float32),
-                       np.zeros((w.S, G), np.float32))
-            c[:w.s], m[:w.s], s[:w.s] = oracle.quantize_rows(X[:w.s])
-            planes.append((c, m, s))
-        for j in range(1, w.n + 1):
-            pos = w.s + j - 1
-            for X, (c, m, s) in zip((K, V), planes):
-                c[pos:pos + 1], m[pos:pos + 1], s[pos:pos + 1] = oracle.quantize_rows(X[pos:pos + 1])
-            oracle.attend(Q[j - 1], oracle.HeadCache(*planes[0], *planes[1]), pos + 1)
-        return time.perf_counter() - t0
-
-    # calibrate on one parallel batch (one pair per thread), then size the sample to the budget
-    with cf.ThreadPoolExecutor(cores) as ex:
-        tb = time.perf_counter()
-        list(ex.map(one_pair, list(r.integers(0, 2**31, cores))))
-        batch = time.perf_counter() - tb
-        n_pairs = int(min(w.b * w.a, max(1, budget_s / max(batch, 1e-3)) * cores))
-        seeds = list(r.integers(0, 2**31, n_pairs))
-        t0 = time.perf_counter()
-        list(ex.map(one_pair, seeds))
-        wall = time.perf_counter() - t0
-    per_pair_bytes = (2 * bytes_quantize(w.s, w.d) + w.n * 2 * bytes_quantize(1, w.d)
-                      + sum(bytes_decode(1, w.s + j, w.d) for j in range(1, w.n + 1)))
-    gbs = n_pairs * per_pair_bytes / wall / 1e9
-    # one thread: the same per-pair job, a few pairs in sequence
-    n1 = 3
-    t1 = sum(one_pair(int(sd)) for sd in r.integers(0, 2**31, n1))
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{n_pairs} of the {w.b * w.a} (batch row, head) pairs of one OPT-175B layer: "
-                       f"prompt quantise (512 tokens) + 32 x (append + dense attention, context 513..544); "
-                       f"{wall:.1f} s wall on {cores} threads"),
-            "layer_tokens_per_s": round(n_pairs / w.a * w.n / wall, 3),
-            "single_thread_gbs": round(n1 * per_pair_bytes / t1 / 1e9, 4),
-            "cpu_model": cpu_model()}
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, affinity))
+    main = oracle_layer_rate(W.OPT_175B, cores, budget_s)
+    t1 = sum(_oracle_pair_seconds(W.OPT_175B, 77 + i)[0] for i in range(3))
+    per_pair_bytes = _oracle_pair_seconds(W.OPT_175B, 80)[1]
+    per_config = {}
+    for w in (W.TINY, W.OPT_6_7B, W.OPT_30B, W.SPARSE):
+        per_config[w.name] = oracle_layer_rate(w, cores, per_config_budget_s)
+    return {"value": main["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": main["sample"] + f"; {main['wall_s']} s wall on {cores} threads",
+            "layer_tokens_per_s": main["layer_tokens_per_s"],
+            "single_thread_gbs": round(3 * per_pair_bytes / t1 / 1e9, 4),
+            "host_cpus_in_affinity": affinity, "os_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(), "per_config": per_config}
 
 
 def cpu_model() -> str:
@@ -548,6 +707,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=0, help="decode steps per job (default 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the C1/C2/C3 configuration legs")
     ap.add_argument("--no-meta16", action="store_true", help="skip the binary16-metadata leg")
     ap.add_argument("--no-proj", action="store_true", help="skip the int4-weight projection leg")
     ap.add_argument("--no-host", action="store_true", help="skip the CPU-delegated attention leg")
@@ -565,31 +725,14 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import workloads as W
 
-    job = Job(args)
-    w = job.w
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        job.step()
-    torch.cuda.synchronize()
-
-    log(f"[bench] timing {args.steps} steps")
-    events = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        job.step(events)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    dec_ms = [a.elapsed_time(b) for a, b, _ in events]
-    dec_bytes = [nb for _, _, nb in events]
-    avg_ms = sum(dec_ms) / len(dec_ms)
-    avg_bytes = sum(dec_bytes) / len(dec_bytes)
-    achieved = avg_bytes / avg_ms / 1e6
-    decode_ms_per_step = sum(dec_ms) / args.steps
-    srt = sorted(dec_ms)
+    w = W.OPT_175B
+    job = Job(w, args.layers or w.layers, args.decode_steps or w.n, args.meta, args.fused)
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    ms_step, events = job.run(args.steps, args.warmup)
+    sm = job.summary(ms_step, events, args.steps)
+    avg_ms, achieved = sm["avg_launch_ms"], sm["achieved_gbs"]
     value = job.b_step / (ms_step / 1e3) / 1e9
 
     traffic = stored_traffic() if job.meta == "f32" else None
@@ -598,7 +741,7 @@ def main():
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
                 "kernel": (("k_decode<128,4,2> (kv_append_attend_q4: append + attention)" if job.fused
                             else "k_decode<128,4,2> (decode_attention_q4)") + f", {job.meta} min/scale planes"),
-                "algorithmic_bytes_per_launch": int(avg_bytes),
+                "algorithmic_bytes_per_launch": sm["algorithmic_bytes_per_launch"],
                 "avg_launch_ms": round(avg_ms, 5), "launches_timed": len(events)}
 
     res = {
@@ -613,22 +756,27 @@ def main():
                             + (", append fused into the attention launch" if job.fused else ", two launches")),
                    "parallelism": "1 GPU"},
         "roofline": roofline,
-        "decode_attention": {"gbs": round(achieved, 1), "pct_of_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
-                             "layer_tokens_per_s": round(w.b / (avg_ms / 1e3), 1),
-                             "stack_tokens_per_s": round(w.b * job.n / (decode_ms_per_step / 1e3), 1),
-                             "launch_ms": {"min": round(srt[0], 5), "median": round(srt[len(srt) // 2], 5),
-                                           "p90": round(srt[int(0.9 * (len(srt) - 1))], 5),
-                                           "max": round(srt[-1], 5), "mean": round(avg_ms, 5),
-                                           "launches": len(srt)}},
+        "decode_attention": sm["decode_attention"],
         "step_bytes": {"prefill": job.b_prefill, "append": job.b_append, "decode": job.b_decode},
     }
     log(f"[bench] step {ms_step:.1f} ms, decode kernel {achieved:.0f} GB/s")
+    del job
+    torch.cuda.empty_cache()
+    log("[bench] read-only HBM ceiling")
+    res["hbm_read_ceiling"] = hbm_read_ceiling()
+    if not args.no_configs:
+        log("[bench] configuration legs: tiny latency, OPT-6.7B (cache-warm layer, 32-layer stack), "
+            "OPT-30B 48-layer stack")
+        res["configs"] = {"tiny": time_tiny_latency(),
+                          "opt-6.7b": {"single_layer_cache_warm": time_cache_warm_layer(W.OPT_6_7B),
+                                       "stack": time_stack(W.OPT_6_7B)},
+                          "opt-30b": {"stack": time_stack(W.OPT_30B)}}
+        torch.cuda.empty_cache()
     if not args.no_topk:
         log("[bench] sparse top-k leg")
         res["sparse_topk"] = time_topk()
         log("[bench] split-context leg")
         res["split_context"] = time_split_context()
-    del job
     torch.cuda.empty_cache()
     if not args.no_meta16:
         log("[bench] binary16 metadata leg")

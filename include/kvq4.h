@@ -295,6 +295,19 @@ int decode_attention_q4_host(const kvq_cache *cache, const void *q_f16, int32_t 
 int kvq_host_simd(void);
 void kvq_host_use_simd(int enable);
 
+/* ------------------------------------------------------------------------
+ * Measurement: the HBM read ceiling the attention kernels are compared
+ * with.  Decode attention is memory-bound (the efficient-inference survey
+ * notes, "Efficiency Analysis": a very low compute-to-memory-access ratio),
+ * so its roofline is the rate at which a kernel can stream memory.  This
+ * call reads `bytes` of device memory at `buf` once, with the same 16-byte
+ * nontemporal loads the cache streams use, and writes nothing but (almost
+ * never) one word per 64 KB to `sink` (device, uint32 [ceil(bytes/65536)],
+ * 4-byte aligned), which keeps the loads from being optimised away.  buf
+ * 16-byte aligned; bytes a positive multiple of 16 (KVQ_ERANGE otherwise).
+ * ---------------------------------------------------------------------- */
+int kvq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream);
+
 /* Static text for a status code. */
 const char *kvq_strerror(int status);
 

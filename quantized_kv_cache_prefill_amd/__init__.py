@@ -22,7 +22,7 @@ __all__ = [
     "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4",
     "decode_attention_q4_topk", "decode_attention_q4_noalloc", "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16",
     "kv_quantize_prefill_host", "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd",
-    "kvq_host_use_simd",
+    "kvq_host_use_simd", "kvq_stream_read",
     "library_path", "load_library", "GROUP",
 ]
 
@@ -40,7 +40,8 @@ EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_quantize_prefill_atten
             "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4", "decode_attention_q4_topk",
             "decode_attention_q4_noalloc",
             "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kv_quantize_prefill_host",
-            "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd", "kvq_host_use_simd", "kvq_strerror")
+            "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd", "kvq_host_use_simd", "kvq_strerror",
+            "kvq_stream_read")
 
 
 class KvqDims(ctypes.Structure):
@@ -114,6 +115,8 @@ def load_library() -> ctypes.CDLL:
     L.kvq_host_simd.restype = ctypes.c_int
     L.kvq_host_use_simd.argtypes = [ctypes.c_int]
     L.kvq_host_use_simd.restype = None
+    L.kvq_stream_read.argtypes = [P, SZ, P, P]
+    L.kvq_stream_read.restype = ctypes.c_int
     L.kvq_strerror.argtypes = [ctypes.c_int]
     L.kvq_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -401,6 +404,18 @@ def gemm_w4a16(x: torch.Tensor, codes: torch.Tensor, mins: torch.Tensor, scales:
     _check(load_library().gemm_w4a16(_ptr(x), M, N, K, _ptr(codes), _ptr(mins), _ptr(scales), _ptr(y), num_splits,
                                      _ptr(ws), need, _stream(stream)), "gemm_w4a16")
     return y
+
+
+# --------------------------------------------------------------- measurement
+def kvq_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read every byte of the device tensor `buf` once (the HBM read ceiling); `sink` is a
+    uint32/int32 device tensor of at least ceil(nbytes / 65536) elements."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA tensor")
+    if sink.element_size() != 4 or not sink.is_cuda or sink.numel() < (nbytes + 65535) // 65536:
+        raise ValueError("sink must be a 4-byte CUDA tensor of ceil(nbytes/65536) elements")
+    _check(load_library().kvq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_stream_read")
 
 
 # ------------------------------------------------------------------ host path

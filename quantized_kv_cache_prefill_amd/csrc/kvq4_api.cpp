@@ -481,6 +481,15 @@ int decode_attention_q4_host(const kvq_cache *cache, const void *q_f16, int32_t 
                : KVQ_ELAUNCH;
 }
 
+int kvq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream)
+{
+    if (check_act(buf) != KVQ_OK || sink == nullptr || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return KVQ_EINVAL;
+    if (bytes < 16 || bytes % 16 != 0 || bytes / 16 / (256 * 16) >= 0x7FFFFFFF)
+        return KVQ_ERANGE;
+    return status_of(kvq::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(hip_stream)));
+}
+
 int kvq_host_simd() { return kvq::host_has_avx512(); }
 
 void kvq_host_use_simd(int enable) { kvq::host_set_simd(enable); }

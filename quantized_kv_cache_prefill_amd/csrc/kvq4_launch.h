@@ -77,6 +77,11 @@ struct GemmArgs {
 int launch_gemm_w4(const GemmArgs &g, hipStream_t st);
 int gemm_row_blocks(int M);
 
+// Read `bytes` (a multiple of 16) of device memory once with the cache
+// streams' load form; sink receives at most one word per 64 KB (normally
+// none).
+int launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
+
 // Quantise W fp16 [N][K] with the binary16-metadata codec: codes [N][K/2],
 // mins/scales binary16 [N][K/64].
 int launch_quantize_weight(const void *w, int N, int K, uint8_t *codes, void *mins, void *scales, hipStream_t st);
