@@ -134,12 +134,11 @@ int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
     return s;
 }
 
-// Split of the K range for gemm_w4a16: as many splits as keep the workgroups
-// within one resident round (256 CUs x the eight-wave workgroups one CU holds
-// at that row-block count: 2 at one block of 16 rows, else 1, set by
-// registers), with at least 4 chunks of 128 k per split; when that leaves one
-// split of an under-filled round, the split count that minimises (rounds x
-// each split's share of K) + a cost for the partials.
+// Split of the K range for gemm_w4a16: as many splits as give every CU one
+// workgroup (a second workgroup on a CU shares its matrix core and vector
+// ALU, so it adds no throughput), with at least 4 chunks of 128 k per split;
+// when that leaves one split of an under-filled round, the split count that
+// minimises (rounds x each split's share of K) + a cost for the partials.
 // Depends on (M, N, K) only.
 constexpr int kGemmChunk = 128;
 constexpr int kGemmCols = 256;
@@ -153,10 +152,11 @@ bool gemm_dims_ok(int M, int N, int K)
 
 // Weight of the split partials in the automatic split choice: each extra
 // split writes and re-reads M*N binary32 partials, 16*M/K of the weight bytes.
-// Fitted to measured sweeps on MI355X (OPT-175B QKV projection, N = 36864,
-// K = 12288, 144 column tiles): at M = 144, 250 us with 1 split, 199 us with
-// 3, 205 us with 5; at M = 64, 141 / 92 / 100 us with 1 / 3 / 7; at M = 32,
-// 147 / 77 / 78 us with 1 / 3 / 7.  The weight 0.3 picks 3, 3 and 7 there.
+// Measured on MI355X with the 32x32x16 kernel (OPT-175B projections, K =
+// 12288): QKV (N = 36864, 144 column tiles) at M = 144: 234 / 258 / 191 / 225
+// / 201 us with 1..5 splits; output (N = 12288) at M = 144: 124 / 95 / 78 / 76
+// us with 2..5; at M = 32: QKV 94 / 96 / 75 / 82 / 77, output 52 / 41 / 35 /
+// 33 with 2..5.  The weight 0.3 picks 3 and 5 at M = 144, 7 and 5 at M = 32.
 constexpr double kGemmPartialWeight = 0.3;
 constexpr int kGemmMaxAutoSplits = 16;
 
@@ -165,10 +165,8 @@ int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
     const int chunks = K / kGemmChunk;
     int s = num_splits;
     if (s <= 0) {
-        const int mb = kvq::gemm_row_blocks(M);
-        const int rows = 16 * mb;
-        const int per_cu = mb == 1 ? 2 : 1;
-        const int64_t slots = (int64_t)kCUs * per_cu;
+        const int rows = 32 * kvq::gemm_row_blocks(M);
+        const int64_t slots = kCUs;
         const int64_t tiles = (int64_t)((N + kGemmCols - 1) / kGemmCols) * ((M + rows - 1) / rows);
         const int max_s = std::max(1, chunks / 4); // at least 4 chunks per split
         // As many splits as one resident round holds ...

@@ -9,20 +9,26 @@
 // so that what one wave consumes per step is contiguous: tile (nt, kt) holds
 // rows 64nt..64nt+63 and k = 128kt..128kt+127, 4 KB of codes (row r at byte
 // 64r, even k in the low nibble) and 128 mins / 128 scales (row r, group h at
-// 2r+h).  The dequantised
-// weight is the binary16 value nearest to min + c*scale, computed with one
-// packed fp16 FMA (exact product and sum, one rounding), and the product runs
-// on the matrix cores: v_mfma_f32_16x16x32_f16, binary32 accumulation.
+// 2r+h).  The dequantised weight is the binary16 value nearest to
+// min + c*scale, computed with one packed fp16 FMA (exact product and sum,
+// one rounding), and the product runs on the matrix cores:
+// v_mfma_f32_32x32x16_f16, binary32 accumulation.  On MI355X that
+// instruction issues back to back at its full rate (32 cycles, 32768 flops);
+// the 16x16x32 form measured 25.4 cycles per 16384 flops, 54% of the peak, so
+// the rows of x are padded to a multiple of 32 instead.
 //
 // Shape of the work (OPT-175B decode: M = 144 tokens, N = K = 12288): the
-// weight stream (N*K/2 bytes) and the matrix-core time are of the same order,
-// so the kernel keeps both busy: a workgroup owns a 16*MB x 256 output tile
-// (MB <= 9 row blocks of 16) and a range of K; its eight waves (two per SIMD)
-// each take 32 columns and all the row blocks, share each 128-wide chunk of x
-// through LDS (double-buffered), and stream and dequantise their own 32
-// weight rows.  Ranges of K are split across
-// workgroups when the column tiles alone cannot fill the 256 CUs; the split
-// partials (binary32) are summed by a second kernel.
+// weight stream (N*K/2 bytes) and the matrix-core time are of the same order.
+// A workgroup owns a 32*RB x 256 output tile (RB <= 5 row blocks of 32) and a
+// range of K; its four waves (one per SIMD) each take 64 columns and all the
+// row blocks.  x goes from HBM straight into LDS (buffer loads to LDS, 16-byte
+// pieces XOR-swizzled within each row so the operand reads hit distinct
+// banks) through a ring of three chunk buffers, two chunks ahead; each wave
+// streams its own 64 weight rows through a ring of registers three chunks
+// ahead and dequantises them as it multiplies, the operands of k-step s+1
+// fetched and dequantised between the products of step s.  Ranges of K are
+// split across workgroups when the column tiles alone cannot fill the 256
+// CUs; the split partials (binary32) are summed by a second kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,338 +39,320 @@ namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
-constexpr int kChunk = 128;          // k per pipeline step
-constexpr int kPitch = kChunk + 8;   // LDS row pitch of the x chunk, halves (breaks bank aliasing)
-constexpr int kColsPerWave = 64;     // four 16-column blocks
-constexpr int kColsPerGroup = 4 * kColsPerWave;
-constexpr int kThreads = 512;        // 8 waves
-// Work of a wave: kGemmWaveColBlocks = 4: 64 columns and half of the row
-// blocks (8 waves = 4 column groups x 2 row halves); 2: 32 columns and all
-// the row blocks (8 waves side by side), each weight dequantised once.
-#ifndef KVQ_GEMM_WAVE_COL_BLOCKS
-#define KVQ_GEMM_WAVE_COL_BLOCKS 2
-#endif
-constexpr int kGemmWaveColBlocks = KVQ_GEMM_WAVE_COL_BLOCKS;
+constexpr int kChunk = 128;           // k per pipeline step
+constexpr int kRowBytes = kChunk * 2; // bytes of one x row of a chunk (16 pieces of 16 bytes)
+constexpr int kCB = 2;                // 32-column blocks per wave
+constexpr int kColsPerWave = 32 * kCB;
+constexpr int kWaves = 4;             // one per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kColsPerGroup = kWaves * kColsPerWave;
+constexpr int kDepth = 3;             // weight chunks in flight per wave (register ring)
+constexpr int kXBuf = 3;              // x chunk buffers in LDS (x runs kXBuf - 1 chunks ahead)
+static_assert(kDepth == kXBuf, "the K loop is unrolled by one ring length for both rings");
 
-__device__ __forceinline__ uint4 ld_nt16(const void *p)
+// Buffer resources: a base, a size in bytes (loads at or past it return zeros
+// and touch no memory) and the raw-buffer flags.  The K loop issues every load
+// unconditionally -- a chunk past the range, and rows past M, get offsets
+// beyond the size -- so the loads keep one fixed order.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes)
 {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kNT = 2;                     // cache policy: nontemporal (the weights are used once)
+constexpr uint32_t kOutside = 0xFFFFFFC0u; // an offset past any resource (+ up to 63 still past it)
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+}
+__device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNT);
+}
+typedef __attribute__((address_space(3))) void lds_void_t;
+// 16 bytes per lane, HBM -> LDS: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)voff, 0, 0, 0);
 }
 
-// Reorder the 8 halves of a 16-byte x piece to (x0,x4,x1,x5,x2,x6,x3,x7): the
-// order in which the weight unpack below yields its pairs.  The contraction
-// index may be permuted freely as long as both operands agree.
-__device__ __forceinline__ uint4 interleave_halves(uint4 v)
+// The 8 codes of a dword (k = k0..k0+7, code i at bits 4i..4i+3) as
+// dequantised binary16 weights, in k order.  Each pair (e_2i, e_2i+1) is made
+// exact in binary16: one byte permute puts byte i of the dword at bytes 0 and
+// 2, the mask keeps e_2i at bits 0..3 and e_2i+1 at bits 20..23, OR-ing the
+// patterns of 1024 and 64 onto them gives (1024 + e_2i, 64 + e_2i+1), and
+// subtracting (1024, 64) is exact.  One packed FMA then forms min + c*scale
+// with a single rounding.  `magic` sits in a VGPR: GFX9's VOP3 takes no
+// literal operand and at most one scalar one.
+__device__ __forceinline__ uint32_t magic_vgpr()
 {
-    // v.x=(x0,x1) v.y=(x2,x3) v.z=(x4,x5) v.w=(x6,x7)
-    uint4 r;
-    r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u); // (x0, x4)
-    r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u); // (x1, x5)
-    r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u); // (x2, x6)
-    r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u); // (x3, x7)
-    return r;
-}
-
-// The 8 codes of a dword (k = k0..k0+7) as dequantised binary16 weights in
-// the order (w0,w4),(w1,w5),(w2,w6),(w3,w7).  Each code is made exact in
-// binary16 (OR-ing the pattern of 1024 onto a nibble at bits 0..3 gives 1024+c,
-// OR-ing 64 onto bits 4..7 gives 64+c; subtracting the bias is exact), then
-// one packed FMA forms min + c*scale with a single rounding.  The OR
-// constants sit in VGPRs (magic) so each pair is one v_and_or_b32: GFX9's
-// VOP3 takes no literal operand.
-struct Magic16 {
-    uint32_t m1024, m64;
-};
-__device__ __forceinline__ Magic16 magic16()
-{
-    Magic16 m;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.m1024));
-    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(m.m64));
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x54006400" : "=v"(m));
     return m;
 }
 
-__device__ __forceinline__ h8 dequant8(uint32_t w, h2 sc, h2 mn, const Magic16 mg)
+__device__ __forceinline__ h8 dequant8(uint32_t w, h2 sc, h2 mn, uint32_t magic)
 {
-    const uint32_t y = w >> 8;
-    const h2 b1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    const h2 b64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-    const h2 c0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) | mg.m1024) + b1024;
-    const h2 c1 = __builtin_bit_cast(h2, (w & 0x00F000F0u) | mg.m64) + b64;
-    const h2 c2 = __builtin_bit_cast(h2, (y & 0x000F000Fu) | mg.m1024) + b1024;
-    const h2 c3 = __builtin_bit_cast(h2, (y & 0x00F000F0u) | mg.m64) + b64;
-    const uint4 d = make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c0, sc, mn)),
-                               __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c1, sc, mn)),
-                               __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c2, sc, mn)),
-                               __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c3, sc, mn)));
-    return __builtin_bit_cast(h8, d);
+    const h2 bias = {(_Float16)-1024.0f, (_Float16)-64.0f};
+    constexpr uint32_t sel[4] = {0x0C000C00u, 0x0C010C01u, 0x0C020C02u, 0x0C030C03u};
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = __builtin_amdgcn_perm(0u, w, sel[i]);
+        const h2 c = __builtin_bit_cast(h2, (t & 0x00F0000Fu) | magic) + bias;
+        d[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, sc, mn));
+    }
+    return __builtin_bit_cast(h8, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
-// One wave's weights for one 128-k chunk: for each of its CB column blocks of
-// 16, lane l holds column (block*16 + l%16), k = 32*(l/16) .. +31 of the chunk
-// (16 code bytes) and that range's group min and scale.
-template <int CB>
+// One wave's weights for one 128-k chunk: for each of its two 32-column
+// blocks, lane l holds column l%32 of the block and k = 64*(l/32) .. +63 of
+// the chunk (32 code bytes, exactly one group) with that group's min and
+// scale.  In k-step s (0..7) the lane's 8 operand values are k = 64*(l/32) +
+// 8s .. +7: the two lane halves give the 16 k of the 32x32x16 product.
 struct WChunk {
-    uint4 code[CB];
-    uint32_t mn[CB], sc[CB]; // binary16 bits, low half
+    uint4 code[kCB][2];
+    uint32_t mn[kCB], sc[kCB]; // binary16 bits, low half
 };
 
-// Element at a 32-bit byte offset from a wave-uniform base (the load then
-// takes the scalar-base + 32-bit-offset form).
-template <typename T>
-__device__ __forceinline__ const T *at_byte(const T *base, uint32_t off)
+// The weight planes of one wave's 64 rows (one row of 64-row tiles of the
+// tiled layout: K/128 tiles of 4 KB codes and 128 mins / 128 scales each).
+struct WStreams {
+    __amdgpu_buffer_rsrc_t codes, mins, scales;
+    uint32_t code_off, meta_off; // the lane's offsets inside a tile
+};
+
+__device__ __forceinline__ WStreams w_streams(const uint8_t *codes, const uint16_t *mins, const uint16_t *scales,
+                                              int64_t n0, int K, int lane)
 {
-    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
+    const int64_t tiles = K / kChunk;
+    const int64_t t0 = (n0 >> 6) * tiles; // wave-uniform
+    WStreams w;
+    w.codes = rsrc(codes + t0 * 4096, (uint32_t)(tiles * 4096));
+    w.mins = rsrc(mins + t0 * 128, (uint32_t)(tiles * 256));
+    w.scales = rsrc(scales + t0 * 128, (uint32_t)(tiles * 256));
+    w.code_off = (uint32_t)((lane & 31) * 64 + 32 * (lane >> 5));
+    w.meta_off = (uint32_t)(4 * (lane & 31) + 2 * (lane >> 5));
+    return w;
 }
 
-// Chunk c of the wave's 16*CB rows starting at n0 (n0 % 64 + 16*CB <= 64):
-// part of one 4 KB tile, lane l reading 16 bytes of row n0%64 + 16b + l%16 at
-// byte 16*(l/16).
-template <int CB>
-__device__ __forceinline__ WChunk<CB> load_w_chunk(const uint8_t *__restrict__ codes,
-                                                   const uint16_t *__restrict__ mins,
-                                                   const uint16_t *__restrict__ scales, int64_t n0, int K, int c,
-                                                   int lane)
+// Chunk c of the wave's rows (an invalid chunk reads zeros): lane l reads 32
+// bytes of row 32b + l%32 at byte 32*(l/32), and that group's min and scale.
+__device__ __forceinline__ WChunk load_w_chunk(const WStreams &ws, uint32_t c, bool valid)
 {
-    const int64_t tile = (n0 >> 6) * (K / kChunk) + c; // wave-uniform
-    const uint8_t *ct = codes + tile * 4096;
-    const uint16_t *mt = mins + tile * 128, *st = scales + tile * 128;
-    WChunk<CB> w;
+    WChunk w;
 #pragma unroll
-    for (int b = 0; b < CB; ++b) {
-        const uint32_t r = (uint32_t)(n0 & 63) + b * 16 + (lane & 15);
-        w.code[b] = ld_nt16(ct + (r * 64 + 16 * (lane >> 4)));
-        w.mn[b] = __builtin_nontemporal_load(at_byte(mt, 4 * r + 2 * (lane >> 5)));
-        w.sc[b] = __builtin_nontemporal_load(at_byte(st, 4 * r + 2 * (lane >> 5)));
+    for (int b = 0; b < kCB; ++b) {
+        const uint32_t co = valid ? c * 4096u + (uint32_t)b * 2048u + ws.code_off : kOutside;
+        const uint32_t mo = valid ? c * 256u + (uint32_t)b * 128u + ws.meta_off : kOutside;
+        w.code[b][0] = bld16(ws.codes, co);
+        w.code[b][1] = bld16(ws.codes, co + 16);
+        w.mn[b] = bld2(ws.mins, mo);
+        w.sc[b] = bld2(ws.scales, mo);
     }
     return w;
 }
 
-// Rows m0 .. m0+16*MB-1 of x[:, kc .. kc+127], in 16*MB*16 pieces of 8
-// halves; thread t holds pieces t, t+512, ...  Loaded into registers first
-// and written to LDS later, so the loads are in flight during the matrix work.
-template <int MB>
-struct XStage {
-    static constexpr int PIECES = 16 * MB * (kChunk / 8);
-    static constexpr int PER_THREAD = (PIECES + kThreads - 1) / kThreads;
-    uint4 v[PER_THREAD];
+// x rows m0 .. m0+32*RB-1 of one chunk in LDS: row r at byte 256 r, its
+// 16-byte piece j at slot j ^ (r & 15).  Thread t's u-th load fills 16-byte
+// position p = 64 * (4u + wave) + lane, i.e. row p/16, slot p%16; off[u]
+// holds the byte offset in x of the piece that belongs there (chunk 0), or
+// kOutside for a row past M.
+template <int RB>
+struct XLoads {
+    static constexpr int PER_THREAD = 32 * RB * 16 / kThreads; // 2 RB
+    uint32_t off[PER_THREAD];
 };
 
-// Per-thread byte offsets of its pieces' rows (fixed over the K loop; rows
-// past M, and pieces past the tile, point at row M-1 and are zeroed), and
-// whether the tile has such rows at all.
-template <int MB>
-struct XOffsets {
-    uint32_t off[XStage<MB>::PER_THREAD];
-    uint32_t ok; // bit i: piece i is a real row
-    bool partial;
-};
-
-template <int MB>
-__device__ __forceinline__ XOffsets<MB> x_offsets(int M, int K, int m0)
+template <int RB>
+__device__ __forceinline__ XLoads<RB> x_loads(int M, int K, int m0, int wave, int lane)
 {
-    XOffsets<MB> o;
-    o.ok = 0;
+    XLoads<RB> o;
 #pragma unroll
-    for (int i = 0; i < XStage<MB>::PER_THREAD; ++i) {
-        const int p = threadIdx.x + kThreads * i;
-        const int row = (p >> 4) % (16 * MB), kp = p & 15;
-        const int rc = min(m0 + row, M - 1);
-        o.off[i] = (uint32_t)(((int64_t)rc * K + 8 * kp) * 2);
-        if (p < XStage<MB>::PIECES && m0 + row < M)
-            o.ok |= 1u << i;
+    for (int u = 0; u < XLoads<RB>::PER_THREAD; ++u) {
+        const int p = 64 * (4 * u + wave) + lane;
+        const int row = p >> 4, slot = p & 15;
+        const int piece = slot ^ (row & 15);
+        o.off[u] = m0 + row < M ? (uint32_t)(((int64_t)(m0 + row) * K + 8 * piece) * 2) : kOutside;
     }
-    o.partial = m0 + 16 * MB > M || XStage<MB>::PIECES % kThreads != 0;
     return o;
 }
 
-// x of chunk kc: a uniform base plus the per-thread offsets (M*K*2 < 2^32).
-template <int MB>
-__device__ __forceinline__ void load_x(const uint16_t *__restrict__ x, int kc, const XOffsets<MB> &o,
-                                       XStage<MB> &xs)
+// Chunk c of x into the LDS buffer `dst` (an invalid chunk, and rows past M,
+// read zeros).
+template <int RB>
+__device__ __forceinline__ void issue_x(__amdgpu_buffer_rsrc_t rx, const XLoads<RB> &o, uint32_t c, bool valid,
+                                        char *dst, int wave)
 {
-    const uint16_t *xb = x + kc;
 #pragma unroll
-    for (int i = 0; i < XStage<MB>::PER_THREAD; ++i)
-        xs.v[i] = ld_nt16(at_byte(xb, o.off[i]));
-    if (o.partial) { // uniform
-#pragma unroll
-        for (int i = 0; i < XStage<MB>::PER_THREAD; ++i)
-            if (!((o.ok >> i) & 1u))
-                xs.v[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < XLoads<RB>::PER_THREAD; ++u)
+        dma16(rx, dst + 1024 * (4 * u + wave), valid && o.off[u] != kOutside ? o.off[u] + c * kRowBytes : kOutside);
 }
 
-// Write a staged chunk to LDS (rows >= M are zero), each piece reordered by
-// interleave_halves.
-template <int MB>
-__device__ __forceinline__ void store_x(const XStage<MB> &xs, _Float16 *__restrict__ sx)
+// One 128-k chunk of one wave: eight k-steps, each multiplying the step's 8
+// dequantised weights of both column blocks with the RB row blocks of the x
+// chunk (lane l reads row 32rb + l%32, piece 8*(l/32) + s).  The x operands
+// and the weights of step s+1 are read and dequantised before the products
+// of step s are issued, and the scheduler spreads them between those
+// products, so their latency and vector work overlap the matrix core.
+template <int RB>
+__device__ __forceinline__ void mma_chunk(const WChunk &cur, const char *__restrict__ sxb, int lane,
+                                          f16v (&acc)[RB][kCB])
 {
+    const uint32_t magic = magic_vgpr();
+    h2 sc[kCB], mn[kCB];
 #pragma unroll
-    for (int i = 0; i < XStage<MB>::PER_THREAD; ++i) {
-        const int p = threadIdx.x + kThreads * i;
-        if (p < XStage<MB>::PIECES)
-            *reinterpret_cast<uint4 *>(sx + (p >> 4) * kPitch + 8 * (p & 15)) = interleave_halves(xs.v[i]);
+    for (int b = 0; b < kCB; ++b) {
+        sc[b] = __builtin_bit_cast(h2, (cur.sc[b] & 0xFFFFu) * 0x00010001u);
+        mn[b] = __builtin_bit_cast(h2, (cur.mn[b] & 0xFFFFu) * 0x00010001u);
     }
-}
-
-// One 128-k chunk of one wave: dequantise its weights k-step by k-step and
-// accumulate its MBW x CB blocks (row blocks rb0 .. rb0+MBW-1 of the x chunk
-// in LDS).
-template <int MBW, int CB>
-__device__ __forceinline__ void mma_chunk(const WChunk<CB> &cur, const _Float16 *__restrict__ sxb, int rb0, int lane,
-                                          f4 (&acc)[MBW > 0 ? MBW : 1][CB])
-{
-    if constexpr (MBW > 0) {
-        const Magic16 mg = magic16();
-        h2 sc[CB], mn[CB];
+    auto word = [&](int b, int s) -> uint32_t {
+        const uint4 q = cur.code[b][s >> 2];
+        const int j = s & 3;
+        return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+    };
+    const int r = lane & 31, h = lane >> 5;
+    const char *xrow = sxb + r * kRowBytes;
+    auto ld_a = [&](int s, h8 (&a)[RB]) {
+        const int slot = (8 * h + s) ^ (r & 15);
 #pragma unroll
-        for (int b = 0; b < CB; ++b) {
-            sc[b] = __builtin_bit_cast(h2, (cur.sc[b] & 0xFFFFu) * 0x00010001u);
-            mn[b] = __builtin_bit_cast(h2, (cur.mn[b] & 0xFFFFu) * 0x00010001u);
+        for (int rb = 0; rb < RB; ++rb)
+            a[rb] = *reinterpret_cast<const h8 *>(xrow + rb * 32 * kRowBytes + 16 * slot);
+    };
+    h8 a[2][RB], bw[2][kCB];
+    ld_a(0, a[0]);
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+        bw[0][b] = dequant8(word(b, 0), sc[b], mn[b], magic);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int cur_i = s & 1, nxt_i = cur_i ^ 1;
+        if (s < 7) {
+            ld_a(s + 1, a[nxt_i]);
+#pragma unroll
+            for (int b = 0; b < kCB; ++b)
+                bw[nxt_i][b] = dequant8(word(b, s + 1), sc[b], mn[b], magic);
         }
-        auto word = [&](int b, int j) -> uint32_t {
-            return j == 0 ? cur.code[b].x : j == 1 ? cur.code[b].y : j == 2 ? cur.code[b].z : cur.code[b].w;
-        };
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h8 bw[CB];
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int b = 0; b < CB; ++b)
-                bw[b] = dequant8(word(b, j), sc[b], mn[b], mg);
-            // all of this k-step's x reads are issued before its products
-            h8 a[MBW];
+            for (int b = 0; b < kCB; ++b)
+                acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur_i][rb], bw[cur_i][b], acc[rb][b], 0, 0, 0);
+        if (s < 7) {
+            // each product followed by part of the next step's reads and vector work
 #pragma unroll
-            for (int mb = 0; mb < MBW; ++mb)
-                a[mb] = *reinterpret_cast<const h8 *>(sxb + ((rb0 + mb) * 16 + (lane & 15)) * kPitch +
-                                                      32 * (lane >> 4) + 8 * j);
-#pragma unroll
-            for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-                for (int b = 0; b < CB; ++b)
-                    acc[mb][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb], bw[b], acc[mb][b], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, MBW, 0);      // the k-step's LDS reads,
-            __builtin_amdgcn_sched_group_barrier(0x008, CB * MBW, 0); // then its products
-        }
-    }
-    // keep the caller's LDS writes of the next x chunk (and their wait on its
-    // global loads) after this chunk's products
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// The K loop and the stores of one wave: its 16*CB columns starting at n0 and
-// its MBW row blocks starting at block rb0 of the tile (the tile's MB blocks
-// are staged in LDS by all waves).  Every wave runs the same sequence of
-// barriers whatever its MBW.
-template <int MB, int MBW, int CB>
-__device__ __forceinline__ void gemm_wave(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
-                                          const uint16_t *__restrict__ mins, const uint16_t *__restrict__ scales,
-                                          _Float16 *__restrict__ y, float *__restrict__ ws, int M, int N, int K,
-                                          int m0, int64_t n0, int rb0, int split, int splits, int c_begin, int c_end,
-                                          _Float16 (*sx)[16 * MB * kPitch])
-{
-    const int lane = threadIdx.x & 63;
-    const bool wave_ok = n0 < N; // N % 64 == 0: a wave's columns are all in range or all out
-    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0.. and store nothing
-    f4 acc[MBW > 0 ? MBW : 1][CB];
-#pragma unroll
-    for (int mb = 0; mb < (MBW > 0 ? MBW : 1); ++mb)
-#pragma unroll
-        for (int b = 0; b < CB; ++b)
-            acc[mb][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    XStage<MB> xs;
-    const XOffsets<MB> xo = x_offsets<MB>(M, K, m0);
-    WChunk<CB> cur{};
-    if (c_begin < c_end) {
-        if constexpr (MBW > 0)
-            cur = load_w_chunk<CB>(codes, mins, scales, nsafe, K, c_begin, lane);
-        load_x<MB>(x, c_begin * kChunk, xo, xs);
-        store_x<MB>(xs, sx[0]);
-    }
-    __syncthreads();
-    for (int c = c_begin; c < c_end; ++c) {
-        const int buf = (c - c_begin) & 1;
-        const bool more = c + 1 < c_end; // uniform
-        WChunk<CB> nxt{};
-        if (more) {
-            if constexpr (MBW > 0)
-                nxt = load_w_chunk<CB>(codes, mins, scales, nsafe, K, c + 1, lane);
-            load_x<MB>(x, (c + 1) * kChunk, xo, xs);
-        }
-        mma_chunk<MBW, CB>(cur, sx[buf], rb0, lane, acc);
-        if (more)
-            store_x<MB>(xs, sx[buf ^ 1]);
-        cur = nxt;
-        __syncthreads();
-    }
-
-    if constexpr (MBW > 0) {
-        if (!wave_ok)
-            return;
-        // D layout: lane l holds rows 4*(l/16) .. +3 of column l%16 of each 16x16 block
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-#pragma unroll
-            for (int b = 0; b < CB; ++b) {
-                const int64_t n = n0 + b * 16 + (lane & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + (rb0 + mb) * 16 + 4 * (lane >> 4) + r;
-                    if (m < M) {
-                        if (splits == 1)
-                            y[(int64_t)m * N + n] = (_Float16)acc[mb][b][r];
-                        else
-                            ws[((int64_t)split * M + m) * N + n] = acc[mb][b][r];
-                    }
-                }
+            for (int i = 0; i < RB * kCB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one product
+                if (i < RB)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // some vector ALU
             }
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // grid.x: column groups of 256 (fastest), grid.y: K splits, grid.z: row tiles
-// of 16*MB.  Eight waves, two per SIMD, so one's dequantisation overlaps the
-// other's matrix work.  CB = 2 (the default): wave w takes columns 32w of the
-// group and all MB row blocks, so every weight is dequantised once.  CB = 4:
-// wave w takes columns 64*(w%4) and the upper (w < 4: ceil(MB/2) blocks) or
-// lower (w >= 4) row blocks; the two waves of a column group stream and
-// dequantise the same weight tile.  Measured on the OPT-175B projections, CB = 2
-// against CB = 4: QKV at M = 144, 64, 32: 251.7 -> 229.7, 157.4 -> 104.9,
-// 123.7 -> 82.3 us; output at M = 64, 32: 59.8 -> 48.3, 58.0 -> 42.6 us
-// (bit-identical results).
-// splits == 1: y written as fp16; else binary32 partials to ws[split][M][N].
-// The next chunk's weights and x are loaded into registers while the current
-// chunk is multiplied; x then goes to the other LDS buffer.
-template <int MB, int CB>
-__global__ __launch_bounds__(kThreads) void k_gemm_w4(const uint16_t *__restrict__ x,
-                                                      const uint8_t *__restrict__ codes,
-                                                      const uint16_t *__restrict__ mins,
-                                                      const uint16_t *__restrict__ scales,
-                                                      _Float16 *__restrict__ y, float *__restrict__ ws, int M,
-                                                      int N, int K, int chunks_per_split)
+// of 32*RB.  Wave w takes columns 64w .. 64w+63 of the group and all RB row
+// blocks, so every weight is dequantised once and each x operand read from
+// LDS feeds two products.  splits == 1: y written as fp16; else binary32
+// partials to ws[split][M][N].
+template <int RB>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_w4(const uint16_t *__restrict__ x,
+                                                         const uint8_t *__restrict__ codes,
+                                                         const uint16_t *__restrict__ mins,
+                                                         const uint16_t *__restrict__ scales,
+                                                         _Float16 *__restrict__ y, float *__restrict__ ws, int M,
+                                                         int N, int K, int chunks_per_split)
 {
-    constexpr int MH = (MB + 1) / 2;
-    __shared__ __attribute__((aligned(16))) _Float16 sx[2][16 * MB * kPitch];
-    const int wave = threadIdx.x >> 6;
+    // the x ring: three separate arrays, so that the compiler can tell the
+    // buffer being read from the ones being filled
+    __shared__ __attribute__((aligned(16))) char sx0[32 * RB * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char sx1[32 * RB * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char sx2[32 * RB * kRowBytes];
+    char *const sx[kXBuf] = {sx0, sx1, sx2};
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: the buffer bases stay scalar
     const int split = blockIdx.y, splits = gridDim.y;
-    const int m0 = blockIdx.z * 16 * MB;
+    const int m0 = blockIdx.z * 32 * RB;
     const int c_begin = split * chunks_per_split;
     const int c_end = min(K / kChunk, c_begin + chunks_per_split);
-    if constexpr (CB == 4) {
-        const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + (wave & 3) * kColsPerWave;
-        if (wave < 4)
-            gemm_wave<MB, MH, 4>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, 0, split, splits, c_begin, c_end,
-                                 sx);
-        else
-            gemm_wave<MB, MB - MH, 4>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, MH, split, splits, c_begin,
-                                      c_end, sx);
-    } else {
-        const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + wave * 16 * CB;
-        gemm_wave<MB, MB, CB>(x, codes, mins, scales, y, ws, M, N, K, m0, n0, 0, split, splits, c_begin, c_end, sx);
+    const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + wave * kColsPerWave;
+    const bool wave_ok = n0 < N;            // N % 64 == 0: a wave's columns are all in range or all out
+    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0.. and store nothing
+
+    f16v acc[RB][kCB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int b = 0; b < kCB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc[rb][b][i] = 0.0f;
+
+    // Both rings run one ring length of chunks ahead of the products: x
+    // (kXBuf - 1 chunks, in LDS) and the weights (kDepth chunks, in
+    // registers).  Every load is issued unconditionally, in the order
+    // [x of chunk c + kXBuf - 1] [products of chunk c] [weights of chunk
+    // c + kDepth] per chunk, so the x of chunk c is complete once at most
+    // 16 + 2 RB younger loads are outstanding.  The loop is unrolled by one
+    // ring length so that every slot is named statically and refilled in
+    // place right after it is consumed; the chunk count is padded to a
+    // multiple of it with chunks that read zeros and add nothing.
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)((int64_t)M * K * 2));
+    const WStreams wst = w_streams(codes, mins, scales, nsafe, K, lane);
+    const XLoads<RB> xl = x_loads<RB>(M, K, m0, wave, lane);
+    auto valid = [&](int c) { return c < c_end; };
+    // prologue in the loop's own order (as if chunks c_begin - 3 .. - 1 had
+    // run): W(c0) | x(c0) W(c0+1) | x(c0+1) W(c0+2), so that every wait the
+    // compiler derives for the loop body holds for the first pass as well
+    WChunk w[kDepth];
+    w[0] = load_w_chunk(wst, (uint32_t)c_begin, valid(c_begin));
+#pragma unroll
+    for (int i = 0; i < kXBuf - 1; ++i) {
+        issue_x<RB>(rx, xl, (uint32_t)(c_begin + i), valid(c_begin + i), sx[i], wave);
+        w[i + 1] = load_w_chunk(wst, (uint32_t)(c_begin + i + 1), valid(c_begin + i + 1));
+    }
+    const int n_pad = (max(c_end - c_begin, 0) + kDepth - 1) / kDepth * kDepth;
+    for (int i = 0; i < n_pad; i += kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            const int c = c_begin + i + u;
+            // x of chunk c has landed (this wave's pieces: the wait), then every
+            // wave's pieces have, and every wave is done reading buffer
+            // (u + 2) % 3 (the barrier).  One statement, no fence: a workgroup
+            // fence would wait for every earlier load into LDS, x of chunks c+1
+            // included.
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(16 + 2 * RB) : "memory");
+            issue_x<RB>(rx, xl, (uint32_t)(c + kXBuf - 1), valid(c + kXBuf - 1), sx[(u + kXBuf - 1) % kXBuf], wave);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_chunk<RB>(w[u], sx[u], lane, acc);
+            w[u] = load_w_chunk(wst, (uint32_t)(c + kDepth), valid(c + kDepth));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if (!wave_ok)
+        return;
+    // D layout: value i of lane l is row 8*(i/4) + 4*(l/32) + i%4 of the
+    // block, column l%32
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+            const int64_t n = n0 + b * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (m < M) {
+                    if (splits == 1)
+                        y[(int64_t)m * N + n] = (_Float16)acc[rb][b][i];
+                    else
+                        ws[((int64_t)split * M + m) * N + n] = acc[rb][b][i];
+                }
+            }
+        }
     }
 }
 
@@ -389,12 +377,12 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ w
     y[i + 3] = (_Float16)s.w;
 }
 
-template <int MB>
-int launch_gemm_mb(const GemmArgs &g, hipStream_t st)
+template <int RB>
+int launch_gemm_rb(const GemmArgs &g, hipStream_t st)
 {
     const dim3 grid((unsigned)((g.N + kColsPerGroup - 1) / kColsPerGroup), (unsigned)g.splits,
-                    (unsigned)((g.M + 16 * MB - 1) / (16 * MB)));
-    hipLaunchKernelGGL((k_gemm_w4<MB, kGemmWaveColBlocks>), grid, dim3(kThreads), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
+                    (unsigned)((g.M + 32 * RB - 1) / (32 * RB)));
+    hipLaunchKernelGGL((k_gemm_w4<RB>), grid, dim3(kThreads), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
                        static_cast<const uint16_t *>(g.mins), static_cast<const uint16_t *>(g.scales),
                        static_cast<_Float16 *>(g.y), g.ws, g.M, g.N, g.K, g.chunks_per_split);
     int e = (int)hipGetLastError();
@@ -408,20 +396,17 @@ int launch_gemm_mb(const GemmArgs &g, hipStream_t st)
 
 } // namespace
 
-int gemm_row_blocks(int M) { return M >= 144 ? 9 : (M + 15) / 16; }
+// Row blocks of 32 per row tile: up to 5 (160 rows; M = 144 pads 16 rows).
+int gemm_row_blocks(int M) { return M > 128 ? 5 : (M + 31) / 32; }
 
 int launch_gemm_w4(const GemmArgs &g, hipStream_t st)
 {
     switch (gemm_row_blocks(g.M)) {
-    case 1: return launch_gemm_mb<1>(g, st);
-    case 2: return launch_gemm_mb<2>(g, st);
-    case 3: return launch_gemm_mb<3>(g, st);
-    case 4: return launch_gemm_mb<4>(g, st);
-    case 5: return launch_gemm_mb<5>(g, st);
-    case 6: return launch_gemm_mb<6>(g, st);
-    case 7: return launch_gemm_mb<7>(g, st);
-    case 8: return launch_gemm_mb<8>(g, st);
-    default: return launch_gemm_mb<9>(g, st);
+    case 1: return launch_gemm_rb<1>(g, st);
+    case 2: return launch_gemm_rb<2>(g, st);
+    case 3: return launch_gemm_rb<3>(g, st);
+    case 4: return launch_gemm_rb<4>(g, st);
+    default: return launch_gemm_rb<5>(g, st);
     }
 }
 

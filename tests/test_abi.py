@@ -259,12 +259,13 @@ def test_gemm_w4_validation_and_workspace(L):
     assert auto > 0 and auto % (144 * 12288 * 4) == 0
     # automatic choices on the OPT-175B projections (K = 12288, 96 chunks of 128), at or within a few %
     # of the fastest measured: QKV (N = 36864, 144 column tiles, one under-filled round) takes 3 splits
-    # at M = 144, 64 and 16, 7 at M = 32; at M = 1 (two workgroups per CU) one round holds 3; the output
-    # projection (48 tiles) 5 at M = 144, 64 and 32, 10 at M = 1; 288 tiles (M = 150) keep 1
-    for M, N, splits in [(144, 36864, 3), (64, 36864, 3), (32, 36864, 7), (16, 36864, 3), (1, 36864, 3),
-                         (144, 12288, 5), (64, 12288, 5), (32, 12288, 5), (1, 12288, 10)]:
+    # at M = 144 and 64, 7 at M = 32 and 16, 16 at M = 1 (partials cost ~nothing); the output
+    # projection (48 tiles) 5 at every M; M = 150 is still one row tile of 160 rows (3 splits), M = 161
+    # makes two (288 tiles) and keeps 1
+    for M, N, splits in [(144, 36864, 3), (64, 36864, 3), (32, 36864, 7), (16, 36864, 7), (1, 36864, 16),
+                         (144, 12288, 5), (64, 12288, 5), (32, 12288, 5), (1, 12288, 5), (150, 36864, 3)]:
         assert L.kvq_gemm_w4_workspace_bytes(M, N, 12288, 0) == splits * M * N * 4, (M, N)
-    assert L.kvq_gemm_w4_workspace_bytes(150, 36864, 12288, 0) == 0
+    assert L.kvq_gemm_w4_workspace_bytes(161, 36864, 12288, 0) == 0
     # a split count that leaves an empty split is reduced: 96 chunks in 7 splits -> 14 per split, 7 splits
     assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 7) == 7 * 64 * 4
     assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 95) == 48 * 64 * 4  # ceil(96/95)=2 chunks each -> 48 splits

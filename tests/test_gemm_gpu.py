@@ -109,7 +109,18 @@ def test_gemm_shapes_full(M, N, K, splits):
     of 144), partial column groups (N = 64, 320), K ranges split 1, 3 ways or automatically."""
     require_gpu()
     if splits > K // 128:
-        pytest.skip("more splits than 128-wide chunks")
+        # more splits than 128-wide chunks of K: refused on the host, nothing enqueued
+        w = _weights(N, K, 5100 + M + N + K + splits)
+        x = W.random_fp16((M, K), 5101 + M + N + K + splits, DEV)
+        codes, mins, scales = kvq.kvq_w4_quantize(w)
+        y = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        with pytest.raises(kvq.KvqError) as ei:
+            kvq.gemm_w4a16(x, codes, mins, scales, y=y, num_splits=splits)
+        assert ei.value.status == -2
+        assert kvq.kvq_gemm_w4_workspace_bytes(M, N, K, splits) == 0
+        torch.cuda.synchronize()
+        assert torch.isnan(y.float()).all()
+        return
     x, _, (c, m, s), y = _run(M, N, K, 5100 + M + N + K + splits)
     xh = x.cpu().numpy()
     ref = oracle.gemm_w4a16(xh, c, m, s)
