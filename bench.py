@@ -698,6 +698,11 @@ def cpu_model() -> str:
 
 
 # --------------------------------------------------------------------- main
+LEGS = {"prefill": lambda: time_prefill(), "proj": lambda: time_projections(), "topk": lambda: time_topk(),
+        "split": lambda: time_split_context(), "meta16": lambda: time_meta_f16(),
+        "host": lambda: time_host_attention(), "read_ceiling": lambda: hbm_read_ceiling()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -716,6 +721,8 @@ def main():
                     help="min/scale plane type of the timed stack (default binary32)")
     ap.add_argument("--fused", action="store_true",
                     help="append and attend in one kv_append_attend_q4 launch per layer-step")
+    ap.add_argument("--leg", choices=tuple(LEGS), default=None,
+                    help="run this one leg alone and print its JSON (for profiling one kernel)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -726,6 +733,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import workloads as W
+
+    if args.leg:
+        log(f"[bench] leg {args.leg} alone")
+        print(json.dumps({args.leg: LEGS[args.leg]()}), flush=True)
+        return
 
     w = W.OPT_175B
     job = Job(w, args.layers or w.layers, args.decode_steps or w.n, args.meta, args.fused)

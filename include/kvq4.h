@@ -308,6 +308,23 @@ void kvq_host_use_simd(int enable);
  * ---------------------------------------------------------------------- */
 int kvq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *hip_stream);
 
+/* ------------------------------------------------------------------------
+ * Verification: the codec's two divisions.  Every quantiser above stores
+ * scale = (max - min)/15 and codes round((x - min) * inv) ("FlexGen研究学术报告"
+ * section 三.2(C): group-wise asymmetric 4-bit, min/max affine code), with
+ * binary32 metadata inv = 15/(max - min), with binary16 metadata scale
+ * rounded to binary16 and inv = 1/scale; each quotient is meant to be the
+ * correctly rounded binary32 value.  The kernels compute them without the
+ * generic division sequence; this call runs that same device code on n
+ * ranges rng[i] > 0 (device, binary32) and writes the stored scale (widened
+ * to binary32) and the inverse to scale[i] and inv[i] (device, binary32), so
+ * that every range the codec can meet can be checked.  meta_dtype
+ * KVQ_META_F32 or KVQ_META_F16 (KVQ_EUNSUPPORTED otherwise); pointers
+ * non-NULL and 4-byte aligned (KVQ_EINVAL); 0 <= n < 2^31 * 256
+ * (KVQ_ERANGE).  Enqueued on hip_stream; nothing is allocated.
+ * ---------------------------------------------------------------------- */
+int kvq_codec_params(const float *rng, int64_t n, int meta_dtype, float *scale, float *inv, void *hip_stream);
+
 /* Static text for a status code. */
 const char *kvq_strerror(int status);
 

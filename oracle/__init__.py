@@ -73,11 +73,12 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_prefill_attend.argtypes = [I, I, I, P, P, P, P]
     L.oracle_attend_rows.argtypes = [I, I, P, P, P, P]
     L.oracle_prefill_attend_rows.argtypes = [I, I, I, P, P, P, I, P, P]
+    L.oracle_codec_params.argtypes = [I, ctypes.c_int64, P, P, P]
     for f in ("oracle_quantize_group", "oracle_quantize_rows", "oracle_quantize_group_m16", "oracle_quantize_rows_m16",
               "oracle_dequant_rows", "oracle_dequant_rows_f16",
               "oracle_scores",
               "oracle_attend", "oracle_attend_subset", "oracle_select_topk", "oracle_attend_topk",
-              "oracle_attend_rows", "oracle_prefill_attend", "oracle_prefill_attend_rows"):
+              "oracle_attend_rows", "oracle_prefill_attend", "oracle_prefill_attend_rows", "oracle_codec_params"):
         getattr(L, f).restype = None
     return L
 
@@ -166,6 +167,16 @@ def quantize_group(x64):
     sc = np.zeros(1, np.float32)
     lib().oracle_quantize_group(_ptr(x), _ptr(codes), _ptr(mn), _ptr(sc))
     return codes, mn[0], sc[0]
+
+
+def codec_params(rng, meta: str = "f32"):
+    """The codec's stored scale (widened to float32) and inverse for each group range in the
+    float32 array `rng` (all > 0), binary32 (meta "f32") or binary16 ("f16") metadata."""
+    r = np.ascontiguousarray(rng, dtype=np.float32).reshape(-1)
+    scale = np.empty_like(r)
+    inv = np.empty_like(r)
+    lib().oracle_codec_params(1 if meta == "f16" else 0, r.size, _ptr(r), _ptr(scale), _ptr(inv))
+    return scale, inv
 
 
 def quantize_rows(x):

@@ -220,6 +220,29 @@ void oracle_quantize_group_m16(const uint16_t *x, uint8_t *codes, uint16_t *out_
     *out_scale = s16;
 }
 
+/* The stored scale and the inverse the codes are taken with, for n group
+ * ranges rng[i] > 0: binary32 metadata (meta16 = 0) as in
+ * oracle_quantize_group (scale = rng/15, inv = 15/rng), binary16 metadata
+ * (meta16 = 1) as in oracle_quantize_group_m16 (scale = rng/15 rounded to
+ * binary16, inv = 1/scale); inv = 0 where the stored scale is 0.  The stored
+ * scale is returned widened to binary32.                                   */
+void oracle_codec_params(int meta16, int64_t n, const float *rng, float *scale, float *inv)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float r = rng[i];
+        float s, v;
+        if (!meta16) {
+            s = r / 15.0f;
+            v = 15.0f / r;
+        } else {
+            s = oracle_f16_to_f32(oracle_f32_to_f16(r / 15.0f));
+            v = s != 0.0f ? 1.0f / s : 0.0f;
+        }
+        scale[i] = s;
+        inv[i] = v;
+    }
+}
+
 /* Quantise one token row of d fp16 values (d a multiple of 64): group g
  * covers elements 64g..64g+63; codes[d/2], mins[d/64], scales[d/64].      */
 void oracle_quantize_row(int d, const uint16_t *x, uint8_t *codes, float *mins, float *scales)

@@ -22,7 +22,7 @@ __all__ = [
     "kv_append_quant", "decode_attention_q4", "decode_attention_q4_tuned", "kv_append_attend_q4",
     "decode_attention_q4_topk", "decode_attention_q4_noalloc", "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16",
     "kv_quantize_prefill_host", "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd",
-    "kvq_host_use_simd", "kvq_stream_read",
+    "kvq_host_use_simd", "kvq_stream_read", "kvq_codec_params",
     "library_path", "load_library", "GROUP",
 ]
 
@@ -41,7 +41,7 @@ EXPORTED = ("kvq_cache_bytes", "kv_quantize_prefill", "kv_quantize_prefill_atten
             "decode_attention_q4_noalloc",
             "kvq_w4_quantize", "kvq_gemm_w4_workspace_bytes", "gemm_w4a16", "kv_quantize_prefill_host",
             "kv_append_quant_host", "decode_attention_q4_host", "kvq_host_simd", "kvq_host_use_simd", "kvq_strerror",
-            "kvq_stream_read")
+            "kvq_stream_read", "kvq_codec_params")
 
 
 class KvqDims(ctypes.Structure):
@@ -117,6 +117,8 @@ def load_library() -> ctypes.CDLL:
     L.kvq_host_use_simd.restype = None
     L.kvq_stream_read.argtypes = [P, SZ, P, P]
     L.kvq_stream_read.restype = ctypes.c_int
+    L.kvq_codec_params.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, P, P]
+    L.kvq_codec_params.restype = ctypes.c_int
     L.kvq_strerror.argtypes = [ctypes.c_int]
     L.kvq_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -416,6 +418,22 @@ def kvq_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     if sink.element_size() != 4 or not sink.is_cuda or sink.numel() < (nbytes + 65535) // 65536:
         raise ValueError("sink must be a 4-byte CUDA tensor of ceil(nbytes/65536) elements")
     _check(load_library().kvq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_stream_read")
+
+
+def kvq_codec_params(rng: torch.Tensor, meta: str = "f32", scale: torch.Tensor | None = None,
+                     inv: torch.Tensor | None = None, stream=None):
+    """The codec's stored scale and inverse scale (binary32) for each range in the float32
+    CUDA tensor `rng` (all > 0), as every quantiser of this library computes them."""
+    if not rng.is_cuda or rng.dtype != torch.float32 or not rng.is_contiguous():
+        raise TypeError("rng must be a contiguous float32 CUDA tensor")
+    scale = _out_like(rng, scale, stream)
+    inv = _out_like(rng, inv, stream)
+    for t, name in ((scale, "scale"), (inv, "inv")):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rng.numel():
+            raise TypeError(f"{name} must be a contiguous float32 CUDA tensor of rng's size")
+    _check(load_library().kvq_codec_params(_ptr(rng), rng.numel(), _META[meta][0], _ptr(scale), _ptr(inv),
+                                           _stream(stream)), "kvq_codec_params")
+    return scale, inv
 
 
 # ------------------------------------------------------------------ host path

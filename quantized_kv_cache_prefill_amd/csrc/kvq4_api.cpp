@@ -488,6 +488,21 @@ int kvq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *hip_str
     return status_of(kvq::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(hip_stream)));
 }
 
+int kvq_codec_params(const float *rng, int64_t n, int meta_dtype, float *scale, float *inv, void *hip_stream)
+{
+    if (n < 0 || n >= (int64_t)0x7FFFFFFF * 256)
+        return KVQ_ERANGE;
+    if (meta_dtype != KVQ_META_F32 && meta_dtype != KVQ_META_F16)
+        return KVQ_EUNSUPPORTED;
+    if (n == 0)
+        return KVQ_OK;
+    for (const void *p : {(const void *)rng, (const void *)scale, (const void *)inv})
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3u) != 0)
+            return KVQ_EINVAL;
+    return status_of(kvq::launch_codec_params(rng, n, meta_dtype == KVQ_META_F16, scale, inv,
+                                              static_cast<hipStream_t>(hip_stream)));
+}
+
 int kvq_host_simd() { return kvq::host_has_avx512(); }
 
 void kvq_host_use_simd(int enable) { kvq::host_set_simd(enable); }

@@ -211,13 +211,37 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // ===========================================================================
 // Quantise.  Each lane loads 8 fp16 values (16 bytes); 8 consecutive lanes
 // hold one 64-element group and reduce its min/max with three DPP steps.
-// Row r of the flattened work list is (pair, token) = (r / s_src, r % s_src),
-// so lanes with consecutive rows write consecutive cache slots: the 16-byte
-// reads are full 256-byte rows and the code/metadata writes are contiguous.
+// R = 4 (a prompt): workgroup x = (pair, chunk of RPB*R tokens of that pair),
+// so the pair and its (batch row, head) are uniform across the workgroup
+// (scalar arithmetic) and lanes with consecutive rows write consecutive cache
+// slots; the 16-byte reads are whole 256-byte rows.  R = 1 (one appended
+// token per pair): RPB consecutive pairs per workgroup.
 // ===========================================================================
+// n / d for 32-bit n (Granlund & Montgomery, "Division by invariant integers
+// using multiplication", the round-up multiplier): l = ceil(log2 d),
+// mul = floor(2^32 (2^l - d) / d) + 1, q = (t + ((n - t) >> min(l,1))) >> max(l-1,0)
+// with t = the high half of mul * n.
+struct FastDiv {
+    uint32_t mul, sh1, sh2;
+};
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f)
+{
+    const uint32_t t = __umulhi(n, f.mul);
+    return (t + ((n - t) >> f.sh1)) >> f.sh2;
+}
+FastDiv make_fast_div(uint32_t d)
+{
+    int l = 0;
+    while ((1ull << l) < d)
+        ++l;
+    const uint64_t mul = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{(uint32_t)mul, (uint32_t)std::min(l, 1), (uint32_t)std::max(l - 1, 0)};
+}
+
 template <int D, int R, typename Meta>
 __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_src, const uint4 *__restrict__ v_src,
-                                                  int64_t rows, int s_src, int a, int S, int t_dst0,
+                                                  int pairs, int s_src, int chunks, FastDiv by_chunks, int a,
+                                                  FastDiv by_a, int S, int t_dst0,
                                                   uint32_t *__restrict__ k_codes, uint32_t *__restrict__ v_codes,
                                                   Meta *__restrict__ k_min, Meta *__restrict__ k_scale,
                                                   Meta *__restrict__ v_min, Meta *__restrict__ v_scale)
@@ -231,23 +255,30 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
     Meta *__restrict__ mins = is_v ? v_min : k_min;
     Meta *__restrict__ scales = is_v ? v_scale : k_scale;
     const int lir = threadIdx.x % LPR;
-    const int64_t row0 = (int64_t)blockIdx.x * (RPB * R) + threadIdx.x / LPR;
+    const int rib = threadIdx.x / LPR; // row within the workgroup's RPB
+
+    int pair, t0;
+    if constexpr (R == 1) {
+        pair = min((int)blockIdx.x * RPB + rib, pairs - 1); // lanes past the last pair redo it, storing nothing
+        t0 = 0;
+    } else {
+        pair = (int)fast_div(blockIdx.x, by_chunks);
+        t0 = ((int)blockIdx.x - pair * chunks) * (RPB * R) + rib;
+    }
+    const int bi = (int)fast_div((uint32_t)pair, by_a);
+    const int ai = pair - bi * a;
+    const uint4 *__restrict__ row0 = src + ((int64_t)bi * s_src * a + ai) * LPR + lir; // token 0 of the pair
+    const int64_t tok_stride = (int64_t)a * LPR;
 
     uint4 x[R];
-    int64_t slot[R];
     bool ok[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        const int64_t row = row0 + (int64_t)u * RPB;
-        ok[u] = row < rows;
-        const int64_t rc = ok[u] ? row : rows - 1;
-        const int64_t pair = rc / s_src;
-        const int64_t ti = rc - pair * s_src;
-        const int64_t bi = pair / a;
-        const int64_t ai = pair - bi * a;
-        x[u] = ld_stream16(src + ((bi * s_src + ti) * a + ai) * (D / 8) + lir);
-        slot[u] = pair * S + t_dst0 + ti;
+        const int t = t0 + u * RPB;
+        ok[u] = R == 1 ? (int)blockIdx.x * RPB + rib < pairs : t < s_src;
+        x[u] = ld_stream16(row0 + (int64_t)min(t, s_src - 1) * tok_stride);
     }
+    const int64_t slot0 = (int64_t)pair * S + t_dst0 + t0;
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         uint32_t word;
@@ -257,10 +288,11 @@ __global__ __launch_bounds__(256) void k_quantize(const uint4 *__restrict__ k_sr
         // and ordinary stores left dirty lines whose write-back slowed the next
         // decode launch by ~5% (measured on MI355X).
         if (ok[u]) {
-            __builtin_nontemporal_store(word, codes + slot[u] * (D / 8) + lir);
+            const int64_t slot = slot0 + u * RPB;
+            __builtin_nontemporal_store(word, codes + slot * (D / 8) + lir);
             if ((lir & 7) == 0) {
-                __builtin_nontemporal_store((Meta)mn, mins + slot[u] * G + (lir >> 3));
-                __builtin_nontemporal_store((Meta)scale, scales + slot[u] * G + (lir >> 3));
+                __builtin_nontemporal_store((Meta)mn, mins + slot * G + (lir >> 3));
+                __builtin_nontemporal_store((Meta)scale, scales + slot * G + (lir >> 3));
             }
         }
     }
@@ -1393,20 +1425,28 @@ template <int D, typename Meta>
 int launch_quantize_d(const CachePlanes &c, const void *k, const void *v, int b, int s_src, int t_dst0,
                       hipStream_t st)
 {
-    const int64_t rows = (int64_t)b * c.a * s_src;
-    const int R = (s_src == 1) ? 1 : 4;
-    const int64_t rows_per_block = (int64_t)(256 / (D / 8)) * R;
-    const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block), 2);
+    constexpr int RPB = 256 / (D / 8);
+    const int pairs = b * c.a; // < 2^31: checked with the cache dimensions
     auto *kc = reinterpret_cast<uint32_t *>(c.k_codes);
     auto *vc = reinterpret_cast<uint32_t *>(c.v_codes);
     const auto *ks = static_cast<const uint4 *>(k);
     const auto *vs = static_cast<const uint4 *>(v);
-    if (R == 1)
-        hipLaunchKernelGGL((k_quantize<D, 1, Meta>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc,
-                           vc, meta<Meta>(c.k_min), meta<Meta>(c.k_scale), meta<Meta>(c.v_min), meta<Meta>(c.v_scale));
-    else
-        hipLaunchKernelGGL((k_quantize<D, 4, Meta>), grid, dim3(256), 0, st, ks, vs, rows, s_src, c.a, c.S, t_dst0, kc,
-                           vc, meta<Meta>(c.k_min), meta<Meta>(c.k_scale), meta<Meta>(c.v_min), meta<Meta>(c.v_scale));
+    const FastDiv by_a = make_fast_div((uint32_t)c.a);
+    if (s_src == 1) {
+        const dim3 grid((unsigned)((pairs + RPB - 1) / RPB), 2);
+        hipLaunchKernelGGL((k_quantize<D, 1, Meta>), grid, dim3(256), 0, st, ks, vs, pairs, 1, 1, make_fast_div(1),
+                           c.a, by_a, c.S, t_dst0, kc, vc, meta<Meta>(c.k_min), meta<Meta>(c.k_scale),
+                           meta<Meta>(c.v_min), meta<Meta>(c.v_scale));
+    } else {
+        constexpr int R = 4;
+        const int chunks = (s_src + RPB * R - 1) / (RPB * R);
+        const int64_t blocks = (int64_t)pairs * chunks;
+        if (blocks > 0x7FFFFFFF)
+            return (int)hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((k_quantize<D, R, Meta>), dim3((unsigned)blocks, 2), dim3(256), 0, st, ks, vs, pairs,
+                           s_src, chunks, make_fast_div((uint32_t)chunks), c.a, by_a, c.S, t_dst0, kc, vc,
+                           meta<Meta>(c.k_min), meta<Meta>(c.k_scale), meta<Meta>(c.v_min), meta<Meta>(c.v_scale));
+    }
     return (int)hipGetLastError();
 }
 
@@ -1629,6 +1669,31 @@ int launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_
     const int64_t blocks = (n16 + 256 * 16 - 1) / (256 * 16);
     hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(256), 0, st, static_cast<const uint4 *>(buf), n16,
                        sink);
+    return (int)hipGetLastError();
+}
+
+// The codec's scale and inverse for each given range (codec_params, the code
+// path every quantiser takes).
+template <typename Meta>
+__global__ __launch_bounds__(256) void k_codec_params(const float *__restrict__ rng, int64_t n,
+                                                      float *__restrict__ scale, float *__restrict__ inv)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+        float s, v;
+        codec_params<Meta>(rng[i], s, v);
+        scale[i] = s;
+        inv[i] = v;
+    }
+}
+
+int launch_codec_params(const float *rng, int64_t n, bool meta_f16, float *scale, float *inv, hipStream_t st)
+{
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (meta_f16)
+        hipLaunchKernelGGL(k_codec_params<_Float16>, grid, dim3(256), 0, st, rng, n, scale, inv);
+    else
+        hipLaunchKernelGGL(k_codec_params<float>, grid, dim3(256), 0, st, rng, n, scale, inv);
     return (int)hipGetLastError();
 }
 

@@ -82,6 +82,10 @@ int gemm_row_blocks(int M);
 // none).
 int launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
+// The codec's stored scale and inverse scale (as binary32) for n group
+// ranges rng[i] > 0, with binary32 (meta_f16 false) or binary16 metadata.
+int launch_codec_params(const float *rng, int64_t n, bool meta_f16, float *scale, float *inv, hipStream_t st);
+
 // Quantise W fp16 [N][K] with the binary16-metadata codec: codes [N][K/2],
 // mins/scales binary16 [N][K/64].
 int launch_quantize_weight(const void *w, int N, int K, uint8_t *codes, void *mins, void *scales, hipStream_t st);

@@ -240,6 +240,38 @@ def pin_codec_constant_group_roundtrip():
         assert np.array_equal(xhat, x.astype(np.float64))
 
 
+def pin_codec_params_are_correctly_rounded_quotients():
+    """The scale and inverse the codec stores / codes with ([FG-report] 三.2(C)): with binary32
+    metadata the IEEE binary32 quotients rng/15 and 15/rng, with binary16 metadata rng/15
+    rounded to binary16 by numpy and its binary32 reciprocal -- numpy's float32 division is
+    the correctly rounded quotient.  Ranges: log-uniform over every binade the codec can meet
+    (2^-24 .. 2^17) plus binade edges; and the same values appear in quantize_group's stored
+    scale for groups {0, .., rng}."""
+    rr = np.random.default_rng(2024)
+    e = rr.uniform(-24.0, 17.0, 200_000)
+    r = np.exp2(e).astype(np.float32)
+    edges = np.array([2.0 ** k for k in range(-24, 18)], np.float32)
+    r = np.concatenate([r, edges, np.nextafter(edges, np.float32(0)), np.nextafter(edges, np.float32(1e9))])
+    r = r[(r >= np.float32(2.0 ** -24)) & (r <= np.float32(2.0 ** 17))].astype(np.float32)
+    s32, i32 = oracle.codec_params(r, "f32")
+    assert np.array_equal(s32, r / np.float32(15)), "binary32 scale is not rng/15"
+    assert np.array_equal(i32, np.float32(15) / r), "binary32 inverse is not 15/rng"
+    s16, i16 = oracle.codec_params(r, "f16")
+    want_s = (r / np.float32(15)).astype(np.float16).astype(np.float32)
+    assert np.array_equal(s16, want_s), "binary16 scale is not rng/15 rounded to binary16"
+    with np.errstate(divide="ignore"):
+        want_i = np.where(want_s != 0, np.float32(1) / want_s, np.float32(0)).astype(np.float32)
+    assert np.array_equal(i16, want_i), "binary16-metadata inverse is not 1/scale (0 for scale 0)"
+    # the group quantisers store these scales: a group {0, v} has range v
+    for v in (np.float16(1.0), np.float16(0.3), np.float16(6.0e-8), np.float16(65504.0), np.float16(2.0e-5)):
+        g = np.zeros(oracle.GROUP, np.float16)
+        g[7] = v
+        _, _, sc = oracle.quantize_group(g)
+        assert sc == oracle.codec_params(np.array([np.float32(v)]), "f32")[0][0]
+        _, _, sc16 = oracle.quantize_group_m16(g)
+        assert np.float32(sc16) == oracle.codec_params(np.array([np.float32(v)]), "f16")[0][0]
+
+
 def pin_codec_rows_are_groupwise():
     """A row of d = 64*G values is G independent groups of 64 contiguous head_dim elements
     (group axis = head_dim), laid out group after group."""

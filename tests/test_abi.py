@@ -287,3 +287,16 @@ def test_noalloc_refusals_before_any_launch(L):
     assert L.decode_attention_q4_noalloc(ctypes.byref(c), None, 4, FAKE, 0, st) == KVQ_EINVAL
     assert L.decode_attention_q4_noalloc(ctypes.byref(c), FAKE, 4, FAKE + 2, 0, st) == KVQ_EINVAL
     assert L.decode_attention_q4_noalloc(None, FAKE, 4, FAKE, 0, st) == KVQ_EINVAL
+
+
+def test_codec_params_refusals_before_any_launch(L):
+    """kvq_codec_params checks its arguments on the host: NULL or misaligned pointers are
+    KVQ_EINVAL, an unknown metadata type KVQ_EUNSUPPORTED, a negative count KVQ_ERANGE; a
+    count of 0 enqueues nothing."""
+    st = ctypes.c_void_p(0)
+    assert L.kvq_codec_params(None, 16, 0, FAKE, FAKE, st) == KVQ_EINVAL
+    assert L.kvq_codec_params(FAKE, 16, 0, FAKE + 2, FAKE, st) == KVQ_EINVAL
+    assert L.kvq_codec_params(FAKE, 16, 0, FAKE, None, st) == KVQ_EINVAL
+    assert L.kvq_codec_params(FAKE, 16, 7, FAKE, FAKE, st) == KVQ_EUNSUPPORTED
+    assert L.kvq_codec_params(FAKE, -1, 0, FAKE, FAKE, st) == KVQ_ERANGE
+    assert L.kvq_codec_params(FAKE, 0, 1, None, None, st) == KVQ_OK

@@ -17,6 +17,11 @@ from tests import oracle_pins
 
 MUTANTS = [
     ("round_half_away", "float r = rintf(t);", "float r = roundf(t);"),
+    ("params_inv_from_scale", "            v = 15.0f / r;\n", "            v = 1.0f / s;\n"),
+    ("params_scale_times_reciprocal", "            s = r / 15.0f;\n", "            s = r * (1.0f / 15.0f);\n"),
+    ("params_m16_scale_not_rounded", "            s = oracle_f16_to_f32(oracle_f32_to_f16(r / 15.0f));\n",
+     "            s = r / 15.0f;\n"),
+    ("params_m16_inv_of_range", "            v = s != 0.0f ? 1.0f / s : 0.0f;\n", "            v = s != 0.0f ? 15.0f / r : 0.0f;\n"),
     ("m16_codes_against_binary32_scale", "        float inv = 1.0f / scale;\n",
      "        float inv = 15.0f / rng;\n"),
     ("m16_scale_truncated", "s16 = oracle_f32_to_f16(rng / 15.0f);",

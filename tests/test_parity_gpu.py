@@ -363,6 +363,35 @@ def test_dense_deterministic_and_ignores_unused_slots():
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
+@pytest.mark.parametrize("meta", ["f32", "f16"])
+@pytest.mark.parametrize("d,b,a,s,S", [(64, 3, 1, 1, 4), (64, 2, 7, 129, 140), (128, 1, 5, 63, 64),
+                                       (128, 3, 3, 65, 70), (128, 2, 96, 200, 210), (256, 2, 3, 33, 40),
+                                       (256, 1, 11, 300, 300), (128, 5, 13, 2, 3)])
+def test_quantize_shapes(meta, d, b, a, s, S):
+    """kv_quantize_prefill planes bit-exact in full for odd head counts (the work split into
+    (batch row, head) pairs and token chunks), prompts of 1, 2, and ragged lengths around the
+    64-, 128- and 256-token chunks, every head dim; then one append past the prompt (the
+    one-token path) -- every slot written compared, and the slots never written still hold
+    their 0xFF fill."""
+    require_gpu()
+    log(f"[quantize] d={d} b={b} a={a} s={s} S={S} meta={meta}")
+    cache = kvq.QuantKVCache(b, a, a * d, s, S - s, device=DEV, fill=0xFF, meta=meta)
+    k = W.random_fp16((b, s, a, d), 7100 + d + a + s, DEV)
+    v = W.random_fp16((b, s, a, d), 7200 + d + a + s, DEV, 0.5)
+    kvq.kv_quantize_prefill(cache, k, v)
+    hc = HostCache(b, a, d, S, meta)
+    hc.prefill(f16_np(k), f16_np(v))
+    if S > s:
+        kn = W.random_fp16((b, 1, a, d), 7300 + d + a, DEV, 3.0)
+        vn = W.random_fp16((b, 1, a, d), 7400 + d + a, DEV)
+        kvq.kv_append_quant(cache, kn, vn, s)
+        hc.append(f16_np(kn), f16_np(vn), s)
+    torch.cuda.synchronize()
+    _check_prefill_full(cache, hc, min(S, s + 1), f"quantize d={d} b={b} a={a} s={s}")
+    if S > s + 1:
+        assert (cache.k_codes[:, :, s + 1:] == 0xFF).all() and (cache.v_codes[:, :, s + 1:] == 0xFF).all()
+
+
 def test_codec_special_values():
     """Constant groups, signed zeros, fp16 extremes, subnormals, huge dynamic range,
     exact ties: the GPU planes equal the oracle's bit for bit."""
