@@ -489,7 +489,7 @@ def time_prefill(reps: int = 6):
     gbs = nb / fused / 1e6
     tfl = fl / fused / 1e9
     return {"workload": f"OPT-175B layer prompt: b={w.b} a={w.a} d={w.d} prompt {w.s}, causal, binary32 min/scale",
-            "kernel": "k_prefill<128,f32> (kv_quantize_prefill_attend)",
+            "kernel": "k_prefill_pp<f32> (kv_quantize_prefill_attend, head_dim 128)",
             "ms_per_call_median": round(fused, 4), "ms_per_call_min": round(all_ms[0], 4),
             "algorithmic_bytes": nb, "flops": fl,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kvq4_device.h"
 #include "kvq4_launch.h"
@@ -52,6 +53,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKeys = 64;    // keys per K/V tile
 constexpr int kWaves = 4;
+constexpr int kPrefillCUs = 256; // one persistent workgroup per compute unit
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -143,6 +145,24 @@ __device__ __forceinline__ void put_group(uint32_t *codes, Meta *mins, Meta *sca
         if ((c & 7) == 0) {
             __builtin_nontemporal_store((Meta)mn, mins + slot * (D / 64) + (c >> 3));
             __builtin_nontemporal_store((Meta)sc, scales + slot * (D / 64) + (c >> 3));
+        }
+    }
+}
+
+// The same for head_dim 128 with the plane bases of one (batch row, head)
+// (uniform) and the token's index within it: 32-bit offsets only.
+template <typename Meta>
+__device__ __forceinline__ void put_row_group(uint32_t *codes, Meta *mins, Meta *scales, int tok, int c, uint4 x,
+                                              bool ok)
+{
+    uint32_t word;
+    float mn, sc;
+    quant_lane8<Meta>(x, word, mn, sc); // every lane of the wave takes part (DPP)
+    if (ok) {
+        __builtin_nontemporal_store(word, codes + (uint32_t)(tok * 16 + c));
+        if ((c & 7) == 0) {
+            __builtin_nontemporal_store((Meta)mn, mins + (uint32_t)(tok * 2 + (c >> 3)));
+            __builtin_nontemporal_store((Meta)sc, scales + (uint32_t)(tok * 2 + (c >> 3)));
         }
     }
 }
@@ -274,8 +294,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
         }
         const _Float16 *lk = lds + (j & 1) * (Sh::LDS_K + Sh::LDS_V);
         const _Float16 *lv = lk + Sh::LDS_K;
-        if (j >= j_diag)
-            quantise_tile<D, Meta>(g, pair, j, lk, lv);
         if (kKeys * j <= qw0 + Sh::QW - 1) { // some key of the tile is visible to some query of the wave
             // S^T = K Q^T: st[c][qt] holds keys 16c + 4*g4 + r, query 16*qt + l16.  The K
             // operands of step kd+1 are read from LDS while the products of step kd run.
@@ -421,10 +439,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
         __syncthreads();
     }
 
+    // The cache planes of this workgroup's own positions: its diagonal tiles (j_diag
+    // and, unless the prompt ends first, j_diag + 1) are the loop's last two, still in
+    // the two tile buffers.  Quantised here, after the loop, so that the loop's waits
+    // for the next tile never wait on these stores as well.
+    for (int j = j_diag; j < n_tiles; ++j) {
+        const _Float16 *lk = lds + (j & 1) * (Sh::LDS_K + Sh::LDS_V);
+        quantise_tile<D, Meta>(g, pair, j, lk, lk + Sh::LDS_K);
+    }
+    __syncthreads(); // the tile buffers are read before the output rows reuse them
+
     // O = O^T / l.  Lane holds d = 16t + 4*g4 .. +3 of query 16*qt + l16; the wave's
     // rows are gathered in LDS (row pitch D + 8 halves) and written to HBM as whole
-    // rows, 16 bytes per lane.  Every wave passed the loop's last barrier, so the tile
-    // buffers are free.
+    // rows, 16 bytes per lane.
     constexpr int OP = D + 8;
     _Float16 *lo = lds + wave * Sh::QW * OP;
 #pragma unroll
@@ -449,6 +476,443 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
             __builtin_nontemporal_store(__builtin_bit_cast(u32x4b, x),
                                         reinterpret_cast<u32x4b *>(g.out + (((int64_t)bi * g.s_len + qtok) * g.a + ai) * D) + cc);
     }
+}
+
+// ===========================================================================
+// head_dim 128: one (batch row, head) at a time per workgroup, persistent.
+//
+// A workgroup of 16 waves walks its (batch row, head) pairs one after the
+// other; each pair's prompt is taken in passes of 256 queries (16 per wave),
+// pass c seeing keys 0 .. 256c + 255.  The K/V tiles (64 keys) of the whole
+// sequence of (pair, pass, tile) steps stream through a ring of three LDS
+// stages, two tiles ahead of the one in use, across pass and pair
+// boundaries, so the matrix cores never wait for a pass to start.  With four
+// waves per SIMD, the softmax of one wave runs beside the products of
+// another.  Pass c quantises its own positions' tiles (keys 256c ..
+// 256c + 255) while they are in LDS, one K row chunk and one V row chunk per
+// thread, so every prompt row is quantised exactly once.  The query rows of
+// the next pass are fetched into registers two steps early, in the same
+// order as the tiles, so the wait for a tile also covers them.
+// ===========================================================================
+namespace pp {
+constexpr int D = 128;
+constexpr int NW = 16;              // waves per workgroup
+constexpr int NT = 64 * NW;         // threads
+constexpr int QW = 16;              // queries per wave (one 16-row matrix-core tile)
+constexpr int QP = QW * NW;         // queries per pass
+constexpr int NSTG = 3;             // ring stages
+constexpr int TILE_H = kKeys * D;   // halves per K or V tile (16 KB)
+constexpr int STAGE_H = 2 * TILE_H; // K tile, then V tile
+constexpr int KS = D / 32;          // k-steps of q.k
+constexpr int DT = D / 16;          // 16-row tiles of O^T
+} // namespace pp
+
+struct PPArgs {
+    const uint16_t *q, *k, *v; // fp16 [b][s_len][a][128]
+    uint16_t *out;             // fp16 [b][s_len][a][128]
+    uint32_t *k_codes, *v_codes;
+    void *k_min, *k_scale, *v_min, *v_scale;
+    int a, S, s_len;
+    int pairs;     // b * a
+    int passes;    // ceil(s_len / 256)
+    int row_bytes; // a * 128 * 2: one token row of all heads
+    int valid_bytes; // (s_len - 1) * row_bytes + 256: a head's prompt, from its token 0
+    float c2, slack;
+};
+
+// The sequence of steps of one workgroup: pairs blockIdx.x, + gridDim.x, ...;
+// passes 0 .. passes-1 of each; key tiles 0 .. nj-1 of each pass.  Uniform
+// across the workgroup (scalar registers).  pair < 0: past the last step.
+struct Step {
+    int pair, c, j, nj;
+    int64_t base; // byte offset of token 0 of the pair's head in q, k, v and out
+};
+__device__ __forceinline__ int pass_tiles(const PPArgs &g, int c)
+{
+    return (min(g.s_len, pp::QP * (c + 1)) + kKeys - 1) / kKeys;
+}
+__device__ __forceinline__ int64_t head_base(const PPArgs &g, int pair)
+{
+    const int bi = pair / g.a, ai = pair - bi * g.a;
+    return ((int64_t)bi * g.s_len * g.a + ai) * pp::D * 2;
+}
+__device__ __forceinline__ Step first_step(const PPArgs &g)
+{
+    const int p = (int)blockIdx.x;
+    return Step{p < g.pairs ? p : -1, 0, 0, pass_tiles(g, 0), p < g.pairs ? head_base(g, p) : 0};
+}
+__device__ __forceinline__ void next_step(const PPArgs &g, Step &u)
+{
+    if (u.pair < 0)
+        return;
+    if (++u.j < u.nj)
+        return;
+    u.j = 0;
+    if (++u.c < g.passes) {
+        u.nj = pass_tiles(g, u.c);
+        return;
+    }
+    u.c = 0;
+    u.pair += (int)gridDim.x;
+    if (u.pair >= g.pairs) {
+        u.pair = -1;
+        return;
+    }
+    u.nj = pass_tiles(g, 0);
+    u.base = head_base(g, u.pair);
+}
+// A buffer resource over one head's prompt rows of x: offsets past the last
+// prompt row's 256 bytes read zeros (a step past the last reads zeros everywhere).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const PPArgs &g, const uint16_t *x, const Step &u)
+{
+    return rsrc(reinterpret_cast<const char *>(x) + u.base, u.pair < 0 ? 0 : g.valid_bytes);
+}
+
+// 16 bytes per lane, HBM -> LDS, as dma16, written out: the compiler does not
+// see an LDS write here, so it adds no wait for these loads before LDS reads of
+// other stages (it cannot tell the stages apart); the kernel's own waits and
+// barriers order every tile.  r: the 128-bit buffer resource words.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4s rsrc_words(const void *p, int bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return u32x4s{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+                  (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+__device__ __forceinline__ void dma16_raw(u32x4s r, _Float16 *dst, int voff)
+{
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
+// s_waitcnt encodings (gfx9): vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8.
+// Through the builtin, so that the compiler's own wait insertion knows of them.
+constexpr int kWaitVm2Lgkm0 = 0x0072; // vmcnt(2) lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
+
+template <typename Meta>
+__global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
+{
+    using namespace pp;
+    using Sh = Shape<D>;
+    // Three stages as three arrays, and the loop unrolled by three so that every
+    // access names its stage: the compiler can then tell that reads of one stage
+    // do not wait for the tile loads into the others.
+    __shared__ __attribute__((aligned(16))) _Float16 lds0[STAGE_H];
+    __shared__ __attribute__((aligned(16))) _Float16 lds1[STAGE_H];
+    __shared__ __attribute__((aligned(16))) _Float16 lds2[STAGE_H];
+    // Each wave's query rows of the current pass (16 rows, chunks swizzled as K's),
+    // loaded by the wave itself and read only by it.
+    __shared__ __attribute__((aligned(16))) _Float16 ldsq[NW * QW * D];
+    auto stage = [&](auto K) -> _Float16 * {
+        if constexpr (decltype(K)::value == 0)
+            return lds0;
+        else if constexpr (decltype(K)::value == 1)
+            return lds1;
+        else
+            return lds2;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64); // uniform: scalar registers
+    const int l16 = lane % 16, g4 = lane / 16;
+    const int tbytes = kKeys * g.row_bytes; // one key tile of a head
+
+    // This thread's 16-byte piece of each tile: LDS position tid (row tid/16,
+    // swizzled chunk tid%16), the unswizzled source chunk of K and of V.
+    const int dr = tid / 16, dcs = tid % 16;
+    const int dk = dr * g.row_bytes + 16 * (dcs ^ Sh::swz_k(dr));
+    const int dv = dr * g.row_bytes + 16 * (dcs ^ Sh::swz_v(dr));
+    auto issue = [&](const Step &u, _Float16 *st) {
+        const int step = u.j * tbytes;
+        const int nb = u.pair < 0 ? 0 : g.valid_bytes; // past the last step: zeros
+        dma16_raw(rsrc_words(reinterpret_cast<const char *>(g.k) + u.base, nb), st + 512 * wave, dk + step);
+        dma16_raw(rsrc_words(reinterpret_cast<const char *>(g.v) + u.base, nb), st + TILE_H + 512 * wave, dv + step);
+    };
+    // The wave's 16 query rows of pass u.c of pair u.pair, HBM -> its LDS rows:
+    // piece 64i + lane is row (64i + lane)/16, swizzled chunk (64i + lane)%16.
+    // Rows at or past the prompt's end read zeros (clamped to keep offsets small).
+    _Float16 *const myq = ldsq + wave * QW * D;
+    auto issue_q = [&](const Step &u) {
+        const u32x4s r = rsrc_words(reinterpret_cast<const char *>(g.q) + u.base, u.pair < 0 ? 0 : g.valid_bytes);
+#pragma unroll
+        for (int i = 0; i < QW * D / 8 / 64; ++i) {
+            const int pos = 64 * i + lane, qr = pos / 16, cs = pos % 16;
+            const int off = min(u.c * QP + wave * QW + qr, g.s_len) * g.row_bytes + 16 * (cs ^ Sh::swz_k(qr));
+            dma16_raw(r, myq + 512 * i, off);
+        }
+    };
+    // The pass after the one of step u.
+    auto next_pass = [&](Step u) {
+        u.j = 0;
+        if (++u.c < g.passes)
+            return u;
+        u.c = 0;
+        u.pair += (int)gridDim.x;
+        if (u.pair >= g.pairs)
+            u.pair = -1;
+        else
+            u.base = head_base(g, u.pair);
+        return u;
+    };
+
+    Step cu = first_step(g);
+    if (cu.pair < 0)
+        return;
+    Step cd = cu;
+    h8 qb[KS];
+    issue_q(cu);
+    issue(cd, lds0);
+    next_step(g, cd);
+    issue(cd, lds1);
+    next_step(g, cd);
+
+    f4 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+        o[t] = f4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    // The output rows of a finished pass go out at the top of the next step,
+    // before that step's loads, so that waiting for a tile never waits for them.
+    bool out_due = false;
+    int64_t out_base = 0;
+    int out_q0 = 0;
+    auto write_out = [&]() {
+        if (out_q0 < g.s_len) {
+            float lt = l;
+            lt += __shfl_xor(lt, 16);
+            lt += __shfl_xor(lt, 32);
+            const float inv = __builtin_amdgcn_rcpf(lt);
+            int ln = lane; // formed here rather than held across the loop
+            asm volatile("" : "+v"(ln));
+            const int qtok = out_q0 + ln % 16;
+            if (qtok < g.s_len) {
+                char *ob = reinterpret_cast<char *>(g.out) + out_base; // uniform
+                const uint32_t off = (uint32_t)(qtok * g.row_bytes + 8 * (ln / 16));
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+                    *reinterpret_cast<h4 *>(ob + off + 32 * t) =
+                        h4{(_Float16)(o[t][0] * inv), (_Float16)(o[t][1] * inv), (_Float16)(o[t][2] * inv),
+                           (_Float16)(o[t][3] * inv)};
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+            o[t] = f4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        l = 0.f;
+    };
+
+    // One step: the tile in stage RS, the loads two steps ahead into stage (RS+2)%3.
+    auto run_step = [&](auto RS) -> bool {
+        if (cu.pair < 0)
+            return false;
+        constexpr int rs = decltype(RS)::value;
+        // This step's tile has landed in every thread (only the loads issued one
+        // step ago may still be in flight: the issue order below keeps the stores
+        // ahead of them), and every wave is done with the stage reused below.
+        __builtin_amdgcn_s_waitcnt(kWaitVm2Lgkm0);
+        __builtin_amdgcn_s_barrier();
+        if (out_due) {
+            write_out();
+            out_due = false;
+        }
+        if (cu.j == 0) {
+            // A new pass: its query rows (loaded ahead of this step's tile, so they
+            // have landed) into the Q^T operand registers -- lane: query l16,
+            // d = 32kd + 8*g4 .. +7 -- then the next pass's rows into the same LDS
+            // rows, once these reads are done.
+            const int sq = Sh::swz_k(l16);
+#pragma unroll
+            for (int kd = 0; kd < KS; ++kd)
+                qb[kd] = *reinterpret_cast<const h8 *>(myq + l16 * D + 8 * ((4 * kd + g4) ^ sq));
+            __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
+            issue_q(next_pass(cu));
+        }
+        const _Float16 *lk = stage(RS);
+        const _Float16 *lv = lk + TILE_H;
+        if (cu.j * kKeys >= cu.c * QP) { // this pass's own positions: quantise them
+            // plane bases of the pair (uniform), 32-bit offsets within its S slots
+            const int64_t slot0 = (int64_t)cu.pair * g.S;
+            int qr = dr, qc = dcs; // formed here rather than held across the loop
+            asm volatile("" : "+v"(qr), "+v"(qc));
+            const int tok = cu.j * kKeys + qr;
+            const uint4 xk = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * (qc ^ Sh::swz_k(qr)));
+            const uint4 xv = *reinterpret_cast<const uint4 *>(lv + qr * D + 8 * (qc ^ Sh::swz_v(qr)));
+            put_row_group<Meta>(g.k_codes + slot0 * (D / 8), static_cast<Meta *>(g.k_min) + slot0 * (D / 64),
+                                static_cast<Meta *>(g.k_scale) + slot0 * (D / 64), tok, qc, xk, tok < g.s_len);
+            put_row_group<Meta>(g.v_codes + slot0 * (D / 8), static_cast<Meta *>(g.v_min) + slot0 * (D / 64),
+                                static_cast<Meta *>(g.v_scale) + slot0 * (D / 64), tok, qc, xv, tok < g.s_len);
+        }
+        // Two steps ahead: its tiles, into the stage released by the barrier above.
+        __builtin_amdgcn_sched_barrier(0);
+        issue(cd, stage(std::integral_constant<int, (rs + 2) % NSTG>{}));
+        __builtin_amdgcn_sched_barrier(0);
+
+        const int qw0 = cu.c * QP + wave * QW; // first query of this wave
+        const int key0 = cu.j * kKeys;
+        if (qw0 < g.s_len && key0 <= qw0 + QW - 1) {
+            // S^T = K Q^T: st[c] holds keys 16c + 4*g4 + r, query l16.
+            f4 st[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                st[c] = f4{0.f, 0.f, 0.f, 0.f};
+            constexpr int NSS = KS * 4, LA = 3;
+            const int sk = Sh::swz_k(l16);
+            auto ld_ka = [&](int n) {
+                return *reinterpret_cast<const h8 *>(lk + (16 * (n % 4) + l16) * D + 8 * ((4 * (n / 4) + g4) ^ sk));
+            };
+            h8 ka[4];
+#pragma unroll
+            for (int i = 0; i < LA; ++i)
+                ka[i] = ld_ka(i);
+#pragma unroll
+            for (int i = 0; i < NSS; ++i) {
+                if (i + LA < NSS)
+                    ka[(i + LA) % 4] = ld_ka(i + LA);
+                st[i % 4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[i % 4], qb[i / 4], st[i % 4], 0, 0, 0);
+                if (i + LA < NSS) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            }
+            if (key0 + kKeys - 1 > qw0) { // the diagonal tile: keys after the query are masked
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int rel = qw0 + ln % 16 - key0 - 4 * (ln / 16);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * c + r > rel)
+                            st[c][r] = -INFINITY;
+            }
+            float mx = st[0][0];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    mx = fmaxf(mx, st[c][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // The reference m moves only when some query's max exceeds it by more than
+            // 8 (log2 units), as in k_prefill.
+            if (__any(mx > m + g.slack)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = exp2_fast((m - m_new) * g.c2);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+                    o[t] *= alpha;
+            }
+            h8 pb[2];
+            {
+                const float mb = -m * g.c2;
+                float ls = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = exp2_fast(__builtin_fmaf(st[c][r], g.c2, mb));
+                        st[c][r] = p;
+                        ls += p;
+                    }
+                l += ls;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pb[ks][r] = (_Float16)st[2 * ks][r];
+                        pb[ks][4 + r] = (_Float16)st[2 * ks + 1][r];
+                    }
+            }
+            // O^T += V^T P^T (operands as in k_prefill).  The read addresses are
+            // formed here, not kept across the loop in 26 registers.
+            const int vrow = 4 * g4 + l16 / 4;
+            int sv = Sh::swz_v(vrow);
+            asm volatile("" : "+v"(sv));
+            const _Float16 *vbase = lv + vrow * D + 4 * (l16 % 2);
+            constexpr int NV = DT * 2;
+            h8 va[4];
+            auto ld_va = [&](int n) {
+                const int t = n / 2, ks = n % 2;
+                const int ch = 8 * ((2 * t + (l16 % 4) / 2) ^ sv);
+                const h4 v0 = ld_tr(vbase + (32 * ks) * D + ch);
+                const h4 v1 = ld_tr(vbase + (32 * ks + 16) * D + ch);
+                return h8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            };
+#pragma unroll
+            for (int i = 0; i < LA; ++i)
+                va[i] = ld_va(i);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                if (i + LA < NV)
+                    va[(i + LA) % 4] = ld_va(i + LA);
+                o[i / 2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i % 4], pb[i % 2], o[i / 2], 0, 0, 0);
+                if (i + LA < NV) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            }
+        }
+        if (cu.j + 1 == cu.nj) { // the pass ends: its output rows go out next step
+            out_due = true;
+            out_base = cu.base;
+            out_q0 = qw0;
+        }
+        next_step(g, cu);
+        next_step(g, cd);
+        return true;
+    };
+
+    for (;;) {
+        if (!run_step(S0{}) || !run_step(S1{}) || !run_step(S2{}))
+            break;
+    }
+    if (out_due)
+        write_out();
+    // no tile load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+}
+
+template <typename Meta>
+int launch_prefill_pp(const CachePlanes &c, int b, const void *q, const void *k, const void *v, int s_len,
+                      void *out, hipStream_t st)
+{
+    PPArgs g;
+    g.q = static_cast<const uint16_t *>(q);
+    g.k = static_cast<const uint16_t *>(k);
+    g.v = static_cast<const uint16_t *>(v);
+    g.out = static_cast<uint16_t *>(out);
+    g.k_codes = reinterpret_cast<uint32_t *>(c.k_codes);
+    g.v_codes = reinterpret_cast<uint32_t *>(c.v_codes);
+    g.k_min = c.k_min;
+    g.k_scale = c.k_scale;
+    g.v_min = c.v_min;
+    g.v_scale = c.v_scale;
+    g.a = c.a;
+    g.S = c.S;
+    g.s_len = s_len;
+    g.pairs = b * c.a;
+    g.passes = (s_len + pp::QP - 1) / pp::QP;
+    g.row_bytes = c.a * pp::D * 2;
+    // every offset formed (up to a key tile past the last prompt row) below 2^31
+    if (((int64_t)s_len + 2 * kKeys) * g.row_bytes > 0x7FFFFFFF)
+        return (int)hipErrorNotSupported;
+    g.valid_bytes = (s_len - 1) * g.row_bytes + pp::D * 2;
+    g.c2 = kLog2e / sqrtf((float)pp::D);
+    g.slack = 8.0f / g.c2;
+    const int grid = std::min(g.pairs, kPrefillCUs);
+    hipLaunchKernelGGL((k_prefill_pp<Meta>), dim3((unsigned)grid), dim3(pp::NT), 0, st, g);
+    return (int)hipGetLastError();
 }
 
 template <int D, typename Meta>
@@ -505,7 +969,7 @@ int launch_prefill_m(const CachePlanes &c, int b, const void *q, const void *k, 
 {
     switch (c.d) {
     case 64: return launch_prefill_d<64, Meta>(c, b, q, k, v, s_len, out, st);
-    case 128: return launch_prefill_d<128, Meta>(c, b, q, k, v, s_len, out, st);
+    case 128: return launch_prefill_pp<Meta>(c, b, q, k, v, s_len, out, st);
     default: return launch_prefill_d<256, Meta>(c, b, q, k, v, s_len, out, st);
     }
 }

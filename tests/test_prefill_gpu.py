@@ -61,6 +61,24 @@ def test_prefill_small_full(d, s_len):
     log(f"prefill d={d} s={s_len}: max abs err {err:.2e}")
 
 
+@pytest.mark.parametrize("s_len", [17, 64, 200, 257])
+def test_prefill_several_pairs_per_workgroup(s_len):
+    """More (batch row, head) pairs (300) than workgroups at head_dim 128, so workgroups take
+    a second pair: the tile ring and the early query fetch run across pair boundaries,
+    including one-tile passes back to back (s <= 64) and a one-query last pass (s = 257).
+    Every plane and every output row."""
+    require_gpu()
+    b, a, d = 3, 100, 128
+    q, k, v, cache, out = _run_small(b, a, d, s_len, s_len + 3, 7600 + s_len)
+    hc = HostCache(b, a, d, s_len + 3)
+    hc.prefill(f16_np(k), f16_np(v))
+    _check_prefill_full(cache, hc, s_len, f"prefill 300 pairs s={s_len}")
+    pairs = [(bi, ai) for bi in range(b) for ai in range(a)]
+    ref = _oracle_rows(f16_np(q), f16_np(k), f16_np(v), pairs)
+    err = assert_close(_gpu_pairs(out, pairs), ref, f"prefill attention 300 pairs s={s_len}")
+    log(f"prefill 300 pairs s={s_len}: max abs err {err:.2e}")
+
+
 @pytest.mark.parametrize("d,s_len", [(64, 129), (128, 65), (256, 300)])
 def test_prefill_small_full_m16(d, s_len):
     """Binary16 min/scale planes: every plane bit-exact with the oracle's binary16 codec and
