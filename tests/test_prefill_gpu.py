@@ -141,10 +141,11 @@ def test_prefill_deterministic():
 
 @pytest.mark.timeout(600)
 def test_prefill_batch_split_across_launches():
-    """Long prompts split the batch into launches whose tensors stay below 2 GiB (here
-    b=48, a=96, d=128, s=2048: 42 batch rows per launch).  Sampled pairs from both
-    launches, including the first and last rows of each: planes bit-exact, attention
-    within the bar."""
+    """A prompt whose tensors exceed 2 GiB (b=48, a=96, d=128, s=2048: 2.4 GB each; eight
+    256-query passes per pair): the kernel addresses each (batch row, head) from its own
+    64-bit base with 32-bit offsets inside it.  Sampled pairs across the batch, including
+    the first and last rows and heads and the rows around 2 GiB: planes bit-exact,
+    attention within the bar."""
     require_gpu()
     b, a, d, s_len = 48, 96, 128, 2048
     log(f"[prefill split] b={b} a={a} d={d} s={s_len}")
