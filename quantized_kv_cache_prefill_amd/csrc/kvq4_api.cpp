@@ -152,11 +152,11 @@ bool gemm_dims_ok(int M, int N, int K)
 
 // Weight of the split partials in the automatic split choice: each extra
 // split writes and re-reads M*N binary32 partials, 16*M/K of the weight bytes.
-// Measured on MI355X with the 32x32x16 kernel (OPT-175B projections, K =
-// 12288): QKV (N = 36864, 144 column tiles) at M = 144: 234 / 258 / 191 / 225
-// / 201 us with 1..5 splits; output (N = 12288) at M = 144: 124 / 95 / 78 / 76
-// us with 2..5; at M = 32: QKV 94 / 96 / 75 / 82 / 77, output 52 / 41 / 35 /
-// 33 with 2..5.  The weight 0.3 picks 3 and 5 at M = 144, 7 and 5 at M = 32.
+// Measured on MI355X with the 32x32x16 kernel (eight 32-column waves, OPT-175B
+// projections, K = 12288): QKV (N = 36864, 144 column tiles) at M = 144:
+// 233 / 184 / 206 / 194 us with 2..5 splits; output (N = 12288) at M = 144:
+// 85 / 69 / 68 / 103 us with 3..6; at M = 32: QKV 90 / 73 / 79 / 75, output
+// 36 / 31 / 31 / 42.  The weight 0.3 picks 3 and 5 at M = 144, 7 and 5 at M = 32.
 constexpr double kGemmPartialWeight = 0.3;
 constexpr int kGemmMaxAutoSplits = 16;
 

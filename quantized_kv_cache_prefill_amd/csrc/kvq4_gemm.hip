@@ -20,13 +20,14 @@
 // Shape of the work (OPT-175B decode: M = 144 tokens, N = K = 12288): the
 // weight stream (N*K/2 bytes) and the matrix-core time are of the same order.
 // A workgroup owns a 32*RB x 256 output tile (RB <= 5 row blocks of 32) and a
-// range of K; its four waves (one per SIMD) each take 64 columns and all the
-// row blocks.  x goes from HBM straight into LDS (buffer loads to LDS, 16-byte
-// pieces XOR-swizzled within each row so the operand reads hit distinct
-// banks) through a ring of three chunk buffers, two chunks ahead; each wave
-// streams its own 64 weight rows through a ring of registers three chunks
-// ahead and dequantises them as it multiplies, the operands of k-step s+1
-// fetched and dequantised between the products of step s.  Ranges of K are
+// range of K; its eight waves (two per SIMD, so that one hides the other's
+// waits) each take 32 columns and all the row blocks.  x goes from HBM
+// straight into LDS (buffer loads to LDS, 16-byte pieces XOR-swizzled within
+// each row so the operand reads hit distinct banks) through a ring of three
+// chunk buffers, two chunks ahead; each wave streams its own 32 weight rows
+// through a ring of registers three chunks ahead and dequantises them as it
+// multiplies, the operands of k-step s+1 fetched and dequantised between the
+// products of step s.  Ranges of K are
 // split across workgroups when the column tiles alone cannot fill the 256
 // CUs; the split partials (binary32) are summed by a second kernel.
 #include <hip/hip_runtime.h>
@@ -43,13 +44,15 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 128;           // k per pipeline step
 constexpr int kRowBytes = kChunk * 2; // bytes of one x row of a chunk (16 pieces of 16 bytes)
-constexpr int kCB = 2;                // 32-column blocks per wave
+constexpr int kCB = 1;                // 32-column blocks per wave
 constexpr int kColsPerWave = 32 * kCB;
-constexpr int kWaves = 4;             // one per SIMD
+constexpr int kWaves = 8;             // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kColsPerGroup = kWaves * kColsPerWave;
 constexpr int kDepth = 3;             // weight chunks in flight per wave (register ring)
 constexpr int kXBuf = 3;              // x chunk buffers in LDS (x runs kXBuf - 1 chunks ahead)
+constexpr int kWLoads = 4 * kCB;      // loads per weight chunk per lane (2 x 16 B codes, 2 x 2 B min/scale per block)
+constexpr int kGroupsPerCU = 1;       // workgroups resident per CU (LDS: the x ring)
 static_assert(kDepth == kXBuf, "the K loop is unrolled by one ring length for both rings");
 
 // Buffer resources: a base, a size in bytes (loads at or past it return zeros
@@ -106,7 +109,7 @@ __device__ __forceinline__ h8 dequant8(uint32_t w, h2 sc, h2 mn, uint32_t magic)
     return __builtin_bit_cast(h8, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
-// One wave's weights for one 128-k chunk: for each of its two 32-column
+// One wave's weights for one 128-k chunk: for each of its kCB 32-column
 // blocks, lane l holds column l%32 of the block and k = 64*(l/32) .. +63 of
 // the chunk (32 code bytes, exactly one group) with that group's min and
 // scale.  In k-step s (0..7) the lane's 8 operand values are k = 64*(l/32) +
@@ -116,7 +119,7 @@ struct WChunk {
     uint32_t mn[kCB], sc[kCB]; // binary16 bits, low half
 };
 
-// The weight planes of one wave's 64 rows (one row of 64-row tiles of the
+// The weight planes of one wave's 32 rows (half a row of 64-row tiles of the
 // tiled layout: K/128 tiles of 4 KB codes and 128 mins / 128 scales each).
 struct WStreams {
     __amdgpu_buffer_rsrc_t codes, mins, scales;
@@ -132,8 +135,9 @@ __device__ __forceinline__ WStreams w_streams(const uint8_t *codes, const uint16
     w.codes = rsrc(codes + t0 * 4096, (uint32_t)(tiles * 4096));
     w.mins = rsrc(mins + t0 * 128, (uint32_t)(tiles * 256));
     w.scales = rsrc(scales + t0 * 128, (uint32_t)(tiles * 256));
-    w.code_off = (uint32_t)((lane & 31) * 64 + 32 * (lane >> 5));
-    w.meta_off = (uint32_t)(4 * (lane & 31) + 2 * (lane >> 5));
+    const uint32_t blk = (uint32_t)((n0 & 63) >> 5); // the wave's first 32-row block inside the tile
+    w.code_off = blk * 2048u + (uint32_t)((lane & 31) * 64 + 32 * (lane >> 5));
+    w.meta_off = blk * 128u + (uint32_t)(4 * (lane & 31) + 2 * (lane >> 5));
     return w;
 }
 
@@ -161,7 +165,7 @@ __device__ __forceinline__ WChunk load_w_chunk(const WStreams &ws, uint32_t c, b
 // kOutside for a row past M.
 template <int RB>
 struct XLoads {
-    static constexpr int PER_THREAD = 32 * RB * 16 / kThreads; // 2 RB
+    static constexpr int PER_THREAD = 32 * RB * 16 / kThreads; // 16 RB pieces per wave-row of lanes
     uint32_t off[PER_THREAD];
 };
 
@@ -171,7 +175,7 @@ __device__ __forceinline__ XLoads<RB> x_loads(int M, int K, int m0, int wave, in
     XLoads<RB> o;
 #pragma unroll
     for (int u = 0; u < XLoads<RB>::PER_THREAD; ++u) {
-        const int p = 64 * (4 * u + wave) + lane;
+        const int p = 64 * (kWaves * u + wave) + lane;
         const int row = p >> 4, slot = p & 15;
         const int piece = slot ^ (row & 15);
         o.off[u] = m0 + row < M ? (uint32_t)(((int64_t)(m0 + row) * K + 8 * piece) * 2) : kOutside;
@@ -187,7 +191,7 @@ __device__ __forceinline__ void issue_x(__amdgpu_buffer_rsrc_t rx, const XLoads<
 {
 #pragma unroll
     for (int u = 0; u < XLoads<RB>::PER_THREAD; ++u)
-        dma16(rx, dst + 1024 * (4 * u + wave), valid && o.off[u] != kOutside ? o.off[u] + c * kRowBytes : kOutside);
+        dma16(rx, dst + 1024 * (kWaves * u + wave), valid && o.off[u] != kOutside ? o.off[u] + c * kRowBytes : kOutside);
 }
 
 // One 128-k chunk of one wave: eight k-steps, each multiplying the step's 8
@@ -254,20 +258,19 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const char *__restr
 }
 
 // grid.x: column groups of 256 (fastest), grid.y: K splits, grid.z: row tiles
-// of 32*RB.  Wave w takes columns 64w .. 64w+63 of the group and all RB row
-// blocks, so every weight is dequantised once and each x operand read from
-// LDS feeds two products.  splits == 1: y written as fp16; else binary32
+// of 32*RB.  Wave w takes columns 32w .. 32w+31 of the group and all RB row
+// blocks, so every weight is dequantised once.  splits == 1: y written as fp16; else binary32
 // partials to ws[split][M][N].
 template <int RB>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_w4(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16_t *__restrict__ x,
                                                          const uint8_t *__restrict__ codes,
                                                          const uint16_t *__restrict__ mins,
                                                          const uint16_t *__restrict__ scales,
                                                          _Float16 *__restrict__ y, float *__restrict__ ws, int M,
                                                          int N, int K, int chunks_per_split)
 {
-    // the x ring: three separate arrays, so that the compiler can tell the
-    // buffer being read from the ones being filled
+    // the x ring: separate arrays, so that the compiler can tell the buffer
+    // being read from the one being filled
     __shared__ __attribute__((aligned(16))) char sx0[32 * RB * kRowBytes];
     __shared__ __attribute__((aligned(16))) char sx1[32 * RB * kRowBytes];
     __shared__ __attribute__((aligned(16))) char sx2[32 * RB * kRowBytes];
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_w4(const uint16_t *__restr
     // registers).  Every load is issued unconditionally, in the order
     // [x of chunk c + kXBuf - 1] [products of chunk c] [weights of chunk
     // c + kDepth] per chunk, so the x of chunk c is complete once at most
-    // 16 + 2 RB younger loads are outstanding.  The loop is unrolled by one
+    // kWLoads (kXBuf - 1) + 2 RB (kXBuf - 2) younger loads are outstanding.  The loop is unrolled by one
     // ring length so that every slot is named statically and refilled in
     // place right after it is consumed; the chunk count is padded to a
     // multiple of it with chunks that read zeros and add nothing.
@@ -304,9 +307,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_w4(const uint16_t *__restr
     const WStreams wst = w_streams(codes, mins, scales, nsafe, K, lane);
     const XLoads<RB> xl = x_loads<RB>(M, K, m0, wave, lane);
     auto valid = [&](int c) { return c < c_end; };
-    // prologue in the loop's own order (as if chunks c_begin - 3 .. - 1 had
-    // run): W(c0) | x(c0) W(c0+1) | x(c0+1) W(c0+2), so that every wait the
-    // compiler derives for the loop body holds for the first pass as well
+    // prologue in the loop's own order (as if the chunks before c_begin had
+    // run): W(c0) | x(c0) W(c0+1), so that every wait the compiler derives for
+    // the loop body holds for the first pass as well
     WChunk w[kDepth];
     w[0] = load_w_chunk(wst, (uint32_t)c_begin, valid(c_begin));
 #pragma unroll
@@ -320,11 +323,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_w4(const uint16_t *__restr
         for (int u = 0; u < kDepth; ++u) {
             const int c = c_begin + i + u;
             // x of chunk c has landed (this wave's pieces: the wait), then every
-            // wave's pieces have, and every wave is done reading buffer
-            // (u + 2) % 3 (the barrier).  One statement, no fence: a workgroup
-            // fence would wait for every earlier load into LDS, x of chunks c+1
-            // included.
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(16 + 2 * RB) : "memory");
+            // wave's pieces have, and every wave is done reading the buffer the
+            // next x goes into (the barrier).  One statement, no fence: a
+            // workgroup fence would wait for every earlier load into LDS.
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWLoads * (kXBuf - 1) + XLoads<RB>::PER_THREAD * (kXBuf - 2))
+                         : "memory");
             issue_x<RB>(rx, xl, (uint32_t)(c + kXBuf - 1), valid(c + kXBuf - 1), sx[(u + kXBuf - 1) % kXBuf], wave);
             __builtin_amdgcn_sched_barrier(0);
             mma_chunk<RB>(w[u], sx[u], lane, acc);
