@@ -403,7 +403,12 @@ def time_projections(copies: int = 3, reps: int = 8):
     fused Q/K/V projection (N = 3h = 36864, K = h = 12288) and the output projection
     (N = K = 12288), M = 144 tokens (the effective batch).  Synthetic weights N(0, 0.02^2),
     activations N(0, 1); `copies` weight sets in rotation so the Infinity Cache cannot
-    serve a repeat; medians of per-launch HIP events."""
+    serve a repeat; medians of per-launch HIP events, timed two ways:
+      * back to back: one projection launched repeatedly (matrix-core load without a
+        break, the clock settles at the chip's sustained power limit);
+      * in decode-layer order: attention over the layer's int4 cache (b=144, a=96,
+        context 544) -> QKV projection -> output projection, repeated, as one decode
+        step runs them."""
     import torch
 
     import quantized_kv_cache_prefill_amd as kvq
@@ -412,33 +417,65 @@ def time_projections(copies: int = 3, reps: int = 8):
     st = torch.cuda.current_stream()
     res = {"workload": f"OPT-175B decode projections, M={M} tokens, int4 weights (group 64, binary16 min/scale), "
                        f"{copies} weight sets in rotation"}
+
+    def rec(lst, fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        lst.append((e0, e1))
+
+    def med_of(lst):
+        ms = sorted(a.elapsed_time(b) for a, b in lst)
+        return ms[len(ms) // 2]
+
+    x = W.random_fp16((M, h), 9100, "cuda")
+    sets, ys, wss = {}, {}, {}
     for label, N in (("qkv", 3 * h), ("out", h)):
-        sets = []
+        sets[label] = []
         for c in range(copies):
             w = W.random_fp16((N, h), 9000 + 10 * c + (N == h), "cuda", 0.02)
-            sets.append(kvq.kvq_w4_quantize(w))
+            sets[label].append(kvq.kvq_w4_quantize(w))
             del w
-        x = W.random_fp16((M, h), 9100, "cuda")
-        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ys[label] = torch.empty((M, N), dtype=torch.float16, device="cuda")
         need = kvq.kvq_gemm_w4_workspace_bytes(M, N, h)
-        ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
+        wss[label] = torch.empty(max(need, 16) // 4, dtype=torch.float32, device="cuda")
         times = []
         for r in range((reps + 1) * copies):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            kvq.gemm_w4a16(x, *sets[r % copies], y=y, ws=ws)
-            e1.record(st)
-            times.append((e0, e1))
+            rec(times, lambda: kvq.gemm_w4a16(x, *sets[label][r % copies], y=ys[label], ws=wss[label]))
         torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in times[copies:])
-        med = ms[len(ms) // 2]
+        med = med_of(times[copies:])
         flops = 2 * M * N * h
         wbytes = N * h // 2 + 2 * 2 * N * (h // 64)
         res[label] = {"N": N, "K": h, "ms_per_call_median": round(med, 4),
                       "tflops": round(flops / med / 1e9, 1),
                       "frac_of_mfma_f16_peak": round(flops / med / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
-                      "weight_gbs": round(wbytes / med / 1e6, 1), "split_workspace_bytes": need}
-        del sets
+                      "weight_gbs": round(wbytes / med / 1e6, 1), "workspace_bytes": need,
+                      "form": "stream" if need == kvq.kvq_gemm_w4_workspace_bytes(M, N, h, kvq.KVQ_GEMM_STREAM)
+                      else "split"}
+    # decode-layer order
+    wl = W.OPT_175B
+    cache = kvq.QuantKVCache(wl.b, wl.a, wl.h, wl.s, wl.n, device="cuda", meta="f32")
+    k, v = W.prefill_kv(wl, 0, "cuda")
+    kvq.kv_quantize_prefill(cache, k, v)
+    del k, v
+    q, kn, vn = W.decode_inputs(wl, 0, 1, "cuda")
+    for j in range(wl.n):
+        kvq.kv_append_quant(cache, kn, vn, wl.s + j)
+    out = torch.empty((wl.b, 1, wl.a, wl.d), dtype=torch.float16, device="cuda")
+    ev = {"attention": [], "qkv": [], "out": []}
+    for r in range((reps + 1) * copies):
+        rec(ev["attention"], lambda: kvq.decode_attention_q4(cache, q, wl.s + wl.n, out=out))
+        for label in ("qkv", "out"):
+            rec(ev[label], lambda: kvq.gemm_w4a16(x, *sets[label][r % copies], y=ys[label], ws=wss[label]))
+    torch.cuda.synchronize()
+    res["decode_layer_order"] = {lab: {"ms_per_call_median": round(med_of(lst[copies:]), 4)} for lab, lst in ev.items()}
+    for label, N in (("qkv", 3 * h), ("out", h)):
+        med = res["decode_layer_order"][label]["ms_per_call_median"]
+        res["decode_layer_order"][label]["frac_of_mfma_f16_peak"] = round(
+            2 * M * N * h / med / 1e9 / MFMA_F16_PEAK_TFLOPS, 4)
+    del sets, cache
+    torch.cuda.empty_cache()
     return res
 
 

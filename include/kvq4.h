@@ -254,15 +254,25 @@ int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t 
 int kvq_w4_quantize(const void *w_f16, int32_t N, int32_t K, uint8_t *codes, void *mins_f16, void *scales_f16,
                     void *hip_stream);
 
-/* Workspace bytes gemm_w4a16 needs: binary32 partial sums [splits][M][N]
- * when the K range is split across workgroups (num_splits 0 = automatic,
- * chosen from M, N, K only), else 0. */
+/* num_splits value of gemm_w4a16 that asks for the stream form: the
+ * (output tile, 128-k chunk) units cut into one equal contiguous range per
+ * compute unit, the tiles cut between ranges summed from binary32 partials by
+ * a second pass.  Needs units x workgroups < 2^32 (KVQ_ERANGE otherwise);
+ * the automatic choice takes it when the split form would need more than one
+ * round of workgroups. */
+#define KVQ_GEMM_STREAM (-1)
+
+/* Workspace bytes gemm_w4a16 needs for num_splits (0 = automatic, chosen
+ * from M, N, K only): binary32 partial sums [splits][M][N] when the K range
+ * is split across workgroups, [workgroups][2][rows of a tile][256] in the
+ * stream form, else 0. */
 size_t kvq_gemm_w4_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t num_splits);
 
 /* y (fp16 [M][N]) = x (fp16 [M][K]) times the transposed dequantised W, with
  * M >= 1 rows (the effective batch of one decode step).  num_splits: 0 =
- * automatic, else 1 <= num_splits <= K/128 ranges of K (KVQ_ERANGE
- * otherwise).  ws: device workspace of ws_bytes >=
+ * automatic, KVQ_GEMM_STREAM = the stream form, else 1 <= num_splits <=
+ * K/128 ranges of K (KVQ_ERANGE otherwise).  Every form gives the same y up
+ * to the order of the binary32 sums.  ws: device workspace of ws_bytes >=
  * kvq_gemm_w4_workspace_bytes(M, N, K, num_splits) (may be NULL when that is
  * 0). */
 int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t *codes, const void *mins_f16,

@@ -32,6 +32,7 @@ META_F16 = 1
 _META = {"f32": (META_F32, torch.float32), "f16": (META_F16, torch.float16)}
 KVQ_TOPK_MAX_CTX = 8192
 KVQ_MAX_SPLITS = 256
+KVQ_GEMM_STREAM = -1  # gemm_w4a16 num_splits: the stream form
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq4.so")

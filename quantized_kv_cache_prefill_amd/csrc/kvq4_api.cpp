@@ -194,6 +194,52 @@ int gemm_splits(int M, int N, int K, int num_splits, int *chunks_per_split)
     return (chunks + cps - 1) / cps; // no empty split
 }
 
+// The launch shape of one gemm_w4a16 call and the workspace it needs.
+struct GemmPlan {
+    int splits;        // 0: the stream form
+    int chunks_per_split;
+    int stream_groups; // workgroups of the stream form
+    size_t ws_bytes;
+};
+
+// Stream form: one workgroup per CU, each over at least 4 (tile, chunk) units;
+// its unit arithmetic is 32-bit (units x workgroups < 2^32).  Automatic choice:
+// the split count above, unless its workgroups (tiles x splits) take more than
+// one resident round -- then the stream form, which gives every CU the same
+// number of units.  Measured on MI355X, OPT-175B projections (K = 12288) in
+// decode-layer order (attention, QKV, output): QKV at M = 144 (3 splits, 432
+// workgroups) 180.5 us split, 166.4 us stream; the output projection (5
+// splits, 240 workgroups, one round) 68.8 us split, 79.3 us stream.
+GemmPlan gemm_plan(int M, int N, int K, int num_splits)
+{
+    GemmPlan p{};
+    const int rows = 32 * kvq::gemm_row_blocks(M);
+    const int64_t tiles = (int64_t)((N + kGemmCols - 1) / kGemmCols) * ((M + rows - 1) / rows);
+    const int64_t units = tiles * (K / kGemmChunk);
+    const int64_t groups = std::min<int64_t>(kCUs, std::max<int64_t>(1, units / 4));
+    const bool stream_ok = units * groups < ((int64_t)1 << 32);
+    if (num_splits != KVQ_GEMM_STREAM) {
+        p.splits = gemm_splits(M, N, K, num_splits, &p.chunks_per_split);
+        p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+        if (num_splits != 0 || tiles * p.splits <= kCUs || !stream_ok)
+            return p;
+    }
+    if (!stream_ok) { // explicit stream form beyond its unit range
+        p.splits = -1;
+        return p;
+    }
+    p.splits = 0;
+    p.chunks_per_split = 0;
+    p.stream_groups = (int)groups;
+    p.ws_bytes = (size_t)groups * 2 * (size_t)rows * kGemmCols * sizeof(float);
+    return p;
+}
+
+bool gemm_splits_ok(int num_splits, int K)
+{
+    return num_splits == KVQ_GEMM_STREAM || (num_splits >= 0 && num_splits <= K / kGemmChunk);
+}
+
 } // namespace
 
 extern "C" {
@@ -405,11 +451,10 @@ int kvq_w4_quantize(const void *w_f16, int32_t N, int32_t K, uint8_t *codes, voi
 
 size_t kvq_gemm_w4_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t num_splits)
 {
-    if (!gemm_dims_ok(M, N, K) || num_splits < 0 || num_splits > K / kGemmChunk)
+    if (!gemm_dims_ok(M, N, K) || !gemm_splits_ok(num_splits, K))
         return 0;
-    int cps;
-    const int s = gemm_splits(M, N, K, num_splits, &cps);
-    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+    const GemmPlan p = gemm_plan(M, N, K, num_splits);
+    return p.splits < 0 ? 0 : p.ws_bytes;
 }
 
 int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t *codes, const void *mins_f16,
@@ -422,16 +467,18 @@ int gemm_w4a16(const void *x_f16, int32_t M, int32_t N, int32_t K, const uint8_t
     for (const void *p : ptrs)
         if (check_act(p) != KVQ_OK)
             return KVQ_EINVAL;
-    if (num_splits < 0 || num_splits > K / kGemmChunk)
+    if (!gemm_splits_ok(num_splits, K))
         return KVQ_ERANGE;
-    int cps;
-    const int s = gemm_splits(M, N, K, num_splits, &cps);
-    const size_t need = s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+    const GemmPlan p = gemm_plan(M, N, K, num_splits);
+    if (p.splits < 0)
+        return KVQ_ERANGE;
+    const size_t need = p.ws_bytes;
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return KVQ_ENOSPACE;
     if (need > 0 && !aligned16(ws))
         return KVQ_EINVAL;
-    kvq::GemmArgs g{x_f16, codes, mins_f16, scales_f16, y_f16, static_cast<float *>(ws), M, N, K, s, cps};
+    kvq::GemmArgs g{x_f16,   codes, mins_f16, scales_f16,         y_f16, static_cast<float *>(ws), M, N, K,
+                    p.splits, p.chunks_per_split, p.stream_groups};
     return status_of(kvq::launch_gemm_w4(g, static_cast<hipStream_t>(hip_stream)));
 }
 

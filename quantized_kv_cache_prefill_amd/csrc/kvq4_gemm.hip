@@ -257,35 +257,21 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const char *__restr
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// grid.x: column groups of 256 (fastest), grid.y: K splits, grid.z: row tiles
-// of 32*RB.  Wave w takes columns 32w .. 32w+31 of the group and all RB row
-// blocks, so every weight is dequantised once.  splits == 1: y written as fp16; else binary32
-// partials to ws[split][M][N].
+// One segment of work of a workgroup: rows m0 .. m0+32*RB-1, the 256 columns
+// of column group cg, chunks c_begin .. c_end-1 of K, accumulated into acc
+// (zeroed here).  Wave w takes columns 32w .. 32w+31 of the group and all RB
+// row blocks, so every weight is dequantised once.  Every wave of the
+// workgroup calls it with the same arguments; the x ring buffers must be free
+// (no wave still reading them) on entry.
 template <int RB>
-__global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16_t *__restrict__ x,
-                                                         const uint8_t *__restrict__ codes,
-                                                         const uint16_t *__restrict__ mins,
-                                                         const uint16_t *__restrict__ scales,
-                                                         _Float16 *__restrict__ y, float *__restrict__ ws, int M,
-                                                         int N, int K, int chunks_per_split)
+__device__ __forceinline__ void gemm_segment(const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+                                             const uint16_t *__restrict__ mins,
+                                             const uint16_t *__restrict__ scales, int M, int N, int K, int m0,
+                                             int cg, int c_begin, int c_end, char *const (&sx)[kXBuf], int wave,
+                                             int lane, f16v (&acc)[RB][kCB])
 {
-    // the x ring: separate arrays, so that the compiler can tell the buffer
-    // being read from the one being filled
-    __shared__ __attribute__((aligned(16))) char sx0[32 * RB * kRowBytes];
-    __shared__ __attribute__((aligned(16))) char sx1[32 * RB * kRowBytes];
-    __shared__ __attribute__((aligned(16))) char sx2[32 * RB * kRowBytes];
-    char *const sx[kXBuf] = {sx0, sx1, sx2};
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: the buffer bases stay scalar
-    const int split = blockIdx.y, splits = gridDim.y;
-    const int m0 = blockIdx.z * 32 * RB;
-    const int c_begin = split * chunks_per_split;
-    const int c_end = min(K / kChunk, c_begin + chunks_per_split);
-    const int64_t n0 = (int64_t)blockIdx.x * kColsPerGroup + wave * kColsPerWave;
-    const bool wave_ok = n0 < N;            // N % 64 == 0: a wave's columns are all in range or all out
-    const int64_t nsafe = wave_ok ? n0 : 0; // waves past N stream rows 0.. and store nothing
-
-    f16v acc[RB][kCB];
+    const int64_t n0 = (int64_t)cg * kColsPerGroup + wave * kColsPerWave;
+    const int64_t nsafe = n0 < N ? n0 : 0; // waves past N stream rows 0.. and store nothing
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -299,17 +285,18 @@ __global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16
     // registers).  Every load is issued unconditionally, in the order
     // [x of chunk c + kXBuf - 1] [products of chunk c] [weights of chunk
     // c + kDepth] per chunk, so the x of chunk c is complete once at most
-    // kWLoads (kXBuf - 1) + 2 RB (kXBuf - 2) younger loads are outstanding.  The loop is unrolled by one
-    // ring length so that every slot is named statically and refilled in
-    // place right after it is consumed; the chunk count is padded to a
-    // multiple of it with chunks that read zeros and add nothing.
+    // kWLoads (kXBuf - 1) + (x loads per chunk) (kXBuf - 2) younger loads are
+    // outstanding.  The loop is unrolled by one ring length so that every
+    // slot is named statically and refilled in place right after it is
+    // consumed; the chunk count is padded to a multiple of it with chunks
+    // that read zeros and add nothing.
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)((int64_t)M * K * 2));
     const WStreams wst = w_streams(codes, mins, scales, nsafe, K, lane);
     const XLoads<RB> xl = x_loads<RB>(M, K, m0, wave, lane);
     auto valid = [&](int c) { return c < c_end; };
     // prologue in the loop's own order (as if the chunks before c_begin had
-    // run): W(c0) | x(c0) W(c0+1), so that every wait the compiler derives for
-    // the loop body holds for the first pass as well
+    // run): W(c0) | x(c0) W(c0+1) | ..., so that every wait the compiler
+    // derives for the loop body holds for the first pass as well
     WChunk w[kDepth];
     w[0] = load_w_chunk(wst, (uint32_t)c_begin, valid(c_begin));
 #pragma unroll
@@ -326,7 +313,8 @@ __global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16
             // wave's pieces have, and every wave is done reading the buffer the
             // next x goes into (the barrier).  One statement, no fence: a
             // workgroup fence would wait for every earlier load into LDS.
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWLoads * (kXBuf - 1) + XLoads<RB>::PER_THREAD * (kXBuf - 2))
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWLoads * (kXBuf - 1) +
+                                                                  XLoads<RB>::PER_THREAD * (kXBuf - 2))
                          : "memory");
             issue_x<RB>(rx, xl, (uint32_t)(c + kXBuf - 1), valid(c + kXBuf - 1), sx[(u + kXBuf - 1) % kXBuf], wave);
             __builtin_amdgcn_sched_barrier(0);
@@ -335,11 +323,20 @@ __global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+}
 
-    if (!wave_ok)
+// The accumulators of a segment to memory: fp16 into y [M][N] (dst32 null),
+// or binary32 into dst32, rows m0.. of a [32*RB][ld] block (ld = N for the
+// split partials, 256 for a stream partial tile).  D layout: value i of lane
+// l is row 8*(i/4) + 4*(l/32) + i%4 of the block, column l%32.
+template <int RB>
+__device__ __forceinline__ void store_segment(const f16v (&acc)[RB][kCB], _Float16 *__restrict__ y,
+                                              float *__restrict__ dst32, int64_t ld32, int64_t col32, int M, int N,
+                                              int m0, int cg, int wave, int lane)
+{
+    const int64_t n0 = (int64_t)cg * kColsPerGroup + wave * kColsPerWave;
+    if (n0 >= N) // N % 64 == 0: a wave's columns are all in range or all out
         return;
-    // D layout: value i of lane l is row 8*(i/4) + 4*(l/32) + i%4 of the
-    // block, column l%32
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -347,16 +344,149 @@ __global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16
             const int64_t n = n0 + b * 32 + (lane & 31);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int m = m0 + rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (m < M) {
-                    if (splits == 1)
-                        y[(int64_t)m * N + n] = (_Float16)acc[rb][b][i];
+                const int r = rb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (m0 + r < M) {
+                    if (dst32 == nullptr)
+                        y[(int64_t)(m0 + r) * N + n] = (_Float16)acc[rb][b][i];
                     else
-                        ws[((int64_t)split * M + m) * N + n] = acc[rb][b][i];
+                        dst32[(int64_t)r * ld32 + col32 + (n - (int64_t)cg * kColsPerGroup)] = acc[rb][b][i];
                 }
             }
         }
     }
+}
+
+// Split-K form.  grid.x: column groups of 256 (fastest), grid.y: K splits,
+// grid.z: row tiles of 32*RB.  splits == 1: y written as fp16; else binary32
+// partials to ws[split][M][N].
+template <int RB>
+__global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4(const uint16_t *__restrict__ x,
+                                                         const uint8_t *__restrict__ codes,
+                                                         const uint16_t *__restrict__ mins,
+                                                         const uint16_t *__restrict__ scales,
+                                                         _Float16 *__restrict__ y, float *__restrict__ ws, int M,
+                                                         int N, int K, int chunks_per_split)
+{
+    // the x ring: separate arrays, so that the compiler can tell the buffer
+    // being read from the ones being filled
+    __shared__ __attribute__((aligned(16))) char sx0[32 * RB * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char sx1[32 * RB * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char sx2[32 * RB * kRowBytes];
+    char *const sx[kXBuf] = {sx0, sx1, sx2};
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: the buffer bases stay scalar
+    const int split = blockIdx.y, splits = gridDim.y;
+    const int m0 = blockIdx.z * 32 * RB;
+    const int c_begin = split * chunks_per_split;
+    const int c_end = min(K / kChunk, c_begin + chunks_per_split);
+    f16v acc[RB][kCB];
+    gemm_segment<RB>(x, codes, mins, scales, M, N, K, m0, (int)blockIdx.x, c_begin, c_end, sx, wave, lane, acc);
+    float *part = splits == 1 ? nullptr : ws + (int64_t)split * M * N + (int64_t)m0 * N;
+    store_segment<RB>(acc, y, part, N, (int64_t)blockIdx.x * kColsPerGroup, M, N, m0, (int)blockIdx.x, wave,
+                      lane);
+}
+
+// Stream form: the (tile, chunk) units -- tile t = row tile * column groups +
+// column group, unit t*C + c for the C chunks of K -- are cut into gridDim.x
+// equal contiguous ranges, one per workgroup (one per CU), so that no CU
+// waits on a second round.  A tile covered whole by one workgroup is written
+// as fp16; the part of a tile at either end of a range goes to one of that
+// workgroup's two partial slots (slot 0: its first tile, slot 1: its last),
+// ws [gridDim.x][2][32*RB][256] binary32, summed by k_gemm_fixup.
+template <int RB>
+__global__ __launch_bounds__(kThreads, kGroupsPerCU) void k_gemm_w4_stream(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes, const uint16_t *__restrict__ mins,
+    const uint16_t *__restrict__ scales, _Float16 *__restrict__ y, float *__restrict__ ws, int M, int N, int K,
+    int64_t units, int col_groups)
+{
+    __shared__ __attribute__((aligned(16))) char sx0[32 * RB * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char sx1[32 * RB * kRowBytes];
+    __shared__ __attribute__((aligned(16))) char sx2[32 * RB * kRowBytes];
+    char *const sx[kXBuf] = {sx0, sx1, sx2};
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int C = K / kChunk;
+    const int64_t G = gridDim.x, g = blockIdx.x;
+    const int64_t u0 = g * units / G, u1 = (g + 1) * units / G;
+    float *const slots = ws + g * 2 * (32 * RB) * kColsPerGroup;
+    int64_t u = u0;
+    while (u < u1) {
+        const int64_t t = u / C;
+        const int c_begin = (int)(u - t * C);
+        const int c_end = (int)min<int64_t>(C, u1 - t * C);
+        const int cg = (int)(t % col_groups), m0 = (int)(t / col_groups) * 32 * RB;
+        // the lane's offsets are recomputed for every segment rather than kept
+        // live across the loop (the empty asm hides that they are invariant)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        f16v acc[RB][kCB];
+        gemm_segment<RB>(x, codes, mins, scales, M, N, K, m0, cg, c_begin, c_end, sx, wave, ln, acc);
+        const bool whole = c_begin == 0 && c_end == C;
+        float *part = whole ? nullptr : slots + (u == u0 ? 0 : 1) * (32 * RB) * kColsPerGroup;
+        store_segment<RB>(acc, y, part, kColsPerGroup, 0, M, N, m0, cg, wave, ln);
+        u = t * C + c_end;
+        __syncthreads(); // the x ring is free (and its last loads have landed) before the next segment
+    }
+}
+
+// The tiles the stream form split: y = fp16(sum of their partial slots, in
+// workgroup order).  grid.x: pieces of kFixRows rows, grid.y: tiles; 256
+// threads, 4 outputs each per row.  32-bit unit arithmetic: units * G < 2^32
+// (checked by the host).
+constexpr int kFixRows = 4;
+__global__ __launch_bounds__(256) void k_gemm_fixup(const float *__restrict__ ws, _Float16 *__restrict__ y, int M,
+                                                    int N, int K, uint32_t units, uint32_t G, int col_groups,
+                                                    int rows)
+{
+    const uint32_t C = (uint32_t)(K / kChunk);
+    const uint32_t t = blockIdx.y;
+    auto start = [&](uint32_t g) { return g * units / G; };
+    const uint32_t a = t * C, b = a + C; // the tile's units
+    uint32_t g0 = a * G / units;         // the workgroup whose range holds unit a
+    while (g0 + 1 < G && start(g0 + 1) <= a)
+        ++g0;
+    while (g0 > 0 && start(g0) > a)
+        --g0;
+    uint32_t g1 = g0 + 1; // one past the last workgroup with units of the tile
+    while (g1 < G && start(g1) < b)
+        ++g1;
+    if (g1 == g0 + 1) // one workgroup covered it: written as fp16
+        return;
+    const int cg = (int)(t % (uint32_t)col_groups), m0 = (int)(t / (uint32_t)col_groups) * rows;
+    const int col = (threadIdx.x & 63) * 4;
+    const int64_t n = (int64_t)cg * kColsPerGroup + col;
+    const int r = blockIdx.x * kFixRows + (threadIdx.x >> 6);
+    if (r >= rows || m0 + r >= M || n >= N)
+        return;
+    // slot 0 of g0 holds the tile when it is g0's first tile; every later
+    // workgroup starts inside the tile (slot 0)
+    const float *p0 = ws + ((int64_t)(g0 * 2 + (start(g0) == a ? 0 : 1)) * rows + r) * kColsPerGroup + col;
+    float4 s = *reinterpret_cast<const float4 *>(p0);
+    const int64_t step = (int64_t)2 * rows * kColsPerGroup; // from slot 0 of g to slot 0 of g + 1
+    const float *p = ws + ((int64_t)(g0 + 1) * 2 * rows + r) * kColsPerGroup + col;
+    uint32_t g = g0 + 1;
+    for (; g + 2 <= g1; g += 2, p += 2 * step) {
+        const float4 v0 = *reinterpret_cast<const float4 *>(p);
+        const float4 v1 = *reinterpret_cast<const float4 *>(p + step);
+        s.x += v0.x;
+        s.y += v0.y;
+        s.z += v0.z;
+        s.w += v0.w;
+        s.x += v1.x;
+        s.y += v1.y;
+        s.z += v1.z;
+        s.w += v1.w;
+    }
+    if (g < g1) {
+        const float4 v0 = *reinterpret_cast<const float4 *>(p);
+        s.x += v0.x;
+        s.y += v0.y;
+        s.z += v0.z;
+        s.w += v0.w;
+    }
+    const h2 lo = {(_Float16)s.x, (_Float16)s.y}, hi = {(_Float16)s.z, (_Float16)s.w};
+    *reinterpret_cast<uint2 *>(y + (int64_t)(m0 + r) * N + n) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // y[m][n] = fp16(sum over splits of ws[s][m][n]), 4 outputs per thread.
@@ -383,8 +513,24 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float *__restrict__ w
 template <int RB>
 int launch_gemm_rb(const GemmArgs &g, hipStream_t st)
 {
-    const dim3 grid((unsigned)((g.N + kColsPerGroup - 1) / kColsPerGroup), (unsigned)g.splits,
-                    (unsigned)((g.M + 32 * RB - 1) / (32 * RB)));
+    const int col_groups = (g.N + kColsPerGroup - 1) / kColsPerGroup;
+    const int row_tiles = (g.M + 32 * RB - 1) / (32 * RB);
+    if (g.splits == 0) { // stream form
+        const int64_t units = (int64_t)col_groups * row_tiles * (g.K / kChunk);
+        hipLaunchKernelGGL((k_gemm_w4_stream<RB>), dim3((unsigned)g.stream_groups), dim3(kThreads), 0, st,
+                           static_cast<const uint16_t *>(g.x), g.codes, static_cast<const uint16_t *>(g.mins),
+                           static_cast<const uint16_t *>(g.scales), static_cast<_Float16 *>(g.y), g.ws, g.M, g.N,
+                           g.K, units, col_groups);
+        int e = (int)hipGetLastError();
+        if (e != 0)
+            return e;
+        hipLaunchKernelGGL(k_gemm_fixup, dim3((unsigned)(32 * RB / kFixRows), (unsigned)(col_groups * row_tiles)),
+                           dim3(256), 0, st, g.ws,
+                           static_cast<_Float16 *>(g.y), g.M, g.N, g.K, (uint32_t)units, (uint32_t)g.stream_groups,
+                           col_groups, 32 * RB);
+        return (int)hipGetLastError();
+    }
+    const dim3 grid((unsigned)col_groups, (unsigned)g.splits, (unsigned)row_tiles);
     hipLaunchKernelGGL((k_gemm_w4<RB>), grid, dim3(kThreads), 0, st, static_cast<const uint16_t *>(g.x), g.codes,
                        static_cast<const uint16_t *>(g.mins), static_cast<const uint16_t *>(g.scales),
                        static_cast<_Float16 *>(g.y), g.ws, g.M, g.N, g.K, g.chunks_per_split);

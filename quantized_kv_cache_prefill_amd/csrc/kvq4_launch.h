@@ -72,7 +72,8 @@ struct GemmArgs {
     void *y;
     float *ws;
     int M, N, K;
-    int splits, chunks_per_split;
+    int splits, chunks_per_split; // splits 0: the stream form over stream_groups workgroups
+    int stream_groups;
 };
 int launch_gemm_w4(const GemmArgs &g, hipStream_t st);
 int gemm_row_blocks(int M);

@@ -245,9 +245,17 @@ def test_gemm_w4_validation_and_workspace(L):
     assert L.kvq_w4_quantize(FAKE, 64, 128, FAKE, FAKE + 2, FAKE, st) == KVQ_EINVAL
     assert L.gemm_w4a16(None, 1, 64, 128, FAKE, FAKE, FAKE, FAKE, 0, None, 0, st) == KVQ_EINVAL
     assert L.gemm_w4a16(FAKE, 1, 64, 128, FAKE, FAKE, FAKE, FAKE + 8, 0, None, 0, st) == KVQ_EINVAL
-    # num_splits range: 0 (auto) .. K/128
+    # num_splits range: KVQ_GEMM_STREAM (-1), 0 (auto) .. K/128
     assert L.gemm_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, FAKE, FAKE, 3, FAKE, 1 << 20, st) == KVQ_ERANGE
-    assert L.gemm_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 1 << 20, st) == KVQ_ERANGE
+    assert L.gemm_w4a16(FAKE, 1, 64, 256, FAKE, FAKE, FAKE, FAKE, -2, FAKE, 1 << 20, st) == KVQ_ERANGE
+    assert L.kvq_gemm_w4_workspace_bytes(1, 64, 256, -2) == 0
+    # stream form: min(256, units / 4) workgroups (units = tiles x K/128), two binary32 partial tiles of
+    # (32 x row blocks) x 256 each
+    assert L.kvq_gemm_w4_workspace_bytes(144, 36864, 12288, -1) == 256 * 2 * 160 * 256 * 4
+    assert L.kvq_gemm_w4_workspace_bytes(33, 1280, 384, -1) == 3 * 2 * 64 * 256 * 4
+    assert L.kvq_gemm_w4_workspace_bytes(1, 64, 256, -1) == 1 * 2 * 32 * 256 * 4
+    assert L.gemm_w4a16(FAKE, 33, 1280, 384, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 3 * 2 * 64 * 256 * 4 - 4,
+                        st) == KVQ_ENOSPACE
     # explicit splits: splits x M x N binary32 partials
     assert L.kvq_gemm_w4_workspace_bytes(144, 256, 1024, 1) == 0
     assert L.kvq_gemm_w4_workspace_bytes(144, 256, 1024, 4) == 4 * 144 * 256 * 4
@@ -257,15 +265,24 @@ def test_gemm_w4_validation_and_workspace(L):
     # automatic: the OPT-175B decode projection (M=144, N=K=12288) splits K over the 48 column tiles
     auto = L.kvq_gemm_w4_workspace_bytes(144, 12288, 12288, 0)
     assert auto > 0 and auto % (144 * 12288 * 4) == 0
-    # automatic choices on the OPT-175B projections (K = 12288, 96 chunks of 128), at or within a few %
-    # of the fastest measured: QKV (N = 36864, 144 column tiles, one under-filled round) takes 3 splits
-    # at M = 144 and 64, 7 at M = 32 and 16, 16 at M = 1 (partials cost ~nothing); the output
-    # projection (48 tiles) 5 at every M; M = 150 is still one row tile of 160 rows (3 splits), M = 161
-    # makes two (288 tiles) and keeps 1
-    for M, N, splits in [(144, 36864, 3), (64, 36864, 3), (32, 36864, 7), (16, 36864, 7), (1, 36864, 16),
-                         (144, 12288, 5), (64, 12288, 5), (32, 12288, 5), (1, 12288, 5), (150, 36864, 3)]:
+    # automatic choices on the OPT-175B projections (K = 12288, 96 chunks of 128): the output projection
+    # (48 column tiles) takes 5 splits at every M -- 240 workgroups, one round; QKV (N = 36864, 144
+    # column tiles) would need more than one round of workgroups at any split count >= 2 and takes the
+    # stream form (256 workgroups, two partial tiles of 32 x row blocks each); so do M = 150 (one row
+    # tile of 160 rows) and M = 161 (two row tiles, 288 tiles: two rounds even unsplit)
+    for M, N, splits in [(144, 12288, 5), (64, 12288, 5), (32, 12288, 5), (1, 12288, 5)]:
         assert L.kvq_gemm_w4_workspace_bytes(M, N, 12288, 0) == splits * M * N * 4, (M, N)
-    assert L.kvq_gemm_w4_workspace_bytes(161, 36864, 12288, 0) == 0
+    for M, rows in [(144, 160), (64, 64), (32, 32), (16, 32), (1, 32), (150, 160), (161, 160)]:
+        want = 256 * 2 * rows * 256 * 4
+        assert L.kvq_gemm_w4_workspace_bytes(M, 36864, 12288, 0) == want, M
+        assert L.kvq_gemm_w4_workspace_bytes(M, 36864, 12288, -1) == want, M
+    # 32-column x 64-row weight (N = 64, K = 128): one unit, one workgroup, one round: unsplit
+    assert L.kvq_gemm_w4_workspace_bytes(1, 64, 128, 0) == 0
+    # the stream form's 32-bit unit range: units x workgroups < 2^32, else refused (workspace 0)
+    big_m = 160 * 100000  # 100000 row tiles x 256 column tiles x 1 chunk = 25.6M units; x 256 >= 2^32
+    assert L.kvq_gemm_w4_workspace_bytes(big_m, 65536, 128, -1) == 0
+    assert L.gemm_w4a16(FAKE, big_m, 65536, 128, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 1 << 40, st) == KVQ_ERANGE
+    assert L.kvq_gemm_w4_workspace_bytes(big_m, 65536, 128, 0) == 0  # automatic: unsplit
     # a split count that leaves an empty split is reduced: 96 chunks in 7 splits -> 14 per split, 7 splits
     assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 7) == 7 * 64 * 4
     assert L.kvq_gemm_w4_workspace_bytes(1, 64, 12288, 95) == 48 * 64 * 4  # ceil(96/95)=2 chunks each -> 48 splits

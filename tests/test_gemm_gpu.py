@@ -103,10 +103,11 @@ def test_w4_quantize_bit_exact():
 
 @pytest.mark.parametrize("M", [1, 7, 16, 33, 144, 150])
 @pytest.mark.parametrize("N,K", [(64, 128), (320, 640), (256, 1024)])
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("splits", [0, 1, 3, kvq.KVQ_GEMM_STREAM])
 def test_gemm_shapes_full(M, N, K, splits):
     """Every output of small shapes: row tiles with ragged ends (M not a multiple of 16 or
-    of 144), partial column groups (N = 64, 320), K ranges split 1, 3 ways or automatically."""
+    of 144), partial column groups (N = 64, 320), K ranges split 1, 3 ways, automatically or
+    in the stream form."""
     require_gpu()
     if splits > K // 128:
         # more splits than 128-wide chunks of K: refused on the host, nothing enqueued
@@ -148,14 +149,16 @@ def test_gemm_special_weights_and_large_inputs():
 
 
 @pytest.mark.timeout(300)
-def test_gemm_opt175b_projection_sampled():
-    """The OPT-175B decode projection (M = 144, N = K = 12288) in the launch configuration
-    the benchmark times: three sampled 64-row weight tiles (first, last, one seeded)
-    bit-exact, their output columns for all 144 rows within the bound."""
+@pytest.mark.parametrize("N", [12288, 36864])
+def test_gemm_opt175b_projection_sampled(N):
+    """The OPT-175B decode projections (M = 144, K = 12288; N = 12288 output, split form;
+    N = 36864 fused QKV, stream form) in the launch configuration the benchmark times:
+    three sampled 64-row weight tiles (first, last, one seeded) bit-exact, their output
+    columns for all 144 rows within the bound."""
     require_gpu()
-    M, N, K = 144, 12288, 12288
+    M, K = 144, 12288
     log(f"[gemm] M={M} N={N} K={K}: quantise + product")
-    w = _weights(N, K, 5300)
+    w = _weights(N, K, 5300 + (N != K))
     x = W.random_fp16((M, K), 5301, DEV)
     codes, mins, scales = kvq.kvq_w4_quantize(w)
     y = kvq.gemm_w4a16(x, codes, mins, scales)
@@ -175,19 +178,41 @@ def test_gemm_opt175b_projection_sampled():
     ref = oracle.gemm_w4a16(xh, c, m, s)
     mag = np.abs(xh.astype(np.float64)) @ np.abs(_w_hat(c, m, s).astype(np.float64)).T
     rel = assert_gemm_close(y.float().cpu().numpy()[:, rows], ref, mag, K, "OPT-175B projection")
-    log(f"[gemm] OPT-175B projection: {len(rows)} columns x 144 rows ok, max err / sum|x w| = {rel:.2e}")
+    log(f"[gemm] OPT-175B projection N={N}: {len(rows)} columns x 144 rows ok, max err / sum|x w| = {rel:.2e}")
+
+
+# (M, N, K): stream-form cuts.  33 x 1280 x 384: 5 tiles of 3 chunks over 3 workgroups of 5
+# units -- whole tiles in the middle of a range, a tile's head and tail in different
+# workgroups; 150 x 1536 x 1920: 90 units over 22 workgroups, every tile cut 4 or 5 ways at
+# ragged places; 161 x 768 x 1152: two row tiles (the second 1 row) of 9 chunks over 13
+# workgroups; 16 x 64 x 2048: one tile cut 4 ways.
+@pytest.mark.parametrize("M,N,K", [(33, 1280, 384), (150, 1536, 1920), (161, 768, 1152), (16, 64, 2048)])
+def test_gemm_stream_form_cuts(M, N, K):
+    """Every output of the stream form where its ranges cut tiles in every way."""
+    require_gpu()
+    x, _, (c, m, s), y = _run(M, N, K, 5500 + M + N + K, splits=kvq.KVQ_GEMM_STREAM)
+    xh = x.cpu().numpy()
+    ref = oracle.gemm_w4a16(xh, c, m, s)
+    mag = np.abs(xh.astype(np.float64)) @ np.abs(_w_hat(c, m, s).astype(np.float64)).T
+    rel = assert_gemm_close(y.float().cpu().numpy(), ref, mag, K, f"stream M={M} N={N} K={K}")
+    log(f"gemm stream M={M} N={N} K={K}: max err / sum|x w| = {rel:.2e}")
 
 
 def test_gemm_deterministic_and_split_invariant():
-    """Two runs are bit-identical; split counts agree to binary32 rounding."""
+    """Two runs are bit-identical; split counts and the stream form agree to binary32
+    rounding."""
     require_gpu()
     M, N, K = 144, 512, 2048
     x, (codes, mins, scales), _, y1 = _run(M, N, K, 5400)
     y2 = kvq.gemm_w4a16(x, codes, mins, scales)
     y3 = kvq.gemm_w4a16(x, codes, mins, scales, num_splits=1)
     y4 = kvq.gemm_w4a16(x, codes, mins, scales, num_splits=16)
+    y5 = kvq.gemm_w4a16(x, codes, mins, scales, num_splits=kvq.KVQ_GEMM_STREAM)
+    y6 = kvq.gemm_w4a16(x, codes, mins, scales, num_splits=kvq.KVQ_GEMM_STREAM)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    a, b, d = y3.float(), y4.float(), y1.float()
+    assert torch.equal(y5.view(torch.int16), y6.view(torch.int16))
+    a, b, d, e = y3.float(), y4.float(), y1.float(), y5.float()
     assert float((a - b).abs().max()) <= float(2.0 ** -9 * a.abs().max() + 1e-3)
     assert float((a - d).abs().max()) <= float(2.0 ** -9 * a.abs().max() + 1e-3)
+    assert float((a - e).abs().max()) <= float(2.0 ** -9 * a.abs().max() + 1e-3)
