@@ -479,6 +479,69 @@ def time_projections(copies: int = 3, reps: int = 8):
     return res
 
 
+def time_projection_sustained(calls: int = 6000):
+    """The OPT-175B QKV projection (M = 144, N = 36864, K = 12288) launched `calls` times
+    back to back, automatic form (stream) and 3 K splits, with the shader clock sampled
+    by rocm-smi every ~0.1 s meanwhile: the matrix-core load without a break settles the
+    clock at the chip's sustained power limit."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    import quantized_kv_cache_prefill_amd as kvq
+    import workloads as W
+    M, h = 144, 12288
+    N = 3 * h
+    sets = [kvq.kvq_w4_quantize(W.random_fp16((N, h), 9000 + 10 * c, "cuda", 0.02)) for c in range(3)]
+    x = W.random_fp16((M, h), 9100, "cuda")
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(kvq.kvq_gemm_w4_workspace_bytes(M, N, h, s) for s in (0, 3)) // 4 + 4,
+                     dtype=torch.float32, device="cuda")
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                m = re.search(r'"sclk clock speed:": "\((\d+)Mhz\)"', out)
+                if m:
+                    samples.append((time.time(), int(m.group(1))))
+            except (OSError, subprocess.SubprocessError):
+                return
+            time.sleep(0.05)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    torch.cuda.synchronize()
+    time.sleep(1.0)
+    res = {"workload": f"OPT-175B QKV projection, M={M}, N={N}, K={h}, {calls} calls back to back, "
+                       f"3 weight sets in rotation"}
+    t_first = time.time()
+    for label, splits in (("auto", 0), ("split3", 3)):
+        t0 = time.time()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(calls):
+            kvq.gemm_w4a16(x, *sets[r % 3], y=y, ws=ws, num_splits=splits)
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        clk = sorted(c for t, c in samples if t0 + 0.3 <= t <= t1)
+        res[label] = {"us_per_call": round(e0.elapsed_time(e1) / calls * 1e3, 1),
+                      "sclk_mhz_median": clk[len(clk) // 2] if clk else None, "clock_samples": len(clk)}
+        time.sleep(1.0)
+    idle = sorted(c for t, c in samples if t < t_first - 0.2)
+    res["sclk_mhz_idle_median"] = idle[len(idle) // 2] if idle else None
+    stop.set()
+    th.join(timeout=15)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def bytes_prefill(b: int, a: int, s: int, d: int, mb: int = 4) -> int:
     """Algorithmic HBM bytes of kv_quantize_prefill_attend: q, k, v read once, out written
     once (fp16 [b][s][a][d] each), plus the K and V planes of s slots (codes d/2 bytes,
@@ -736,6 +799,7 @@ def cpu_model() -> str:
 
 # --------------------------------------------------------------------- main
 LEGS = {"prefill": lambda: time_prefill(), "proj": lambda: time_projections(), "topk": lambda: time_topk(),
+        "proj_sustained": lambda: time_projection_sustained(),
         "split": lambda: time_split_context(), "meta16": lambda: time_meta_f16(),
         "host": lambda: time_host_attention(), "read_ceiling": lambda: hbm_read_ceiling()}
 
