@@ -149,21 +149,22 @@ __device__ __forceinline__ void put_group(uint32_t *codes, Meta *mins, Meta *sca
     }
 }
 
-// The same for head_dim 128 with the plane bases of one (batch row, head)
-// (uniform) and the token's index within it: 32-bit offsets only.
+// head_dim 128: one lane's 16-element piece of a token row (elements 16cc ..
+// 16cc + 15, cc = 0..7), quantised by quant_lane16, and its stores with the
+// plane bases of one (batch row, head) (uniform) and the token's index within
+// it: 32-bit offsets only.
+struct QPiece {
+    uint32_t w0, w1; // codes of elements 16cc .. 16cc + 7 and 16cc + 8 .. 16cc + 15
+    float mn, sc;    // the group's stored min and scale
+};
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <typename Meta>
-__device__ __forceinline__ void put_row_group(uint32_t *codes, Meta *mins, Meta *scales, int tok, int c, uint4 x,
-                                              bool ok)
+__device__ __forceinline__ void put_piece(uint32_t *codes, Meta *mins, Meta *scales, int tok, int cc, const QPiece &q)
 {
-    uint32_t word;
-    float mn, sc;
-    quant_lane8<Meta>(x, word, mn, sc); // every lane of the wave takes part (DPP)
-    if (ok) {
-        __builtin_nontemporal_store(word, codes + (uint32_t)(tok * 16 + c));
-        if ((c & 7) == 0) {
-            __builtin_nontemporal_store((Meta)mn, mins + (uint32_t)(tok * 2 + (c >> 3)));
-            __builtin_nontemporal_store((Meta)sc, scales + (uint32_t)(tok * 2 + (c >> 3)));
-        }
+    __builtin_nontemporal_store(u32x2{q.w0, q.w1}, reinterpret_cast<u32x2 *>(codes + (uint32_t)(tok * 16 + 2 * cc)));
+    if ((cc & 3) == 0) {
+        __builtin_nontemporal_store((Meta)q.mn, mins + (uint32_t)(tok * 2 + (cc >> 2)));
+        __builtin_nontemporal_store((Meta)q.sc, scales + (uint32_t)(tok * 2 + (cc >> 2)));
     }
 }
 
@@ -710,6 +711,20 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
         l = 0.f;
     };
 
+    // The V pieces quantised at the end of a step, stored at the top of the next
+    // one (before its tile loads, like the output rows).
+    QPiece vq{0u, 0u, 0.f, 0.f};
+    bool vq_due = false;
+    int64_t vq_slot0 = 0;
+    int vq_tok0 = 0;
+    auto put_vq = [&]() {
+        int t = tid - 64 * (NW / 2);
+        asm volatile("" : "+v"(t));
+        const int tok = vq_tok0 + t / 8;
+        if (tok < g.s_len)
+            put_piece<Meta>(g.v_codes + vq_slot0 * (D / 8), static_cast<Meta *>(g.v_min) + vq_slot0 * (D / 64),
+                            static_cast<Meta *>(g.v_scale) + vq_slot0 * (D / 64), tok, t % 8, vq);
+    };
     // One step: the tile in stage RS, the loads two steps ahead into stage (RS+2)%3.
     auto run_step = [&](auto RS) -> bool {
         if (cu.pair < 0)
@@ -723,6 +738,10 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
         if (out_due) {
             write_out();
             out_due = false;
+        }
+        if (vq_due) {
+            put_vq();
+            vq_due = false;
         }
         if (cu.j == 0) {
             // A new pass: its query rows (loaded ahead of this step's tile, so they
@@ -738,18 +757,26 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
         }
         const _Float16 *lk = stage(RS);
         const _Float16 *lv = lk + TILE_H;
-        if (cu.j * kKeys >= cu.c * QP) { // this pass's own positions: quantise them
-            // plane bases of the pair (uniform), 32-bit offsets within its S slots
-            const int64_t slot0 = (int64_t)cu.pair * g.S;
-            int qr = dr, qc = dcs; // formed here rather than held across the loop
-            asm volatile("" : "+v"(qr), "+v"(qc));
+        // This pass's own positions (keys 256c ..) are quantised while their tile
+        // is in LDS, one 16-element piece of a row per thread: the K rows by
+        // waves 0..7 here, the V rows by waves 8..15 after their products (stored
+        // at the top of the next step), so that half of the waves run the codec
+        // while the other half run the matrix cores.
+        const bool own = cu.j * kKeys >= cu.c * QP;
+        if (own && wave < NW / 2) {
+            int t = tid; // formed here rather than held across the loop
+            asm volatile("" : "+v"(t));
+            const int qr = t / 8, cc = t % 8, sk = Sh::swz_k(qr);
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * ((2 * cc) ^ sk));
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * ((2 * cc + 1) ^ sk));
+            QPiece qp;
+            quant_lane16<Meta>(x0, x1, qp.w0, qp.w1, qp.mn, qp.sc); // every lane of the wave takes part (DPP)
             const int tok = cu.j * kKeys + qr;
-            const uint4 xk = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * (qc ^ Sh::swz_k(qr)));
-            const uint4 xv = *reinterpret_cast<const uint4 *>(lv + qr * D + 8 * (qc ^ Sh::swz_v(qr)));
-            put_row_group<Meta>(g.k_codes + slot0 * (D / 8), static_cast<Meta *>(g.k_min) + slot0 * (D / 64),
-                                static_cast<Meta *>(g.k_scale) + slot0 * (D / 64), tok, qc, xk, tok < g.s_len);
-            put_row_group<Meta>(g.v_codes + slot0 * (D / 8), static_cast<Meta *>(g.v_min) + slot0 * (D / 64),
-                                static_cast<Meta *>(g.v_scale) + slot0 * (D / 64), tok, qc, xv, tok < g.s_len);
+            if (tok < g.s_len) {
+                const int64_t slot0 = (int64_t)cu.pair * g.S; // plane bases of the pair (uniform)
+                put_piece<Meta>(g.k_codes + slot0 * (D / 8), static_cast<Meta *>(g.k_min) + slot0 * (D / 64),
+                                static_cast<Meta *>(g.k_scale) + slot0 * (D / 64), tok, cc, qp);
+            }
         }
         // Two steps ahead: its tiles, into the stage released by the barrier above.
         __builtin_amdgcn_sched_barrier(0);
@@ -863,6 +890,17 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
                 }
             }
         }
+        if (own && wave >= NW / 2) {
+            int t = tid - 64 * (NW / 2);
+            asm volatile("" : "+v"(t));
+            const int qr = t / 8, cc = t % 8, sv = Sh::swz_v(qr);
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(lv + qr * D + 8 * ((2 * cc) ^ sv));
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(lv + qr * D + 8 * ((2 * cc + 1) ^ sv));
+            quant_lane16<Meta>(x0, x1, vq.w0, vq.w1, vq.mn, vq.sc);
+            vq_due = true;
+            vq_slot0 = (int64_t)cu.pair * g.S;
+            vq_tok0 = cu.j * kKeys;
+        }
         if (cu.j + 1 == cu.nj) { // the pass ends: its output rows go out next step
             out_due = true;
             out_base = cu.base;
@@ -879,6 +917,8 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
     }
     if (out_due)
         write_out();
+    if (vq_due)
+        put_vq();
     // no tile load may still be writing this workgroup's LDS when it ends
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
