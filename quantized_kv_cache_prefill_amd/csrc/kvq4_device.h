@@ -183,54 +183,5 @@ __device__ __forceinline__ void quant_lane8(const uint4 x, uint32_t &word, float
     scale_out = scale;
 }
 
-// The codes of 8 consecutive fp16 values against a group's stored min and
-// inverse scale, element i at bits 4i..4i+3 (the code step of quant_lane8).
-template <typename Meta>
-__device__ __forceinline__ uint32_t codes8(const uint4 x, float mn, float inv)
-{
-#pragma clang fp contract(off)
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    uint32_t ev = 0, od = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float te = sub_lo16(w[j], mn) * inv;
-        float to = sub_hi16(w[j], mn) * inv;
-        if constexpr (sizeof(Meta) != 4) {
-            te = fminf(te, 15.0f);
-            to = fminf(to, 15.0f);
-        }
-        ev = __builtin_amdgcn_cvt_pk_u8_f32(te, j, ev);
-        od = __builtin_amdgcn_cvt_pk_u8_f32(to, j, od);
-    }
-    return ev | (od << 4);
-}
-
-// The same codec for one lane's 16 consecutive fp16 values (x0: elements
-// 0..7, x1: 8..15); 4 consecutive lanes (an aligned quad) hold one
-// 64-element group, so the group reduction takes two cross-lane steps and the
-// stored min and scale are formed once per 16 elements.  Same arithmetic,
-// same results as quant_lane8 on the group.
-template <typename Meta>
-__device__ __forceinline__ void quant_lane16(const uint4 x0, const uint4 x1, uint32_t &w0, uint32_t &w1, float &mn_out,
-                                             float &scale_out)
-{
-#pragma clang fp contract(off)
-    const uint32_t lo = pk_min16(pk_min16(pk_min16(x0.x, x0.y), pk_min16(x0.z, x0.w)),
-                                 pk_min16(pk_min16(x1.x, x1.y), pk_min16(x1.z, x1.w)));
-    const uint32_t hi = pk_max16(pk_max16(pk_max16(x0.x, x0.y), pk_max16(x0.z, x0.w)),
-                                 pk_max16(pk_max16(x1.x, x1.y), pk_max16(x1.z, x1.w)));
-    uint32_t p = pk_min_neg_hi(lo, hi);
-    p = pk_min16(p, dpp_u<kQuadXor1>(p));
-    p = pk_min16(p, dpp_u<kQuadXor2>(p));
-    const float mn = h2f_lo(p) + 0.0f; // -0 -> +0
-    const float mx = -h2f_hi(p) + 0.0f;
-    float scale, inv;
-    codec_params<Meta>(mx - mn, scale, inv);
-    w0 = codes8<Meta>(x0, mn, inv);
-    w1 = codes8<Meta>(x1, mn, inv);
-    mn_out = mn;
-    scale_out = scale;
-}
-
 } // namespace
 } // namespace kvq
