@@ -242,6 +242,28 @@ __device__ __forceinline__ void quantise_tile(const PrefillArgs &g, int64_t pair
     }
 }
 
+// Lane l and lane l ^ 16 (l ^ 32) combined, through the gfx950 lane swaps
+// instead of an LDS permute: with both operands a copy of x, v_permlane16_swap
+// leaves rows (0, 0, 2, 2) of x in one result and rows (1, 1, 3, 3) in the
+// other (v_permlane32_swap: halves (lo, lo) and (hi, hi)), so every lane holds
+// its own value and its partner's, in the same order in both lanes.
+template <bool ADD>
+__device__ __forceinline__ float xor_lanes16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+    return ADD ? a + b : fmaxf(a, b);
+}
+template <bool ADD>
+__device__ __forceinline__ float xor_lanes32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+    return ADD ? a + b : fmaxf(a, b);
+}
+
 // 8 bytes through the transposing LDS read.
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
@@ -405,10 +427,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
             }
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
-                mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 16));
+                mx[qt] = xor_lanes16<false>(mx[qt]);
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
-                mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32));
+                mx[qt] = xor_lanes32<false>(mx[qt]);
             // The reference m only moves when some query's max exceeds it by more than
             // 8 (log2 units): probabilities up to 2^8 are exact enough in fp16 and the
             // sum and accumulators are binary32, so the result is the same softmax with
@@ -508,8 +530,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         float lt = l[qt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        lt = xor_lanes16<true>(lt);
+        lt = xor_lanes32<true>(lt);
         const float inv = 1.0f / lt;
 #pragma unroll
         for (int t = 0; t < DT; ++t)
@@ -738,8 +760,8 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
     auto write_out = [&]() {
         if (out_q0 < g.s_len) {
             float lt = l;
-            lt += __shfl_xor(lt, 16);
-            lt += __shfl_xor(lt, 32);
+            lt = xor_lanes16<true>(lt);
+            lt = xor_lanes32<true>(lt);
             const float inv = __builtin_amdgcn_rcpf(lt);
             int ln = lane; // formed here rather than held across the loop
             asm volatile("" : "+v"(ln));
@@ -877,8 +899,8 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     mx = fmaxf(mx, st[c][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = xor_lanes16<false>(mx);
+            mx = xor_lanes32<false>(mx);
             // The reference m moves only when some query's max exceeds it by more than
             // 8 (log2 units), as in k_prefill.
             if (__any(mx > m + g.slack)) {
