@@ -834,20 +834,37 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
         // waves 0..7 here, the V rows by waves 8..15 after their products (stored
         // at the top of the next step), so that half of the waves run the codec
         // while the other half run the matrix cores.
-        const bool own = cu.j * kKeys >= cu.c * QP;
+        // own tile jj of the pass (keys 256c + 64jj ..): waves w < 4jj have no
+        // query at or after its keys, so from jj = 1 on the low waves 0..7 take
+        // the V rows too, before the others' products; on jj = 0 every wave has
+        // products and the V rows go to waves 8..15 after theirs.
+        const int jj = cu.j - cu.c * (QP / kKeys);
+        const bool own = jj >= 0;
         if (own && wave < NW / 2) {
             int t = tid; // formed here rather than held across the loop
             asm volatile("" : "+v"(t));
-            const int qr = t / 8, cc = t % 8, sk = Sh::swz_k(qr);
-            const uint4 x0 = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * ((2 * cc) ^ sk));
-            const uint4 x1 = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * ((2 * cc + 1) ^ sk));
-            QPiece qp;
-            quant_lane16<Meta>(x0, x1, qp.w0, qp.w1, qp.mn, qp.sc); // every lane of the wave takes part (DPP)
+            const int qr = t / 8, cc = t % 8;
             const int tok = cu.j * kKeys + qr;
-            if (tok < g.s_len) {
-                const int64_t slot0 = (int64_t)cu.pair * g.S; // plane bases of the pair (uniform)
-                put_piece<Meta>(g.k_codes + slot0 * (D / 8), static_cast<Meta *>(g.k_min) + slot0 * (D / 64),
-                                static_cast<Meta *>(g.k_scale) + slot0 * (D / 64), tok, cc, qp);
+            const int64_t slot0 = (int64_t)cu.pair * g.S; // plane bases of the pair (uniform)
+            {
+                const int sk = Sh::swz_k(qr);
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * ((2 * cc) ^ sk));
+                const uint4 x1 = *reinterpret_cast<const uint4 *>(lk + qr * D + 8 * ((2 * cc + 1) ^ sk));
+                QPiece qp;
+                quant_lane16<Meta>(x0, x1, qp.w0, qp.w1, qp.mn, qp.sc); // every lane of the wave takes part (DPP)
+                if (tok < g.s_len)
+                    put_piece<Meta>(g.k_codes + slot0 * (D / 8), static_cast<Meta *>(g.k_min) + slot0 * (D / 64),
+                                    static_cast<Meta *>(g.k_scale) + slot0 * (D / 64), tok, cc, qp);
+            }
+            if (jj > 0) {
+                const int sv = Sh::swz_v(qr);
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(lv + qr * D + 8 * ((2 * cc) ^ sv));
+                const uint4 x1 = *reinterpret_cast<const uint4 *>(lv + qr * D + 8 * ((2 * cc + 1) ^ sv));
+                QPiece qp;
+                quant_lane16<Meta>(x0, x1, qp.w0, qp.w1, qp.mn, qp.sc);
+                if (tok < g.s_len)
+                    put_piece<Meta>(g.v_codes + slot0 * (D / 8), static_cast<Meta *>(g.v_min) + slot0 * (D / 64),
+                                    static_cast<Meta *>(g.v_scale) + slot0 * (D / 64), tok, cc, qp);
             }
         }
         // Two steps ahead: its tiles, into the stage released by the barrier above.
@@ -962,7 +979,7 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
                 }
             }
         }
-        if (own && wave >= NW / 2) {
+        if (jj == 0 && wave >= NW / 2) {
             int t = tid - 64 * (NW / 2);
             asm volatile("" : "+v"(t));
             const int qr = t / 8, cc = t % 8, sv = Sh::swz_v(qr);
