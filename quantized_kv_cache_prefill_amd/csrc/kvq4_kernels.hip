@@ -635,12 +635,15 @@ __global__ __launch_bounds__(256) void k_decode(uint8_t *kc, uint8_t *vc, Meta *
         for (int it = 0; it < n_rest; ++it, tb += TPW)
             decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
     } else {
+        // the new row is quantised and stored right after the first iteration
+        // (its load arrived with the first rows), so the codec and its lane
+        // exchanges overlap the rest of the wave's stream instead of ending it
+        const NewRow nr = append_rows<D, Meta>(new_raw, pc, T - 1, S, kc, vc, kmin, ksc, vmin, vsc, lane);
         const int nr1 = (last - w_begin - nf * TPI) / TPW;
         for (int it = 1; it < nf; ++it, tb += TPI)
             decode_iter<D, U>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
         for (int it = 0; it < nr1; ++it, tb += TPW)
             decode_iter<D, 1>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc);
-        const NewRow nr = append_rows<D, Meta>(new_raw, pc, T - 1, S, kc, vc, kmin, ksc, vmin, vsc, lane);
         decode_iter<D, 1, true>(cr, tb, t_end, qs, mg, c2, m, l, bsum, acc, nr, T - 1);
     }
 #pragma unroll
