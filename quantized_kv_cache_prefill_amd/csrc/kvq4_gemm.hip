@@ -224,16 +224,19 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const char *__restr
         for (int rb = 0; rb < RB; ++rb)
             a[rb] = *reinterpret_cast<const h8 *>(xrow + rb * 32 * kRowBytes + 16 * slot);
     };
-    h8 a[2][RB], bw[2][kCB];
+    // x operands two k-steps ahead (a ring of three), weights one step ahead
+    h8 a[3][RB], bw[2][kCB];
     ld_a(0, a[0]);
+    ld_a(1, a[1]);
 #pragma unroll
     for (int b = 0; b < kCB; ++b)
         bw[0][b] = dequant8(word(b, 0), sc[b], mn[b], magic);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const int cur_i = s & 1, nxt_i = cur_i ^ 1;
+        if (s < 6)
+            ld_a(s + 2, a[(s + 2) % 3]);
         if (s < 7) {
-            ld_a(s + 1, a[nxt_i]);
 #pragma unroll
             for (int b = 0; b < kCB; ++b)
                 bw[nxt_i][b] = dequant8(word(b, s + 1), sc[b], mn[b], magic);
@@ -242,13 +245,13 @@ __device__ __forceinline__ void mma_chunk(const WChunk &cur, const char *__restr
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int b = 0; b < kCB; ++b)
-                acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[cur_i][rb], bw[cur_i][b], acc[rb][b], 0, 0, 0);
+                acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s % 3][rb], bw[cur_i][b], acc[rb][b], 0, 0, 0);
         if (s < 7) {
-            // each product followed by part of the next step's reads and vector work
+            // each product followed by part of the reads and vector work ahead
 #pragma unroll
             for (int i = 0; i < RB * kCB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one product
-                if (i < RB)
+                if (i < RB && s < 6)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // some vector ALU
             }
