@@ -88,6 +88,7 @@ enum { KVQ_META_F32 = 0, KVQ_META_F16 = 1 };
 #define KVQ_MAX_HEAD_DIM 256    /* d = h/a must be 64, 128 or 256                            */
 #define KVQ_MAX_SPLITS 256      /* largest num_splits accepted by decode_attention_q4       */
 #define KVQ_TOPK_MAX_CTX 8192   /* longest context decode_attention_q4_topk accepts        */
+#define KVQ_TOPK_FUSED_MAX_CTX 2048 /* decode_attention_q4_topk up to this context: one launch */
 
 /* Problem dimensions in the pages' notation: b batch (the effective batch of
  * one launch), a heads, h hidden size (d = h/a per head), s prompt length,
@@ -156,8 +157,9 @@ int kv_append_quant(const kvq_cache *cache, const void *k_f16, const void *v_f16
 
 /* Workspace bytes decode_attention_q4 needs for (ctx_len, num_splits) -- 0
  * when the resolved split count is 1 -- or, when k_top > 0, the bytes
- * decode_attention_q4_topk needs (b*a*ctx_len*4: one fp32 score per token).
- * Host only; returns 0 on invalid arguments. */
+ * decode_attention_q4_topk needs: 0 for ctx_len <= KVQ_TOPK_FUSED_MAX_CTX,
+ * else b*a*ctx_len*4 (one fp32 score per token).  Host only; returns 0 on
+ * invalid arguments. */
 size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_splits, int32_t k_top);
 
 /* Decode-phase attention over slots 0..ctx_len-1 (1 <= ctx_len <= s+n) of
@@ -223,11 +225,15 @@ int kv_append_attend_q4(const kvq_cache *cache, const void *q_f16, const void *k
  * decode_attention_q4, subnormal query elements taken as 0 as there.
  * 1 <= k_top <= ctx_len <= min(s+n, KVQ_TOPK_MAX_CTX); the pages' rule keeps
  * k_top = ceil(0.1 * ctx_len).  sel_idx (device int32 [b][a][k_top], may be
- * NULL) receives the kept token indices in ascending order.  ws: device
- * workspace of ws_bytes >= kvq_workspace_bytes(dims, ctx_len, 0, k_top),
- * 16-byte aligned; it holds the scores between the two kernels, and when the
- * stream work is done it still holds them: fp32 [b][a][ctx_len], in log2
- * units (q . k * log2(e) / sqrt(d)), the values the selection ranked. */
+ * NULL) receives the kept token indices in ascending order.
+ * ws: the scores, fp32 [b][a][ctx_len] in log2 units (q . k * log2(e) /
+ * sqrt(d)), the values the selection ranked.  Up to KVQ_TOPK_FUSED_MAX_CTX
+ * tokens the call is one launch that keeps the scores on chip: ws may be NULL
+ * (ws_bytes is then ignored), and a ws that is given receives the scores as
+ * well, which costs that launch some 10%.  Longer contexts pass them between
+ * two launches through ws, which is then required.  A ws that is given must
+ * be 16-byte aligned with ws_bytes >= b*a*ctx_len*4 (KVQ_EINVAL, KVQ_ENOSPACE
+ * otherwise). */
 int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, int32_t k_top,
                              void *out_f16, int32_t *sel_idx, void *ws, size_t ws_bytes, void *hip_stream);
 

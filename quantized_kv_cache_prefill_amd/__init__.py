@@ -31,6 +31,7 @@ META_F32 = 0
 META_F16 = 1
 _META = {"f32": (META_F32, torch.float32), "f16": (META_F16, torch.float16)}
 KVQ_TOPK_MAX_CTX = 8192
+KVQ_TOPK_FUSED_MAX_CTX = 2048
 KVQ_MAX_SPLITS = 256
 KVQ_GEMM_STREAM = -1  # gemm_w4a16 num_splits: the stream form
 
@@ -341,12 +342,14 @@ def decode_attention_q4_topk(cache: QuantKVCache, q: torch.Tensor, ctx_len: int,
     if sel_idx is not None and (sel_idx.dtype != torch.int32 or not sel_idx.is_contiguous()
                                 or sel_idx.numel() != cache.b * cache.a * k_top):
         raise ValueError("sel_idx must be a contiguous int32 tensor of b*a*k_top elements")
+    # ws: the scores; optional up to KVQ_TOPK_FUSED_MAX_CTX tokens (a ws that is given receives them)
     need = kvq_workspace_bytes(cache, ctx_len, 0, k_top)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         with _on(stream):
             ws = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load_library().decode_attention_q4_topk(cache.struct_ref(), _ptr(q), ctx_len, k_top, _ptr(out),
-                                                   _ptr(sel_idx), _ptr(ws), need, _stream(stream)),
+                                                   _ptr(sel_idx), _ptr(ws), ws_bytes, _stream(stream)),
            "decode_attention_q4_topk")
     return out, sel_idx
 

@@ -315,7 +315,7 @@ size_t kvq_workspace_bytes(const kvq_dims *dims, int32_t ctx_len, int32_t num_sp
         return 0;
     const int pairs = dims->b * dims->a;
     if (k_top > 0)
-        return kvq::topk_ws_floats(pairs, ctx_len) * sizeof(float);
+        return ctx_len <= KVQ_TOPK_FUSED_MAX_CTX ? 0 : kvq::topk_ws_floats(pairs, ctx_len) * sizeof(float);
     const int hd = dims->h / dims->a;
     int len;
     const int s = resolve_splits(pairs, ctx_len, num_splits, &len);
@@ -430,8 +430,10 @@ int decode_attention_q4_topk(const kvq_cache *cache, const void *q_f16, int32_t 
         return KVQ_EINVAL;
     const int pairs = cache->dims.b * cache->dims.a;
     const size_t need = kvq::topk_ws_floats(pairs, ctx_len) * sizeof(float);
-    if (ws == nullptr || !aligned16(ws) || ws_bytes < need)
-        return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
+    if (ws != nullptr || ctx_len > KVQ_TOPK_FUSED_MAX_CTX) { // scores kept in ws: it must hold them
+        if (ws == nullptr || !aligned16(ws) || ws_bytes < need)
+            return ws_bytes < need ? KVQ_ENOSPACE : KVQ_EINVAL;
+    }
     return status_of(kvq::launch_topk(c, pairs, q_f16, ctx_len, k_top, out_f16, sel_idx, static_cast<float *>(ws),
                                       static_cast<hipStream_t>(hip_stream)));
 }

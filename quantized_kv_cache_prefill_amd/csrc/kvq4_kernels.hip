@@ -771,18 +771,17 @@ __global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ ws, _F
 }
 
 // ===========================================================================
-// Top-k sparse decode attention, in two kernels.
+// Top-k sparse decode attention.
 //
-// k_topk_scores streams every key once (same lane layout and folded codec as
-// k_decode; each wave takes a contiguous token range) and writes the scores,
-// in log2 units, to a workspace of 4 bytes per token -- 5% of the key bytes.
-// k_topk_select then runs one 256-thread workgroup per (batch row, head):
-// scores into LDS, the exact k-th largest by a 4-pass 8-bit radix select on
-// order-preserving 32-bit keys, compaction of the kept tokens in ascending
-// order (ties to the smaller index), softmax over the kept scores and P.V
-// over their gathered V rows.  Splitting the stream from the latency-bound
-// selection keeps the stream at full bandwidth; fused, the selection of one
-// workgroup left the memory pipeline idle.
+// Contexts up to 2048 tokens: one kernel, k_topk_fused (below), scores in LDS.
+// Longer contexts: two kernels.  k_topk_scores streams every key once (same
+// lane layout and folded codec as k_decode; each wave takes a contiguous token
+// range) and writes the scores, in log2 units, to a workspace of 4 bytes per
+// token -- 5% of the key bytes.  k_topk_select then runs one 256-thread
+// workgroup per (batch row, head): scores into LDS, the exact k-th largest by
+// a 4-pass 8-bit radix select on order-preserving 32-bit keys, compaction of
+// the kept tokens in ascending order (ties to the smaller index), softmax over
+// the kept scores and P.V over their gathered V rows.
 // ===========================================================================
 __device__ __forceinline__ uint32_t order_key(float z)
 {
@@ -1095,27 +1094,36 @@ __global__ __launch_bounds__(256) void k_topk_select(const uint8_t *__restrict__
             sel_out[pair * k_top + j] = sel[j];
 }
 
-// Selection for contexts up to 2048 tokens: one wave per (batch row, head),
-// four pairs per workgroup, no workgroup barrier.  The scores are loaded
-// coalesced and transposed through LDS so that lane l holds the keys of the
-// KPL consecutive tokens KPL*l .. KPL*l+KPL-1 in registers (KPL = 16 for
-// contexts up to 1024, else 32); ascending token order is then lane-major
-// order.
-//
-// The threshold (the k_top-th largest key) is found in two levels.  A
-// 256-bin histogram of the scores over [min, max] (LDS atomics; the bin is a
-// monotone function of the score, so every key in a higher bin is larger)
-// gives the bin b* that holds the k_top-th largest key and the number A of
-// keys in higher bins.  The keys of bin b* (at most 64, one per lane) are then
-// searched bit by bit for their (k_top - A)-th largest: the largest v with at
-// least k_top - A of them >= v.  When bin b* holds more than 64 keys (scores
-// crowded into a narrow range), the same bit-by-bit search runs over all the
-// keys instead.  A search step that finds exactly the wanted count has found
-// the selection itself and stops early.
-//
-// One prefix sum over the lanes then places each lane's kept tokens (ties to
-// the smaller index); their indices and softmax weights go to LDS, and the
-// wave gathers the kept V rows, all of a round's loads in flight together.
+// Contexts up to 2048 tokens: the whole call in one launch, one workgroup of
+// NWV waves (1, 2 or 4) per (batch row, head).
+//  (1) Scores: wave w streams the keys of the w-th of NWV equal parts of the
+//      context (the lane layout and folded codec of k_decode) and writes each
+//      score into LDS, transposed so that lane l of wave 0 can then hold the
+//      keys of the KPL consecutive tokens KPL*l .. KPL*l+KPL-1 in registers
+//      (KPL = 16 for contexts up to 1024, else 32); ascending token order is
+//      then lane-major order.  The scores go to the workspace as well when one
+//      is given.
+//  (2) Threshold and compaction, by wave 0 alone.  The threshold (the
+//      k_top-th largest key) is found in two levels.  A 256-bin histogram of
+//      the scores over [min, max] (LDS atomics; the bin is a monotone function
+//      of the score, so every key in a higher bin is larger) gives the bin b*
+//      that holds the k_top-th largest key and the number A of keys in higher
+//      bins.  The keys of bin b* (at most 64, one per lane) are then searched
+//      bit by bit for their (k_top - A)-th largest: the largest v with at
+//      least k_top - A of them >= v.  When bin b* holds more than 64 keys
+//      (scores crowded into a narrow range), the same bit-by-bit search runs
+//      over all the keys instead.  A search step that finds exactly the wanted
+//      count has found the selection itself and stops early.  One prefix sum
+//      over the lanes then places each lane's kept tokens (ties to the smaller
+//      index); their indices and softmax weights go to LDS.
+//  (3) P.V: the waves gather the kept V rows in rounds of TPW * UG rows, UG
+//      rows per lane in flight; with NWV > 1 their partial sums are added in
+//      LDS.
+// The scores never leave the chip, and while one wave selects, the other
+// waves resident on its compute unit keep streaming keys.  One wave per pair
+// needs no workgroup barrier and leaves no wave idle during the selection;
+// two or four share a pair when there are too few pairs to fill the compute
+// units that way.
 // v <- sum of v over the lanes congruent to this one modulo STEP (STEP a power
 // of two, 2..32): row rotations by STEP, 2 STEP, .. 8 inside each 16-lane row
 // (DPP, no LDS), then exchanges across rows.
@@ -1151,26 +1159,26 @@ __device__ __forceinline__ int wave_sum_small(int c) // 0 <= c < 64 in every lan
     return s;
 }
 
-// The largest v such that at least `want` of the wave's keys (N per lane) are
-// >= v: the want-th largest key.  With EARLY, a candidate that has exactly
-// `want` keys >= it ends the search, returning that candidate minus one (the
-// keys > the result are then exactly the wanted ones); this is only valid
-// when the keys searched are all the keys.  Keys of 0 never count: every
-// candidate is >= 1.
-template <int N, bool EARLY>
-__device__ __forceinline__ uint32_t greedy_threshold(const uint32_t (&key)[N], int want)
+// The largest v such that at least `want` of the wave's keys (key_at(0) ..
+// key_at(N-1) in each lane) are >= v: the want-th largest key.  With EARLY, a
+// candidate that has exactly `want` keys >= it ends the search, returning that
+// candidate minus one (the keys > the result are then exactly the wanted
+// ones); this is only valid when the keys searched are all the keys.  Keys of
+// 0 never count: every candidate is >= 1.
+template <int N, bool EARLY, typename KeyAt>
+__device__ __forceinline__ uint32_t greedy_threshold(KeyAt key_at, int want)
 {
     uint32_t thr = 0;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = thr | (1u << b);
         int cnt;
         if constexpr (N == 1) {
-            cnt = __popcll(__ballot(key[0] >= cand));
+            cnt = __popcll(__ballot(key_at(0) >= cand));
         } else {
             int c = 0;
 #pragma unroll
             for (int i = 0; i < N; ++i)
-                c += key[i] >= cand;
+                c += key_at(i) >= cand;
             cnt = wave_sum_small(c);
         }
         if (cnt >= want) {
@@ -1182,169 +1190,228 @@ __device__ __forceinline__ uint32_t greedy_threshold(const uint32_t (&key)[N], i
     return thr;
 }
 
-template <int D, int KPL, int UG, typename Meta>
-__global__ __launch_bounds__(256, 3) void k_topk_select_w(const uint8_t *__restrict__ vc,
-                                                          const Meta *__restrict__ vmin,
-                                                          const Meta *__restrict__ vsc,
-                                                          const float *__restrict__ scores, uint4 *__restrict__ out,
-                                                          int32_t *__restrict__ sel_out, int pairs, int S, int T,
-                                                          int k_top, int region_bytes)
+// Scores of one iteration's rows into the transposed LDS layout (and into
+// srow when it is given): every lane of a token row holds the row's score
+// after token_sum, lane `part` writes rows u = part, part + LPT, ...
+template <int D, int UU, int KPL>
+__device__ __forceinline__ void put_scores(const KRows<UU> &r, int tb, int t_end, const QSlice &qs, const Magic mg,
+                                           float c2, int part, float *__restrict__ tr, float *__restrict__ srow)
 {
     constexpr int LPT = D / 32;
     constexpr int TPW = 64 / LPT;
+    float zs[UU];
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+        const float dq = dot_keys(qs, r.kx[u], mg);
+        const float sp = __builtin_fmaf(r.ks[u], dq, r.km[u] * qs.qsum);
+        zs[u] = token_sum<LPT>(sp) * c2;
+    }
+#pragma unroll
+    for (int i = 0; i < (UU + LPT - 1) / LPT; ++i) {
+        const int u = part + i * LPT; // this lane's row of the iteration
+        float z = zs[0];
+#pragma unroll
+        for (int uu = 1; uu < UU; ++uu)
+            z = u == uu ? zs[uu] : z;
+        const int t = tb + u * TPW;
+        if (u < UU && t < t_end) {
+            tr[(t / KPL) * (KPL + 1) + t % KPL] = z;
+            if (srow != nullptr)
+                __builtin_nontemporal_store(z, srow + t);
+        }
+    }
+}
+
+template <int D, int UU, int KPL, typename Meta>
+__device__ __forceinline__ void score_iter_lds(const CacheRow<Meta> &cr, int tb, int t_end, const QSlice &qs,
+                                               const Magic mg, float c2, int part, float *__restrict__ tr,
+                                               float *__restrict__ srow)
+{
+    KRows<UU> r;
+    load_k_rows<D, UU>(cr, tb, t_end, r);
+    put_scores<D, UU, KPL>(r, tb, t_end, qs, mg, c2, part, tr, srow);
+}
+
+// Dynamic LDS: the transposed scores [64][KPL + 1]; the waves' partial sums
+// [4][D] and their softmax sums [4]; then `region_bytes` for wave 0's
+// histogram [256] (+64 discard counters) and bin b*'s keys [64] (+64 discard
+// slots), later the kept tokens' scores relative to the maximum and their
+// indices [k_top] (+64 discard slots each).
+template <int D, int NWV, int U, int KPL, int UG, typename Meta>
+__global__ __launch_bounds__(64 * NWV) void k_topk_fused(const uint8_t *__restrict__ kc, const Meta *__restrict__ kmin,
+                                                    const Meta *__restrict__ ksc, const uint8_t *__restrict__ vc,
+                                                    const Meta *__restrict__ vmin, const Meta *__restrict__ vsc,
+                                                    const uint4 *__restrict__ q, float *__restrict__ scores,
+                                                    _Float16 *__restrict__ out, int32_t *__restrict__ sel_out, int S,
+                                                    int T, int k_top, int part_len, float c2)
+{
+    constexpr int LPT = D / 32;
+    constexpr int TPW = 64 / LPT;
+    constexpr int TPI = U * TPW;
     constexpr int G = D / 64;
-    // KPL keys per lane (T <= 64 * KPL); UG gathered rows per lane in flight,
-    // TPW * UG rows per round
     constexpr int ROW = KPL + 1; // LDS row of one lane's keys, padded against bank conflicts
     extern __shared__ __attribute__((aligned(16))) float sm_dyn[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int pair_v = blockIdx.x * 4 + wave;
-    if (pair_v >= pairs)
-        return;
-    const int64_t pair = __builtin_amdgcn_readfirstlane(pair_v);
-    char *region = reinterpret_cast<char *>(sm_dyn) + (size_t)wave * region_bytes;
-    // Region use, in turn: the transposed scores [64][ROW]; the histogram [256]
-    // (+64 discard counters) and bin b*'s keys [64] (+64 discard slots); the
-    // kept tokens' scores relative to the maximum and their indices [k_top]
-    // (+64 discard slots each).
-    float *__restrict__ tr = reinterpret_cast<float *>(region);
+    float *__restrict__ tr = sm_dyn;
+    float *__restrict__ red = sm_dyn + 64 * ROW; // [NWV][D], then the NWV sums
+    char *__restrict__ region = reinterpret_cast<char *>(red + NWV * D + 4);
     int *__restrict__ hist = reinterpret_cast<int *>(region);
     uint32_t *__restrict__ cand = reinterpret_cast<uint32_t *>(region + 4 * (256 + 64));
     float *__restrict__ sel_z = reinterpret_cast<float *>(region);
     uint16_t *__restrict__ sel_t = reinterpret_cast<uint16_t *>(region + 4 * (size_t)(k_top + 64));
 
-    // (1) scores: token lane + 64j is loaded by lane `lane` (coalesced; every
-    // load issued unconditionally with a clamped index) and stored at row
-    // t / KPL, column t % KPL; lane l then reads row l.  Keys of t >= T are 0,
-    // below every finite score's key.
-    const float *__restrict__ srow = scores + pair * T;
-    {
-        float zl[KPL];
-#pragma unroll
-        for (int j = 0; j < KPL; ++j)
-            zl[j] = ld_stream(at_byte(srow, 4u * (uint32_t)min(lane + 64 * j, T - 1)));
-#pragma unroll
-        for (int j = 0; j < KPL; ++j)
-            tr[(j * (64 / KPL) + lane / KPL) * ROW + lane % KPL] = zl[j];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    uint32_t key[KPL];
-    float zmax = -INFINITY, zmin = INFINITY;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const float z = tr[lane * ROW + i];
-        const bool valid = KPL * lane + i < T;
-        zmax = fmaxf(zmax, valid ? z : -INFINITY);
-        zmin = fminf(zmin, valid ? z : INFINITY);
-        key[i] = valid ? order_key(z) : 0u;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        zmax = fmaxf(zmax, __shfl_xor(zmax, off));
-        zmin = fminf(zmin, __shfl_xor(zmin, off));
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier(); // the reads of tr are done before hist reuses the region
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t pair = blockIdx.x;
+    const int part = lane % LPT, lt = lane / LPT;
 
-    // (2) threshold.  Bins: bin(z) = (int)min((z - zmin) * bscale, 255), monotone
-    // in z; a zero (or unrepresentable) range gives one bin and the full search.
-    // No branch: the keys of t >= T count in their lane's own discard counter.
-    const float zrange = zmax - zmin;
-    const float bscale = (zrange > 1e-30f && zrange <= 3e38f) ? 256.0f / zrange : 0.0f;
-    reinterpret_cast<int4 *>(hist)[lane] = make_int4(0, 0, 0, 0); // the discard counters are never read
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    uint32_t bins[KPL / 4]; // four 8-bit bins per register
-#pragma unroll
-    for (int r = 0; r < KPL / 4; ++r)
-        bins[r] = 0u;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int bi = key_bin(key[i], zmin, bscale);
-        bins[i / 4] |= (uint32_t)bi << (8 * (i % 4));
-        atomicAdd(&hist[key[i] != 0u ? bi : 256 + lane], 1);
+    // (1) scores of the wave's part of the context
+    {
+        const int w_begin = wave * part_len;
+        const int t_end = min(T, w_begin + part_len);
+        if (t_end > w_begin) {
+            const int n_full = (t_end - w_begin) / TPI;
+            const int n_rest = (t_end - w_begin - n_full * TPI + TPW - 1) / TPW;
+            const CacheRow<Meta> cr = cache_row<D, Meta>(kc, nullptr, kmin, ksc, nullptr, nullptr, (int)pair, S, part);
+            float *__restrict__ srow = scores != nullptr ? scores + pair * T : nullptr;
+            int tb = w_begin + lt;
+            // the first iteration's rows are requested right behind the query
+            const QRaw qraw = load_q_raw(q + pair * (D / 8) + part * 4);
+            KRows<U> first;
+            if (n_full > 0)
+                load_k_rows<D, U>(cr, tb, t_end, first);
+            const QSlice qs = q_slice(qraw);
+            const Magic mg = magic_vgprs();
+            if (n_full > 0) {
+                put_scores<D, U, KPL>(first, tb, t_end, qs, mg, c2, part, tr, srow);
+                tb += TPI;
+            }
+            for (int it = 1; it < n_full; ++it, tb += TPI)
+                score_iter_lds<D, U, KPL>(cr, tb, t_end, qs, mg, c2, part, tr, srow);
+            for (int it = 0; it < n_rest; ++it, tb += TPW)
+                score_iter_lds<D, 1, KPL>(cr, tb, t_end, qs, mg, c2, part, tr, srow);
+        }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // counts of the keys in bins >= b, from the top: lane l holds bins 4l..4l+3
-    const int4 h4 = reinterpret_cast<const int4 *>(hist)[lane];
-    const int lsum = h4.x + h4.y + h4.z + h4.w;
-    const int lincl = wave_incl_scan(lsum, lane);
-    const int above_lane = __shfl(lincl, 63) - lincl; // keys in bins of higher lanes
-    const int ge3 = above_lane + h4.w, ge2 = ge3 + h4.z, ge1 = ge2 + h4.y, ge0 = ge1 + h4.x;
-    // bin b* holds the k_top-th largest: ge(b*+1) < k_top <= ge(b*)
-    int my_bin = -1, my_above = 0, my_n = 0;
-    if (above_lane < k_top && k_top <= ge3) { my_bin = 4 * lane + 3; my_above = above_lane; my_n = h4.w; }
-    if (ge3 < k_top && k_top <= ge2) { my_bin = 4 * lane + 2; my_above = ge3; my_n = h4.z; }
-    if (ge2 < k_top && k_top <= ge1) { my_bin = 4 * lane + 1; my_above = ge2; my_n = h4.y; }
-    if (ge1 < k_top && k_top <= ge0) { my_bin = 4 * lane; my_above = ge1; my_n = h4.x; }
-    const uint64_t owner = __ballot(my_bin >= 0);
-    const int src = (int)__builtin_ctzll(owner);
-    const int bstar = __shfl(my_bin, src), n_star = __shfl(my_n, src), a_star = __shfl(my_above, src);
-    uint32_t thr;
-    if (n_star <= 64) {
-        // bin b*'s keys, one per lane; the others go to discard slots
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < KPL; ++i)
-            c += (key[i] != 0u) & ((int)((bins[i / 4] >> (8 * (i % 4))) & 255u) == bstar);
-        int p = wave_incl_scan(c, lane) - c;
+    __syncthreads();
+
+    // (2) threshold and compaction (wave 0)
+    if (wave == 0) {
+        // lane l: tokens KPL*l .. KPL*l+KPL-1; keys of t >= T are 0, below every
+        // finite score's key
+        uint32_t key[KPL];
+        float zmax = -INFINITY, zmin = INFINITY;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
-            const bool in = (key[i] != 0u) & ((int)((bins[i / 4] >> (8 * (i % 4))) & 255u) == bstar);
-            cand[in ? p : 64 + lane] = key[i];
-            p += in;
+            const float z = tr[lane * ROW + i];
+            const bool valid = KPL * lane + i < T;
+            zmax = fmaxf(zmax, valid ? z : -INFINITY);
+            zmin = fminf(zmin, valid ? z : INFINITY);
+            key[i] = valid ? order_key(z) : 0u;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            zmax = fmaxf(zmax, __shfl_xor(zmax, off));
+            zmin = fminf(zmin, __shfl_xor(zmin, off));
+        }
+
+        // Bins: bin(z) = (int)min((z - zmin) * bscale, 255), monotone in z; a
+        // zero (or unrepresentable) range gives one bin and the full search.
+        // No branch: the keys of t >= T count in their lane's own discard counter.
+        const float zrange = zmax - zmin;
+        const float bscale = (zrange > 1e-30f && zrange <= 3e38f) ? 256.0f / zrange : 0.0f;
+        reinterpret_cast<int4 *>(hist)[lane] = make_int4(0, 0, 0, 0); // the discard counters are never read
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint32_t bins[KPL / 4]; // four 8-bit bins per register
+#pragma unroll
+        for (int r = 0; r < KPL / 4; ++r)
+            bins[r] = 0u;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const int bi = key_bin(key[i], zmin, bscale);
+            bins[i / 4] |= (uint32_t)bi << (8 * (i % 4));
+            atomicAdd(&hist[key[i] != 0u ? bi : 256 + lane], 1);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        const uint32_t ck[1] = {lane < n_star ? cand[lane] : 0u};
-        thr = greedy_threshold<1, false>(ck, k_top - a_star); // an exact key: lower bins stay below
-    } else {
-        thr = greedy_threshold<KPL, true>(key, k_top);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier(); // hist and cand are read before sel_z/sel_t reuse the region
-
-    // (3) compaction in ascending token order: one prefix sum over the lanes of
-    // (keys > thr) and (keys == thr); the first `remaining` keys equal to thr
-    // (smallest indices) are kept.  Dropped keys write to discard slots.
-    int gt = 0, eq = 0;
+        // counts of the keys in bins >= b, from the top: lane l holds bins 4l..4l+3
+        const int4 h4 = reinterpret_cast<const int4 *>(hist)[lane];
+        const int lsum = h4.x + h4.y + h4.z + h4.w;
+        const int lincl = wave_incl_scan(lsum, lane);
+        const int above_lane = __shfl(lincl, 63) - lincl; // keys in bins of higher lanes
+        const int ge3 = above_lane + h4.w, ge2 = ge3 + h4.z, ge1 = ge2 + h4.y, ge0 = ge1 + h4.x;
+        // bin b* holds the k_top-th largest: ge(b*+1) < k_top <= ge(b*)
+        int my_bin = -1, my_above = 0, my_n = 0;
+        if (above_lane < k_top && k_top <= ge3) { my_bin = 4 * lane + 3; my_above = above_lane; my_n = h4.w; }
+        if (ge3 < k_top && k_top <= ge2) { my_bin = 4 * lane + 2; my_above = ge3; my_n = h4.z; }
+        if (ge2 < k_top && k_top <= ge1) { my_bin = 4 * lane + 1; my_above = ge2; my_n = h4.y; }
+        if (ge1 < k_top && k_top <= ge0) { my_bin = 4 * lane; my_above = ge1; my_n = h4.x; }
+        const uint64_t owner = __ballot(my_bin >= 0);
+        const int src = (int)__builtin_ctzll(owner);
+        const int bstar = __shfl(my_bin, src), n_star = __shfl(my_n, src), a_star = __shfl(my_above, src);
+        uint32_t thr;
+        if (n_star <= 64) {
+            // bin b*'s keys, one per lane; the others go to discard slots
+            int c = 0;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        gt += key[i] > thr;
-        eq += key[i] == thr;
-    }
-    const int packed = gt | (eq << 16);
-    const int incl = wave_incl_scan(packed, lane);
-    const int tot = __shfl(incl, 63);
-    const int excl = incl - packed;
-    const int remaining = k_top - (tot & 0xFFFF);
-    int eq_rank = excl >> 16;
-    int pos = (excl & 0xFFFF) + min(eq_rank, remaining);
+            for (int i = 0; i < KPL; ++i)
+                c += (key[i] != 0u) & ((int)((bins[i / 4] >> (8 * (i % 4))) & 255u) == bstar);
+            int p = wave_incl_scan(c, lane) - c;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const uint32_t kb = key[i];
-        const bool is_eq = kb == thr;
-        const bool keep = (kb > thr) | (is_eq & (eq_rank < remaining));
-        eq_rank += is_eq;
-        const int slot = keep ? pos : k_top + lane;
-        sel_z[slot] = tr_key_to_z(kb) - zmax;
-        sel_t[slot] = (uint16_t)(KPL * lane + i);
-        pos += keep;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+            for (int i = 0; i < KPL; ++i) {
+                const bool in = (key[i] != 0u) & ((int)((bins[i / 4] >> (8 * (i % 4))) & 255u) == bstar);
+                cand[in ? p : 64 + lane] = key[i];
+                p += in;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t ck = lane < n_star ? cand[lane] : 0u;
+            // an exact key: lower bins stay below
+            thr = greedy_threshold<1, false>([&](int) { return ck; }, k_top - a_star);
+        } else {
+            thr = greedy_threshold<KPL, true>([&](int i) { return key[i]; }, k_top);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier(); // hist and cand are read before sel_z/sel_t reuse the region
 
-    // (4) P.V over the kept rows, UG rows per lane in flight
-    const int part = lane % LPT, lt = lane / LPT;
-    const CacheRow<Meta> cr = cache_row<D, Meta>(nullptr, vc, nullptr, nullptr, vmin, vsc, (int)pair, S, part);
+        // compaction in ascending token order: one prefix sum over the lanes of
+        // (keys > thr) and (keys == thr); the first `remaining` keys equal to thr
+        // (smallest indices) are kept.  Dropped keys write to discard slots.
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            gt += key[i] > thr;
+            eq += key[i] == thr;
+        }
+        const int packed = gt | (eq << 16);
+        const int incl = wave_incl_scan(packed, lane);
+        const int tot = __shfl(incl, 63);
+        const int excl = incl - packed;
+        const int remaining = k_top - (tot & 0xFFFF);
+        int eq_rank = excl >> 16;
+        int pos = (excl & 0xFFFF) + min(eq_rank, remaining);
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const uint32_t kb = key[i];
+            const bool is_eq = kb == thr;
+            const bool keep = (kb > thr) | (is_eq & (eq_rank < remaining));
+            eq_rank += is_eq;
+            const int slot = keep ? pos : k_top + lane;
+            sel_z[slot] = tr_key_to_z(kb) - zmax;
+            sel_t[slot] = (uint16_t)(KPL * lane + i);
+            pos += keep;
+        }
+    }
+    __syncthreads();
+
+    // (3) P.V over the kept rows: wave w takes rounds w, w + NWV, .. of TPW * UG
+    // rows, UG rows per lane in flight
+    const CacheRow<Meta> cv = cache_row<D, Meta>(nullptr, vc, nullptr, nullptr, vmin, vsc, (int)pair, S, part);
     float l = 0.0f, bsum = 0.0f;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         acc[i] = 0.0f;
-    for (int j0 = 0; j0 < k_top; j0 += TPW * UG) {
+    for (int j0 = wave * (TPW * UG); j0 < k_top; j0 += NWV * (TPW * UG)) {
         uint4 vx[UG];
         float vm[UG], vs[UG], p[UG];
 #pragma unroll
@@ -1352,9 +1419,9 @@ __global__ __launch_bounds__(256, 3) void k_topk_select_w(const uint8_t *__restr
             const int j = j0 + u * TPW + lt;
             const int jc = min(j, k_top - 1);
             const uint32_t t = sel_t[jc];
-            vx[u] = ld_stream16(cr.vb + (t * (D / 2) + cr.code_off));
-            vm[u] = ld_meta(at_byte(cr.vmb, t * (uint32_t)(sizeof(Meta) * G) + cr.meta_off));
-            vs[u] = ld_meta(at_byte(cr.vsb, t * (uint32_t)(sizeof(Meta) * G) + cr.meta_off));
+            vx[u] = ld_stream16(cv.vb + (t * (D / 2) + cv.code_off));
+            vm[u] = ld_meta(at_byte(cv.vmb, t * (uint32_t)(sizeof(Meta) * G) + cv.meta_off));
+            vs[u] = ld_meta(at_byte(cv.vsb, t * (uint32_t)(sizeof(Meta) * G) + cv.meta_off));
             p[u] = j < k_top ? exp2_fast(sel_z[jc]) : 0.0f;
         }
 #pragma unroll
@@ -1364,32 +1431,42 @@ __global__ __launch_bounds__(256, 3) void k_topk_select_w(const uint8_t *__restr
             axpy_values(acc, p[u] * (vs[u] * kTwo24), vx[u]);
         }
     }
+    if (sel_out != nullptr)
+        for (int j = tid; j < k_top; j += 64 * NWV)
+            sel_out[pair * k_top + j] = sel_t[j];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         acc[i] += bsum;
     // sum over the token lanes (lanes of equal `part`): rotations inside each
-    // 16-lane row (DPP), then across rows
+    // 16-lane row (DPP), then across rows; then over the NWV waves in LDS
     lane_group_sum<LPT>(l);
 #pragma unroll
     for (int i = 0; i < 32; ++i)
         lane_group_sum<LPT>(acc[i]);
     if (lt == 0) {
-        const float inv = 1.0f / l;
-        uint32_t h[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const _Float16 lo16 = (_Float16)(acc[2 * i] * inv);
-            const _Float16 hi16 = (_Float16)(acc[2 * i + 1] * inv);
-            h[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo16) | ((uint32_t)__builtin_bit_cast(uint16_t, hi16) << 16);
-        }
-        uint4 *dst = out + pair * (D / 8) + part * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+        for (int i = 0; i < 32; ++i)
+            red[wave * D + 32 * part + i] = acc[i];
+        if (part == 0)
+            red[NWV * D + wave] = l;
     }
-    if (sel_out != nullptr)
-        for (int j = lane; j < k_top; j += 64)
-            sel_out[pair * k_top + j] = sel_t[j];
+    __syncthreads();
+    if (wave == 0) {
+        float lsum = red[NWV * D];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w)
+            lsum += red[NWV * D + w];
+        const float inv = 1.0f / lsum;
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) {
+            const int i = lane * (D / 64) + e;
+            float o = red[i];
+#pragma unroll
+            for (int w = 1; w < NWV; ++w)
+                o += red[w * D + i];
+            out[pair * D + i] = (_Float16)(o * inv);
+        }
+    }
 }
 
 // ===========================================================================
@@ -1497,7 +1574,27 @@ int launch_decode_d(const CachePlanes &c, int pairs, const void *q, int T, void 
     }
 }
 
-constexpr int kTopkWaveMaxCtx = 2048; // k_topk_select_w holds 32 keys per lane
+constexpr int kTopkCUs = 256; // compute units of MI355X
+
+// k_topk_fused with NWV waves per pair: U = 8 key rows per lane in flight,
+// UG gathered V rows per lane chosen so that one round of the waves covers at
+// least 208 rows at head_dim 128 (the top 10% of contexts up to 2080).
+template <int D, int NWV, int KPL, typename Meta>
+int launch_topk_fused(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
+                      float *ws, float c2, hipStream_t st)
+{
+    constexpr int TPW = 64 / (D / 32);
+    constexpr int UG = NWV == 1 ? 13 : NWV == 2 ? 7 : 4;
+    const int part = ((T + NWV - 1) / NWV + TPW - 1) / TPW * TPW; // tokens per wave
+    const size_t sel_bytes = (size_t)(k_top + 64) * (sizeof(float) + sizeof(uint16_t));
+    const size_t region = (std::max(sel_bytes, (size_t)4 * (256 + 64 + 128)) + 15) / 16 * 16;
+    const size_t lds = (size_t)4 * (64 * (KPL + 1) + NWV * D + 4) + region;
+    hipLaunchKernelGGL((k_topk_fused<D, NWV, 8, KPL, UG, Meta>), dim3((unsigned)pairs), dim3(64 * NWV), lds, st,
+                       c.k_codes, meta<Meta>(c.k_min), meta<Meta>(c.k_scale), c.v_codes, meta<Meta>(c.v_min),
+                       meta<Meta>(c.v_scale), static_cast<const uint4 *>(q), ws, static_cast<_Float16 *>(out), sel, c.S,
+                       T, k_top, part, c2);
+    return (int)hipGetLastError();
+}
 
 template <int D, typename Meta>
 int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_top, void *out, int32_t *sel,
@@ -1505,6 +1602,24 @@ int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_t
 {
     constexpr int TPW = 64 / (D / 32);
     const float c2 = 1.4426950408889634f / sqrtf((float)D);
+    if (T <= KVQ_TOPK_FUSED_MAX_CTX) {
+        // waves per pair: one when the pairs alone give every compute unit 12
+        // waves (three per SIMD, the occupancy of these kernels), else two or
+        // four (measured on MI355X at 768 .. 6144 pairs)
+        const int nwv = pairs >= 12 * kTopkCUs ? 1 : pairs >= 3 * kTopkCUs ? 2 : 4;
+        if (T <= 1024) {
+            switch (nwv) {
+            case 1: return launch_topk_fused<D, 1, 16, Meta>(c, pairs, q, T, k_top, out, sel, ws, c2, st);
+            case 2: return launch_topk_fused<D, 2, 16, Meta>(c, pairs, q, T, k_top, out, sel, ws, c2, st);
+            default: return launch_topk_fused<D, 4, 16, Meta>(c, pairs, q, T, k_top, out, sel, ws, c2, st);
+            }
+        }
+        switch (nwv) {
+        case 1: return launch_topk_fused<D, 1, 32, Meta>(c, pairs, q, T, k_top, out, sel, ws, c2, st);
+        case 2: return launch_topk_fused<D, 2, 32, Meta>(c, pairs, q, T, k_top, out, sel, ws, c2, st);
+        default: return launch_topk_fused<D, 4, 32, Meta>(c, pairs, q, T, k_top, out, sel, ws, c2, st);
+        }
+    }
     const int chunk = std::min(128, (T + TPW - 1) / TPW * TPW);
     const int n_chunks = (T + chunk - 1) / chunk;
     const int64_t waves = (int64_t)pairs * n_chunks;
@@ -1513,26 +1628,9 @@ int launch_topk_d(const CachePlanes &c, int pairs, const void *q, int T, int k_t
     int e = (int)hipGetLastError();
     if (e != 0)
         return e;
-    if (T <= kTopkWaveMaxCtx) {
-        // per wave: the transposed scores (64 rows of KPL + 1 floats), later the
-        // kept tokens' scores and indices with 64 discard slots each
-        const int kpl = T <= 1024 ? 16 : 32;
-        const size_t sel_bytes = (size_t)(k_top + 64) * (sizeof(float) + sizeof(uint16_t));
-        const int region = (int)((std::max(sel_bytes, (size_t)64 * (kpl + 1) * sizeof(float)) + 15) / 16 * 16);
-        const dim3 grid((unsigned)((pairs + 3) / 4));
-        if (kpl == 16)
-            hipLaunchKernelGGL((k_topk_select_w<D, 16, 4, Meta>), grid, dim3(256), (size_t)4 * region, st, c.v_codes,
-                               meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<uint4 *>(out), sel, pairs,
-                               c.S, T, k_top, region);
-        else
-            hipLaunchKernelGGL((k_topk_select_w<D, 32, 13, Meta>), grid, dim3(256), (size_t)4 * region, st, c.v_codes,
-                               meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<uint4 *>(out), sel, pairs,
-                               c.S, T, k_top, region);
-    } else {
-        const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
-        hipLaunchKernelGGL((k_topk_select<D, Meta>), dim3((unsigned)pairs), dim3(256), lds, st, c.v_codes,
-                           meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<_Float16 *>(out), sel, c.S, T, k_top);
-    }
+    const size_t lds = (size_t)T * sizeof(float) + ((size_t)k_top * sizeof(uint16_t) + 15) / 16 * 16;
+    hipLaunchKernelGGL((k_topk_select<D, Meta>), dim3((unsigned)pairs), dim3(256), lds, st, c.v_codes,
+                       meta<Meta>(c.v_min), meta<Meta>(c.v_scale), ws, static_cast<_Float16 *>(out), sel, c.S, T, k_top);
     return (int)hipGetLastError();
 }
 

@@ -176,11 +176,19 @@ def test_workspace_sizing_and_enospace(L):
     assert auto > 0 and auto % (130 * 4) == 0
     assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4096, FAKE, 7, FAKE, 7 * 130 * 4 - 4, st) == KVQ_ENOSPACE
     assert L.decode_attention_q4(ctypes.byref(c), FAKE, 4096, FAKE, 7, None, 0, st) == KVQ_ENOSPACE
-    # the top-k path holds one fp32 score per (pair, token) between its two kernels
-    assert L.kvq_workspace_bytes(ctypes.byref(d), 2048, 0, 205) == 1 * 1 * 2048 * 4
+    # the top-k path: up to KVQ_TOPK_FUSED_MAX_CTX tokens one launch keeps the scores on chip
+    # (no workspace needed; one that is given must hold them); beyond, it holds one fp32 score
+    # per (pair, token) between its two kernels
+    assert kvq.KVQ_TOPK_FUSED_MAX_CTX == 2048
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 2048, 0, 205) == 0
+    assert L.kvq_workspace_bytes(ctypes.byref(d), 2049, 0, 205) == 1 * 1 * 2049 * 4
     assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2048, 205, FAKE, None, FAKE, 2048 * 4 - 4,
                                       st) == KVQ_ENOSPACE
-    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2048, 205, FAKE, None, None, 0, st) == KVQ_ENOSPACE
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2048, 205, FAKE, None, FAKE + 4, 2048 * 4,
+                                      st) == KVQ_EINVAL
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2049, 205, FAKE, None, FAKE, 2049 * 4 - 4,
+                                      st) == KVQ_ENOSPACE
+    assert L.decode_attention_q4_topk(ctypes.byref(c), FAKE, 2049, 205, FAKE, None, None, 0, st) == KVQ_ENOSPACE
 
 
 def test_append_attend_validation(L):

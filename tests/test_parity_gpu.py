@@ -510,12 +510,12 @@ def _topk_keys(case, b, a, d, T, seed):
 @pytest.mark.parametrize("T", [37, 300, 1024, 1025, 2048, 4000])
 @pytest.mark.parametrize("case", ["normal", "outlier", "five_rows", "tie_block", "wide"])
 def test_topk_selection_exact_on_own_scores(case, T):
-    """Exact check of the selection logic, free of any tolerance: the call leaves every
-    token's score in the workspace (fp32 [b][a][T]); the kept set must be exactly the k
+    """Exact check of the selection logic, free of any tolerance: a workspace given to the call
+    receives every token's score (fp32 [b][a][T]); the kept set must be exactly the k
     largest of those scores, ties to the smaller index, in ascending order.  The k-th score
     falls in a crowded range, among exact ties (also inside a 48-key tie block), or next to
-    an outlier; k runs from 1 to T.  T <= 1024 uses the wave select with 16 keys per lane, up to 2048 with 32, and 4000
-    the workgroup select."""
+    an outlier; k runs from 1 to T.  T <= 1024 uses the one-launch select with 16 keys per
+    lane, up to 2048 with 32, and 4000 the two-launch workgroup select."""
     require_gpu()
     b, a, d = 1, 3, 128
     seed = 4100 + T + ["normal", "outlier", "five_rows", "tie_block", "wide"].index(case)
@@ -524,7 +524,7 @@ def test_topk_selection_exact_on_own_scores(case, T):
     q = W.random_fp16((b, 1, a, d), seed + 2, DEV)
     cache = kvq.QuantKVCache(b, a, a * d, T, 0, device=DEV, fill=0xFF)
     kvq.kv_quantize_prefill(cache, k, v)
-    ws = torch.empty(kvq.kvq_workspace_bytes(cache, T, 0, T) // 4, dtype=torch.float32, device=DEV)
+    ws = torch.empty(b * a * T, dtype=torch.float32, device=DEV)    # receives the scores
     kvq.decode_attention_q4_topk(cache, q, T, 1, ws=ws)
     torch.cuda.synchronize()
     scores = ws[: b * a * T].view(b * a, T).cpu().numpy().copy()
@@ -550,16 +550,16 @@ def test_topk_selection_exact_on_own_scores(case, T):
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_topk_head_dims(d, T):
     """Sparse attention at every supported head_dim (2, 4 or 8 lanes per token row in the
-    score pass, the gather and the final lane sums), both wave-select key layouts (16 keys
-    per lane up to T = 1024, 32 up to 2048) and the workgroup select (T > 2048): the
-    selection is exactly the top k of the kernel's own scores, and the output matches the
-    oracle on the GPU's selection; k = 1, 10% and T."""
+    score pass, the gather and the final lane sums), both one-launch key layouts (16 keys
+    per lane up to T = 1024, 32 up to 2048) and the two-launch workgroup select (T > 2048):
+    the selection is exactly the top k of the kernel's own scores, and the output matches
+    the oracle on the GPU's selection; k = 1, 10% and T."""
     require_gpu()
     b, a = 2, 3
     cache, hc, q = _small_cache(b, a, d, T, 0, 5200 + d + T)
     pairs = all_pairs(b, a)
     qh = f16_np(q)
-    ws = torch.empty(kvq.kvq_workspace_bytes(cache, T, 0, T) // 4, dtype=torch.float32, device=DEV)
+    ws = torch.empty(b * a * T, dtype=torch.float32, device=DEV)    # receives the scores
     for k_top in sorted({1, math.ceil(0.1 * T), T}):
         out, sel = kvq.decode_attention_q4_topk(cache, q, T, k_top, out=_nan_out(b, a, d), ws=ws)
         torch.cuda.synchronize()
@@ -569,6 +569,35 @@ def test_topk_head_dims(d, T):
             want = np.sort(np.lexsort((np.arange(T), -scores[p]))[:k_top])
             assert np.array_equal(got[p], want), f"d={d} T={T} k={k_top} pair {p}: selection differs"
         _topk_checks(hc, qh, T, k_top, pairs, _gpu_rows(out, pairs), sel.cpu().numpy(), f"topk d={d} T={T} k={k_top}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("b,T", [(2, 1500), (8, 700), (8, 1500), (16, 2048), (32, 700), (32, 1500)])
+def test_topk_waves_per_pair(b, T):
+    """The one-launch top-k takes one, two or four waves per (batch row, head) by the number
+    of pairs (a = 96: 192 pairs -> four, 768 and 1536 -> two, 3072 -> one), with 16 or 32 keys
+    per lane by the context.  At each: the selection is exactly the top k of the kernel's own
+    scores for every pair, the output matches the oracle on the GPU's selection for 48
+    sampled pairs, and the call without a workspace (scores kept on chip only) gives a
+    bit-identical output and selection."""
+    require_gpu()
+    a, d = 96, 128
+    k_top = math.ceil(0.1 * T)
+    cache, hc, q = _small_cache(b, a, d, T, 0, 7300 + b + T)
+    log(f"[topk waves] b={b} a={a} T={T} k={k_top}")
+    ws = torch.empty(b * a * T, dtype=torch.float32, device=DEV)    # receives the scores
+    out, sel = kvq.decode_attention_q4_topk(cache, q, T, k_top, out=_nan_out(b, a, d), ws=ws)
+    out2, sel2 = kvq.decode_attention_q4_topk(cache, q, T, k_top, out=_nan_out(b, a, d))
+    torch.cuda.synchronize()
+    assert torch.equal(sel, sel2), "selection differs without the workspace"
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "output differs without the workspace"
+    scores = ws.view(b * a, T).cpu().numpy()
+    got = sel.view(b * a, k_top).cpu().numpy()
+    for p in range(b * a):
+        want = np.sort(np.lexsort((np.arange(T), -scores[p]))[:k_top])
+        assert np.array_equal(got[p], want), f"b={b} T={T} pair {p}: selection differs"
+    pairs = sample_pairs(b, a, 48, 7400 + b + T)
+    _topk_checks(hc, f16_np(q), T, k_top, pairs, _gpu_rows(out, pairs), sel.cpu().numpy(), f"topk b={b} T={T}")
 
 
 def test_topk_deterministic():
