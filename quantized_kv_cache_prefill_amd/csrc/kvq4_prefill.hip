@@ -634,12 +634,6 @@ __device__ __forceinline__ void next_step(const PPArgs &g, Step &u)
     u.nj = pass_tiles(g, 0);
     u.base = head_base(g, u.pair);
 }
-// A buffer resource over one head's prompt rows of x: offsets past the last
-// prompt row's 256 bytes read zeros (a step past the last reads zeros everywhere).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const PPArgs &g, const uint16_t *x, const Step &u)
-{
-    return rsrc(reinterpret_cast<const char *>(x) + u.base, u.pair < 0 ? 0 : g.valid_bytes);
-}
 
 // 16 bytes per lane, HBM -> LDS, as dma16, written out: the compiler does not
 // see an LDS write here, so it adds no wait for these loads before LDS reads of
