@@ -100,11 +100,32 @@ constexpr int kCUs = 256;
 constexpr int kSplitAlign = 128;
 constexpr int kMaxAutoSplits = 64;
 
+// Fewer pairs than give every CU two workgroups of two-wave pairs: four waves
+// per pair, and splits until the launch has 1,024 waves (4 per CU) and no
+// wave streams more than 512 tokens, but no more than 3,072 waves (12 per
+// CU) and no split shorter than 512 tokens.  Measured on MI355X, HBM-cold,
+// 32..768 pairs at contexts 544..65536, against 1..32 splits with two or
+// four waves per pair: short contexts gain most from few splits (the reduce
+// pass and the partials are then a large part of the call), long ones from
+// about 512 tokens per wave (32 pairs at 16384 tokens: 8 splits, 27.0 us
+// against 38.1 us for the balance rule below; 512 pairs at 544 tokens: no
+// split, 14.9 against 18.8 us).
+constexpr int kFewPairs = 2 * kCUs * kPairsPerGroup;
+constexpr int kFewPairsMinWaves = 4 * kCUs;
+constexpr int kFewPairsMaxWaves = 12 * kCUs;
+constexpr int kFewPairsWaveTokens = 512;
+constexpr int kFewPairsMinSplit = 512;
+
 int resolve_splits(int pairs, int ctx, int num_splits, int *split_len)
 {
     int s;
     if (num_splits > 0) {
         s = num_splits;
+    } else if (pairs < kFewPairs) {
+        const int by_waves = (kFewPairsMinWaves + 4 * pairs - 1) / (4 * pairs);
+        const int by_length = (ctx + 4 * kFewPairsWaveTokens - 1) / (4 * kFewPairsWaveTokens);
+        s = std::min(std::max(by_waves, by_length), std::max(1, kFewPairsMaxWaves / (4 * pairs)));
+        s = std::min(s, std::max(1, std::min(ctx / kFewPairsMinSplit, kMaxAutoSplits)));
     } else {
         const int64_t groups = (pairs + kPairsPerGroup - 1) / kPairsPerGroup;
         // With at least four workgroups per CU there is parallelism enough and the
@@ -352,8 +373,8 @@ int decode_common(const kvq_cache *cache, const void *q_f16, int32_t ctx_len, vo
     sh.unroll = unroll;
     sh.splits = resolve_splits(pairs, ctx_len, num_splits, &sh.split_len);
     sh.waves_per_pair = waves_per_pair != kAutoWavesPerPair ? waves_per_pair
-                        : (sh.splits == 1 && ctx_len >= kLongCtxFourWaves) ? 4
-                                                                           : kDefaultWavesPerPair;
+                        : (pairs < kFewPairs || (sh.splits == 1 && ctx_len >= kLongCtxFourWaves)) ? 4
+                                                                                                 : kDefaultWavesPerPair;
     const size_t need = kvq::decode_ws_floats(pairs, c.d, sh.splits) * sizeof(float);
     if (use_scratch) {
         if (need > KVQ_NOALLOC_SCRATCH_BYTES)

@@ -237,6 +237,26 @@ def test_auto_splits_only_when_the_pairs_cannot_fill_the_card(L):
     assert L.kvq_workspace_bytes(ctypes.byref(long), 65536, 0, 0) > 0
 
 
+@pytest.mark.parametrize("b,a,ctx,splits", [
+    (16, 32, 544, 1),      # 512 pairs: four waves each, 2,048 waves, no split
+    (4, 32, 544, 1),       # 128 pairs: splits would be shorter than 512 tokens
+    (4, 32, 2048, 2),      # 128 pairs: two splits make 1,024 waves
+    (1, 32, 4096, 8),      # 32 pairs: eight splits of 512 tokens
+    (1, 32, 16384, 8),     # 32 pairs: 1,024 waves
+    (1, 96, 65536, 8),     # 96 pairs: no wave streams more than 2,048 tokens
+    (1, 1, 4096, 8),       # one pair: as many 512-token splits as the context holds
+    (31, 33, 544, 1),      # 1,023 pairs, the last of the few-pairs range
+])
+def test_auto_shape_for_few_pairs(L, b, a, ctx, splits):
+    """Fewer pairs than fill every CU with two workgroups of two-wave pairs: four waves per
+    pair and splits until the launch has 1,024 waves or no wave streams more than 2,048
+    tokens, each split at least 512 tokens.  Read through the workspace size: splits x
+    pairs x (d + 2) floats, 0 for one split."""
+    d = dims(b=b, a=a, h=a * 128, s=ctx, n=0)
+    want = 0 if splits == 1 else splits * b * a * 130 * 4
+    assert L.kvq_workspace_bytes(ctypes.byref(d), ctx, 0, 0) == want
+
+
 def test_strerror(L):
     for s in (0, -1, -2, -3, -4, -5, -99):
         assert len(L.kvq_strerror(s)) > 0
