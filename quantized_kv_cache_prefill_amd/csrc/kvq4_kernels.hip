@@ -789,15 +789,38 @@ __device__ __forceinline__ uint32_t order_key(float z)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+// Inclusive prefix sum over the 64 lanes, in DPP moves (no LDS): row shifts
+// by 1, 2, 4 and 8 inside each 16-lane row (lanes with no source add 0), then
+// lane 15 of each row added to the next row (row_bcast:15, rows 1 and 3) and
+// lane 31 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/)
 {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int n = __shfl_up(v, off);
-        if (lane >= off)
-            v += n;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true); // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true); // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true); // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true); // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
     return v;
+}
+
+// The maximum (MAX) or minimum of v over the 64 lanes, in every lane: DPP
+// exchanges inside each 16-lane row (xor 1, xor 2, mirror of 8, mirror of
+// 16), then the row swaps across rows (permlane16 and permlane32).
+template <bool MAX>
+__device__ __forceinline__ float wave_extreme(float v)
+{
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    v = op(v, dpp<kQuadXor1>(v));
+    v = op(v, dpp<kQuadXor2>(v));
+    v = op(v, dpp<kHalfRowMirror>(v));
+    v = op(v, dpp<0x140>(v)); // row_mirror: lane i <-> lane 15-i
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                      false, false);
+    v = op(__builtin_bit_cast(float, (uint32_t)r16[0]), __builtin_bit_cast(float, (uint32_t)r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                      false, false);
+    return op(__builtin_bit_cast(float, (uint32_t)r32[0]), __builtin_bit_cast(float, (uint32_t)r32[1]));
 }
 
 // Exclusive prefix sum over the 256 threads of the block (in thread order).
@@ -1307,11 +1330,8 @@ __global__ __launch_bounds__(64 * NWV) void k_topk_fused(const uint8_t *__restri
             zmin = fminf(zmin, valid ? z : INFINITY);
             key[i] = valid ? order_key(z) : 0u;
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            zmax = fmaxf(zmax, __shfl_xor(zmax, off));
-            zmin = fminf(zmin, __shfl_xor(zmin, off));
-        }
+        zmax = wave_extreme<true>(zmax);
+        zmin = wave_extreme<false>(zmin);
 
         // Bins: bin(z) = (int)min((z - zmin) * bscale, 255), monotone in z; a
         // zero (or unrepresentable) range gives one bin and the full search.
@@ -1337,7 +1357,7 @@ __global__ __launch_bounds__(64 * NWV) void k_topk_fused(const uint8_t *__restri
         const int4 h4 = reinterpret_cast<const int4 *>(hist)[lane];
         const int lsum = h4.x + h4.y + h4.z + h4.w;
         const int lincl = wave_incl_scan(lsum, lane);
-        const int above_lane = __shfl(lincl, 63) - lincl; // keys in bins of higher lanes
+        const int above_lane = __builtin_amdgcn_readlane(lincl, 63) - lincl; // keys in bins of higher lanes
         const int ge3 = above_lane + h4.w, ge2 = ge3 + h4.z, ge1 = ge2 + h4.y, ge0 = ge1 + h4.x;
         // bin b* holds the k_top-th largest: ge(b*+1) < k_top <= ge(b*)
         int my_bin = -1, my_above = 0, my_n = 0;
@@ -1347,7 +1367,8 @@ __global__ __launch_bounds__(64 * NWV) void k_topk_fused(const uint8_t *__restri
         if (ge1 < k_top && k_top <= ge0) { my_bin = 4 * lane; my_above = ge1; my_n = h4.x; }
         const uint64_t owner = __ballot(my_bin >= 0);
         const int src = (int)__builtin_ctzll(owner);
-        const int bstar = __shfl(my_bin, src), n_star = __shfl(my_n, src), a_star = __shfl(my_above, src);
+        const int bstar = __builtin_amdgcn_readlane(my_bin, src), n_star = __builtin_amdgcn_readlane(my_n, src),
+                  a_star = __builtin_amdgcn_readlane(my_above, src);
         uint32_t thr;
         if (n_star <= 64) {
             // bin b*'s keys, one per lane; the others go to discard slots
@@ -1384,7 +1405,7 @@ __global__ __launch_bounds__(64 * NWV) void k_topk_fused(const uint8_t *__restri
         }
         const int packed = gt | (eq << 16);
         const int incl = wave_incl_scan(packed, lane);
-        const int tot = __shfl(incl, 63);
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
         const int excl = incl - packed;
         const int remaining = k_top - (tot & 0xFFFF);
         int eq_rank = excl >> 16;
