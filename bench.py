@@ -231,7 +231,8 @@ def time_cache_warm_layer(w, reps=60):
 def time_tiny_latency(reps=200):
     """Latency of one decode layer-step on the tiny configuration (b=2, a=2, d=64, prompt 16,
     context 17..20): append + attention (two launches), attention alone, and the fused launch;
-    medians of HIP events around each, launch overhead included."""
+    then the two-launch and the fused step as HIP graph replays; medians of HIP events around
+    each, launch overhead included."""
     import torch
 
     import quantized_kv_cache_prefill_amd as kvq
@@ -263,6 +264,41 @@ def time_tiny_latency(reps=200):
         torch.cuda.synchronize()
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev[10:])
         res[label] = {"us_median": round(us[len(us) // 2], 2), "us_min": round(us[0], 2)}
+    # The steps captured as HIP graphs and replayed (the library enqueues kernels only, so
+    # every call is capturable): one graph per step, and one graph holding all n steps of the
+    # layer, reported per step.
+    for label in ("graph_append_then_attend", "graph_fused"):
+        def one_step(j):
+            q, kn, vn = inputs[j - 1]
+            pos = w.s + j - 1
+            if label == "graph_fused":
+                kvq.kv_append_attend_q4(cache, q, kn, vn, pos, out=out)
+            else:
+                kvq.kv_append_quant(cache, kn, vn, pos)
+                kvq.decode_attention_q4(cache, q, pos + 1, out=out)
+        graphs = []
+        for j in range(1, w.n + 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_step(j)
+            graphs.append(g)
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for j in range(1, w.n + 1):
+                one_step(j)
+        for key, run, per in ((label, lambda r: graphs[r % w.n].replay(), 1),
+                              (label + f"_{w.n}_steps_per_graph", lambda r: g_all.replay(), w.n)):
+            ev = []
+            for r in range(reps + 10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                run(r)
+                e1.record(st)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            us = sorted(a.elapsed_time(b) * 1e3 / per for a, b in ev[10:])
+            res[key] = {"us_median": round(us[len(us) // 2], 2), "us_min": round(us[0], 2)}
+        del graphs, g_all
     res["workload"] = f"tiny: b={w.b} a={w.a} d={w.d}, prompt {w.s}, contexts {w.s + 1}..{w.S}, one layer"
     res["bytes_per_step"] = bytes_decode(w.b * w.a, w.S, w.d)
     return res
@@ -806,7 +842,8 @@ def cpu_model() -> str:
 LEGS = {"prefill": lambda: time_prefill(), "proj": lambda: time_projections(), "topk": lambda: time_topk(),
         "proj_sustained": lambda: time_projection_sustained(),
         "split": lambda: time_split_context(), "meta16": lambda: time_meta_f16(),
-        "host": lambda: time_host_attention(), "read_ceiling": lambda: hbm_read_ceiling()}
+        "host": lambda: time_host_attention(), "read_ceiling": lambda: hbm_read_ceiling(),
+        "tiny": lambda: time_tiny_latency()}
 
 
 def main():
