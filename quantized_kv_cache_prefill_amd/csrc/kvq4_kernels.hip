@@ -401,32 +401,43 @@ __device__ __forceinline__ void load_kv_rows(const CacheRow<Meta> &cr, int tb, i
     }
 }
 
-// Scores of the rows, online-softmax update of (m, l, bsum, acc).
+// Scores of the rows, online-softmax update of (m, l, bsum, acc).  m is a
+// reference, not the running maximum: it moves, and l, bsum and acc are
+// rescaled, only when a score exceeds it by more than kSlack (log2 units).
+// The probabilities 2^(z - m) then stay below 2^kSlack, far from the binary32
+// range at any context, and the rescale runs a few times per token sequence
+// instead of at nearly every iteration (with 64 lanes, some lane's maximum
+// moves almost every time).  The merges over lanes, waves and splits take any
+// reference.
+constexpr float kSlack = 8.0f;
+
 template <int D, int UU>
 __device__ __forceinline__ void attend_kv_rows(const KVRows<UU> &r, const QSlice &qs, const Magic mg, float c2,
                                                float &m, float &l, float &bsum, float (&acc)[32])
 {
     constexpr int LPT = D / 32;
     float z[UU];
-    float mx = m;
+    float zmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
         const float dq = dot_keys(qs, r.kx[u], mg);
         float sp = __builtin_fmaf(r.ks[u], dq, r.km[u] * qs.qsum);
         sp = token_sum<LPT>(sp);
         z[u] = r.valid[u] ? sp * c2 : -INFINITY;
-        mx = fmaxf(mx, z[u]);
+        zmax = fmaxf(zmax, z[u]);
     }
-    const float mref = (mx == -INFINITY) ? 0.0f : mx;
-    if (__any(mx != m)) {
-        const float alpha = exp2_fast(m - mref);
+    const bool grow = zmax > m + kSlack; // false while every score seen is -inf
+    if (__any(grow)) {
+        const float m_new = grow ? zmax : m;
+        const float alpha = exp2_fast(m - ((m_new == -INFINITY) ? 0.0f : m_new)); // 0 from m = -inf
         l *= alpha;
         bsum *= alpha;
 #pragma unroll
         for (int i = 0; i < 32; ++i)
             acc[i] *= alpha;
+        m = m_new;
     }
-    m = mx;
+    const float mref = (m == -INFINITY) ? 0.0f : m;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
         const float p = exp2_fast(z[u] - mref);
