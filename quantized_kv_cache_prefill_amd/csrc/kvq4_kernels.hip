@@ -427,17 +427,17 @@ __device__ __forceinline__ void attend_kv_rows(const KVRows<UU> &r, const QSlice
         zmax = fmaxf(zmax, z[u]);
     }
     const bool grow = zmax > m + kSlack; // false while every score seen is -inf
+    const float m_new = grow ? zmax : m;
+    const float mref = (m_new == -INFINITY) ? 0.0f : m_new;
     if (__any(grow)) {
-        const float m_new = grow ? zmax : m;
-        const float alpha = exp2_fast(m - ((m_new == -INFINITY) ? 0.0f : m_new)); // 0 from m = -inf
+        const float alpha = exp2_fast(m - mref); // 1 where m stays, 0 from m = -inf
         l *= alpha;
         bsum *= alpha;
 #pragma unroll
         for (int i = 0; i < 32; ++i)
             acc[i] *= alpha;
-        m = m_new;
     }
-    const float mref = (m == -INFINITY) ? 0.0f : m;
+    m = m_new;
 #pragma unroll
     for (int u = 0; u < UU; ++u) {
         const float p = exp2_fast(z[u] - mref);
