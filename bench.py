@@ -596,11 +596,11 @@ def flops_prefill(b: int, a: int, s: int, d: int) -> int:
     return 4 * d * b * a * (s * (s + 1) // 2)
 
 
-def time_prefill(reps: int = 6):
+def time_prefill(reps: int = 12, warm: int = 8):
     """The prompt phase of one OPT-175B layer (b=144, a=96, d=128, prompt 512): the fused
     kv_quantize_prefill_attend (causal attention on the matrix cores + the cache planes)
-    against kv_quantize_prefill alone; two caches in rotation; medians of per-launch HIP
-    events."""
+    against kv_quantize_prefill alone; two caches in rotation; after `warm` untimed calls,
+    medians of `reps` per-launch HIP events."""
     import torch
 
     import quantized_kv_cache_prefill_amd as kvq
@@ -613,15 +613,17 @@ def time_prefill(reps: int = 6):
     caches = [kvq.QuantKVCache(w.b, w.a, w.h, w.s, w.n, device="cuda") for _ in range(2)]
 
     def med(fn):
+        for r in range(warm):  # the clock settles under the load before the timed calls
+            fn(caches[r % 2])
         ms = []
-        for r in range(reps + 2):
+        for r in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
             fn(caches[r % 2])
             e1.record(st)
             ms.append((e0, e1))
         torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ms[2:])
+        t = sorted(a.elapsed_time(b) for a, b in ms)
         return t[len(t) // 2], t
     fused, all_ms = med(lambda c: kvq.kv_quantize_prefill_attend(c, q, k, v, out=out))
     quant, _ = med(lambda c: kvq.kv_quantize_prefill(c, k, v))

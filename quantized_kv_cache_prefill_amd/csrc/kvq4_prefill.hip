@@ -387,6 +387,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
 #pragma unroll
             for (int i = 0; i < LA; ++i)
                 ka[i] = ld_ka(i);
+            // The first LA reads form a group of their own, ahead of the (read,
+            // products) groups: without it the scheduler fills those groups' read
+            // slots with them and every product waits on the read just before it.
+            __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const int kd = i / 4, c = i % 4;
@@ -494,6 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_prefill(PrefillArgs g)
 #pragma unroll
             for (int i = 0; i < LA; ++i)
                 va[i] = ld_va(i);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0); // as for K
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const int t = i / 2, ks = i % 2;
@@ -874,7 +879,7 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 st[c] = f4{0.f, 0.f, 0.f, 0.f};
-            constexpr int NSS = KS * 4, LA = 3;
+            constexpr int NSS = KS * 4, LA = 2;
             const int sk = Sh::swz_k(l16);
             auto ld_ka = [&](int n) {
                 return *reinterpret_cast<const h8 *>(lk + (16 * (n % 4) + l16) * D + 8 * ((4 * (n / 4) + g4) ^ sk));
@@ -883,6 +888,10 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
 #pragma unroll
             for (int i = 0; i < LA; ++i)
                 ka[i] = ld_ka(i);
+            // The first LA reads form a group of their own, ahead of the (read,
+            // product) pairs: without it the scheduler fills the pairs' read slots
+            // with them and every product waits on the read issued just before it.
+            __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
             for (int i = 0; i < NSS; ++i) {
                 if (i + LA < NSS)
@@ -962,6 +971,7 @@ __global__ __launch_bounds__(pp::NT, 1) void k_prefill_pp(PPArgs g)
 #pragma unroll
             for (int i = 0; i < LA; ++i)
                 va[i] = ld_va(i);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0); // as for K
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 if (i + LA < NV)
